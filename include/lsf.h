@@ -1,0 +1,273 @@
+/*
+ * lsf.h - C ABI of the layer-streamed frozen-base NF4 + LoRA training library
+ * (liblsf.so, built for AMD Instinct MI355X / gfx950).
+ *
+ * The method: LoRA adapters are trained over a frozen base whose decoder
+ * layers stay in page-locked host memory, NF4-quantised, and reach the GPU one
+ * layer at a time through two fixed device buffers; each layer is read twice
+ * per micro-batch (forward, then a recomputed forward inside the backward
+ * walk), and the input gradient still flows through the frozen weight.
+ *
+ * Pages cited below (by address and section title):
+ *   [NEWS]     aizxs.com/ai-learning/13312.html - section "the principle:
+ *              frozen layers streamed through the card".
+ *   [README]   feinterview.poetries.top/ai-monitor/news/makazhanalpamys-soup -
+ *              the project README: the layer-streaming paragraph, the soup.yaml
+ *              block, the preference-loss paragraph, the preprint/v3 paragraph.
+ *   [REVIEW]   repodaily.xyz/zh/projects/2026-08-17/soup/ - section
+ *              "architecture: how layer streaming fits in 4 GB".
+ *   [BLOG]     agentlenshq.com/zh-TW/blogs/2a477d3d-636b-4b92-baad-75af680d87d9
+ *              - sections "layer streaming: implementation and memory
+ *              efficiency" and "DPO support / reference model without memory".
+ *   [TUTORIAL] alphalab.site/soup-layer-streaming - section "the four-stage
+ *              data path" items 1 (NF4), 2 (pinned memory), 3 (forward +
+ *              backward), 4 (RAM-first); section "step 2: one YAML".
+ *
+ * Conventions shared by every entry point
+ *   - Every call returns lsf_status.  Nothing aborts, and no C++ exception
+ *     crosses the ABI.  On failure lsf_last_error() returns a message (owned
+ *     by the library, valid until the calling thread's next call).
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     failed validation enqueues nothing.
+ *   - Pointers are borrowed, never freed or retained beyond the call, except
+ *     for the stack handle, which keeps the pointers given to stack_create
+ *     until stack_destroy.  Device pointers must come from device memory
+ *     (hipMalloc / torch); "host" pointers are host memory.
+ *   - Work is enqueued on the given HIP stream (lsf_stream is a hipStream_t;
+ *     NULL is the null stream) and the call returns without waiting; faults
+ *     surface at the caller's next synchronisation.
+ *   - bf16 tensors are passed as uint16_t bit patterns; matrices are
+ *     row-major.  Weights are [out, in] as in nn.Linear; LoRA A is [r, in]
+ *     and B is [out, r], fp32.
+ *   - Results are deterministic: no floating-point atomics, and the same
+ *     inputs give the same bits wherever the weights live.
+ */
+#ifndef LSF_H
+#define LSF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* lsf_stream; /* hipStream_t */
+
+typedef enum {
+  LSF_OK = 0,
+  LSF_ERR_INVALID_ARG = 1, /* NULL where a pointer is required, bad flag, bad count */
+  LSF_ERR_SHAPE = 2,       /* a size the kernels do not support (see each call) */
+  LSF_ERR_ALIGN = 3,       /* a pointer or stride below the required alignment */
+  LSF_ERR_NOT_PINNED = 4,  /* host store is not page-locked (and pageable not allowed) */
+  LSF_ERR_UNSUPPORTED = 5, /* a feature the pages describe that this library does not build */
+  LSF_ERR_HIP = 6,         /* the HIP runtime reported an error (message has hipGetErrorString) */
+  LSF_ERR_WORKSPACE = 7    /* workspace smaller than the matching *_workspace_bytes() */
+} lsf_status;
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* lsf_last_error(void);
+/* Library version string. */
+const char* lsf_version(void);
+
+/* ------------------------------------------------------------------ NF4 --
+ * [TUTORIAL] item 1: the decoder's Linear weights are stored offline as QLoRA
+ * NF4; compute runs in higher precision.  Blocks of `blocksize` (= 64)
+ * consecutive elements of the flattened weight, one fp32 absmax each.
+ * code = number of fp32 midpoints of the 16 NF4 levels strictly below
+ * w / absmax (IEEE fp32 division); all-zero block -> absmax 0, codes 7.
+ * Packing: byte j = code[2j] << 4 | code[2j+1].
+ */
+
+/* Quantise n fp32 values (device) into packed codes (device, n/2 bytes) and
+ * absmax (device, n/blocksize floats).  n % 64 == 0 and blocksize == 64, else
+ * LSF_ERR_SHAPE.  Pointers must be 16-byte aligned (LSF_ERR_ALIGN). */
+lsf_status nf4_quantize(const float* w, int64_t n, int32_t blocksize,
+                        uint8_t* packed, float* absmax, lsf_stream stream);
+
+/* Dequantise: out[i] = bf16_rne(level[code[i]] * absmax[i / blocksize]).
+ * Same shape rules as nf4_quantize; out is device bf16 [n]. */
+lsf_status nf4_dequantize(const uint8_t* packed, const float* absmax, int64_t n,
+                          int32_t blocksize, uint16_t* out, lsf_stream stream);
+
+/* --------------------------------------------------------- layer config -- */
+
+typedef struct {
+  int32_t hidden;       /* H; multiple of 128 */
+  int32_t intermediate; /* I; multiple of 128 */
+  int32_t n_heads;      /* query heads */
+  int32_t n_kv_heads;   /* key/value heads; n_heads % n_kv_heads == 0 */
+  int32_t head_dim;     /* 128 (the attention kernels are built for it) */
+  int32_t rank;         /* LoRA rank r of every adapter, 1..64 */
+  float lora_scale;     /* s = alpha / r */
+  float rope_theta;     /* RoPE base, e.g. 500000 */
+  float rms_eps;        /* RMSNorm epsilon, e.g. 1e-5 */
+  int32_t batch;        /* sequences per micro-batch (>= 1) */
+  int32_t seq;          /* tokens per sequence (>= 1); positions restart at 0 */
+} lsf_layer_cfg;
+
+/* Weight storage formats of the frozen projections. */
+#define LSF_FMT_NF4 0    /* data = packed codes [out*in/2], scale = fp32 absmax [out*in/64] */
+#define LSF_FMT_BF16 1   /* data = bf16 [out*in], scale = NULL (unquantised streamed base) */
+#define LSF_FMT_NF4_DQ 2 /* data = packed codes, scale = uint8 absmax codes [out*in/64],
+                            scale2 = fp32 [ceil(out*in/64/256)] second-level
+                            scales + offset (see nf4dq_quantize) */
+
+typedef struct {
+  const void* data;
+  const void* scale;
+  const float* scale2;
+} lsf_weight;
+
+/* The frozen weights of one decoder layer.  q|k|v and gate|up are row
+ * concatenations: qkv is [(nq + 2 nkv) * d, H] with q rows first, gate_up is
+ * [2 I, H] with gate rows first. */
+typedef struct {
+  int32_t format; /* LSF_FMT_* */
+  lsf_weight qkv, o, gate_up, down;
+  const uint16_t* norm1; /* bf16 [H], input RMSNorm weight */
+  const uint16_t* norm2; /* bf16 [H], post-attention RMSNorm weight */
+} lsf_layer_weights;
+
+/* One projection's adapter.  A == NULL means no adapter on that projection
+ * (the pages' narrow q/v-only setting, [TUTORIAL] "step 2").  dA/dB receive
+ * gradients, accumulated (+=) in fp32; they may be NULL in forward-only use. */
+typedef struct {
+  const float* A; /* [r, in] */
+  const float* B; /* [out, r] */
+  float* dA;      /* [r, in] */
+  float* dB;      /* [out, r] */
+} lsf_lora_proj;
+
+typedef struct {
+  lsf_lora_proj q, k, v, o, gate, up, down;
+  int32_t enabled; /* 0: adapters switched off for this call (the frozen base
+                      alone, as the DPO reference pass of [README]/[BLOG]) */
+} lsf_layer_lora;
+
+/* -------------------------------------------------------- one NF4 linear --
+ * y = x W^T + s (x A^T) B^T   (LoRA on a frozen NF4 weight; [NEWS], [TUTORIAL]
+ * item 3).  x: device bf16 [tokens, n_in]; y: device bf16 [tokens, n_out].
+ * n_out % 128 == 0, n_in % 64 == 0, tokens >= 1, 1 <= rank <= 64.
+ * A/B may be NULL (no adapter).  ws: device workspace of at least
+ * linear_workspace_bytes() bytes. */
+size_t linear_workspace_bytes(int32_t tokens, int32_t n_out, int32_t n_in, int32_t rank);
+lsf_status linear_fwd(const lsf_weight* w, int32_t format, int32_t n_out, int32_t n_in,
+                      const float* A, const float* B, int32_t rank, float scale,
+                      const uint16_t* x, int32_t tokens, uint16_t* y,
+                      void* ws, size_t ws_bytes, lsf_stream stream);
+/* Backward of linear_fwd: dx = dy W + s (dy B) A (the input gradient through the
+ * frozen weight, [TUTORIAL] item 3); dA += s (dy B)^T x; dB += s dy^T (x A^T).
+ * dx: device bf16 [tokens, n_in]. dA/dB accumulate. */
+lsf_status linear_bwd(const lsf_weight* w, int32_t format, int32_t n_out, int32_t n_in,
+                      const float* A, const float* B, int32_t rank, float scale,
+                      const uint16_t* x, const uint16_t* dy, int32_t tokens, uint16_t* dx,
+                      float* dA, float* dB, void* ws, size_t ws_bytes, lsf_stream stream);
+
+/* ------------------------------------------------------ one decoder layer --
+ * Llama-style layer: h1 = rmsnorm(x); q,k,v = LoRA-linear(h1) with rotate-half
+ * RoPE on q,k; causal GQA attention; x2 = x + LoRA-linear_o(attn);
+ * h2 = rmsnorm(x2); a = silu(gate(h2)) * up(h2); y = x2 + down(a).
+ * x, y: device bf16 [batch*seq, H].  Requires hidden, intermediate and
+ * (nq + 2 nkv) * d to be multiples of 128 and head_dim == 128. */
+size_t layer_workspace_bytes(const lsf_layer_cfg* cfg);
+lsf_status layer_fwd(const lsf_layer_cfg* cfg, const lsf_layer_weights* w,
+                     const lsf_layer_lora* lora, const uint16_t* x, uint16_t* y,
+                     void* ws, size_t ws_bytes, lsf_stream stream);
+/* Recomputes the forward from the checkpoint x (the layer input), then walks
+ * it backward ([TUTORIAL] item 3: each layer is read a second time and
+ * dL/dx = W^T dL/dy still needs the frozen weight).  dy, dx: device bf16
+ * [batch*seq, H]; dA/dB of every adapted projection accumulate (+=). */
+lsf_status layer_bwd(const lsf_layer_cfg* cfg, const lsf_layer_weights* w,
+                     const lsf_layer_lora* lora, const uint16_t* x, const uint16_t* dy,
+                     uint16_t* dx, void* ws, size_t ws_bytes, lsf_stream stream);
+
+/* ------------------------------------------------------------ host store --
+ * One contiguous blob per layer ([REVIEW]: the frozen store is pinned in RAM
+ * and cut into per-layer slices).  NF4 blob, in order, each section 256-byte
+ * aligned: packed qkv, packed o, packed gate_up, packed down, absmax qkv,
+ * absmax o, absmax gate_up, absmax down, norm1 (bf16), norm2 (bf16).
+ * layer_blob_layout fills the byte offsets of those ten sections and the blob
+ * size; the stride between blobs in a store is the size rounded up to 4096. */
+typedef struct {
+  uint64_t off[10];
+  uint64_t bytes;  /* size of one blob */
+  uint64_t stride; /* bytes rounded up to 4096 */
+} lsf_blob_layout;
+lsf_status layer_blob_layout(const lsf_layer_cfg* cfg, int32_t format, lsf_blob_layout* out);
+/* Point a lsf_layer_weights at a blob (host or device address). */
+lsf_status layer_weights_from_blob(const lsf_layer_cfg* cfg, int32_t format, const void* blob,
+                                   lsf_layer_weights* out);
+
+/* --------------------------------------------------- the streamed stack --
+ * [REVIEW], [BLOG], [TUTORIAL] item 2: two fixed device buffers; while layer i
+ * computes from one, a dedicated copy stream loads layer i+1 into the other
+ * from page-locked host memory with an asynchronous host-to-device copy.
+ * Order of one micro-batch: forward layers 0..L-1, head and loss, backward
+ * layers L-1..0 (each re-read and recomputed; [TUTORIAL] item 3).  The two
+ * layers still resident at the turn are reused unless
+ * LSF_STACK_NO_TURN_REUSE is given (2L-2 copies per micro-batch instead of 2L).
+ */
+typedef struct lsf_stack lsf_stack;
+
+#define LSF_STACK_ALLOW_PAGEABLE 0x1u /* accept a pageable host store (slow fallback, [TUTORIAL] item 2) */
+#define LSF_STACK_NO_TURN_REUSE 0x2u  /* copy every layer twice per micro-batch */
+#define LSF_STACK_TIMING 0x4u         /* record copy-busy and compute-wait events for stack_stats */
+
+typedef struct {
+  int32_t n_layers;
+  int32_t format;           /* LSF_FMT_* of every blob */
+  uint64_t blob_stride;     /* bytes between blobs; >= layout.bytes, multiple of 256 */
+  const void* host_store;   /* host memory holding n_layers blobs (page-locked) */
+  void* dev_buf[2];         /* two device buffers of >= layout.bytes each, 256-B aligned */
+  const void* resident_store; /* optional: device copy of the whole store (RESIDENT mode) */
+  lsf_stream compute;       /* stream the layer kernels run on */
+  lsf_stream copy;          /* dedicated stream for host-to-device layer copies */
+  uint32_t flags;           /* LSF_STACK_* */
+} lsf_stack_desc;
+
+lsf_status stack_create(const lsf_layer_cfg* cfg, const lsf_stack_desc* desc, lsf_stack** out);
+lsf_status stack_destroy(lsf_stack* st);
+
+#define LSF_MODE_STREAMED 0x0u   /* weights come through the two buffers */
+#define LSF_MODE_RESIDENT 0x1u   /* weights read in place from resident_store */
+#define LSF_MODE_FWD_ONLY 0x2u   /* stop after the loss (no backward) */
+#define LSF_MODE_ZERO_GRADS 0x4u /* zero every dA/dB before accumulating */
+
+typedef struct {
+  const int32_t* ids;          /* device [batch, seq] token ids in [0, vocab) */
+  const uint16_t* embed;       /* device bf16 [vocab, H] (resident, frozen) */
+  const uint16_t* final_norm;  /* device bf16 [H] */
+  const uint16_t* lm_head;     /* device bf16 [vocab, H] (resident, frozen, untied) */
+  int32_t vocab;               /* multiple of 128... any >= 2 (head GEMM pads) */
+  const lsf_layer_lora* lora;  /* host array [n_layers] of adapter descriptors */
+  uint16_t* ckpt;              /* device bf16 [n_layers + 1, batch*seq, H]: layer inputs */
+  float* logits;               /* device fp32 [batch*seq, vocab] */
+  float* loss;                 /* device fp32 [1]: mean CE over batch*(seq-1) positions */
+  void* ws;                    /* device workspace */
+  size_t ws_bytes;             /* >= stack_workspace_bytes(cfg, vocab) */
+  float loss_scale;            /* multiplies dL/dlogits (e.g. 1/accumulation) */
+  uint32_t mode;               /* LSF_MODE_* */
+} lsf_stack_io;
+
+size_t stack_workspace_bytes(const lsf_layer_cfg* cfg, int32_t vocab);
+/* One SFT micro-batch: embedding gather, streamed forward, final RMSNorm,
+ * lm_head, cross-entropy over next-token labels, lm_head input gradient,
+ * streamed recompute + backward, LoRA gradients accumulated. */
+lsf_status stream_stack_step(lsf_stack* st, const lsf_stack_io* io);
+
+typedef struct {
+  int64_t steps;       /* stream_stack_step calls since create / reset */
+  int64_t copies;      /* host-to-device layer copies enqueued */
+  int64_t bytes;       /* bytes those copies moved */
+  double copy_ms;      /* summed copy durations (LSF_STACK_TIMING only) */
+  double wait_ms;      /* summed compute-stream stalls on copies (LSF_STACK_TIMING only) */
+} lsf_stack_stats;
+/* Waits for the recorded events (synchronises the copy and compute streams). */
+lsf_status stack_stats(lsf_stack* st, lsf_stack_stats* out);
+lsf_status stack_reset_stats(lsf_stack* st);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LSF_H */

@@ -1,0 +1,665 @@
+// C ABI of liblsf.so: argument validation, error reporting, NF4 and single
+// linear entry points, layer entry points, the host-store layout and the
+// two-buffer layer streamer with the stack step.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/lsf.h"
+#include "kernels.h"
+#include "layer.h"
+
+using namespace lsf;
+
+namespace {
+
+thread_local std::string g_err;
+
+lsf_status fail(lsf_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+lsf_status ok() {
+  g_err.clear();
+  return LSF_OK;
+}
+
+#define HIPCK(x)                                                                                  \
+  do {                                                                                            \
+    hipError_t e_ = (x);                                                                          \
+    if (e_ != hipSuccess) return fail(LSF_ERR_HIP, "%s: %s", #x, hipGetErrorString(e_));        \
+  } while (0)
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool valid_rank(int r) { return r == 4 || r == 8 || r == 16 || r == 32 || r == 64; }
+
+lsf_status check_cfg(const lsf_layer_cfg* c) {
+  if (c == nullptr) return fail(LSF_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->batch < 1 || c->seq < 1) return fail(LSF_ERR_SHAPE, "batch and seq must be >= 1 (got %d, %d)", c->batch, c->seq);
+  if (c->hidden <= 0 || c->hidden % 128) return fail(LSF_ERR_SHAPE, "hidden must be a positive multiple of 128");
+  if (c->intermediate <= 0 || c->intermediate % 128)
+    return fail(LSF_ERR_SHAPE, "intermediate must be a positive multiple of 128");
+  if (c->head_dim != 128) return fail(LSF_ERR_SHAPE, "head_dim must be 128");
+  if (c->n_heads <= 0 || c->n_kv_heads <= 0 || c->n_heads % c->n_kv_heads)
+    return fail(LSF_ERR_SHAPE, "n_heads must be a positive multiple of n_kv_heads");
+  if (!valid_rank(c->rank)) return fail(LSF_ERR_SHAPE, "rank must be one of 4, 8, 16, 32, 64");
+  if ((int64_t)c->batch * c->seq > (1 << 20)) return fail(LSF_ERR_SHAPE, "too many tokens per call");
+  return LSF_OK;
+}
+
+lsf_status check_weight(const lsf_weight& w, int fmt, const char* name) {
+  if (w.data == nullptr || !aligned(w.data, 16)) return fail(LSF_ERR_ALIGN, "%s: data NULL or not 16-byte aligned", name);
+  if (fmt == LSF_FMT_NF4 && (w.scale == nullptr || !aligned(w.scale, 4)))
+    return fail(LSF_ERR_INVALID_ARG, "%s: NF4 absmax missing", name);
+  if (fmt == LSF_FMT_NF4_DQ && (w.scale == nullptr || w.scale2 == nullptr || !aligned(w.scale2, 8)))
+    return fail(LSF_ERR_INVALID_ARG, "%s: double-quantised scales missing", name);
+  return LSF_OK;
+}
+
+lsf_status check_weights(const lsf_layer_weights* w) {
+  if (w == nullptr) return fail(LSF_ERR_INVALID_ARG, "weights is NULL");
+  if (w->format != LSF_FMT_NF4 && w->format != LSF_FMT_BF16 && w->format != LSF_FMT_NF4_DQ)
+    return fail(LSF_ERR_INVALID_ARG, "unknown weight format %d", w->format);
+  lsf_status s;
+  if ((s = check_weight(w->qkv, w->format, "qkv")) != LSF_OK) return s;
+  if ((s = check_weight(w->o, w->format, "o")) != LSF_OK) return s;
+  if ((s = check_weight(w->gate_up, w->format, "gate_up")) != LSF_OK) return s;
+  if ((s = check_weight(w->down, w->format, "down")) != LSF_OK) return s;
+  if (w->norm1 == nullptr || w->norm2 == nullptr || !aligned(w->norm1, 16) || !aligned(w->norm2, 16))
+    return fail(LSF_ERR_ALIGN, "norm weights NULL or not 16-byte aligned");
+  return LSF_OK;
+}
+
+lsf_status check_lora(const lsf_layer_lora* l) {
+  if (l == nullptr) return LSF_OK;
+  const lsf_lora_proj* p = &l->q;
+  for (int i = 0; i < 7; ++i) {
+    if (p[i].A == nullptr) continue;
+    if (p[i].B == nullptr) return fail(LSF_ERR_INVALID_ARG, "adapter %d has A but no B", i);
+    if (!aligned(p[i].A, 16) || !aligned(p[i].B, 4)) return fail(LSF_ERR_ALIGN, "adapter %d not aligned", i);
+  }
+  return LSF_OK;
+}
+
+lsf_status check_dev(const void* p, const char* name) {
+  if (p == nullptr) return fail(LSF_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(p, 16)) return fail(LSF_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return LSF_OK;
+}
+
+hipStream_t S(lsf_stream s) { return static_cast<hipStream_t>(s); }
+
+// ------------------------------------------------------------ blob layout
+struct Blob {
+  uint64_t off[10];
+  uint64_t bytes, stride;
+};
+
+uint64_t al256(uint64_t v) { return (v + 255) / 256 * 256; }
+
+Blob blob_layout(const lsf_layer_cfg& c, int fmt) {
+  const uint64_t H = c.hidden, I = c.intermediate, Dq = (uint64_t)c.n_heads * c.head_dim;
+  const uint64_t Nqkv = (uint64_t)(c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const uint64_t n[4] = {Nqkv * H, H * Dq, 2 * I * H, H * I};
+  Blob b{};
+  uint64_t p = 0;
+  for (int i = 0; i < 4; ++i) {
+    b.off[i] = p;
+    p += al256(fmt == LSF_FMT_BF16 ? n[i] * 2 : n[i] / 2);
+  }
+  for (int i = 0; i < 4; ++i) {
+    b.off[4 + i] = p;
+    if (fmt == LSF_FMT_NF4) p += al256(n[i] / 64 * 4);
+    else if (fmt == LSF_FMT_NF4_DQ) p += al256(n[i] / 64) + al256((n[i] / 64 + 255) / 256 * 8);
+    // BF16 has no scales: the section is empty
+  }
+  b.off[8] = p;
+  p += al256(H * 2);
+  b.off[9] = p;
+  p += al256(H * 2);
+  b.bytes = p;
+  b.stride = (p + 4095) / 4096 * 4096;
+  return b;
+}
+
+void weights_from_blob(const lsf_layer_cfg& c, int fmt, const void* blob, lsf_layer_weights* w) {
+  const Blob b = blob_layout(c, fmt);
+  const uint64_t H = c.hidden, I = c.intermediate, Dq = (uint64_t)c.n_heads * c.head_dim;
+  const uint64_t Nqkv = (uint64_t)(c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const uint64_t n[4] = {Nqkv * H, H * Dq, 2 * I * H, H * I};
+  const char* base = static_cast<const char*>(blob);
+  lsf_weight* ws[4] = {&w->qkv, &w->o, &w->gate_up, &w->down};
+  w->format = fmt;
+  for (int i = 0; i < 4; ++i) {
+    ws[i]->data = base + b.off[i];
+    ws[i]->scale = (fmt == LSF_FMT_BF16) ? nullptr : base + b.off[4 + i];
+    ws[i]->scale2 = (fmt == LSF_FMT_NF4_DQ)
+                        ? reinterpret_cast<const float*>(base + b.off[4 + i] + al256(n[i] / 64))
+                        : nullptr;
+  }
+  w->norm1 = reinterpret_cast<const uint16_t*>(base + b.off[8]);
+  w->norm2 = reinterpret_cast<const uint16_t*>(base + b.off[9]);
+}
+
+}  // namespace
+
+// ================================================================ C ABI ==
+extern "C" {
+
+const char* lsf_last_error(void) { return g_err.c_str(); }
+const char* lsf_version(void) { return "lsf 0.1.0 (gfx950)"; }
+
+lsf_status nf4_quantize(const float* w, int64_t n, int32_t blocksize, uint8_t* packed, float* absmax,
+                        lsf_stream stream) {
+  if (blocksize != 64) return fail(LSF_ERR_SHAPE, "blocksize must be 64");
+  if (n < 0 || n % 64) return fail(LSF_ERR_SHAPE, "n must be a non-negative multiple of 64 (got %lld)", (long long)n);
+  if (n == 0) return ok();
+  lsf_status s;
+  if ((s = check_dev(w, "w")) || (s = check_dev(packed, "packed")) || (s = check_dev(absmax, "absmax"))) return s;
+  HIPCK(nf4_quantize_launch(w, n, packed, absmax, S(stream)));
+  return ok();
+}
+
+lsf_status nf4_dequantize(const uint8_t* packed, const float* absmax, int64_t n, int32_t blocksize, uint16_t* out,
+                          lsf_stream stream) {
+  if (blocksize != 64) return fail(LSF_ERR_SHAPE, "blocksize must be 64");
+  if (n < 0 || n % 64) return fail(LSF_ERR_SHAPE, "n must be a non-negative multiple of 64 (got %lld)", (long long)n);
+  if (n == 0) return ok();
+  lsf_status s;
+  if ((s = check_dev(packed, "packed")) || (s = check_dev(absmax, "absmax")) || (s = check_dev(out, "out"))) return s;
+  HIPCK(nf4_dequantize_launch(packed, absmax, n, out, S(stream)));
+  return ok();
+}
+
+// ----------------------------------------------------------- single linear
+size_t linear_workspace_bytes(int32_t tokens, int32_t n_out, int32_t n_in, int32_t rank) {
+  if (tokens <= 0 || n_out <= 0 || n_in <= 0) return 0;
+  const size_t T = tokens, r = rank > 0 ? rank : 1;
+  const size_t N = n_out > n_in ? n_out : n_in;
+  return 3 * 256 + (T * r * 4 + 255) / 256 * 256 * 2 + (size_t)8 * T * N * 4;
+}
+
+static lsf_status linear_common(const lsf_weight* w, int32_t format, int32_t n_out, int32_t n_in, const float* A,
+                                const float* B, int32_t rank, int32_t tokens, void* ws, size_t ws_bytes) {
+  if (w == nullptr) return fail(LSF_ERR_INVALID_ARG, "weight is NULL");
+  if (format != LSF_FMT_NF4 && format != LSF_FMT_BF16 && format != LSF_FMT_NF4_DQ)
+    return fail(LSF_ERR_INVALID_ARG, "unknown weight format %d", format);
+  if (n_out <= 0 || n_out % 128) return fail(LSF_ERR_SHAPE, "n_out must be a positive multiple of 128");
+  if (n_in <= 0 || n_in % 128) return fail(LSF_ERR_SHAPE, "n_in must be a positive multiple of 128");
+  if (tokens < 1) return fail(LSF_ERR_SHAPE, "tokens must be >= 1");
+  if (A != nullptr && (B == nullptr || !valid_rank(rank)))
+    return fail(LSF_ERR_SHAPE, "adapter needs B and a rank in {4, 8, 16, 32, 64}");
+  if (A != nullptr && !aligned(A, 16)) return fail(LSF_ERR_ALIGN, "A not 16-byte aligned");
+  lsf_status s = check_weight(*w, format, "w");
+  if (s) return s;
+  if (ws == nullptr || ws_bytes < linear_workspace_bytes(tokens, n_out, n_in, rank))
+    return fail(LSF_ERR_WORKSPACE, "workspace too small (need %zu bytes)", linear_workspace_bytes(tokens, n_out, n_in, rank));
+  return LSF_OK;
+}
+
+struct LinWs {
+  float *U, *dU, *part;
+  size_t part_floats;
+};
+static LinWs lin_ws(void* ws, int32_t tokens, int32_t n_out, int32_t n_in, int32_t rank) {
+  uintptr_t p = ((uintptr_t)ws + 255) / 256 * 256;
+  const size_t T = tokens, r = rank > 0 ? rank : 1;
+  LinWs l;
+  l.U = (float*)p;
+  p += (T * r * 4 + 255) / 256 * 256;
+  l.dU = (float*)p;
+  p += (T * r * 4 + 255) / 256 * 256;
+  l.part = (float*)p;
+  l.part_floats = (size_t)8 * T * (n_out > n_in ? n_out : n_in);
+  return l;
+}
+
+lsf_status linear_fwd(const lsf_weight* w, int32_t format, int32_t n_out, int32_t n_in, const float* A, const float* B,
+                      int32_t rank, float scale, const uint16_t* x, int32_t tokens, uint16_t* y, void* ws,
+                      size_t ws_bytes, lsf_stream stream) {
+  lsf_status s = linear_common(w, format, n_out, n_in, A, B, rank, tokens, ws, ws_bytes);
+  if (s) return s;
+  if ((s = check_dev(x, "x")) || (s = check_dev(y, "y"))) return s;
+  const LinWs l = lin_ws(ws, tokens, n_out, n_in, rank);
+  GemmArgs g;
+  g.M = tokens; g.N = n_out; g.K = n_in; g.A = x; g.lda = n_in; g.W = weight_ref(*w, format, n_in);
+  if (A != nullptr) {
+    LoraDown d;
+    d.M = tokens; d.K = n_in; d.X = x; d.ldx = n_in; d.nsec = 1; d.r = rank; d.mat[0] = A; d.scale = 1.0f;
+    d.U = l.U; d.ldu = rank;
+    HIPCK(lora_down(d, S(stream)));
+    g.ext.kx = rank; g.ext.u = l.U; g.ext.ldu = rank; g.ext.uscale = scale; g.ext.nsec = 1; g.ext.r = rank;
+    g.ext.mat[0] = B; g.ext.row_off[1] = n_out;
+  }
+  EpiArgs e; e.kind = EPI_BF16; e.C = y; e.ldc = n_out;
+  HIPCK(run_gemm(false, g, e, l.part, l.part_floats, S(stream)));
+  return ok();
+}
+
+lsf_status linear_bwd(const lsf_weight* w, int32_t format, int32_t n_out, int32_t n_in, const float* A, const float* B,
+                      int32_t rank, float scale, const uint16_t* x, const uint16_t* dy, int32_t tokens, uint16_t* dx,
+                      float* dA, float* dB, void* ws, size_t ws_bytes, lsf_stream stream) {
+  lsf_status s = linear_common(w, format, n_out, n_in, A, B, rank, tokens, ws, ws_bytes);
+  if (s) return s;
+  if ((s = check_dev(x, "x")) || (s = check_dev(dy, "dy")) || (s = check_dev(dx, "dx"))) return s;
+  const LinWs l = lin_ws(ws, tokens, n_out, n_in, rank);
+  GemmArgs g;
+  g.M = tokens; g.N = n_in; g.K = n_out; g.A = dy; g.lda = n_out; g.W = weight_ref(*w, format, n_in);
+  if (A != nullptr) {
+    LoraDown d;
+    d.M = tokens; d.K = n_in; d.X = x; d.ldx = n_in; d.nsec = 1; d.r = rank; d.mat[0] = A; d.scale = 1.0f;
+    d.U = l.U; d.ldu = rank;
+    HIPCK(lora_down(d, S(stream)));
+    LoraDown b;
+    b.M = tokens; b.K = n_out; b.X = dy; b.ldx = n_out; b.nsec = 1; b.r = rank; b.mat[0] = B; b.bside = true;
+    b.ksec[0] = n_out; b.scale = scale; b.U = l.dU; b.ldu = rank;
+    HIPCK(lora_down(b, S(stream)));
+    g.ext.kx = rank; g.ext.u = l.dU; g.ext.ldu = rank; g.ext.nsec = 1; g.ext.r = rank; g.ext.mat[0] = A;
+    g.ext.ldmat = n_in;
+  }
+  EpiArgs e; e.kind = EPI_BF16; e.C = dx; e.ldc = n_in;
+  HIPCK(run_gemm(true, g, e, l.part, l.part_floats, S(stream)));
+  if (A != nullptr) {
+    LoraGradSec ga, gb;
+    ga.P = l.dU; ga.ldp = rank; ga.Q = x; ga.ldq = n_in; ga.nq = n_in; ga.out = dA; ga.scale = 1.0f;
+    gb.P = l.U; gb.ldp = rank; gb.Q = dy; gb.ldq = n_out; gb.nq = n_out; gb.out = dB; gb.transposed = true;
+    gb.scale = scale;
+    if (dA) HIPCK(lora_grad(&ga, 1, tokens, rank, S(stream)));
+    if (dB) HIPCK(lora_grad(&gb, 1, tokens, rank, S(stream)));
+  }
+  return ok();
+}
+
+// ------------------------------------------------------------------ layer
+size_t layer_workspace_bytes(const lsf_layer_cfg* cfg) {
+  if (check_cfg(cfg) != LSF_OK) return 0;
+  return LayerWs::bytes(*cfg);
+}
+
+lsf_status layer_fwd(const lsf_layer_cfg* cfg, const lsf_layer_weights* w, const lsf_layer_lora* lora,
+                     const uint16_t* x, uint16_t* y, void* ws, size_t ws_bytes, lsf_stream stream) {
+  lsf_status s;
+  if ((s = check_cfg(cfg)) || (s = check_weights(w)) || (s = check_lora(lora))) return s;
+  if ((s = check_dev(x, "x")) || (s = check_dev(y, "y"))) return s;
+  if (ws == nullptr || ws_bytes < LayerWs::bytes(*cfg))
+    return fail(LSF_ERR_WORKSPACE, "workspace too small (need %zu bytes)", LayerWs::bytes(*cfg));
+  const LayerWs l = LayerWs::carve(*cfg, ws);
+  HIPCK(layer_forward(*cfg, *w, lora, x, y, l, false, false, S(stream)));
+  return ok();
+}
+
+lsf_status layer_bwd(const lsf_layer_cfg* cfg, const lsf_layer_weights* w, const lsf_layer_lora* lora,
+                     const uint16_t* x, const uint16_t* dy, uint16_t* dx, void* ws, size_t ws_bytes,
+                     lsf_stream stream) {
+  lsf_status s;
+  if ((s = check_cfg(cfg)) || (s = check_weights(w)) || (s = check_lora(lora))) return s;
+  if ((s = check_dev(x, "x")) || (s = check_dev(dy, "dy")) || (s = check_dev(dx, "dx"))) return s;
+  if (ws == nullptr || ws_bytes < LayerWs::bytes(*cfg))
+    return fail(LSF_ERR_WORKSPACE, "workspace too small (need %zu bytes)", LayerWs::bytes(*cfg));
+  const LayerWs l = LayerWs::carve(*cfg, ws);
+  HIPCK(layer_backward(*cfg, *w, lora, x, dy, dx, l, false, S(stream)));
+  return ok();
+}
+
+lsf_status layer_blob_layout(const lsf_layer_cfg* cfg, int32_t format, lsf_blob_layout* out) {
+  lsf_status s;
+  if ((s = check_cfg(cfg))) return s;
+  if (out == nullptr) return fail(LSF_ERR_INVALID_ARG, "out is NULL");
+  if (format != LSF_FMT_NF4 && format != LSF_FMT_BF16 && format != LSF_FMT_NF4_DQ)
+    return fail(LSF_ERR_INVALID_ARG, "unknown weight format %d", format);
+  const Blob b = blob_layout(*cfg, format);
+  for (int i = 0; i < 10; ++i) out->off[i] = b.off[i];
+  out->bytes = b.bytes;
+  out->stride = b.stride;
+  return ok();
+}
+
+lsf_status layer_weights_from_blob(const lsf_layer_cfg* cfg, int32_t format, const void* blob,
+                                   lsf_layer_weights* out) {
+  lsf_status s;
+  if ((s = check_cfg(cfg))) return s;
+  if (out == nullptr || blob == nullptr) return fail(LSF_ERR_INVALID_ARG, "blob or out is NULL");
+  if (!aligned(blob, 256)) return fail(LSF_ERR_ALIGN, "blob must be 256-byte aligned");
+  weights_from_blob(*cfg, format, blob, out);
+  return ok();
+}
+
+}  // extern "C"
+
+// ============================================================ the streamer
+struct lsf_stack {
+  lsf_layer_cfg cfg;
+  lsf_stack_desc d;
+  Blob blob;
+  hipEvent_t ready[2], freed[2];
+  bool used[2];
+  int slot_layer[2];
+  // timing (LSF_STACK_TIMING)
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_next = 0;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> copy_ev, wait_ev;
+  lsf_stack_stats stats;
+};
+
+namespace {
+
+hipEvent_t timing_event(lsf_stack* st) {
+  if (st->ev_next == st->ev_pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    st->ev_pool.push_back(e);
+  }
+  return st->ev_pool[st->ev_next++];
+}
+
+// Make layer j resident in buffer b: copy unless the buffer already holds it.
+lsf_status acquire(lsf_stack* st, int j, int b, bool allow_reuse) {
+  if (allow_reuse && st->slot_layer[b] == j) return LSF_OK;
+  hipStream_t cs = S(st->d.copy);
+  if (st->used[b]) HIPCK(hipStreamWaitEvent(cs, st->freed[b], 0));
+  const bool timing = st->d.flags & LSF_STACK_TIMING;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (timing) {
+    e0 = timing_event(st);
+    e1 = timing_event(st);
+    if (!e0 || !e1) return fail(LSF_ERR_HIP, "hipEventCreate failed");
+    HIPCK(hipEventRecord(e0, cs));
+  }
+  const char* src = static_cast<const char*>(st->d.host_store) + (uint64_t)j * st->d.blob_stride;
+  HIPCK(hipMemcpyAsync(st->d.dev_buf[b], src, st->blob.bytes, hipMemcpyHostToDevice, cs));
+  if (timing) {
+    HIPCK(hipEventRecord(e1, cs));
+    st->copy_ev.emplace_back(e0, e1);
+  }
+  HIPCK(hipEventRecord(st->ready[b], cs));
+  st->slot_layer[b] = j;
+  st->stats.copies += 1;
+  st->stats.bytes += (int64_t)st->blob.bytes;
+  return LSF_OK;
+}
+
+// Order the compute stream after the copy into buffer b.
+lsf_status wait_ready(lsf_stack* st, int b) {
+  hipStream_t cs = S(st->d.compute);
+  const bool timing = st->d.flags & LSF_STACK_TIMING;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (timing) {
+    e0 = timing_event(st);
+    e1 = timing_event(st);
+    if (!e0 || !e1) return fail(LSF_ERR_HIP, "hipEventCreate failed");
+    HIPCK(hipEventRecord(e0, cs));
+  }
+  HIPCK(hipStreamWaitEvent(cs, st->ready[b], 0));
+  if (timing) {
+    HIPCK(hipEventRecord(e1, cs));
+    st->wait_ev.emplace_back(e0, e1);
+  }
+  return LSF_OK;
+}
+
+struct StackWs {
+  LayerWs layer;
+  uint16_t *hN, *dhN, *dlog, *dx[2];
+  float *rstdN, *row_loss, *part;
+  size_t part_floats;
+};
+
+size_t head_part_floats(const lsf_layer_cfg& c) { return (size_t)8 * c.batch * c.seq * c.hidden; }
+
+size_t stack_ws_bytes(const lsf_layer_cfg& c, int V) {
+  const size_t T = (size_t)c.batch * c.seq, H = c.hidden;
+  size_t b = LayerWs::bytes(c);
+  b += al256(T * H * 2) * 4;  // hN, dhN, dx[0], dx[1]
+  b += al256(T * (size_t)V * 2);
+  b += al256(T * 4) * 2;
+  b += al256(head_part_floats(c) * 4);
+  return b + 512;
+}
+
+StackWs carve_stack(const lsf_layer_cfg& c, int V, void* base) {
+  const size_t T = (size_t)c.batch * c.seq, H = c.hidden;
+  StackWs w;
+  w.layer = LayerWs::carve(c, base);
+  uintptr_t p = ((uintptr_t)base + LayerWs::bytes(c) + 255) / 256 * 256;
+  auto take = [&](size_t n) {
+    void* r = (void*)p;
+    p += al256(n);
+    return r;
+  };
+  w.hN = (uint16_t*)take(T * H * 2);
+  w.dhN = (uint16_t*)take(T * H * 2);
+  w.dx[0] = (uint16_t*)take(T * H * 2);
+  w.dx[1] = (uint16_t*)take(T * H * 2);
+  w.dlog = (uint16_t*)take(T * (size_t)V * 2);
+  w.rstdN = (float*)take(T * 4);
+  w.row_loss = (float*)take(T * 4);
+  w.part_floats = head_part_floats(c);
+  w.part = (float*)take(w.part_floats * 4);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+lsf_status stack_create(const lsf_layer_cfg* cfg, const lsf_stack_desc* desc, lsf_stack** out) {
+  lsf_status s;
+  if ((s = check_cfg(cfg))) return s;
+  if (desc == nullptr || out == nullptr) return fail(LSF_ERR_INVALID_ARG, "desc or out is NULL");
+  *out = nullptr;
+  if (desc->n_layers < 1) return fail(LSF_ERR_INVALID_ARG, "n_layers must be >= 1");
+  if (desc->format != LSF_FMT_NF4 && desc->format != LSF_FMT_BF16 && desc->format != LSF_FMT_NF4_DQ)
+    return fail(LSF_ERR_INVALID_ARG, "unknown weight format %d", desc->format);
+  const Blob b = blob_layout(*cfg, desc->format);
+  if (desc->blob_stride < b.bytes || desc->blob_stride % 256)
+    return fail(LSF_ERR_SHAPE, "blob_stride %llu must be >= %llu and a multiple of 256",
+                (unsigned long long)desc->blob_stride, (unsigned long long)b.bytes);
+  if (desc->dev_buf[0] == nullptr || desc->dev_buf[1] == nullptr)
+    return fail(LSF_ERR_INVALID_ARG, "two device buffers are required");
+  if (!aligned(desc->dev_buf[0], 256) || !aligned(desc->dev_buf[1], 256))
+    return fail(LSF_ERR_ALIGN, "device buffers must be 256-byte aligned");
+  if (desc->resident_store != nullptr && !aligned(desc->resident_store, 256))
+    return fail(LSF_ERR_ALIGN, "resident store must be 256-byte aligned");
+  if (desc->host_store == nullptr) {
+    if (desc->resident_store == nullptr) return fail(LSF_ERR_INVALID_ARG, "no host store and no resident store");
+  } else {
+    hipPointerAttribute_t attr;
+    const hipError_t e = hipPointerGetAttributes(&attr, desc->host_store);
+    bool pinned = (e == hipSuccess) && (attr.type == hipMemoryTypeHost);
+    if (e != hipSuccess) (void)hipGetLastError();  // clear the sticky error of a pageable query
+    if (!pinned && !(desc->flags & LSF_STACK_ALLOW_PAGEABLE))
+      return fail(LSF_ERR_NOT_PINNED, "host store is not page-locked (pass LSF_STACK_ALLOW_PAGEABLE to accept it)");
+  }
+  lsf_stack* st = new (std::nothrow) lsf_stack();
+  if (st == nullptr) return fail(LSF_ERR_INVALID_ARG, "out of host memory");
+  st->cfg = *cfg;
+  st->d = *desc;
+  st->blob = b;
+  for (int i = 0; i < 2; ++i) {
+    st->used[i] = false;
+    st->slot_layer[i] = -1;
+    if (hipEventCreateWithFlags(&st->ready[i], hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&st->freed[i], hipEventDisableTiming) != hipSuccess) {
+      delete st;
+      return fail(LSF_ERR_HIP, "hipEventCreateWithFlags failed");
+    }
+  }
+  std::memset(&st->stats, 0, sizeof(st->stats));
+  *out = st;
+  return ok();
+}
+
+lsf_status stack_destroy(lsf_stack* st) {
+  if (st == nullptr) return ok();
+  for (int i = 0; i < 2; ++i) {
+    (void)hipEventDestroy(st->ready[i]);
+    (void)hipEventDestroy(st->freed[i]);
+  }
+  for (hipEvent_t e : st->ev_pool) (void)hipEventDestroy(e);
+  delete st;
+  return ok();
+}
+
+size_t stack_workspace_bytes(const lsf_layer_cfg* cfg, int32_t vocab) {
+  if (check_cfg(cfg) != LSF_OK || vocab <= 0) return 0;
+  return stack_ws_bytes(*cfg, vocab);
+}
+
+lsf_status stream_stack_step(lsf_stack* st, const lsf_stack_io* io) {
+  if (st == nullptr || io == nullptr) return fail(LSF_ERR_INVALID_ARG, "stack or io is NULL");
+  const lsf_layer_cfg& c = st->cfg;
+  const int L = st->d.n_layers;
+  const int V = io->vocab;
+  const int T = c.batch * c.seq, H = c.hidden;
+  lsf_status s;
+  if (V < 128 || V % 128) return fail(LSF_ERR_SHAPE, "vocab must be a positive multiple of 128 (got %d)", V);
+  if ((s = check_dev(io->ids, "ids")) || (s = check_dev(io->embed, "embed")) ||
+      (s = check_dev(io->final_norm, "final_norm")) || (s = check_dev(io->lm_head, "lm_head")) ||
+      (s = check_dev(io->ckpt, "ckpt")) || (s = check_dev(io->logits, "logits")) || (s = check_dev(io->loss, "loss")))
+    return s;
+  if (io->lora == nullptr) return fail(LSF_ERR_INVALID_ARG, "lora array is NULL");
+  for (int i = 0; i < L; ++i)
+    if ((s = check_lora(&io->lora[i]))) return s;
+  const bool resident = io->mode & LSF_MODE_RESIDENT;
+  if (resident && st->d.resident_store == nullptr) return fail(LSF_ERR_INVALID_ARG, "RESIDENT mode needs a resident store");
+  if (!resident && st->d.host_store == nullptr) return fail(LSF_ERR_INVALID_ARG, "STREAMED mode needs a host store");
+  if (io->ws == nullptr || io->ws_bytes < stack_ws_bytes(c, V))
+    return fail(LSF_ERR_WORKSPACE, "workspace too small (need %zu bytes)", stack_ws_bytes(c, V));
+
+  hipStream_t cs = S(st->d.compute);
+  const StackWs w = carve_stack(c, V, io->ws);
+  const size_t act = (size_t)T * H;
+  st->ev_next = 0;
+  st->copy_ev.clear();
+  st->wait_ev.clear();
+  st->stats.steps += 1;
+
+  if (io->mode & LSF_MODE_ZERO_GRADS) {
+    for (int i = 0; i < L; ++i) {
+      const lsf_layer_lora& l = io->lora[i];
+      const lsf_lora_proj* p = &l.q;
+      const lsf_layer_cfg& cc = c;
+      const int64_t H_ = cc.hidden, I_ = cc.intermediate, Dq = (int64_t)cc.n_heads * cc.head_dim,
+                    Dk = (int64_t)cc.n_kv_heads * cc.head_dim;
+      const int64_t in[7] = {H_, H_, H_, Dq, H_, H_, I_};
+      const int64_t outd[7] = {Dq, Dk, Dk, H_, I_, I_, H_};
+      for (int k = 0; k < 7; ++k) {
+        if (p[k].A == nullptr) continue;
+        if (p[k].dA) HIPCK(zero_f32(p[k].dA, (int64_t)cc.rank * in[k], cs));
+        if (p[k].dB) HIPCK(zero_f32(p[k].dB, (int64_t)cc.rank * outd[k], cs));
+      }
+    }
+  }
+
+  HIPCK(rope_table(c.seq, c.head_dim, c.rope_theta, w.layer.rope, cs));
+  HIPCK(embed_gather(io->ids, io->embed, T, H, V, io->ckpt, cs));
+
+  auto weights_of = [&](int j, int b) {
+    lsf_layer_weights lw;
+    const void* blob = resident ? static_cast<const char*>(st->d.resident_store) + (uint64_t)j * st->d.blob_stride
+                                : st->d.dev_buf[b];
+    weights_from_blob(c, st->d.format, blob, &lw);
+    return lw;
+  };
+
+  // ---- forward: layer i computes from buffer i % 2 while i + 1 loads
+  if (!resident) {
+    st->slot_layer[0] = st->slot_layer[1] = -1;  // buffers hold nothing valid across steps
+    if ((s = acquire(st, 0, 0, false))) return s;
+    if (L > 1 && (s = acquire(st, 1, 1, false))) return s;
+  }
+  for (int i = 0; i < L; ++i) {
+    const int b = i & 1;
+    if (!resident && (s = wait_ready(st, b))) return s;
+    const lsf_layer_weights lw = weights_of(i, b);
+    HIPCK(layer_forward(c, lw, &io->lora[i], io->ckpt + (size_t)i * act, io->ckpt + (size_t)(i + 1) * act, w.layer,
+                        false, true, cs));
+    if (!resident) {
+      HIPCK(hipEventRecord(st->freed[b], cs));
+      st->used[b] = true;
+      if (i + 2 < L && (s = acquire(st, i + 2, b, false))) return s;
+    }
+  }
+
+  // ---- head: final norm, lm_head, cross-entropy, lm_head input gradient
+  const uint16_t* xL = io->ckpt + (size_t)L * act;
+  HIPCK(rmsnorm_fwd(xL, io->final_norm, T, H, c.rms_eps, w.hN, w.rstdN, cs));
+  {
+    GemmArgs g;
+    g.M = T; g.N = V; g.K = H; g.A = w.hN; g.lda = H;
+    g.W.fmt = FMT_BF16; g.W.bf16 = io->lm_head; g.W.ld = H;
+    EpiArgs e; e.kind = EPI_F32; e.C = io->logits; e.ldc = V;
+    HIPCK(gemm_nt(g, e, cs));
+  }
+  HIPCK(cross_entropy(io->logits, io->ids, c.batch, c.seq, V, io->loss_scale, w.dlog, w.row_loss, io->loss, cs));
+  if (io->mode & LSF_MODE_FWD_ONLY) return ok();
+  {
+    GemmArgs g;
+    g.M = T; g.N = H; g.K = V; g.A = w.dlog; g.lda = V;
+    g.W.fmt = FMT_BF16; g.W.bf16 = io->lm_head; g.W.ld = H;
+    EpiArgs e; e.kind = EPI_BF16; e.C = w.dhN; e.ldc = H;
+    HIPCK(run_gemm(true, g, e, w.part, w.part_floats, cs));
+  }
+  HIPCK(rmsnorm_bwd(w.dhN, xL, io->final_norm, w.rstdN, nullptr, T, H, w.dx[L & 1], cs));
+
+  // ---- backward: layers L-1 .. 0, layer j again from buffer j % 2
+  const bool reuse = !(st->d.flags & LSF_STACK_NO_TURN_REUSE);
+  if (!resident) {
+    if ((s = acquire(st, L - 1, (L - 1) & 1, reuse))) return s;
+    if (L > 1 && (s = acquire(st, L - 2, (L - 2) & 1, reuse))) return s;
+  }
+  for (int j = L - 1; j >= 0; --j) {
+    const int b = j & 1;
+    if (!resident && (s = wait_ready(st, b))) return s;
+    const lsf_layer_weights lw = weights_of(j, b);
+    HIPCK(layer_backward(c, lw, &io->lora[j], io->ckpt + (size_t)j * act, w.dx[(j + 1) & 1], w.dx[j & 1], w.layer,
+                         true, cs));
+    if (!resident) {
+      HIPCK(hipEventRecord(st->freed[b], cs));
+      st->used[b] = true;
+      if (j - 2 >= 0 && (s = acquire(st, j - 2, b, false))) return s;
+    }
+  }
+  return ok();
+}
+
+lsf_status stack_stats(lsf_stack* st, lsf_stack_stats* out) {
+  if (st == nullptr || out == nullptr) return fail(LSF_ERR_INVALID_ARG, "stack or out is NULL");
+  lsf_stack_stats r = st->stats;
+  r.copy_ms = 0.0;
+  r.wait_ms = 0.0;
+  for (auto& pr : st->copy_ev) {
+    HIPCK(hipEventSynchronize(pr.second));
+    float ms = 0.0f;
+    HIPCK(hipEventElapsedTime(&ms, pr.first, pr.second));
+    r.copy_ms += ms;
+  }
+  for (auto& pr : st->wait_ev) {
+    HIPCK(hipEventSynchronize(pr.second));
+    float ms = 0.0f;
+    HIPCK(hipEventElapsedTime(&ms, pr.first, pr.second));
+    r.wait_ms += ms;
+  }
+  *out = r;
+  return ok();
+}
+
+lsf_status stack_reset_stats(lsf_stack* st) {
+  if (st == nullptr) return fail(LSF_ERR_INVALID_ARG, "stack is NULL");
+  std::memset(&st->stats, 0, sizeof(st->stats));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,256 @@
+// Bandwidth-bound kernels: RMSNorm forward/backward, RoPE, embedding gather,
+// cross-entropy, fills.  Rows are processed by one 256-thread workgroup with
+// 16-byte vector accesses; reductions go lane -> wave (shuffles) -> workgroup
+// (LDS, fixed order), so results do not depend on scheduling.
+#include "common.h"
+#include "kernels.h"
+
+namespace lsf {
+namespace {
+
+// Sum over the 256 threads of a workgroup, the same order every time.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = warp_sum(v);
+  const int wid = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wid] = v;
+  __syncthreads();
+  return ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+__device__ __forceinline__ void unpack8(const u32x4& q, float f[8]) {
+  f[0] = bf16lo(q.x); f[1] = bf16hi(q.x); f[2] = bf16lo(q.y); f[3] = bf16hi(q.y);
+  f[4] = bf16lo(q.z); f[5] = bf16hi(q.z); f[6] = bf16lo(q.w); f[7] = bf16hi(q.w);
+}
+__device__ __forceinline__ u32x4 pack8(const float f[8]) {
+  return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+}
+
+__global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ w, int H, float eps,
+                                                          uint16_t* __restrict__ y, float* __restrict__ rstd) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * H;
+  float ss = 0.0f;
+  for (int i = threadIdx.x * 8; i < H; i += 256 * 8) {
+    float f[8];
+    unpack8(*reinterpret_cast<const u32x4*>(xr + i), f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+  }
+  ss = block_sum(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
+  for (int i = threadIdx.x * 8; i < H; i += 256 * 8) {
+    float f[8], g[8];
+    unpack8(*reinterpret_cast<const u32x4*>(xr + i), f);
+    unpack8(*reinterpret_cast<const u32x4*>(w + i), g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = f[e] * r * g[e];
+    *reinterpret_cast<u32x4*>(y + row * H + i) = pack8(f);
+  }
+  if (threadIdx.x == 0 && rstd != nullptr) rstd[row] = r;
+}
+
+__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const uint16_t* __restrict__ dy,
+                                                          const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ w,
+                                                          const float* __restrict__ rstd,
+                                                          const uint16_t* __restrict__ resid, int H,
+                                                          uint16_t* __restrict__ dx) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const int64_t base = row * H;
+  float dot = 0.0f;
+  for (int i = threadIdx.x * 8; i < H; i += 256 * 8) {
+    float a[8], b[8], c[8];
+    unpack8(*reinterpret_cast<const u32x4*>(dy + base + i), a);
+    unpack8(*reinterpret_cast<const u32x4*>(w + i), b);
+    unpack8(*reinterpret_cast<const u32x4*>(x + base + i), c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dot = fmaf(a[e] * b[e], c[e], dot);
+  }
+  dot = block_sum(dot, red);
+  const float r = rstd[row];
+  const float k = r * r * r * dot / (float)H;
+  for (int i = threadIdx.x * 8; i < H; i += 256 * 8) {
+    float a[8], b[8], c[8], o[8];
+    unpack8(*reinterpret_cast<const u32x4*>(dy + base + i), a);
+    unpack8(*reinterpret_cast<const u32x4*>(w + i), b);
+    unpack8(*reinterpret_cast<const u32x4*>(x + base + i), c);
+    if (resid != nullptr) unpack8(*reinterpret_cast<const u32x4*>(resid + base + i), o);
+    else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] += r * (a[e] * b[e]) - c[e] * k;
+    *reinterpret_cast<u32x4*>(dx + base + i) = pack8(o);
+  }
+}
+
+__global__ void rope_table_kernel(int seq, int half, float theta, float2* tab) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= seq * half) return;
+  const int pos = idx / half, i = idx - pos * half;
+  const double inv = pow((double)theta, -2.0 * (double)i / (double)(2 * half));
+  const double ang = (double)pos * inv;
+  tab[idx] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+// One thread: 8 consecutive pairs (i, i + d/2) of one head of one token.
+__global__ __launch_bounds__(256) void rope_apply_kernel(uint16_t* __restrict__ qk, int64_t ld, int T, int seq,
+                                                         int nheads, int d, const float2* __restrict__ tab,
+                                                         int inverse) {
+  const int half = d >> 1, groups = half >> 3;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)T * nheads * groups;
+  if (idx >= total) return;
+  const int gi = (int)(idx % groups);
+  const int64_t th = idx / groups;
+  const int h = (int)(th % nheads);
+  const int t = (int)(th / nheads);
+  const int pos = t % seq;
+  uint16_t* p = qk + (int64_t)t * ld + (int64_t)h * d + gi * 8;
+  float a[8], b[8];
+  unpack8(*reinterpret_cast<const u32x4*>(p), a);
+  unpack8(*reinterpret_cast<const u32x4*>(p + half), b);
+  const float sgn = inverse ? -1.0f : 1.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float2 cs = tab[pos * half + gi * 8 + e];
+    const float s = sgn * cs.y;
+    const float x1 = a[e], x2 = b[e];
+    a[e] = x1 * cs.x - x2 * s;
+    b[e] = x2 * cs.x + x1 * s;
+  }
+  *reinterpret_cast<u32x4*>(p) = pack8(a);
+  *reinterpret_cast<u32x4*>(p + half) = pack8(b);
+}
+
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ ids, const uint16_t* __restrict__ E,
+                                                    int H, int V, uint16_t* __restrict__ x) {
+  const int64_t t = blockIdx.x;
+  int id = ids[t];
+  id = id < 0 ? 0 : (id >= V ? V - 1 : id);
+  const u32x4* src = reinterpret_cast<const u32x4*>(E + (int64_t)id * H);
+  u32x4* dst = reinterpret_cast<u32x4*>(x + t * H);
+  for (int i = threadIdx.x; i < H / 8; i += 256) dst[i] = src[i];
+}
+
+// One workgroup per row of logits.  Pass 1: running (max, sum of exp) per
+// thread, merged in a fixed order; pass 2: softmax minus one-hot, scaled.
+__global__ __launch_bounds__(256) void ce_row_kernel(const float* __restrict__ logits, const int32_t* __restrict__ ids,
+                                                     int seq, int V, float coef, uint16_t* __restrict__ dlogits,
+                                                     float* __restrict__ row_loss) {
+  __shared__ float sm[4], ss[4];
+  const int64_t t = blockIdx.x;
+  const float* z = logits + t * V;
+  const bool valid = (t % seq) < seq - 1;
+  int label = valid ? ids[t + 1] : 0;
+  label = label < 0 ? 0 : (label >= V ? V - 1 : label);
+  float m = -INFINITY, s = 0.0f;
+  for (int v = threadIdx.x; v < V; v += 256) {
+    const float x = z[v];
+    if (x > m) {
+      s = s * __expf(m - x) + 1.0f;
+      m = x;
+    } else {
+      s += __expf(x - m);
+    }
+  }
+  // merge within the wave
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+    const float mm = fmaxf(m, m2);
+    s = (m == -INFINITY ? 0.0f : s * __expf(m - mm)) + (m2 == -INFINITY ? 0.0f : s2 * __expf(m2 - mm));
+    m = mm;
+  }
+  const int wid = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { sm[wid] = m; ss[wid] = s; }
+  __syncthreads();
+  float M = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+  float S = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) S += ss[w] * __expf(sm[w] - M);
+  const float lse = M + __logf(S);
+  if (threadIdx.x == 0) row_loss[t] = valid ? (lse - z[label]) : 0.0f;
+  uint16_t* d = dlogits + t * V;
+  for (int v = threadIdx.x; v < V; v += 256) {
+    float g = 0.0f;
+    if (valid) g = (__expf(z[v] - lse) - (v == label ? 1.0f : 0.0f)) * coef;
+    d[v] = f32_to_bf16(g);
+  }
+}
+
+__global__ __launch_bounds__(256) void mean_kernel(const float* __restrict__ x, int n, float inv, float* out) {
+  __shared__ float red[4];
+  float s = 0.0f;
+  for (int i = threadIdx.x; i < n; i += 256) s += x[i];
+  s = block_sum(s, red);
+  if (threadIdx.x == 0) *out = s * inv;
+}
+
+__global__ void fill_kernel(float* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0.0f;
+}
+
+}  // namespace
+
+hipError_t rmsnorm_fwd(const uint16_t* x, const uint16_t* w, int T, int H, float eps, uint16_t* y, float* rstd,
+                       hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rmsnorm_fwd_kernel, dim3(T), dim3(256), 0, s, x, w, H, eps, y, rstd);
+  return hipGetLastError();
+}
+
+hipError_t rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const uint16_t* w, const float* rstd,
+                       const uint16_t* resid, int T, int H, uint16_t* dx, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3(T), dim3(256), 0, s, dy, x, w, rstd, resid, H, dx);
+  return hipGetLastError();
+}
+
+hipError_t rope_table(int seq, int d, float theta, float2* tab, hipStream_t s) {
+  const int n = seq * (d / 2);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, s, seq, d / 2, theta, tab);
+  return hipGetLastError();
+}
+
+hipError_t rope_apply(uint16_t* qk, int64_t ld, int T, int seq, int n_heads_total, int d, const float2* tab,
+                      bool inverse, hipStream_t s) {
+  const int64_t total = (int64_t)T * n_heads_total * (d / 16);
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_apply_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, qk, ld, T, seq,
+                     n_heads_total, d, tab, inverse ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t embed_gather(const int32_t* ids, const uint16_t* E, int T, int H, int V, uint16_t* x, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(embed_kernel, dim3(T), dim3(256), 0, s, ids, E, H, V, x);
+  return hipGetLastError();
+}
+
+hipError_t cross_entropy(const float* logits, const int32_t* ids, int batch, int seq, int V, float loss_scale,
+                         uint16_t* dlogits, float* row_loss, float* loss, hipStream_t s) {
+  const int T = batch * seq;
+  const int count = batch * (seq - 1);
+  const float coef = count > 0 ? loss_scale / (float)count : 0.0f;
+  hipLaunchKernelGGL(ce_row_kernel, dim3(T), dim3(256), 0, s, logits, ids, seq, V, coef, dlogits, row_loss);
+  hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(256), 0, s, row_loss, T, count > 0 ? 1.0f / (float)count : 0.0f,
+                     loss);
+  return hipGetLastError();
+}
+
+hipError_t zero_f32(float* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int grid = (int)std::min<int64_t>((n + 255) / 256, 8192);
+  hipLaunchKernelGGL(fill_kernel, dim3(grid), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+}  // namespace lsf

@@ -1,0 +1,420 @@
+// Fused NF4-dequant bf16 MFMA GEMMs for gfx950.
+//
+// Forward (NT):  C[M, N] = A[M, K] . deq(W)[N, K]^T  (+ LoRA, + epilogue)
+// Backward (NN): C[M, N] = A[M, K] . deq(W)[K, N]    (the input gradient
+//                dX = dY W through the frozen weight; W gets no gradient)
+//
+// The frozen weight is never materialised in HBM: every 128x64 (NT) or
+// 64x128 (NN) weight tile is read as packed 4-bit codes plus one fp32 absmax
+// per 64-element block, decoded in registers to exactly the bf16 values
+// nf4_dequantize writes (bf16_rne(level * absmax)), and staged in LDS for the
+// MFMA.  The LoRA side path is folded in as extra contraction steps: the
+// rank-r activations U (already scaled) and the adapter matrix form a 64-wide
+// extension of A and W, so the scaled add happens inside the accumulator.
+//
+// Tiling: 256 threads = 4 waves (2 x 2), 128 x 128 C tile, 64-deep k tiles,
+// v_mfma_f32_16x16x32_bf16, LDS double-buffered (64 KB per workgroup, two
+// workgroups per CU).  Split-K over grid.z with a fixed-order reduction keeps
+// results deterministic.
+#include "common.h"
+#include "kernels.h"
+
+namespace lsf {
+namespace {
+
+constexpr int BM = 128, BN = 128, BK = 64, NTHR = 256;
+constexpr int TILE_ELEMS = BM * BK;  // 8192 bf16 per operand tile
+
+// LDS layouts (in bf16 elements).  R8: 64 bf16 per row (8 chunks of 16 B),
+// chunk' = chunk ^ (row & 7).  R16: 128 bf16 per row (16 chunks), chunk' =
+// chunk ^ swz16(row), which keeps both 16-B row reads and 2-B column gathers
+// (8 consecutive rows per lane group) free of bank conflicts.
+__device__ __forceinline__ int swz16(int row) { return (row & 15) ^ (((row >> 4) & 1) << 2); }
+__device__ __forceinline__ int off_r8(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
+__device__ __forceinline__ int off_r16(int row, int chunk) { return row * 128 + ((chunk ^ swz16(row)) << 3); }
+
+__device__ __forceinline__ u32x4 lds_read16(const uint16_t* base, int off) {
+  return *reinterpret_cast<const u32x4*>(base + off);
+}
+__device__ __forceinline__ void lds_write16(uint16_t* base, int off, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(base + off) = v;
+}
+
+__device__ __forceinline__ u32x4 gload16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Row of the weight that feeds physical tile column c (NT).
+__device__ __forceinline__ int64_t nt_wrow(const GemmArgs& g, int ntile, int c) {
+  if (g.pair_I > 0) {
+    const int j = ntile * 64 + (c >> 5) * 16 + (c & 15);
+    return ((c >> 4) & 1) ? (int64_t)g.pair_I + j : (int64_t)j;
+  }
+  return (int64_t)ntile * BN + c;
+}
+
+__device__ __forceinline__ void decode32(float absmax, const u32x4& q, u32x4 out[4]) {
+  const Nf4Table t = nf4_table(absmax);
+  uint32_t o[4];
+  nf4_decode8(t, q.x, o); out[0] = u32x4{o[0], o[1], o[2], o[3]};
+  nf4_decode8(t, q.y, o); out[1] = u32x4{o[0], o[1], o[2], o[3]};
+  nf4_decode8(t, q.z, o); out[2] = u32x4{o[0], o[1], o[2], o[3]};
+  nf4_decode8(t, q.w, o); out[3] = u32x4{o[0], o[1], o[2], o[3]};
+}
+
+// Absmax of the 64-block holding element e of an NF4_DQ weight: 8-bit code
+// times the group's scale plus the group's offset (groups of 256 blocks).
+__device__ __forceinline__ float dq_absmax(const WeightRef& w, int64_t block) {
+  const float2 so = reinterpret_cast<const float2*>(w.dq2)[block >> 8];
+  return (float)w.absq[block] * so.x + so.y;
+}
+
+__device__ __forceinline__ float block_absmax(const WeightRef& w, int64_t elem) {
+  const int64_t b = elem >> 6;
+  return (w.fmt == FMT_NF4_DQ) ? dq_absmax(w, b) : w.absmax[b];
+}
+
+struct Stage {
+  u32x4 a[4];
+  u32x4 b[4];
+  float absmax;
+};
+
+template <bool NN, int FMT>
+__device__ __forceinline__ void load_main(const GemmArgs& g, int m0, int ntile, int k0, int tid, Stage& st) {
+  // A tile: 128 rows x 64 k, 4 chunks of 16 B per thread.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + NTHR * i;
+    const int row = idx >> 3, ch = idx & 7;
+    const int gm = m0 + row;
+    st.a[i] = (gm < g.M) ? gload16(g.A + (int64_t)gm * g.lda + k0 + ch * 8) : u32x4{0, 0, 0, 0};
+  }
+  if constexpr (!NN) {
+    if constexpr (FMT == FMT_BF16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int idx = tid + NTHR * i;
+        const int row = idx >> 3, ch = idx & 7;
+        st.b[i] = gload16(g.W.bf16 + nt_wrow(g, ntile, row) * g.W.ld + k0 + ch * 8);
+      }
+    } else {
+      const int row = tid >> 1, h = tid & 1;
+      const int64_t e = nt_wrow(g, ntile, row) * g.W.ld + k0;
+      st.b[0] = gload16(g.W.packed + (e >> 1) + h * 16);
+      st.absmax = block_absmax(g.W, e);
+    }
+  } else {
+    const int n0 = ntile * BN;
+    if constexpr (FMT == FMT_BF16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int idx = tid + NTHR * i;
+        const int row = idx >> 4, ch = idx & 15;
+        st.b[i] = gload16(g.W.bf16 + (int64_t)(k0 + row) * g.W.ld + n0 + ch * 8);
+      }
+    } else {
+      const int row = tid >> 2, seg = tid & 3;
+      const int64_t e = (int64_t)(k0 + row) * g.W.ld + n0 + seg * 32;
+      st.b[0] = gload16(g.W.packed + (e >> 1));
+      st.absmax = block_absmax(g.W, e);
+    }
+  }
+}
+
+template <bool NN, int FMT>
+__device__ __forceinline__ void store_main(const Stage& st, int tid, uint16_t* As, uint16_t* Bs) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + NTHR * i;
+    lds_write16(As, off_r8(idx >> 3, idx & 7), st.a[i]);
+  }
+  if constexpr (FMT == FMT_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + NTHR * i;
+      if constexpr (!NN) lds_write16(Bs, off_r8(idx >> 3, idx & 7), st.b[i]);
+      else lds_write16(Bs, off_r16(idx >> 4, idx & 15), st.b[i]);
+    }
+  } else {
+    u32x4 d[4];
+    decode32(st.absmax, st.b[0], d);
+    if constexpr (!NN) {
+      const int row = tid >> 1, h = tid & 1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lds_write16(Bs, off_r8(row, h * 4 + i), d[i]);
+    } else {
+      const int row = tid >> 2, seg = tid & 3;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lds_write16(Bs, off_r16(row, seg * 4 + i), d[i]);
+    }
+  }
+}
+
+// LoRA extension tile number `xt` written straight into LDS.
+template <bool NN>
+__device__ void store_ext(const GemmArgs& g, int m0, int ntile, int xt, int tid, uint16_t* As, uint16_t* Bs) {
+  const LoraExt& x = g.ext;
+  const int jb = xt * BK;
+  {  // A: 128 rows x 64 columns of U, scaled, rounded to bf16
+    const int row = tid >> 1, h = tid & 1;
+    const int gm = m0 + row;
+    uint32_t w[16];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      float v[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int j = jb + h * 32 + p * 2 + q;
+        v[q] = (gm < g.M && j < x.kx) ? x.uscale * x.u[(int64_t)gm * x.ldu + j] : 0.0f;
+      }
+      w[p] = pack_bf16x2(v[0], v[1]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lds_write16(As, off_r8(row, h * 4 + i), u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]});
+  }
+  if constexpr (!NN) {  // B: tile row c = weight row, column = U column j
+    const int row = tid >> 1, h = tid & 1;
+    const int64_t wr = nt_wrow(g, ntile, row);
+    int sec = 0;
+    for (int s = 1; s < x.nsec; ++s)
+      if (wr >= x.row_off[s]) sec = s;
+    const float* bm = x.mat[sec];
+    const int64_t lr = wr - x.row_off[sec];
+    uint32_t w[16];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      float v[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int j = jb + h * 32 + p * 2 + q;
+        const int jl = j - sec * x.r;
+        v[q] = (bm != nullptr && j < x.kx && jl >= 0 && jl < x.r) ? bm[lr * x.r + jl] : 0.0f;
+      }
+      w[p] = pack_bf16x2(v[0], v[1]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lds_write16(Bs, off_r8(row, h * 4 + i), u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]});
+  } else {  // B: tile row = U column j (contraction), columns = output n
+    const int row = tid >> 2, seg = tid & 3;
+    const int j = jb + row;
+    const int sec = (x.r > 0) ? j / x.r : 0;
+    const float* am = (j < x.kx && sec < x.nsec) ? x.mat[sec] : nullptr;
+    const int n0 = ntile * BN + seg * 32;
+    uint32_t w[16];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      float v0 = 0.0f, v1 = 0.0f;
+      if (am != nullptr) {
+        const float* src = am + (int64_t)(j - sec * x.r) * x.ldmat + n0 + p * 2;
+        v0 = src[0];
+        v1 = src[1];
+      }
+      w[p] = pack_bf16x2(v0, v1);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lds_write16(Bs, off_r16(row, seg * 4 + i), u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]});
+  }
+}
+
+template <bool NN>
+__device__ __forceinline__ void compute_tile(const uint16_t* As, const uint16_t* Bs, int lane, int wm, int wn,
+                                             f32x4 (&acc)[4][4]) {
+  const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    u32x4 af[4], bf[4];
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf) af[mf] = lds_read16(As, off_r8(wm * 64 + mf * 16 + lr, s * 4 + lg));
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf) {
+      if constexpr (!NN) {
+        bf[nf] = lds_read16(Bs, off_r8(wn * 64 + nf * 16 + lr, s * 4 + lg));
+      } else {
+        const int n = wn * 64 + nf * 16 + lr;
+        const int ch = n >> 3, e = n & 7;
+        uint32_t w[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int c0 = s * 32 + lg * 8 + 2 * p;
+          const uint32_t lo = Bs[off_r16(c0, ch) + e];
+          const uint32_t hi = Bs[off_r16(c0 + 1, ch) + e];
+          w[p] = lo | (hi << 16);
+        }
+        bf[nf] = u32x4{w[0], w[1], w[2], w[3]};
+      }
+    }
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mfma16x16x32(af[mf], bf[nf], acc[mf][nf]);
+  }
+}
+
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+
+template <bool NN>
+__device__ void epilogue(const GemmArgs& g, const EpiArgs& e, const f32x4 (&acc)[4][4], int m0, int ntile,
+                         int lane, int wm, int wn, int z) {
+  const int lr = lane & 15, lg = lane >> 4;
+  if (e.kind == EPI_SWIGLU) {
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+      for (int np = 0; np < 2; ++np) {
+        const int j = ntile * 64 + (2 * wn + np) * 16 + lr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + wm * 64 + mf * 16 + lg * 4 + i;
+          if (m >= g.M) continue;
+          const float gv = acc[mf][2 * np][i], uv = acc[mf][2 * np + 1][i];
+          static_cast<uint16_t*>(e.C)[(int64_t)m * e.ldc + j] = f32_to_bf16(silu(gv) * uv);
+          if (e.g != nullptr) {
+            e.g[(int64_t)m * e.ldgu + j] = f32_to_bf16(gv);
+            e.u[(int64_t)m * e.ldgu + j] = f32_to_bf16(uv);
+          }
+        }
+      }
+    return;
+  }
+#pragma unroll
+  for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf) {
+      const int n = ntile * BN + wn * 64 + nf * 16 + lr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wm * 64 + mf * 16 + lg * 4 + i;
+        if (m >= g.M) continue;
+        const float v = acc[mf][nf][i];
+        switch (e.kind) {
+          case EPI_F32:
+            static_cast<float*>(e.C)[(int64_t)z * g.M * g.N + (int64_t)m * e.ldc + n] = v;
+            break;
+          case EPI_BF16:
+            static_cast<uint16_t*>(e.C)[(int64_t)m * e.ldc + n] = f32_to_bf16(v);
+            break;
+          case EPI_RESID_BF16:
+            static_cast<uint16_t*>(e.C)[(int64_t)m * e.ldc + n] =
+                f32_to_bf16(bf16_to_f32(e.R[(int64_t)m * e.ldr + n]) + v);
+            break;
+          case EPI_SWIGLU_BWD: {
+            const float gv = bf16_to_f32(e.g[(int64_t)m * e.ldgu + n]);
+            const float uv = bf16_to_f32(e.u[(int64_t)m * e.ldgu + n]);
+            const float sg = 1.0f / (1.0f + __expf(-gv));
+            uint16_t* C = static_cast<uint16_t*>(e.C);
+            C[(int64_t)m * e.ldc + n] = f32_to_bf16(v * uv * sg * (1.0f + gv * (1.0f - sg)));
+            C[(int64_t)m * e.ldc + g.N + n] = f32_to_bf16(v * gv * sg);
+            break;
+          }
+        }
+      }
+    }
+}
+
+template <bool NN, int FMT>
+__global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs g, EpiArgs e) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2 * TILE_ELEMS];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  const int mt = (g.M + BM - 1) / BM, nt = g.N / BN;
+  const int total = mt * nt;
+  int t = blockIdx.x;
+  if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);  // keep an XCD on neighbouring tiles
+  const int mtile = t % mt, ntile = t / mt;
+  const int m0 = mtile * BM;
+
+  const int z = blockIdx.z;
+  const int kch = g.K / BK;
+  const int per = (kch + g.splits - 1) / g.splits;
+  const int kb = z * per;
+  const int ke = min(kch, kb + per);
+  const int nmain = max(0, ke - kb);
+  const int next = (z == g.splits - 1 && g.ext.kx > 0) ? (g.ext.kx + BK - 1) / BK : 0;
+  const int iters = nmain + next;
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+
+  Stage st;
+  if (iters > 0) {
+    if (nmain > 0) {
+      load_main<NN, FMT>(g, m0, ntile, kb * BK, tid, st);
+      store_main<NN, FMT>(st, tid, lds[0], lds[0] + TILE_ELEMS);
+    } else {
+      store_ext<NN>(g, m0, ntile, 0, tid, lds[0], lds[0] + TILE_ELEMS);
+    }
+  }
+  __syncthreads();
+  for (int it = 0; it < iters; ++it) {
+    const int nx = it + 1;
+    const bool pre = nx < nmain;
+    if (pre) load_main<NN, FMT>(g, m0, ntile, (kb + nx) * BK, tid, st);
+    uint16_t* cur = lds[it & 1];
+    compute_tile<NN>(cur, cur + TILE_ELEMS, lane, wm, wn, acc);
+    if (nx < iters) {
+      uint16_t* nb = lds[nx & 1];
+      if (pre) store_main<NN, FMT>(st, tid, nb, nb + TILE_ELEMS);
+      else store_ext<NN>(g, m0, ntile, nx - nmain, tid, nb, nb + TILE_ELEMS);
+    }
+    __syncthreads();
+  }
+  epilogue<NN>(g, e, acc, m0, ntile, lane, wm, wn, z);
+}
+
+template <bool NN>
+hipError_t launch(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
+  const int mt = (g.M + BM - 1) / BM, nt = g.N / BN;
+  dim3 grid(mt * nt, 1, g.splits), block(NTHR);
+  switch (g.W.fmt) {
+    case FMT_NF4: hipLaunchKernelGGL((gemm_kernel<NN, FMT_NF4>), grid, block, 0, s, g, e); break;
+    case FMT_BF16: hipLaunchKernelGGL((gemm_kernel<NN, FMT_BF16>), grid, block, 0, s, g, e); break;
+    case FMT_NF4_DQ: hipLaunchKernelGGL((gemm_kernel<NN, FMT_NF4_DQ>), grid, block, 0, s, g, e); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+__global__ void splitk_reduce_kernel(const float* part, int splits, int M, int N, EpiArgs e) {
+  const int64_t MN = (int64_t)M * N;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < MN; i += (int64_t)gridDim.x * blockDim.x) {
+    float v = part[i];
+    for (int zz = 1; zz < splits; ++zz) v += part[zz * MN + i];
+    const int64_t m = i / N, n = i - m * N;
+    switch (e.kind) {
+      case EPI_F32: static_cast<float*>(e.C)[m * e.ldc + n] = v; break;
+      case EPI_BF16: static_cast<uint16_t*>(e.C)[m * e.ldc + n] = f32_to_bf16(v); break;
+      case EPI_RESID_BF16:
+        static_cast<uint16_t*>(e.C)[m * e.ldc + n] = f32_to_bf16(bf16_to_f32(e.R[m * e.ldr + n]) + v);
+        break;
+      case EPI_SWIGLU_BWD: {
+        const float gv = bf16_to_f32(e.g[m * e.ldgu + n]);
+        const float uv = bf16_to_f32(e.u[m * e.ldgu + n]);
+        const float sg = 1.0f / (1.0f + __expf(-gv));
+        uint16_t* C = static_cast<uint16_t*>(e.C);
+        C[m * e.ldc + n] = f32_to_bf16(v * uv * sg * (1.0f + gv * (1.0f - sg)));
+        C[m * e.ldc + N + n] = f32_to_bf16(v * gv * sg);
+        break;
+      }
+      default: break;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t gemm_nt(const GemmArgs& g, const EpiArgs& e, hipStream_t s) { return launch<false>(g, e, s); }
+hipError_t gemm_nn(const GemmArgs& g, const EpiArgs& e, hipStream_t s) { return launch<true>(g, e, s); }
+
+hipError_t splitk_reduce(const float* part, int splits, int M, int N, const EpiArgs& e, hipStream_t s) {
+  const int64_t MN = (int64_t)M * N;
+  const int blocks = (int)std::min<int64_t>((MN + 255) / 256, 4096);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, part, splits, M, N, e);
+  return hipGetLastError();
+}
+
+}  // namespace lsf

@@ -1,0 +1,40 @@
+// Layer composition (host side, internal).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "../../include/lsf.h"
+#include "kernels.h"
+
+namespace lsf {
+
+// Scratch layout of one decoder layer's forward + recompute + backward.
+struct LayerWs {
+  uint16_t *h1, *qkv, *att, *x2, *h2, *g, *u, *a, *y;
+  float *rstd1, *rstd2, *lse, *Uqkv, *Uo, *Ugu, *Ud;
+  float2* rope;
+  uint16_t *dgu, *dh, *dx2, *dob, *dqkv;
+  float *dU, *attn_scratch, *part;
+  size_t part_floats;
+  static size_t bytes(const lsf_layer_cfg& c);
+  static LayerWs carve(const lsf_layer_cfg& c, void* base);
+};
+
+WeightRef weight_ref(const lsf_weight& w, int fmt, int64_t ld);
+
+// x -> y.  save keeps every intermediate the backward needs; rope_ready skips
+// rebuilding the RoPE table already in ws.rope.  y may be NULL when only the
+// saved state is wanted (the recompute inside the backward).
+hipError_t layer_forward(const lsf_layer_cfg& c, const lsf_layer_weights& w, const lsf_layer_lora* lora,
+                         const uint16_t* x, uint16_t* y, const LayerWs& ws, bool save, bool rope_ready,
+                         hipStream_t s);
+hipError_t layer_backward(const lsf_layer_cfg& c, const lsf_layer_weights& w, const lsf_layer_lora* lora,
+                          const uint16_t* x, const uint16_t* dy, uint16_t* dx, const LayerWs& ws, bool rope_ready,
+                          hipStream_t s);
+
+// Split count for a GEMM with `tiles` output tiles and contraction K.
+int choose_splits(int tiles, int K);
+
+// One GEMM with split-K and the final epilogue handled.
+hipError_t run_gemm(bool nn, GemmArgs g, const EpiArgs& e, float* part, size_t part_floats, hipStream_t s);
+
+}  // namespace lsf

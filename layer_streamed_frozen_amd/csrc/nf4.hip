@@ -1,0 +1,100 @@
+// NF4 quantise and dequantise kernels.
+//
+// Quantise: 16 lanes own one 64-element block (a float4 each), reduce max|w|
+// across the 16 lanes, divide each element by the absmax with IEEE fp32
+// division and count how many fp32 midpoints of the 16 levels lie strictly
+// below it (a tie goes to the lower level).  Codes are packed two per byte,
+// the first element in the high nibble.
+//
+// Dequantise: a thread owns 32 consecutive elements (16 packed bytes, one
+// absmax) and decodes them with the same table routine the GEMMs use, so the
+// bytes this kernel writes are exactly the bf16 weights the GEMMs multiply.
+#include "common.h"
+#include "kernels.h"
+
+namespace lsf {
+namespace {
+
+struct Mid {
+  float t[15];
+};
+constexpr Mid make_mid() {
+  constexpr float L[16] = {
+      -1.0f, -0.6961928009986877f, -0.5250730514526367f, -0.39491748809814453f,
+      -0.28444138169288635f, -0.18477343022823334f, -0.09105003625154495f, 0.0f,
+      0.07958029955625534f, 0.16093020141124725f, 0.24611230194568634f, 0.33791524171829224f,
+      0.44070982933044434f, 0.5626170039176941f, 0.7229568362236023f, 1.0f};
+  Mid m{};
+  for (int k = 0; k < 15; ++k) m.t[k] = (L[k] + L[k + 1]) * 0.5f;  // fp32 sum, exact halving
+  return m;
+}
+constexpr Mid kMid = make_mid();
+
+__device__ __forceinline__ uint32_t code_of(float x) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int k = 0; k < 15; ++k) c += (x > kMid.t[k]) ? 1u : 0u;
+  return c;
+}
+
+__global__ __launch_bounds__(256) void nf4_quantize_kernel(const float* __restrict__ w, int64_t nblocks,
+                                                           uint8_t* __restrict__ packed,
+                                                           float* __restrict__ absmax) {
+  const int sub = threadIdx.x & 15;
+  const int64_t groups_per_grid = (int64_t)gridDim.x * (blockDim.x >> 4);
+  for (int64_t b = (int64_t)blockIdx.x * (blockDim.x >> 4) + (threadIdx.x >> 4); b < nblocks + 0;
+       b += groups_per_grid) {
+    const float4 v = reinterpret_cast<const float4*>(w + b * 64)[sub];
+    float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
+    uint32_t c0 = 7, c1 = 7, c2 = 7, c3 = 7;
+    if (m > 0.0f) {
+      c0 = code_of(v.x / m);
+      c1 = code_of(v.y / m);
+      c2 = code_of(v.z / m);
+      c3 = code_of(v.w / m);
+    }
+    // elements 4*sub .. 4*sub+3 -> bytes 2*sub, 2*sub+1 (little-endian u16)
+    const uint16_t out = (uint16_t)(((c0 << 4) | c1) | (((c2 << 4) | c3) << 8));
+    reinterpret_cast<uint16_t*>(packed + b * 32)[sub] = out;
+    if (sub == 0) absmax[b] = m;
+  }
+}
+
+__global__ __launch_bounds__(256) void nf4_dequantize_kernel(const uint8_t* __restrict__ packed,
+                                                             const float* __restrict__ absmax, int64_t nunits,
+                                                             uint16_t* __restrict__ out) {
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < nunits; u += (int64_t)gridDim.x * blockDim.x) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(packed + u * 16);
+    const Nf4Table t = nf4_table(absmax[u >> 1]);
+    uint32_t o[4];
+    u32x4* dst = reinterpret_cast<u32x4*>(out + u * 32);
+    nf4_decode8(t, q.x, o); dst[0] = u32x4{o[0], o[1], o[2], o[3]};
+    nf4_decode8(t, q.y, o); dst[1] = u32x4{o[0], o[1], o[2], o[3]};
+    nf4_decode8(t, q.z, o); dst[2] = u32x4{o[0], o[1], o[2], o[3]};
+    nf4_decode8(t, q.w, o); dst[3] = u32x4{o[0], o[1], o[2], o[3]};
+  }
+}
+
+}  // namespace
+
+hipError_t nf4_quantize_launch(const float* w, int64_t n, uint8_t* packed, float* absmax, hipStream_t s) {
+  const int64_t nblocks = n / 64;
+  if (nblocks == 0) return hipSuccess;
+  const int64_t want = (nblocks + 15) / 16;
+  const int grid = (int)std::min<int64_t>(want, 65536);
+  hipLaunchKernelGGL(nf4_quantize_kernel, dim3(grid), dim3(256), 0, s, w, nblocks, packed, absmax);
+  return hipGetLastError();
+}
+
+hipError_t nf4_dequantize_launch(const uint8_t* packed, const float* absmax, int64_t n, uint16_t* out,
+                                 hipStream_t s) {
+  const int64_t units = n / 32;
+  if (units == 0) return hipSuccess;
+  const int grid = (int)std::min<int64_t>((units + 255) / 256, 65536);
+  hipLaunchKernelGGL(nf4_dequantize_kernel, dim3(grid), dim3(256), 0, s, packed, absmax, units, out);
+  return hipGetLastError();
+}
+
+}  // namespace lsf

@@ -1,0 +1,247 @@
+"""Host-side plumbing: layer shapes, frozen-weight stores and adapter sets.
+
+PyTorch provides the memory (device tensors, page-locked host tensors); every
+quantisation and every byte of the layer blobs is produced by the HIP library
+(``nf4_quantize``) or copied verbatim.  Seeded inputs come from ``synth``.
+"""
+import ctypes
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import binding as B
+from . import synth
+
+PROJ = ("q", "k", "v", "o", "gate", "up", "down")
+
+
+@dataclass
+class LayerShape:
+    hidden: int = 4096
+    intermediate: int = 14336
+    n_heads: int = 32
+    n_kv_heads: int = 8
+    head_dim: int = 128
+    rank: int = 16
+    alpha: float = 16.0
+    rope_theta: float = 500000.0
+    rms_eps: float = 1e-5
+
+    @property
+    def lora_scale(self):
+        return self.alpha / self.rank
+
+    def proj_shapes(self):
+        H, I = self.hidden, self.intermediate
+        q, kv = self.n_heads * self.head_dim, self.n_kv_heads * self.head_dim
+        return {"q": (q, H), "k": (kv, H), "v": (kv, H), "o": (H, q), "gate": (I, H), "up": (I, H), "down": (H, I)}
+
+    def cfg(self, batch, seq):
+        return B.layer_cfg(self.hidden, self.intermediate, self.n_heads, self.n_kv_heads, self.head_dim, self.rank,
+                           self.lora_scale, self.rope_theta, self.rms_eps, batch, seq)
+
+
+# The decoder layer of a Llama-3.1-8B-shaped model (LoRA rank 16, alpha 16).
+LLAMA8B = LayerShape()
+
+
+def layer_weights_fp32(prefix, shape, std=0.02):
+    """Seeded frozen weights of one layer (host fp32, N(0, std)); norms 1.0."""
+    W = {n: synth.normal(f"{prefix}.{n}.W", s, std) for n, s in shape.proj_shapes().items()}
+    one = np.full(shape.hidden, 0x3F80, dtype=np.uint16)  # bf16 1.0
+    W["norm1"] = one.copy()
+    W["norm2"] = one.copy()
+    return W
+
+
+def random_norms(prefix, shape):
+    """Non-trivial bf16 norm weights for tests (1 + N(0, 0.1), bf16-exact)."""
+    out = {}
+    for k in ("norm1", "norm2"):
+        _, bits = synth.bf16_exact(1.0 + synth.normal(f"{prefix}.{k}", (shape.hidden,), 0.1))
+        out[k] = bits
+    return out
+
+
+def _sections(W):
+    return [np.concatenate([W["q"], W["k"], W["v"]], axis=0), W["o"],
+            np.concatenate([W["gate"], W["up"]], axis=0), W["down"]]
+
+
+def build_layer_blob(shape, W, fmt=B.FMT_NF4, device="cuda", out=None):
+    """Assemble one layer blob on the device.
+
+    NF4: every section is quantised by the library's nf4_quantize.  BF16: the
+    fp32 weights must already be bfloat16-exact; their bits are copied.
+    Returns a uint8 device tensor of ``stride`` bytes (or fills ``out``).
+    """
+    cfg = shape.cfg(1, 1)
+    lay = B.layer_blob_layout(cfg, fmt)
+    blob = out if out is not None else torch.zeros(lay.stride, dtype=torch.uint8, device=device)
+    for i, w in enumerate(_sections(W)):
+        n = w.size
+        wd = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).to(device)
+        if fmt == B.FMT_NF4:
+            packed = blob[lay.off[i]: lay.off[i] + n // 2]
+            absmax = blob[lay.off[4 + i]: lay.off[4 + i] + n // 16].view(torch.float32)
+            B.nf4_quantize(wd.reshape(-1), packed, absmax)
+        elif fmt == B.FMT_BF16:
+            bits = (wd.reshape(-1).view(torch.int32) >> 16).to(torch.int16)
+            blob[lay.off[i]: lay.off[i] + 2 * n].view(torch.int16).copy_(bits)
+        else:
+            raise ValueError("use nf4dq.build_layer_blob for the double-quantised format")
+        del wd
+    for k, sec in (("norm1", 8), ("norm2", 9)):
+        nb = torch.from_numpy(np.ascontiguousarray(W[k]).view(np.int16)).to(device)
+        blob[lay.off[sec]: lay.off[sec] + 2 * shape.hidden].view(torch.int16).copy_(nb)
+    return blob
+
+
+class Store:
+    """The frozen decoder stack: one blob per layer, in pinned host memory
+    (streamed mode) and optionally also resident on the device."""
+
+    def __init__(self, shape, n_layers, fmt=B.FMT_NF4, device="cuda", resident=False, pinned=True,
+                 weights_fn=None, prefix="layer"):
+        self.shape, self.n_layers, self.fmt = shape, n_layers, fmt
+        cfg = shape.cfg(1, 1)
+        self.layout = B.layer_blob_layout(cfg, fmt)
+        self.stride = self.layout.stride
+        total = self.stride * n_layers
+        self.host = torch.empty(total, dtype=torch.uint8, pin_memory=pinned)
+        self.dev = torch.empty(total, dtype=torch.uint8, device=device) if resident else None
+        tmp = torch.zeros(self.stride, dtype=torch.uint8, device=device)
+        for i in range(n_layers):
+            W = weights_fn(i) if weights_fn is not None else layer_weights_fp32(f"{prefix}{i}", shape)
+            tmp.zero_()
+            build_layer_blob(shape, W, fmt, device, out=tmp)
+            if self.dev is not None:
+                self.dev[i * self.stride:(i + 1) * self.stride].copy_(tmp)
+            self.host[i * self.stride:(i + 1) * self.stride].copy_(tmp.cpu())
+        torch.cuda.synchronize()
+
+    def blob_bytes(self):
+        return self.layout.bytes
+
+
+class LoraSet:
+    """Trainable adapters of a stack: fp32 A [r, in], B [out, r] and their
+    gradients, per layer and projection (``targets`` picks the projections)."""
+
+    def __init__(self, shape, n_layers, targets=PROJ, device="cuda", prefix="lora", b_zero=False):
+        self.shape, self.n_layers, self.targets = shape, n_layers, tuple(targets)
+        self.A, self.B, self.dA, self.dB = [], [], [], []
+        r = shape.rank
+        for i in range(n_layers):
+            a, b, da, db = {}, {}, {}, {}
+            for n, (o, inn) in shape.proj_shapes().items():
+                if n not in self.targets:
+                    continue
+                lim = 1.0 / np.sqrt(inn)
+                a[n] = torch.from_numpy(synth.uniform(f"{prefix}{i}.{n}.A", (r, inn), -lim, lim)).to(device)
+                bb = synth.normal(f"{prefix}{i}.{n}.B", (o, r), 0.01)
+                b[n] = torch.from_numpy(np.zeros_like(bb) if b_zero else bb).to(device)
+                da[n] = torch.zeros((r, inn), dtype=torch.float32, device=device)
+                db[n] = torch.zeros((o, r), dtype=torch.float32, device=device)
+            self.A.append(a)
+            self.B.append(b)
+            self.dA.append(da)
+            self.dB.append(db)
+        self._arr = None
+
+    def struct(self, i, enabled=True, grads=True):
+        L = B.LayerLora()
+        for n in PROJ:
+            p = getattr(L, n)
+            if n in self.targets:
+                p.A, p.B = B.ptr(self.A[i][n]), B.ptr(self.B[i][n])
+                if grads:
+                    p.dA, p.dB = B.ptr(self.dA[i][n]), B.ptr(self.dB[i][n])
+        L.enabled = 1 if enabled else 0
+        return L
+
+    def array(self, enabled=True, grads=True):
+        arr = (B.LayerLora * self.n_layers)()
+        for i in range(self.n_layers):
+            arr[i] = self.struct(i, enabled, grads)
+        self._arr = arr
+        return arr
+
+    def zero_grads(self):
+        for i in range(self.n_layers):
+            for n in self.targets:
+                self.dA[i][n].zero_()
+                self.dB[i][n].zero_()
+
+    def numpy(self, i, enabled=True):
+        """LoRA dict in the oracle's form (fp64 numpy), None where absent."""
+        if not enabled:
+            return None
+        return {n: ((self.A[i][n].double().cpu().numpy(), self.B[i][n].double().cpu().numpy())
+                    if n in self.targets else None) for n in PROJ}
+
+    def grads_numpy(self, i):
+        return {n: (self.dA[i][n].double().cpu().numpy(), self.dB[i][n].double().cpu().numpy())
+                for n in self.targets}
+
+
+class Stack:
+    """A streamed stack: store + two device buffers + streams + handle."""
+
+    def __init__(self, shape, store, batch, seq, vocab, flags=0, device="cuda"):
+        self.shape, self.store, self.batch, self.seq, self.vocab = shape, store, batch, seq, vocab
+        self.cfg = shape.cfg(batch, seq)
+        nbytes = store.layout.bytes
+        self.bufs = [torch.empty(nbytes, dtype=torch.uint8, device=device) for _ in range(2)]
+        self.compute = torch.cuda.current_stream()
+        self.copy = torch.cuda.Stream()
+        d = B.StackDesc()
+        d.n_layers = store.n_layers
+        d.format = store.fmt
+        d.blob_stride = store.stride
+        d.host_store = store.host.data_ptr()
+        d.dev_buf[0] = self.bufs[0].data_ptr()
+        d.dev_buf[1] = self.bufs[1].data_ptr()
+        d.resident_store = store.dev.data_ptr() if store.dev is not None else None
+        d.compute = self.compute.cuda_stream
+        d.copy = self.copy.cuda_stream
+        d.flags = flags
+        self.handle = B.stack_create(self.cfg, d)
+        T = batch * seq
+        H = shape.hidden
+        self.ws = torch.empty(B.stack_workspace_bytes(self.cfg, vocab), dtype=torch.uint8, device=device)
+        self.ckpt = torch.empty((store.n_layers + 1, T, H), dtype=torch.bfloat16, device=device)
+        self.logits = torch.empty((T, vocab), dtype=torch.float32, device=device)
+        self.loss = torch.zeros(1, dtype=torch.float32, device=device)
+
+    def step(self, ids, embed, final_norm, lm_head, lora_arr, mode=B.MODE_STREAMED, loss_scale=1.0):
+        io = B.StackIO()
+        io.ids = ids.data_ptr()
+        io.embed = embed.data_ptr()
+        io.final_norm = final_norm.data_ptr()
+        io.lm_head = lm_head.data_ptr()
+        io.vocab = self.vocab
+        io.lora = ctypes.cast(lora_arr, ctypes.POINTER(B.LayerLora))
+        io.ckpt = self.ckpt.data_ptr()
+        io.logits = self.logits.data_ptr()
+        io.loss = self.loss.data_ptr()
+        io.ws = self.ws.data_ptr()
+        io.ws_bytes = self.ws.numel()
+        io.loss_scale = loss_scale
+        io.mode = mode
+        B.stream_stack_step(self.handle, io)
+
+    def stats(self):
+        return B.stack_stats(self.handle)
+
+    def close(self):
+        if self.handle is not None:
+            B.stack_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
