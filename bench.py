@@ -1,0 +1,254 @@
+"""Throughput of the streamed NF4 + LoRA training step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload stack1|stack4]
+
+Workload (default "stack1"): 32 Llama-3.1-8B-shaped decoder layers (hidden
+4096, intermediate 14336, 32 query / 8 kv heads of 128, RoPE theta 500000),
+frozen base NF4-quantised (64-element blocks, fp32 absmax) in page-locked host
+memory, streamed through two device buffers; LoRA rank 16 (alpha 16) on q, k,
+v, o, gate, up, down; resident untied bf16 embedding and lm_head over a
+128256-token vocabulary; one sequence of 512 random token ids per step;
+cross-entropy loss; forward, head, and recomputing backward (all LoRA
+gradients).  "stack4" is 4 sequences of 512 per micro-batch and 4 micro-batches
+(gradient accumulation) per step.  Inputs and weights are seeded synthetic data.
+
+Prints one JSON line.  ``value`` is tokens per second over the timed steps,
+with every input already resident (the frozen store in pinned host memory is
+the method's input; its per-step host-to-device traffic is part of the step).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "train tokens/sec (fwd+bwd) streamed 8B-shape NF4+LoRA, seq 512; H2D GB/s"
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBPS = 8000.0
+PCIE5_X16_GBPS = 63.0            # theoretical per direction after 128b/130b encoding
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", choices=["stack1", "stack4"], default="stack1")
+    p.add_argument("--layers", type=int, default=32)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-timing", action="store_true", help="skip the per-kernel event probes")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def gemm_flops(T, shape):
+    H, I = shape.hidden, shape.intermediate
+    q, kv = shape.n_heads * shape.head_dim, shape.n_kv_heads * shape.head_dim
+    n = {"qkv": (q + 2 * kv) * H, "o": H * q, "gate_up": 2 * I * H, "down": H * I}
+    return {k: 2.0 * T * v for k, v in n.items()}
+
+
+def measure_link_peak(torch, nbytes=1 << 30, reps=5):
+    """Best pinned host -> device copy rate (GB/s) of one large hipMemcpyAsync."""
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    best = 0.0
+    with torch.cuda.stream(s):
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            dst.copy_(src, non_blocking=True)
+            e1.record(s)
+            e1.synchronize()
+            best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src, dst
+    return best
+
+
+def cpu_baseline(shape, T_layer=512):
+    """The oracle (fp64 NumPy) on a bounded sample of the same workload: one
+    decoder layer forward + backward over 512 tokens, and the head over a
+    1/16 slice of the vocabulary; scaled to the full step."""
+    from layer_streamed_frozen_amd import store as S
+    from layer_streamed_frozen_amd import synth
+    from oracle import model as M
+    from oracle import nf4 as onf4
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 0) for d in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count()
+    W = S.layer_weights_fp32("layer0", shape)
+    dense = {}
+    for n in S.PROJ:
+        p, a = onf4.nf4_quantize(W[n])
+        dense[n] = onf4.nf4_dequantize(p, a, W[n].shape).astype(np.float64)
+    dense["norm1"] = np.ones(shape.hidden)
+    dense["norm2"] = np.ones(shape.hidden)
+    ldict = {}  # the same adapter values LoraSet draws for layer 0
+    for n, (o, inn) in shape.proj_shapes().items():
+        lim = 1.0 / np.sqrt(inn)
+        ldict[n] = (synth.uniform(f"lora0.{n}.A", (shape.rank, inn), -lim, lim).astype(np.float64),
+                    synth.normal(f"lora0.{n}.B", (o, shape.rank), 0.01).astype(np.float64))
+    oc = M.LayerShape(shape.hidden, shape.intermediate, shape.n_heads, shape.n_kv_heads, shape.head_dim,
+                      rms_eps=shape.rms_eps, rope_theta=shape.rope_theta, lora_scale=shape.lora_scale)
+    x = synth.normal("cpu.x", (1, T_layer, shape.hidden)).astype(np.float64)
+    dy = synth.normal("cpu.dy", (1, T_layer, shape.hidden)).astype(np.float64)
+    t0 = time.perf_counter()
+    y, cache = M.layer_fwd(x, dense, ldict, oc)
+    M.layer_bwd(dy, dense, ldict, oc, cache)
+    t_layer = time.perf_counter() - t0
+    V16 = 128256 // 16
+    head = synth.normal("cpu.head", (V16, shape.hidden), 0.02).astype(np.float64)
+    h = synth.normal("cpu.h", (T_layer, shape.hidden)).astype(np.float64)
+    ids = synth.token_ids("cpu.ids", (1, T_layer), V16)
+    t0 = time.perf_counter()
+    logits = h @ head.T
+    lab, val = M.shifted_labels(ids)
+    _, dz = M.cross_entropy_fwd_bwd(logits, lab, val)
+    _ = dz @ head
+    t_head = (time.perf_counter() - t0) * 16
+    t_step = 32 * t_layer + t_head
+    return {"value": T_layer / t_step, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"one 8B-shaped layer fwd+bwd on {T_layer} tokens ({t_layer:.2f} s, x32 layers) plus "
+                       f"head fwd+CE+dX on a 1/16 vocabulary slice ({t_head / 16:.2f} s, x16); fp64 NumPy"),
+            "seconds_measured": round(t_layer + t_head / 16, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); multi-GPU data-parallel sharding "
+              f"is not built in this library.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from layer_streamed_frozen_amd import binding as B
+    from layer_streamed_frozen_amd import store as S
+    from layer_streamed_frozen_amd import synth
+
+    B.lib()  # fail loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+    shape = S.LLAMA8B
+    L, V, seq = args.layers, 128256, 512
+    batch, accum = (1, 1) if args.workload == "stack1" else (4, 4)
+    T = batch * seq
+
+    t0 = time.time()
+    log(f"building the NF4 store: {L} layers")
+    store = S.Store(shape, L, resident=False, pinned=True)
+    log(f"store built in {time.time() - t0:.1f}s: {store.stride * L / 1e9:.3f} GB pinned, "
+        f"blob {store.blob_bytes()} B")
+    lora = S.LoraSet(shape, L)
+    H = shape.hidden
+    emb = torch.from_numpy(synth.bf16_exact(synth.normal("embed", (V, H), 1.0))[1].view(np.int16)) \
+        .view(torch.bfloat16).cuda()
+    head = torch.from_numpy(synth.bf16_exact(synth.normal("lm_head", (V, H), 0.02))[1].view(np.int16)) \
+        .view(torch.bfloat16).cuda()
+    fnorm = torch.ones(H, dtype=torch.bfloat16, device="cuda")
+    ids = [torch.from_numpy(synth.token_ids(f"ids{m}", (batch, seq), V)).cuda() for m in range(accum)]
+    flags = 0 if args.no_timing else B.STACK_TIMING
+    stack = S.Stack(shape, store, batch, seq, V, flags=flags)
+    arr = lora.array()
+    torch.cuda.synchronize()
+
+    def step():
+        for m in range(accum):
+            mode = B.MODE_STREAMED | (B.MODE_ZERO_GRADS if m == 0 else 0)
+            stack.step(ids[m], emb, fnorm, head, arr, mode=mode, loss_scale=1.0 / accum)
+
+    log("measuring the host link")
+    link_peak = measure_link_peak(torch)
+    log(f"pinned H2D peak {link_peak:.1f} GB/s; warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    B.stack_reset_stats(stack.handle)
+    torch.cuda.reset_peak_memory_stats()
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    st = stack.stats()
+    loss = float(stack.loss.item())
+    tokens = args.steps * accum * T
+    value = tokens / elapsed
+    ms_step = elapsed / args.steps * 1e3
+    log(f"{value:.1f} tok/s, {ms_step:.2f} ms/step, loss {loss:.4f}")
+
+    bytes_step = st.bytes / args.steps
+    h2d = {"bytes_per_step": int(bytes_step), "copies_per_step": st.copies / args.steps,
+           "GBps_over_step": bytes_step / (ms_step * 1e-3) / 1e9,
+           "measured_link_peak_GBps": round(link_peak, 2), "pcie5_x16_theoretical_GBps": PCIE5_X16_GBPS}
+    if st.copy_ms > 0:
+        busy = st.bytes / (st.copy_ms * 1e-3) / 1e9
+        h2d.update({"GBps_while_copying": round(busy, 2), "frac_of_measured_peak": round(busy / link_peak, 4),
+                    "frac_of_theoretical": round(busy / PCIE5_X16_GBPS, 4),
+                    "copy_busy_frac_of_step": round(st.copy_ms / (elapsed * 1e3), 4),
+                    "compute_wait_ms_per_step": round(st.wait_ms / args.steps, 3)})
+    h2d["GBps_over_step"] = round(h2d["GBps_over_step"], 2)
+
+    flops = gemm_flops(T, shape)
+    kernels, roof = {}, None
+    for k, name in enumerate(B.KERNELS):
+        n = st.kernel_launches[k]
+        if n == 0:
+            continue
+        avg_ms = st.kernel_ms[k] / n
+        ent = {"launches_per_step": n / args.steps, "avg_us": round(avg_ms * 1e3, 2),
+               "ms_per_step": round(st.kernel_ms[k] / args.steps, 3)}
+        base = name.rsplit("_", 1)[0]
+        if base in flops:
+            tf = flops[base] / (avg_ms * 1e-3) / 1e12
+            ent["TFLOPs"] = round(tf, 1)
+            ent["mfma_frac"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
+        kernels[name] = ent
+    dom = "gate_up_fwd"
+    if dom in kernels:
+        k = B.KERNELS.index(dom)
+        avg = st.kernel_ms[k] / st.kernel_launches[k] * 1e-3
+        ach = flops["gate_up"] / avg / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": f"fused NF4 gate|up GEMM + SwiGLU epilogue, {T}x{2 * shape.intermediate}x{H}",
+                "flop_per_launch": flops["gate_up"], "avg_launch_us": round(avg * 1e6, 2)}
+    gemm_ms = sum(st.kernel_ms[B.KERNELS.index(n)] for n in B.KERNELS if n.rsplit("_", 1)[0] in flops)
+    gemm_flop = sum(flops[n.rsplit("_", 1)[0]] * st.kernel_launches[B.KERNELS.index(n)]
+                    for n in B.KERNELS if n.rsplit("_", 1)[0] in flops)
+    layer_gemms = None
+    if gemm_ms > 0:
+        tf = gemm_flop / (gemm_ms * 1e-3) / 1e12
+        layer_gemms = {"TFLOPs": round(tf, 1), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                       "ms_per_step": round(gemm_ms / args.steps, 2)}
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded random weights and token ids)",
+        "config": {"workload": (f"streamed {L}-layer Llama-3.1-8B-shaped stack, NF4 base (bs 64, fp32 absmax), "
+                                f"LoRA r16 on q,k,v,o,gate,up,down, vocab {V}, "
+                                f"batch {batch} x seq {seq}, accumulation {accum}"),
+                   "global_batch": batch * accum, "seq_len": seq, "layers": L, "vocab": V,
+                   "parallelism": "single GPU"},
+        "h2d": h2d, "roofline": roof, "layer_gemms": layer_gemms, "kernels": kernels,
+        "peak_device_GB": round(torch.cuda.max_memory_allocated() / 1e9, 3),
+        "loss": loss,
+    }
+    stack.close()
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(shape)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

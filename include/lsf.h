@@ -239,7 +239,7 @@ typedef struct {
   const uint16_t* embed;       /* device bf16 [vocab, H] (resident, frozen) */
   const uint16_t* final_norm;  /* device bf16 [H] */
   const uint16_t* lm_head;     /* device bf16 [vocab, H] (resident, frozen, untied) */
-  int32_t vocab;               /* multiple of 128... any >= 2 (head GEMM pads) */
+  int32_t vocab;               /* positive multiple of 128 */
   const lsf_layer_lora* lora;  /* host array [n_layers] of adapter descriptors */
   uint16_t* ckpt;              /* device bf16 [n_layers + 1, batch*seq, H]: layer inputs */
   float* logits;               /* device fp32 [batch*seq, vocab] */
@@ -256,15 +256,29 @@ size_t stack_workspace_bytes(const lsf_layer_cfg* cfg, int32_t vocab);
  * streamed recompute + backward, LoRA gradients accumulated. */
 lsf_status stream_stack_step(lsf_stack* st, const lsf_stack_io* io);
 
+/* Kernel classes timed with HIP events under LSF_STACK_TIMING (index into
+ * lsf_stack_stats.kernel_ms / kernel_launches).  A GEMM's time includes its
+ * split-K reduction when it has one. */
+enum {
+  LSF_K_QKV_FWD = 0, LSF_K_O_FWD, LSF_K_GATEUP_FWD, LSF_K_DOWN_FWD, /* fused NF4 GEMMs, forward */
+  LSF_K_QKV_BWD, LSF_K_O_BWD, LSF_K_GATEUP_BWD, LSF_K_DOWN_BWD,     /* fused NF4 GEMMs, input gradient */
+  LSF_K_ATTN_FWD, LSF_K_ATTN_BWD, LSF_K_HEAD_FWD, LSF_K_HEAD_BWD,
+  LSF_K_COUNT
+};
+
 typedef struct {
   int64_t steps;       /* stream_stack_step calls since create / reset */
   int64_t copies;      /* host-to-device layer copies enqueued */
   int64_t bytes;       /* bytes those copies moved */
   double copy_ms;      /* summed copy durations (LSF_STACK_TIMING only) */
   double wait_ms;      /* summed compute-stream stalls on copies (LSF_STACK_TIMING only) */
+  double kernel_ms[16];        /* summed durations per LSF_K_* class (LSF_STACK_TIMING only) */
+  int64_t kernel_launches[16]; /* launches per class (LSF_STACK_TIMING only) */
 } lsf_stack_stats;
-/* Waits for the recorded events (synchronises the copy and compute streams). */
+/* Counters and event timings since the last reset (or create).  Waits for the
+ * recorded events, so it synchronises with the work they bracket. */
 lsf_status stack_stats(lsf_stack* st, lsf_stack_stats* out);
+/* Zero the counters and drop the recorded events. */
 lsf_status stack_reset_stats(lsf_stack* st);
 
 #ifdef __cplusplus

@@ -81,7 +81,12 @@ class StackIO(ctypes.Structure):
 
 class StackStats(ctypes.Structure):
     _fields_ = [("steps", c_int64), ("copies", c_int64), ("bytes", c_int64), ("copy_ms", ctypes.c_double),
-                ("wait_ms", ctypes.c_double)]
+                ("wait_ms", ctypes.c_double), ("kernel_ms", ctypes.c_double * 16),
+                ("kernel_launches", c_int64 * 16)]
+
+
+KERNELS = ["qkv_fwd", "o_fwd", "gate_up_fwd", "down_fwd", "qkv_bwd", "o_bwd", "gate_up_bwd", "down_bwd",
+           "attn_fwd", "attn_bwd", "head_fwd", "head_bwd"]
 
 
 _PROTOS = {

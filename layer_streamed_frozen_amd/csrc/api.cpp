@@ -339,6 +339,73 @@ lsf_status layer_weights_from_blob(const lsf_layer_cfg* cfg, int32_t format, con
 }  // extern "C"
 
 // ============================================================ the streamer
+namespace {
+
+// Timing events: created on demand, returned to a free list once harvested.
+struct EventPool {
+  std::vector<hipEvent_t> all, free;
+  hipEvent_t get() {
+    if (!free.empty()) {
+      hipEvent_t e = free.back();
+      free.pop_back();
+      return e;
+    }
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    all.push_back(e);
+    return e;
+  }
+  void put(hipEvent_t e) { free.push_back(e); }
+};
+
+using EvPairs = std::vector<std::pair<hipEvent_t, hipEvent_t>>;
+
+// Add the durations of the recorded pairs that have completed (all of them,
+// waiting, when `wait`), recycle their events, keep the rest.  Pairs of one
+// list complete in order (they sit on one stream).
+hipError_t harvest(EventPool& pool, EvPairs& v, double& ms_sum, int64_t* count, bool wait) {
+  size_t done = 0;
+  for (; done < v.size(); ++done) {
+    if (wait) {
+      hipError_t e = hipEventSynchronize(v[done].second);
+      if (e != hipSuccess) return e;
+    } else if (hipEventQuery(v[done].second) != hipSuccess) {
+      (void)hipGetLastError();  // clear the not-ready status
+      break;
+    }
+    float ms = 0.0f;
+    hipError_t e = hipEventElapsedTime(&ms, v[done].first, v[done].second);
+    if (e != hipSuccess) return e;
+    ms_sum += ms;
+    if (count) ++*count;
+    pool.put(v[done].first);
+    pool.put(v[done].second);
+  }
+  v.erase(v.begin(), v.begin() + done);
+  return hipSuccess;
+}
+
+// Brackets the big kernels of every layer call with events (LSF_STACK_TIMING).
+struct KernelProbe : Probe {
+  EventPool* pool = nullptr;
+  hipEvent_t open[LSF_K_COUNT] = {};
+  EvPairs ev[LSF_K_COUNT];
+  hipError_t begin(int kind, hipStream_t s) override {
+    open[kind] = pool->get();
+    if (open[kind] == nullptr) return hipErrorOutOfMemory;
+    return hipEventRecord(open[kind], s);
+  }
+  hipError_t end(int kind, hipStream_t s) override {
+    hipEvent_t e = pool->get();
+    if (e == nullptr) return hipErrorOutOfMemory;
+    hipError_t r = hipEventRecord(e, s);
+    ev[kind].emplace_back(open[kind], e);
+    return r;
+  }
+};
+
+}  // namespace
+
 struct lsf_stack {
   lsf_layer_cfg cfg;
   lsf_stack_desc d;
@@ -346,22 +413,26 @@ struct lsf_stack {
   hipEvent_t ready[2], freed[2];
   bool used[2];
   int slot_layer[2];
-  // timing (LSF_STACK_TIMING)
-  std::vector<hipEvent_t> ev_pool;
-  size_t ev_next = 0;
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> copy_ev, wait_ev;
-  lsf_stack_stats stats;
+  // timing (LSF_STACK_TIMING), accumulated until stack_reset_stats
+  EventPool events;
+  KernelProbe probe;
+  EvPairs copy_ev, wait_ev;
+  lsf_stack_stats stats;  // counters; the *_ms fields accumulate harvested durations
 };
 
 namespace {
 
-hipEvent_t timing_event(lsf_stack* st) {
-  if (st->ev_next == st->ev_pool.size()) {
-    hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
-    st->ev_pool.push_back(e);
-  }
-  return st->ev_pool[st->ev_next++];
+hipEvent_t timing_event(lsf_stack* st) { return st->events.get(); }
+
+hipError_t harvest_all(lsf_stack* st, bool wait) {
+  hipError_t e;
+  if ((e = harvest(st->events, st->copy_ev, st->stats.copy_ms, nullptr, wait)) != hipSuccess) return e;
+  if ((e = harvest(st->events, st->wait_ev, st->stats.wait_ms, nullptr, wait)) != hipSuccess) return e;
+  for (int k = 0; k < LSF_K_COUNT; ++k)
+    if ((e = harvest(st->events, st->probe.ev[k], st->stats.kernel_ms[k], &st->stats.kernel_launches[k], wait)) !=
+        hipSuccess)
+      return e;
+  return hipSuccess;
 }
 
 // Make layer j resident in buffer b: copy unless the buffer already holds it.
@@ -507,7 +578,8 @@ lsf_status stack_destroy(lsf_stack* st) {
     (void)hipEventDestroy(st->ready[i]);
     (void)hipEventDestroy(st->freed[i]);
   }
-  for (hipEvent_t e : st->ev_pool) (void)hipEventDestroy(e);
+  (void)harvest_all(st, true);  // no event may be destroyed while still pending
+  for (hipEvent_t e : st->events.all) (void)hipEventDestroy(e);
   delete st;
   return ok();
 }
@@ -539,11 +611,14 @@ lsf_status stream_stack_step(lsf_stack* st, const lsf_stack_io* io) {
     return fail(LSF_ERR_WORKSPACE, "workspace too small (need %zu bytes)", stack_ws_bytes(c, V));
 
   hipStream_t cs = S(st->d.compute);
-  const StackWs w = carve_stack(c, V, io->ws);
+  StackWs w = carve_stack(c, V, io->ws);
+  const bool timing = st->d.flags & LSF_STACK_TIMING;
+  if (timing) {
+    st->probe.pool = &st->events;
+    w.layer.probe = &st->probe;
+    HIPCK(harvest_all(st, false));  // recycle the events of work that has finished
+  }
   const size_t act = (size_t)T * H;
-  st->ev_next = 0;
-  st->copy_ev.clear();
-  st->wait_ev.clear();
   st->stats.steps += 1;
 
   if (io->mode & LSF_MODE_ZERO_GRADS) {
@@ -601,7 +676,9 @@ lsf_status stream_stack_step(lsf_stack* st, const lsf_stack_io* io) {
     g.M = T; g.N = V; g.K = H; g.A = w.hN; g.lda = H;
     g.W.fmt = FMT_BF16; g.W.bf16 = io->lm_head; g.W.ld = H;
     EpiArgs e; e.kind = EPI_F32; e.C = io->logits; e.ldc = V;
+    if (timing) HIPCK(st->probe.begin(LSF_K_HEAD_FWD, cs));
     HIPCK(gemm_nt(g, e, cs));
+    if (timing) HIPCK(st->probe.end(LSF_K_HEAD_FWD, cs));
   }
   HIPCK(cross_entropy(io->logits, io->ids, c.batch, c.seq, V, io->loss_scale, w.dlog, w.row_loss, io->loss, cs));
   if (io->mode & LSF_MODE_FWD_ONLY) return ok();
@@ -610,7 +687,9 @@ lsf_status stream_stack_step(lsf_stack* st, const lsf_stack_io* io) {
     g.M = T; g.N = H; g.K = V; g.A = w.dlog; g.lda = V;
     g.W.fmt = FMT_BF16; g.W.bf16 = io->lm_head; g.W.ld = H;
     EpiArgs e; e.kind = EPI_BF16; e.C = w.dhN; e.ldc = H;
+    if (timing) HIPCK(st->probe.begin(LSF_K_HEAD_BWD, cs));
     HIPCK(run_gemm(true, g, e, w.part, w.part_floats, cs));
+    if (timing) HIPCK(st->probe.end(LSF_K_HEAD_BWD, cs));
   }
   HIPCK(rmsnorm_bwd(w.dhN, xL, io->final_norm, w.rstdN, nullptr, T, H, w.dx[L & 1], cs));
 
@@ -637,27 +716,14 @@ lsf_status stream_stack_step(lsf_stack* st, const lsf_stack_io* io) {
 
 lsf_status stack_stats(lsf_stack* st, lsf_stack_stats* out) {
   if (st == nullptr || out == nullptr) return fail(LSF_ERR_INVALID_ARG, "stack or out is NULL");
-  lsf_stack_stats r = st->stats;
-  r.copy_ms = 0.0;
-  r.wait_ms = 0.0;
-  for (auto& pr : st->copy_ev) {
-    HIPCK(hipEventSynchronize(pr.second));
-    float ms = 0.0f;
-    HIPCK(hipEventElapsedTime(&ms, pr.first, pr.second));
-    r.copy_ms += ms;
-  }
-  for (auto& pr : st->wait_ev) {
-    HIPCK(hipEventSynchronize(pr.second));
-    float ms = 0.0f;
-    HIPCK(hipEventElapsedTime(&ms, pr.first, pr.second));
-    r.wait_ms += ms;
-  }
-  *out = r;
+  HIPCK(harvest_all(st, true));
+  *out = st->stats;
   return ok();
 }
 
 lsf_status stack_reset_stats(lsf_stack* st) {
   if (st == nullptr) return fail(LSF_ERR_INVALID_ARG, "stack is NULL");
+  HIPCK(harvest_all(st, true));  // pending events must finish before they are recycled
   std::memset(&st->stats, 0, sizeof(st->stats));
   return ok();
 }

@@ -131,6 +131,14 @@ hipError_t run_gemm(bool nn, GemmArgs g, const EpiArgs& e, float* part, size_t p
     if (e_ != hipSuccess) return e_;        \
   } while (0)
 
+static hipError_t timed_gemm(const LayerWs& ws, int kind, bool nn, const GemmArgs& g, const EpiArgs& e,
+                             hipStream_t s) {
+  if (ws.probe) CK(ws.probe->begin(kind, s));
+  CK(run_gemm(nn, g, e, ws.part, ws.part_floats, s));
+  if (ws.probe) CK(ws.probe->end(kind, s));
+  return hipSuccess;
+}
+
 hipError_t layer_forward(const lsf_layer_cfg& c, const lsf_layer_weights& w, const lsf_layer_lora* lora,
                          const uint16_t* x, uint16_t* y, const LayerWs& ws, bool save, bool rope_ready,
                          hipStream_t s) {
@@ -165,14 +173,16 @@ hipError_t layer_forward(const lsf_layer_cfg& c, const lsf_layer_weights& w, con
       g.ext.row_off[3] = (int)z.Nqkv;
     }
     EpiArgs e; e.kind = EPI_BF16; e.C = ws.qkv; e.ldc = z.Nqkv;
-    CK(run_gemm(false, g, e, ws.part, ws.part_floats, s));
+    CK(timed_gemm(ws, LSF_K_QKV_FWD, false, g, e, s));
   }
   CK(rope_apply(ws.qkv, z.Nqkv, T, c.seq, c.n_heads + c.n_kv_heads, c.head_dim, ws.rope, false, s));
   {
     AttnArgs a;
     a.batch = c.batch; a.seq = c.seq; a.nq = c.n_heads; a.nkv = c.n_kv_heads;
     a.qkv = ws.qkv; a.ldqkv = z.Nqkv; a.o = ws.att; a.lse = ws.lse;
+    if (ws.probe) CK(ws.probe->begin(LSF_K_ATTN_FWD, s));
     CK(attention_fwd(a, s));
+    if (ws.probe) CK(ws.probe->end(LSF_K_ATTN_FWD, s));
   }
   {
     const lsf_lora_proj* po = proj(lora, PO);
@@ -187,7 +197,7 @@ hipError_t layer_forward(const lsf_layer_cfg& c, const lsf_layer_weights& w, con
     }
     g.N = H; g.K = (int)z.Dq; g.A = ws.att; g.lda = z.Dq; g.W = weight_ref(w.o, fmt, z.Dq);
     EpiArgs e; e.kind = EPI_RESID_BF16; e.C = ws.x2; e.ldc = H; e.R = x; e.ldr = H;
-    CK(run_gemm(false, g, e, ws.part, ws.part_floats, s));
+    CK(timed_gemm(ws, LSF_K_O_FWD, false, g, e, s));
   }
   // MLP block
   CK(rmsnorm_fwd(ws.x2, w.norm2, T, H, c.rms_eps, ws.h2, ws.rstd2, s));
@@ -208,7 +218,7 @@ hipError_t layer_forward(const lsf_layer_cfg& c, const lsf_layer_weights& w, con
     g.N = 2 * I; g.K = H; g.A = ws.h2; g.lda = H; g.W = weight_ref(w.gate_up, fmt, H); g.pair_I = I;
     EpiArgs e; e.kind = EPI_SWIGLU; e.C = ws.a; e.ldc = I;
     if (save) { e.g = ws.g; e.u = ws.u; e.ldgu = I; }
-    CK(run_gemm(false, g, e, ws.part, ws.part_floats, s));
+    CK(timed_gemm(ws, LSF_K_GATEUP_FWD, false, g, e, s));
   }
   {
     const lsf_lora_proj* pd = proj(lora, PD);
@@ -226,7 +236,7 @@ hipError_t layer_forward(const lsf_layer_cfg& c, const lsf_layer_weights& w, con
       }
       g.N = H; g.K = I; g.A = ws.a; g.lda = I; g.W = weight_ref(w.down, fmt, I);
       EpiArgs e; e.kind = EPI_RESID_BF16; e.C = y; e.ldc = H; e.R = ws.x2; e.ldr = H;
-      CK(run_gemm(false, g, e, ws.part, ws.part_floats, s));
+      CK(timed_gemm(ws, LSF_K_DOWN_FWD, false, g, e, s));
     }
   }
   return hipSuccess;
@@ -295,7 +305,7 @@ hipError_t layer_backward(const lsf_layer_cfg& c, const lsf_layer_weights& w, co
       g.ext.ldmat = I;
     }
     EpiArgs e; e.kind = EPI_SWIGLU_BWD; e.C = ws.dgu; e.ldc = 2 * (int64_t)I; e.g = ws.g; e.u = ws.u; e.ldgu = I;
-    CK(run_gemm(true, g, e, ws.part, ws.part_floats, s));
+    CK(timed_gemm(ws, LSF_K_DOWN_BWD, true, g, e, s));
     if (p[0]) {
       const int yo[1] = {0}, ny[1] = {H};
       CK(lora_grads(T, r, sc, 1, p, ws.dU, ws.a, I, I, ws.Ud, dy, H, yo, ny, s));
@@ -315,7 +325,7 @@ hipError_t layer_backward(const lsf_layer_cfg& c, const lsf_layer_weights& w, co
       g.ext.ldmat = H;
     }
     EpiArgs e; e.kind = EPI_BF16; e.C = ws.dh; e.ldc = H;
-    CK(run_gemm(true, g, e, ws.part, ws.part_floats, s));
+    CK(timed_gemm(ws, LSF_K_GATEUP_BWD, true, g, e, s));
     if (any) {
       const int yo[2] = {0, I}, ny[2] = {I, I};
       CK(lora_grads(T, r, sc, 2, p, ws.dU, ws.h2, H, H, ws.Ugu, ws.dgu, 2 * (int64_t)I, yo, ny, s));
@@ -333,7 +343,7 @@ hipError_t layer_backward(const lsf_layer_cfg& c, const lsf_layer_weights& w, co
       g.ext.ldmat = z.Dq;
     }
     EpiArgs e; e.kind = EPI_BF16; e.C = ws.dob; e.ldc = z.Dq;
-    CK(run_gemm(true, g, e, ws.part, ws.part_floats, s));
+    CK(timed_gemm(ws, LSF_K_O_BWD, true, g, e, s));
     if (p[0]) {
       const int yo[1] = {0}, ny[1] = {H};
       CK(lora_grads(T, r, sc, 1, p, ws.dU, ws.att, z.Dq, (int)z.Dq, ws.Uo, ws.dx2, H, yo, ny, s));
@@ -345,7 +355,9 @@ hipError_t layer_backward(const lsf_layer_cfg& c, const lsf_layer_weights& w, co
     a.batch = c.batch; a.seq = c.seq; a.nq = c.n_heads; a.nkv = c.n_kv_heads;
     a.qkv = ws.qkv; a.ldqkv = z.Nqkv; a.o = ws.att; a.lse = ws.lse; a.dout = ws.dob; a.Dsum = ws.attn_scratch;
     a.dqkv = ws.dqkv;
+    if (ws.probe) CK(ws.probe->begin(LSF_K_ATTN_BWD, s));
     CK(attention_bwd(a, s));
+    if (ws.probe) CK(ws.probe->end(LSF_K_ATTN_BWD, s));
   }
   CK(rope_apply(ws.dqkv, z.Nqkv, T, c.seq, c.n_heads + c.n_kv_heads, c.head_dim, ws.rope, true, s));
   // q|k|v projection
@@ -363,7 +375,7 @@ hipError_t layer_backward(const lsf_layer_cfg& c, const lsf_layer_weights& w, co
       g.ext.ldmat = H;
     }
     EpiArgs e; e.kind = EPI_BF16; e.C = ws.dh; e.ldc = H;
-    CK(run_gemm(true, g, e, ws.part, ws.part_floats, s));
+    CK(timed_gemm(ws, LSF_K_QKV_BWD, true, g, e, s));
     if (any) {
       const int ny[3] = {qd, kd, kd};
       CK(lora_grads(T, r, sc, 3, p, ws.dU, ws.h1, H, H, ws.Uqkv, ws.dqkv, z.Nqkv, xo, ny, s));

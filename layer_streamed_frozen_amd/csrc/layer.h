@@ -7,6 +7,13 @@
 
 namespace lsf {
 
+// Optional event probe around the big kernels (used by the streamer's timing).
+struct Probe {
+  virtual hipError_t begin(int kind, hipStream_t s) = 0;
+  virtual hipError_t end(int kind, hipStream_t s) = 0;
+  virtual ~Probe() = default;
+};
+
 // Scratch layout of one decoder layer's forward + recompute + backward.
 struct LayerWs {
   uint16_t *h1, *qkv, *att, *x2, *h2, *g, *u, *a, *y;
@@ -15,6 +22,7 @@ struct LayerWs {
   uint16_t *dgu, *dh, *dx2, *dob, *dqkv;
   float *dU, *attn_scratch, *part;
   size_t part_floats;
+  Probe* probe = nullptr;
   static size_t bytes(const lsf_layer_cfg& c);
   static LayerWs carve(const lsf_layer_cfg& c, void* base);
 };

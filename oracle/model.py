@@ -327,7 +327,7 @@ def stack_forward(ids, emb, layers, loras, final_norm, head, cfg,
     the activation type the layer-to-layer checkpoints are stored in.
     Returns (logits [B*T, V], state for ``stack_backward``).
     """
-    x = np.asarray(emb, dtype=dtype)[ids]
+    x = np.asarray(emb)[ids].astype(dtype)
     caches = []
     for i in range(len(loras)):
         y, cache = layer_fwd(x, layers[i], loras[i], cfg)

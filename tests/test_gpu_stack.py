@@ -1,0 +1,226 @@
+"""The streamed stack step through the C ABI: oracle parity, the pages'
+bit-equality of streamed and resident runs, copy accounting, accumulation,
+forward-only mode and the pinned / pageable host-store rules."""
+import numpy as np
+import pytest
+import torch
+
+from layer_streamed_frozen_amd import binding as B
+from layer_streamed_frozen_amd import store as S
+from layer_streamed_frozen_amd import synth
+from oracle import model as M
+from oracle import nf4 as onf4
+from tests._util import TOL, bf16_tensor_to_np, report
+from tests.test_gpu_layer import SMALL, oracle_layer_weights, oracle_shape
+
+pytestmark = pytest.mark.gpu
+
+
+def bf16_param(name, shape, std):
+    vals, bits = synth.bf16_exact(synth.normal(name, shape, std))
+    return vals, torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+class Setup:
+    def __init__(self, shape, n_layers, vocab, batch, seq, prefix, resident=True, targets=S.PROJ, flags=0,
+                 pinned=True, random_norms=True):
+        print(f"[stack] {prefix} L={n_layers} V={vocab} B={batch} S={seq}", flush=True)
+        self.shape, self.L, self.V, self.batch, self.seq = shape, n_layers, vocab, batch, seq
+        self.prefix = prefix
+
+        def wfn(i):
+            W = S.layer_weights_fp32(f"{prefix}.layer{i}", shape)
+            if random_norms:
+                W.update(S.random_norms(f"{prefix}.layer{i}", shape))
+            return W
+
+        self.wfn = wfn
+        self.store = S.Store(shape, n_layers, resident=resident, weights_fn=wfn, pinned=pinned)
+        self.lora = S.LoraSet(shape, n_layers, targets=targets, prefix=prefix + ".lora")
+        H = shape.hidden
+        self.emb_np, self.emb = bf16_param(prefix + ".embed", (vocab, H), 1.0)
+        self.head_np, self.head = bf16_param(prefix + ".head", (vocab, H), 0.02)
+        fn = np.full(H, 0x3F80, np.uint16)
+        self.fnorm_np = onf4.bf16_to_f32(fn)
+        self.fnorm = torch.from_numpy(fn.view(np.int16)).view(torch.bfloat16).cuda()
+        self.ids_np = synth.token_ids(prefix + ".ids", (batch, seq), vocab)
+        self.ids = torch.from_numpy(self.ids_np).cuda()
+        self.stack = S.Stack(shape, self.store, batch, seq, vocab, flags=flags)
+
+    def step(self, mode=B.MODE_STREAMED, loss_scale=1.0, enabled=True, ids=None):
+        arr = self.lora.array(enabled=enabled)
+        self.stack.step(self.ids if ids is None else ids, self.emb, self.fnorm, self.head, arr, mode=mode,
+                        loss_scale=loss_scale)
+        torch.cuda.synchronize()
+
+    def snapshot(self):
+        g = [{n: (self.lora.dA[i][n].clone(), self.lora.dB[i][n].clone()) for n in self.lora.targets}
+             for i in range(self.L)]
+        return self.stack.logits.clone(), self.stack.loss.clone(), g
+
+    def oracle(self, loss_scale=1.0, ids=None):
+        layers = [oracle_layer_weights(self.wfn(i)) for i in range(self.L)]
+        loras = [self.lora.numpy(i) for i in range(self.L)]
+        return M.stack_step(self.ids_np if ids is None else ids, self.emb_np, layers, loras,
+                            self.fnorm_np.astype(np.float64), self.head_np.astype(np.float64),
+                            oracle_shape(self.shape), loss_scale=loss_scale)
+
+
+def same(a, b):
+    la, sa, ga = a
+    lb, sb, gb = b
+    if not (torch.equal(la, lb) and torch.equal(sa, sb)):
+        return False
+    for x, y in zip(ga, gb):
+        for n in x:
+            if not (torch.equal(x[n][0], y[n][0]) and torch.equal(x[n][1], y[n][1])):
+                return False
+    return True
+
+
+@pytest.fixture(scope="module")
+def small():
+    return Setup(SMALL, 3, 1024, 2, 100, "ss")
+
+
+def test_small_stack_matches_oracle(small):
+    small.step(mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+    ref = small.oracle()
+    loss = float(small.stack.loss.item())
+    print(f"  loss gpu={loss:.6f} oracle={ref['loss']:.6f}", flush=True)
+    assert abs(loss - ref["loss"]) / abs(ref["loss"]) < TOL
+    assert report("logits", small.stack.logits.double().cpu().numpy(), ref["logits"]) < TOL
+    for i in range(small.L):
+        g = small.lora.grads_numpy(i)
+        for n in S.PROJ:
+            assert report(f"L{i}.dA_{n}", g[n][0], ref["grads"][i][n][0]) < TOL
+            assert report(f"L{i}.dB_{n}", g[n][1], ref["grads"][i][n][1]) < TOL
+
+
+def test_streamed_equals_resident_bitwise(small):
+    small.step(mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+    a = small.snapshot()
+    small.step(mode=B.MODE_RESIDENT | B.MODE_ZERO_GRADS)
+    b = small.snapshot()
+    print(f"  max|logit diff| = {float((a[0] - b[0]).abs().max()):.1f}", flush=True)
+    assert same(a, b)
+
+
+def test_forward_and_backward_bit_equal_separately(small):
+    # forward claim: logits and loss of a forward-only step
+    small.step(mode=B.MODE_STREAMED | B.MODE_FWD_ONLY)
+    fa = (small.stack.logits.clone(), small.stack.loss.clone())
+    small.step(mode=B.MODE_RESIDENT | B.MODE_FWD_ONLY)
+    assert torch.equal(fa[0], small.stack.logits) and torch.equal(fa[1], small.stack.loss)
+    # backward claim: the gradients
+    small.step(mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+    a = small.snapshot()
+    small.step(mode=B.MODE_RESIDENT | B.MODE_ZERO_GRADS)
+    assert same(a, small.snapshot())
+
+
+def test_run_to_run_determinism(small):
+    small.step(mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+    a = small.snapshot()
+    small.step(mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+    assert same(a, small.snapshot())
+
+
+def test_copy_accounting(small):
+    B.stack_reset_stats(small.stack.handle)
+    small.step(mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+    st = small.stack.stats()
+    assert st.steps == 1
+    assert st.copies == 2 * small.L - 2          # the two layers resident at the turn are reused
+    assert st.bytes == st.copies * small.store.blob_bytes()
+    B.stack_reset_stats(small.stack.handle)
+    small.step(mode=B.MODE_STREAMED | B.MODE_FWD_ONLY)
+    assert small.stack.stats().copies == small.L
+    B.stack_reset_stats(small.stack.handle)
+    small.step(mode=B.MODE_RESIDENT | B.MODE_ZERO_GRADS)
+    assert small.stack.stats().copies == 0
+
+
+def test_no_turn_reuse_and_timing_give_same_bits():
+    s = Setup(SMALL, 3, 1024, 1, 64, "nt", flags=B.STACK_NO_TURN_REUSE | B.STACK_TIMING)
+    B.stack_reset_stats(s.stack.handle)
+    s.step(mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+    st = s.stack.stats()
+    assert st.copies == 2 * s.L
+    assert st.copy_ms > 0.0
+    a = s.snapshot()
+    s.step(mode=B.MODE_RESIDENT | B.MODE_ZERO_GRADS)
+    assert same(a, s.snapshot())
+
+
+def test_gradient_accumulation_matches_oracle():
+    s = Setup(SMALL, 2, 512, 1, 80, "acc", random_norms=False)
+    ids2 = synth.token_ids("acc.ids2", (1, 80), 512)
+    s.step(mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS, loss_scale=0.5)
+    s.step(mode=B.MODE_STREAMED, loss_scale=0.5, ids=torch.from_numpy(ids2).cuda())
+    r1 = s.oracle(loss_scale=0.5)
+    r2 = s.oracle(loss_scale=0.5, ids=ids2)
+    for i in range(s.L):
+        g = s.lora.grads_numpy(i)
+        for n in ("q", "o", "down"):
+            assert report(f"L{i}.dA_{n}", g[n][0], r1["grads"][i][n][0] + r2["grads"][i][n][0]) < TOL
+            assert report(f"L{i}.dB_{n}", g[n][1], r1["grads"][i][n][1] + r2["grads"][i][n][1]) < TOL
+
+
+def test_adapters_disabled_changes_only_through_lora():
+    s = Setup(SMALL, 2, 512, 1, 48, "dis", targets=("q", "v"))
+    s.step(mode=B.MODE_STREAMED | B.MODE_FWD_ONLY, enabled=False)
+    layers = [oracle_layer_weights(s.wfn(i)) for i in range(s.L)]
+    logits, _ = M.stack_forward(s.ids_np, s.emb_np, layers, [None] * s.L,
+                                s.fnorm_np.astype(np.float64), s.head_np.astype(np.float64), oracle_shape(s.shape))
+    assert report("logits", s.stack.logits.double().cpu().numpy(), logits) < TOL
+
+
+def test_pageable_store_rules():
+    st = S.Store(SMALL, 2, resident=False, pinned=False, prefix="pg")
+    with pytest.raises(B.LsfError) as e:
+        S.Stack(SMALL, st, 1, 32, 256)
+    assert e.value.status == B.LSF_ERR_NOT_PINNED
+    # accepted with the explicit flag (the slow fallback); results unchanged
+    pinned = S.Store(SMALL, 2, resident=False, pinned=True, prefix="pg")
+    lora = S.LoraSet(SMALL, 2, prefix="pg.lora")
+    emb = bf16_param("pg.embed", (256, SMALL.hidden), 1.0)[1]
+    head = bf16_param("pg.head", (256, SMALL.hidden), 0.02)[1]
+    fn = torch.ones(SMALL.hidden, dtype=torch.bfloat16, device="cuda")
+    ids = torch.from_numpy(synth.token_ids("pg.ids", (1, 32), 256)).cuda()
+    outs = []
+    for store, flags in ((st, B.STACK_ALLOW_PAGEABLE), (pinned, 0)):
+        sk = S.Stack(SMALL, store, 1, 32, 256, flags=flags)
+        sk.step(ids, emb, fn, head, lora.array(), mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+        torch.cuda.synchronize()
+        outs.append((sk.logits.clone(), lora.dA[1]["q"].clone()))
+        sk.close()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_bad_arguments_are_rejected():
+    cfg = SMALL.cfg(1, 16)
+    d = B.StackDesc()
+    d.n_layers = 0
+    with pytest.raises(B.LsfError) as e:
+        B.stack_create(cfg, d)
+    assert e.value.status == B.LSF_ERR_INVALID_ARG
+
+
+def test_full_8b_shapes_two_layers_match_oracle():
+    # Llama-3.1-8B-shaped layers and the full 128256-entry vocabulary, seq 512
+    s = Setup(S.LLAMA8B, 2, 128256, 1, 512, "s8b2", random_norms=False)
+    s.step(mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+    a = s.snapshot()
+    s.step(mode=B.MODE_RESIDENT | B.MODE_ZERO_GRADS)
+    assert same(a, s.snapshot())
+    ref = s.oracle()
+    loss = float(s.stack.loss.item())
+    print(f"  loss gpu={loss:.6f} oracle={ref['loss']:.6f}", flush=True)
+    assert abs(loss - ref["loss"]) / abs(ref["loss"]) < TOL
+    assert report("logits", s.stack.logits.double().cpu().numpy(), ref["logits"]) < TOL
+    for i in range(s.L):
+        g = s.lora.grads_numpy(i)
+        for n in S.PROJ:
+            assert report(f"L{i}.dA_{n}", g[n][0], ref["grads"][i][n][0]) < TOL
+            assert report(f"L{i}.dB_{n}", g[n][1], ref["grads"][i][n][1]) < TOL
