@@ -52,6 +52,13 @@
 extern "C" {
 #endif
 
+/* Every function below is exported from liblsf.so; nothing else is. */
+#if defined(__GNUC__)
+#define LSF_API __attribute__((visibility("default")))
+#else
+#define LSF_API
+#endif
+
 typedef void* lsf_stream; /* hipStream_t */
 
 typedef enum {
@@ -66,9 +73,9 @@ typedef enum {
 } lsf_status;
 
 /* Message of the calling thread's last failed call ("" if none). */
-const char* lsf_last_error(void);
+LSF_API const char* lsf_last_error(void);
 /* Library version string. */
-const char* lsf_version(void);
+LSF_API const char* lsf_version(void);
 
 /* ------------------------------------------------------------------ NF4 --
  * [TUTORIAL] item 1: the decoder's Linear weights are stored offline as QLoRA
@@ -82,12 +89,12 @@ const char* lsf_version(void);
 /* Quantise n fp32 values (device) into packed codes (device, n/2 bytes) and
  * absmax (device, n/blocksize floats).  n % 64 == 0 and blocksize == 64, else
  * LSF_ERR_SHAPE.  Pointers must be 16-byte aligned (LSF_ERR_ALIGN). */
-lsf_status nf4_quantize(const float* w, int64_t n, int32_t blocksize,
+LSF_API lsf_status nf4_quantize(const float* w, int64_t n, int32_t blocksize,
                         uint8_t* packed, float* absmax, lsf_stream stream);
 
 /* Dequantise: out[i] = bf16_rne(level[code[i]] * absmax[i / blocksize]).
  * Same shape rules as nf4_quantize; out is device bf16 [n]. */
-lsf_status nf4_dequantize(const uint8_t* packed, const float* absmax, int64_t n,
+LSF_API lsf_status nf4_dequantize(const uint8_t* packed, const float* absmax, int64_t n,
                           int32_t blocksize, uint16_t* out, lsf_stream stream);
 
 /* --------------------------------------------------------- layer config -- */
@@ -151,15 +158,15 @@ typedef struct {
  * n_out % 128 == 0, n_in % 64 == 0, tokens >= 1, 1 <= rank <= 64.
  * A/B may be NULL (no adapter).  ws: device workspace of at least
  * linear_workspace_bytes() bytes. */
-size_t linear_workspace_bytes(int32_t tokens, int32_t n_out, int32_t n_in, int32_t rank);
-lsf_status linear_fwd(const lsf_weight* w, int32_t format, int32_t n_out, int32_t n_in,
+LSF_API size_t linear_workspace_bytes(int32_t tokens, int32_t n_out, int32_t n_in, int32_t rank);
+LSF_API lsf_status linear_fwd(const lsf_weight* w, int32_t format, int32_t n_out, int32_t n_in,
                       const float* A, const float* B, int32_t rank, float scale,
                       const uint16_t* x, int32_t tokens, uint16_t* y,
                       void* ws, size_t ws_bytes, lsf_stream stream);
 /* Backward of linear_fwd: dx = dy W + s (dy B) A (the input gradient through the
  * frozen weight, [TUTORIAL] item 3); dA += s (dy B)^T x; dB += s dy^T (x A^T).
  * dx: device bf16 [tokens, n_in]. dA/dB accumulate. */
-lsf_status linear_bwd(const lsf_weight* w, int32_t format, int32_t n_out, int32_t n_in,
+LSF_API lsf_status linear_bwd(const lsf_weight* w, int32_t format, int32_t n_out, int32_t n_in,
                       const float* A, const float* B, int32_t rank, float scale,
                       const uint16_t* x, const uint16_t* dy, int32_t tokens, uint16_t* dx,
                       float* dA, float* dB, void* ws, size_t ws_bytes, lsf_stream stream);
@@ -170,15 +177,15 @@ lsf_status linear_bwd(const lsf_weight* w, int32_t format, int32_t n_out, int32_
  * h2 = rmsnorm(x2); a = silu(gate(h2)) * up(h2); y = x2 + down(a).
  * x, y: device bf16 [batch*seq, H].  Requires hidden, intermediate and
  * (nq + 2 nkv) * d to be multiples of 128 and head_dim == 128. */
-size_t layer_workspace_bytes(const lsf_layer_cfg* cfg);
-lsf_status layer_fwd(const lsf_layer_cfg* cfg, const lsf_layer_weights* w,
+LSF_API size_t layer_workspace_bytes(const lsf_layer_cfg* cfg);
+LSF_API lsf_status layer_fwd(const lsf_layer_cfg* cfg, const lsf_layer_weights* w,
                      const lsf_layer_lora* lora, const uint16_t* x, uint16_t* y,
                      void* ws, size_t ws_bytes, lsf_stream stream);
 /* Recomputes the forward from the checkpoint x (the layer input), then walks
  * it backward ([TUTORIAL] item 3: each layer is read a second time and
  * dL/dx = W^T dL/dy still needs the frozen weight).  dy, dx: device bf16
  * [batch*seq, H]; dA/dB of every adapted projection accumulate (+=). */
-lsf_status layer_bwd(const lsf_layer_cfg* cfg, const lsf_layer_weights* w,
+LSF_API lsf_status layer_bwd(const lsf_layer_cfg* cfg, const lsf_layer_weights* w,
                      const lsf_layer_lora* lora, const uint16_t* x, const uint16_t* dy,
                      uint16_t* dx, void* ws, size_t ws_bytes, lsf_stream stream);
 
@@ -194,9 +201,9 @@ typedef struct {
   uint64_t bytes;  /* size of one blob */
   uint64_t stride; /* bytes rounded up to 4096 */
 } lsf_blob_layout;
-lsf_status layer_blob_layout(const lsf_layer_cfg* cfg, int32_t format, lsf_blob_layout* out);
+LSF_API lsf_status layer_blob_layout(const lsf_layer_cfg* cfg, int32_t format, lsf_blob_layout* out);
 /* Point a lsf_layer_weights at a blob (host or device address). */
-lsf_status layer_weights_from_blob(const lsf_layer_cfg* cfg, int32_t format, const void* blob,
+LSF_API lsf_status layer_weights_from_blob(const lsf_layer_cfg* cfg, int32_t format, const void* blob,
                                    lsf_layer_weights* out);
 
 /* --------------------------------------------------- the streamed stack --
@@ -205,8 +212,11 @@ lsf_status layer_weights_from_blob(const lsf_layer_cfg* cfg, int32_t format, con
  * from page-locked host memory with an asynchronous host-to-device copy.
  * Order of one micro-batch: forward layers 0..L-1, head and loss, backward
  * layers L-1..0 (each re-read and recomputed; [TUTORIAL] item 3).  The two
- * layers still resident at the turn are reused unless
- * LSF_STACK_NO_TURN_REUSE is given (2L-2 copies per micro-batch instead of 2L).
+ * layers still resident at the turn are reused, and so are layers 0 and 1,
+ * which a full step leaves in the buffers for the next step's forward, unless
+ * LSF_STACK_NO_TURN_REUSE is given: 2L-2 copies for the first micro-batch,
+ * 2L-4 for each later one, instead of 2L.  Reuse assumes what the frozen base
+ * is: the host store does not change while the stack exists.
  */
 typedef struct lsf_stack lsf_stack;
 
@@ -226,8 +236,8 @@ typedef struct {
   uint32_t flags;           /* LSF_STACK_* */
 } lsf_stack_desc;
 
-lsf_status stack_create(const lsf_layer_cfg* cfg, const lsf_stack_desc* desc, lsf_stack** out);
-lsf_status stack_destroy(lsf_stack* st);
+LSF_API lsf_status stack_create(const lsf_layer_cfg* cfg, const lsf_stack_desc* desc, lsf_stack** out);
+LSF_API lsf_status stack_destroy(lsf_stack* st);
 
 #define LSF_MODE_STREAMED 0x0u   /* weights come through the two buffers */
 #define LSF_MODE_RESIDENT 0x1u   /* weights read in place from resident_store */
@@ -250,11 +260,11 @@ typedef struct {
   uint32_t mode;               /* LSF_MODE_* */
 } lsf_stack_io;
 
-size_t stack_workspace_bytes(const lsf_layer_cfg* cfg, int32_t vocab);
+LSF_API size_t stack_workspace_bytes(const lsf_layer_cfg* cfg, int32_t vocab);
 /* One SFT micro-batch: embedding gather, streamed forward, final RMSNorm,
  * lm_head, cross-entropy over next-token labels, lm_head input gradient,
  * streamed recompute + backward, LoRA gradients accumulated. */
-lsf_status stream_stack_step(lsf_stack* st, const lsf_stack_io* io);
+LSF_API lsf_status stream_stack_step(lsf_stack* st, const lsf_stack_io* io);
 
 /* Kernel classes timed with HIP events under LSF_STACK_TIMING (index into
  * lsf_stack_stats.kernel_ms / kernel_launches).  A GEMM's time includes its
@@ -277,9 +287,9 @@ typedef struct {
 } lsf_stack_stats;
 /* Counters and event timings since the last reset (or create).  Waits for the
  * recorded events, so it synchronises with the work they bracket. */
-lsf_status stack_stats(lsf_stack* st, lsf_stack_stats* out);
+LSF_API lsf_status stack_stats(lsf_stack* st, lsf_stack_stats* out);
 /* Zero the counters and drop the recorded events. */
-lsf_status stack_reset_stats(lsf_stack* st);
+LSF_API lsf_status stack_reset_stats(lsf_stack* st);
 
 #ifdef __cplusplus
 }

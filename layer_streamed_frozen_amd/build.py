@@ -21,7 +21,7 @@ OBJDIR = os.path.join(ROOT, "_build", "obj")
 SOURCES = ["nf4.hip", "gemm.hip", "lora.hip", "elementwise.hip", "attention.hip", "layer.cpp", "api.cpp"]
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     "-I" + os.path.join(ROOT, "include"),

@@ -238,7 +238,7 @@ lsf_status linear_fwd(const lsf_weight* w, int32_t format, int32_t n_out, int32_
   if (A != nullptr) {
     LoraDown d;
     d.M = tokens; d.K = n_in; d.X = x; d.ldx = n_in; d.nsec = 1; d.r = rank; d.mat[0] = A; d.scale = 1.0f;
-    d.U = l.U; d.ldu = rank;
+    d.U = l.U; d.ldu = rank; d.part = l.part; d.part_floats = l.part_floats;
     HIPCK(lora_down(d, S(stream)));
     g.ext.kx = rank; g.ext.u = l.U; g.ext.ldu = rank; g.ext.uscale = scale; g.ext.nsec = 1; g.ext.r = rank;
     g.ext.mat[0] = B; g.ext.row_off[1] = n_out;
@@ -260,11 +260,11 @@ lsf_status linear_bwd(const lsf_weight* w, int32_t format, int32_t n_out, int32_
   if (A != nullptr) {
     LoraDown d;
     d.M = tokens; d.K = n_in; d.X = x; d.ldx = n_in; d.nsec = 1; d.r = rank; d.mat[0] = A; d.scale = 1.0f;
-    d.U = l.U; d.ldu = rank;
+    d.U = l.U; d.ldu = rank; d.part = l.part; d.part_floats = l.part_floats;
     HIPCK(lora_down(d, S(stream)));
     LoraDown b;
     b.M = tokens; b.K = n_out; b.X = dy; b.ldx = n_out; b.nsec = 1; b.r = rank; b.mat[0] = B; b.bside = true;
-    b.ksec[0] = n_out; b.scale = scale; b.U = l.dU; b.ldu = rank;
+    b.ksec[0] = n_out; b.scale = scale; b.U = l.dU; b.ldu = rank; b.part = l.part; b.part_floats = l.part_floats;
     HIPCK(lora_down(b, S(stream)));
     g.ext.kx = rank; g.ext.u = l.dU; g.ext.ldu = rank; g.ext.nsec = 1; g.ext.r = rank; g.ext.mat[0] = A;
     g.ext.ldmat = n_in;
@@ -649,11 +649,14 @@ lsf_status stream_stack_step(lsf_stack* st, const lsf_stack_io* io) {
     return lw;
   };
 
-  // ---- forward: layer i computes from buffer i % 2 while i + 1 loads
+  // ---- forward: layer i computes from buffer i % 2 while i + 1 loads.  A
+  // full step ends with layers 1 and 0 in buffers 1 and 0, which is what the
+  // next forward reads first: the frozen store never changes, so they are
+  // reused unless LSF_STACK_NO_TURN_REUSE asks for every copy.
+  const bool reuse = !(st->d.flags & LSF_STACK_NO_TURN_REUSE);
   if (!resident) {
-    st->slot_layer[0] = st->slot_layer[1] = -1;  // buffers hold nothing valid across steps
-    if ((s = acquire(st, 0, 0, false))) return s;
-    if (L > 1 && (s = acquire(st, 1, 1, false))) return s;
+    if ((s = acquire(st, 0, 0, reuse))) return s;
+    if (L > 1 && (s = acquire(st, 1, 1, reuse))) return s;
   }
   for (int i = 0; i < L; ++i) {
     const int b = i & 1;
@@ -694,7 +697,6 @@ lsf_status stream_stack_step(lsf_stack* st, const lsf_stack_io* io) {
   HIPCK(rmsnorm_bwd(w.dhN, xL, io->final_norm, w.rstdN, nullptr, T, H, w.dx[L & 1], cs));
 
   // ---- backward: layers L-1 .. 0, layer j again from buffer j % 2
-  const bool reuse = !(st->d.flags & LSF_STACK_NO_TURN_REUSE);
   if (!resident) {
     if ((s = acquire(st, L - 1, (L - 1) & 1, reuse))) return s;
     if (L > 1 && (s = acquire(st, L - 2, (L - 2) & 1, reuse))) return s;

@@ -254,11 +254,11 @@ __device__ __forceinline__ void compute_tile(const uint16_t* As, const uint16_t*
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 
-template <bool NN>
+template <bool NN, int EPI>
 __device__ void epilogue(const GemmArgs& g, const EpiArgs& e, const f32x4 (&acc)[4][4], int m0, int ntile,
                          int lane, int wm, int wn, int z) {
   const int lr = lane & 15, lg = lane >> 4;
-  if (e.kind == EPI_SWIGLU) {
+  if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
     for (int mf = 0; mf < 4; ++mf)
 #pragma unroll
@@ -288,32 +288,26 @@ __device__ void epilogue(const GemmArgs& g, const EpiArgs& e, const f32x4 (&acc)
         const int m = m0 + wm * 64 + mf * 16 + lg * 4 + i;
         if (m >= g.M) continue;
         const float v = acc[mf][nf][i];
-        switch (e.kind) {
-          case EPI_F32:
-            static_cast<float*>(e.C)[(int64_t)z * g.M * g.N + (int64_t)m * e.ldc + n] = v;
-            break;
-          case EPI_BF16:
-            static_cast<uint16_t*>(e.C)[(int64_t)m * e.ldc + n] = f32_to_bf16(v);
-            break;
-          case EPI_RESID_BF16:
-            static_cast<uint16_t*>(e.C)[(int64_t)m * e.ldc + n] =
-                f32_to_bf16(bf16_to_f32(e.R[(int64_t)m * e.ldr + n]) + v);
-            break;
-          case EPI_SWIGLU_BWD: {
-            const float gv = bf16_to_f32(e.g[(int64_t)m * e.ldgu + n]);
-            const float uv = bf16_to_f32(e.u[(int64_t)m * e.ldgu + n]);
-            const float sg = 1.0f / (1.0f + __expf(-gv));
-            uint16_t* C = static_cast<uint16_t*>(e.C);
-            C[(int64_t)m * e.ldc + n] = f32_to_bf16(v * uv * sg * (1.0f + gv * (1.0f - sg)));
-            C[(int64_t)m * e.ldc + g.N + n] = f32_to_bf16(v * gv * sg);
-            break;
-          }
+        if constexpr (EPI == EPI_F32) {
+          static_cast<float*>(e.C)[(int64_t)z * g.M * g.N + (int64_t)m * e.ldc + n] = v;
+        } else if constexpr (EPI == EPI_BF16) {
+          static_cast<uint16_t*>(e.C)[(int64_t)m * e.ldc + n] = f32_to_bf16(v);
+        } else if constexpr (EPI == EPI_RESID_BF16) {
+          static_cast<uint16_t*>(e.C)[(int64_t)m * e.ldc + n] =
+              f32_to_bf16(bf16_to_f32(e.R[(int64_t)m * e.ldr + n]) + v);
+        } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+          const float gv = bf16_to_f32(e.g[(int64_t)m * e.ldgu + n]);
+          const float uv = bf16_to_f32(e.u[(int64_t)m * e.ldgu + n]);
+          const float sg = 1.0f / (1.0f + __expf(-gv));
+          uint16_t* C = static_cast<uint16_t*>(e.C);
+          C[(int64_t)m * e.ldc + n] = f32_to_bf16(v * uv * sg * (1.0f + gv * (1.0f - sg)));
+          C[(int64_t)m * e.ldc + g.N + n] = f32_to_bf16(v * gv * sg);
         }
       }
     }
 }
 
-template <bool NN, int FMT>
+template <bool NN, int FMT, int EPI>
 __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs g, EpiArgs e) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2 * TILE_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -363,20 +357,39 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs g, EpiArgs e) {
     }
     __syncthreads();
   }
-  epilogue<NN>(g, e, acc, m0, ntile, lane, wm, wn, z);
+  epilogue<NN, EPI>(g, e, acc, m0, ntile, lane, wm, wn, z);
+}
+
+template <bool NN, int EPI>
+hipError_t launch_fmt(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
+  const int mt = (g.M + BM - 1) / BM, nt = g.N / BN;
+  dim3 grid(mt * nt, 1, g.splits), block(NTHR);
+  switch (g.W.fmt) {
+    case FMT_NF4: hipLaunchKernelGGL((gemm_kernel<NN, FMT_NF4, EPI>), grid, block, 0, s, g, e); break;
+    case FMT_BF16: hipLaunchKernelGGL((gemm_kernel<NN, FMT_BF16, EPI>), grid, block, 0, s, g, e); break;
+    case FMT_NF4_DQ: hipLaunchKernelGGL((gemm_kernel<NN, FMT_NF4_DQ, EPI>), grid, block, 0, s, g, e); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <bool NN>
 hipError_t launch(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
-  const int mt = (g.M + BM - 1) / BM, nt = g.N / BN;
-  dim3 grid(mt * nt, 1, g.splits), block(NTHR);
-  switch (g.W.fmt) {
-    case FMT_NF4: hipLaunchKernelGGL((gemm_kernel<NN, FMT_NF4>), grid, block, 0, s, g, e); break;
-    case FMT_BF16: hipLaunchKernelGGL((gemm_kernel<NN, FMT_BF16>), grid, block, 0, s, g, e); break;
-    case FMT_NF4_DQ: hipLaunchKernelGGL((gemm_kernel<NN, FMT_NF4_DQ>), grid, block, 0, s, g, e); break;
-    default: return hipErrorInvalidValue;
+  switch (e.kind) {
+    case EPI_F32: return launch_fmt<NN, EPI_F32>(g, e, s);
+    case EPI_BF16: return launch_fmt<NN, EPI_BF16>(g, e, s);
+    case EPI_RESID_BF16:
+      if constexpr (!NN) return launch_fmt<NN, EPI_RESID_BF16>(g, e, s);
+      break;
+    case EPI_SWIGLU:
+      if constexpr (!NN) return launch_fmt<NN, EPI_SWIGLU>(g, e, s);
+      break;
+    case EPI_SWIGLU_BWD:
+      if constexpr (NN) return launch_fmt<NN, EPI_SWIGLU_BWD>(g, e, s);
+      break;
+    default: break;
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 __global__ void splitk_reduce_kernel(const float* part, int splits, int M, int N, EpiArgs e) {

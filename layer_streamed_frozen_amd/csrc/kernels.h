@@ -90,6 +90,8 @@ struct LoraDown {
   float* U = nullptr;
   int ldu = 0;
   bool bside = false;  // false: A-side [r, K]; true: B-side [K, r]
+  float* part = nullptr;  // scratch for the per-chunk partial products
+  size_t part_floats = 0;
 };
 hipError_t lora_down(const LoraDown& a, hipStream_t s);
 

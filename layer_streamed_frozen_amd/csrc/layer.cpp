@@ -157,6 +157,7 @@ hipError_t layer_forward(const lsf_layer_cfg& c, const lsf_layer_weights& w, con
     const bool any = pq[0] || pq[1] || pq[2];
     if (any) {
       LoraDown d;
+      d.part = ws.part; d.part_floats = ws.part_floats;
       d.M = T; d.K = H; d.X = ws.h1; d.ldx = H; d.nsec = 3; d.r = r;
       for (int i = 0; i < 3; ++i) d.mat[i] = pq[i] ? pq[i]->A : nullptr;
       d.scale = 1.0f; d.U = ws.Uqkv; d.ldu = 3 * r;
@@ -189,6 +190,7 @@ hipError_t layer_forward(const lsf_layer_cfg& c, const lsf_layer_weights& w, con
     g = GemmArgs(); g.M = T;
     if (po) {
       LoraDown d;
+      d.part = ws.part; d.part_floats = ws.part_floats;
       d.M = T; d.K = (int)z.Dq; d.X = ws.att; d.ldx = z.Dq; d.nsec = 1; d.r = r; d.mat[0] = po->A;
       d.scale = 1.0f; d.U = ws.Uo; d.ldu = r;
       CK(lora_down(d, s));
@@ -207,6 +209,7 @@ hipError_t layer_forward(const lsf_layer_cfg& c, const lsf_layer_weights& w, con
     g = GemmArgs(); g.M = T;
     if (any) {
       LoraDown d;
+      d.part = ws.part; d.part_floats = ws.part_floats;
       d.M = T; d.K = H; d.X = ws.h2; d.ldx = H; d.nsec = 2; d.r = r;
       for (int i = 0; i < 2; ++i) d.mat[i] = pg[i] ? pg[i]->A : nullptr;
       d.scale = 1.0f; d.U = ws.Ugu; d.ldu = 2 * r;
@@ -224,6 +227,7 @@ hipError_t layer_forward(const lsf_layer_cfg& c, const lsf_layer_weights& w, con
     const lsf_lora_proj* pd = proj(lora, PD);
     if (pd) {
       LoraDown d;
+      d.part = ws.part; d.part_floats = ws.part_floats;
       d.M = T; d.K = I; d.X = ws.a; d.ldx = I; d.nsec = 1; d.r = r; d.mat[0] = pd->A;
       d.scale = 1.0f; d.U = ws.Ud; d.ldu = r;
       CK(lora_down(d, s));
@@ -246,8 +250,10 @@ namespace {
 
 // dU = s * dY_sec B_sec for up to three column sections of dY.
 hipError_t lora_dU(const uint16_t* dY, int64_t ld, int T, int r, float sc, int nsec, const lsf_lora_proj* const* p,
-                   const int* xoff, const int* ksec, float* dU, hipStream_t s) {
+                   const int* xoff, const int* ksec, float* dU, const LayerWs& ws, hipStream_t s) {
   LoraDown d;
+  d.part = ws.part;
+  d.part_floats = ws.part_floats;
   d.M = T; d.X = dY; d.ldx = ld; d.nsec = nsec; d.r = r; d.bside = true; d.scale = sc; d.U = dU;
   d.ldu = nsec * r;
   d.K = ksec[0];
@@ -298,7 +304,7 @@ hipError_t layer_backward(const lsf_layer_cfg& c, const lsf_layer_weights& w, co
   {
     const lsf_lora_proj* p[1] = {proj(lora, PD)};
     const int xo[1] = {0}, ks[1] = {H};
-    if (p[0]) CK(lora_dU(dy, H, T, r, sc, 1, p, xo, ks, ws.dU, s));
+    if (p[0]) CK(lora_dU(dy, H, T, r, sc, 1, p, xo, ks, ws.dU, ws, s));
     GemmArgs g; g.M = T; g.N = I; g.K = H; g.A = dy; g.lda = H; g.W = weight_ref(w.down, fmt, I);
     if (p[0]) {
       g.ext.kx = r; g.ext.u = ws.dU; g.ext.ldu = r; g.ext.nsec = 1; g.ext.r = r; g.ext.mat[0] = p[0]->A;
@@ -316,7 +322,7 @@ hipError_t layer_backward(const lsf_layer_cfg& c, const lsf_layer_weights& w, co
     const lsf_lora_proj* p[2] = {proj(lora, PG), proj(lora, PU)};
     const bool any = p[0] || p[1];
     const int xo[2] = {0, I}, ks[2] = {I, I};
-    if (any) CK(lora_dU(ws.dgu, 2 * (int64_t)I, T, r, sc, 2, p, xo, ks, ws.dU, s));
+    if (any) CK(lora_dU(ws.dgu, 2 * (int64_t)I, T, r, sc, 2, p, xo, ks, ws.dU, ws, s));
     GemmArgs g; g.M = T; g.N = H; g.K = 2 * I; g.A = ws.dgu; g.lda = 2 * (int64_t)I;
     g.W = weight_ref(w.gate_up, fmt, H);
     if (any) {
@@ -336,7 +342,7 @@ hipError_t layer_backward(const lsf_layer_cfg& c, const lsf_layer_weights& w, co
   {
     const lsf_lora_proj* p[1] = {proj(lora, PO)};
     const int xo[1] = {0}, ks[1] = {H};
-    if (p[0]) CK(lora_dU(ws.dx2, H, T, r, sc, 1, p, xo, ks, ws.dU, s));
+    if (p[0]) CK(lora_dU(ws.dx2, H, T, r, sc, 1, p, xo, ks, ws.dU, ws, s));
     GemmArgs g; g.M = T; g.N = (int)z.Dq; g.K = H; g.A = ws.dx2; g.lda = H; g.W = weight_ref(w.o, fmt, z.Dq);
     if (p[0]) {
       g.ext.kx = r; g.ext.u = ws.dU; g.ext.ldu = r; g.ext.nsec = 1; g.ext.r = r; g.ext.mat[0] = p[0]->A;
@@ -366,7 +372,7 @@ hipError_t layer_backward(const lsf_layer_cfg& c, const lsf_layer_weights& w, co
     const bool any = p[0] || p[1] || p[2];
     const int qd = c.n_heads * c.head_dim, kd = c.n_kv_heads * c.head_dim;
     const int xo[3] = {0, qd, qd + kd}, ks[3] = {qd, kd, kd};
-    if (any) CK(lora_dU(ws.dqkv, z.Nqkv, T, r, sc, 3, p, xo, ks, ws.dU, s));
+    if (any) CK(lora_dU(ws.dqkv, z.Nqkv, T, r, sc, 3, p, xo, ks, ws.dU, ws, s));
     GemmArgs g; g.M = T; g.N = H; g.K = (int)z.Nqkv; g.A = ws.dqkv; g.lda = z.Nqkv;
     g.W = weight_ref(w.qkv, fmt, H);
     if (any) {

@@ -1,68 +1,104 @@
-// LoRA side paths that are not folded into the base GEMMs.
+// LoRA side paths that are not folded into the base GEMMs, on MFMA.
 //
-// lora_down: the rank-r projections U = s X A^T (forward) and dU = s dY B
-// (backward).  Skinny [M, K] x [K, r] products on MFMA: a workgroup owns 16
-// rows and 16 adapter columns of one section; its four waves split the
-// contraction and their partial tiles are summed in a fixed order in LDS.
+// lora_down: the rank-r projections U = X A^T (forward) and dU = s dY B
+// (backward): [M, K] x [K, r] with r <= 64 and K up to 28672.  The
+// contraction is cut into 256-wide chunks; a workgroup owns 64 rows and one
+// chunk of one section, stages that chunk of the adapter matrix in LDS as
+// bf16 [r][256] and runs v_mfma_f32_16x16x32_bf16 over it.  The per-chunk
+// partial products are then summed in a fixed order by a second kernel.
 //
 // lora_grad: the adapter gradients dA = dU^T X and dB = s dY^T U, reductions
-// over the tokens.  A lane owns one input/output feature and all r adapter
-// columns; the four waves of a workgroup take interleaved token rows and are
-// summed in a fixed order, then added (+=) into the fp32 gradient.  No atomics,
-// so the result is the same bits on every run.
+// over the tokens: Out[j, k] += scale * sum_t P[t, j] Q[t, k].  A workgroup
+// owns 64 columns k and all r rows j; each wave takes a quarter of the tokens
+// in 32-row chunks, staged in LDS so the MFMA operands can run along the token
+// axis (P transposed, Q gathered down its rows).  The four partial tiles are
+// summed in a fixed order and added (+=) into the fp32 gradient.  No atomics:
+// the same inputs give the same bits on every run.
 #include "common.h"
 #include "kernels.h"
 
 namespace lsf {
 namespace {
 
-__global__ __launch_bounds__(256) void lora_down_kernel(LoraDown a) {
-  __shared__ float red[4][16][17];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
-  const int m0 = blockIdx.x * 16;
-  const int sec = blockIdx.y;
-  const int j0 = blockIdx.z * 16;
+constexpr int KC = 256;       // contraction chunk of lora_down
+constexpr int MS_LD = KC + 8; // LDS row stride (bf16) of the staged adapter chunk
+
+__device__ __forceinline__ int off_r8(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
+
+__host__ __device__ __forceinline__ int sec_k(const LoraDown& a, int sec) {
+  return a.ksec[sec] > 0 ? a.ksec[sec] : a.K;
+}
+
+__global__ __launch_bounds__(256) void lora_down_part_kernel(LoraDown a, int nch_max) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ms[64 * MS_LD];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, lr = lane & 15, lg = lane >> 4;
+  const int sec = blockIdx.y / nch_max, c = blockIdx.y % nch_max;
+  const int Ks = sec_k(a, sec);
+  const int k0 = c * KC;
   const float* mat = a.mat[sec];
-  f32x4 acc = {0, 0, 0, 0};
-  if (mat != nullptr) {
-    const int m = m0 + lr;
-    const int j = j0 + lr;
-    const uint16_t* xrow = a.X + (int64_t)min(m, a.M - 1) * a.ldx + a.xoff[sec];
-    const int Ks = a.ksec[sec] > 0 ? a.ksec[sec] : a.K;
-    const int steps = Ks / 32;
-    for (int st = wid; st < steps; st += 4) {
-      const int k = st * 32 + lg * 8;
-      u32x4 xa = *reinterpret_cast<const u32x4*>(xrow + k);
-      if (m >= a.M) xa = u32x4{0, 0, 0, 0};
-      float v[8];
-      if (j < a.r) {
-        if (!a.bside) {
-          const float4* src = reinterpret_cast<const float4*>(mat + (int64_t)j * a.K + k);
-          const float4 p = src[0], q = src[1];
-          v[0] = p.x; v[1] = p.y; v[2] = p.z; v[3] = p.w; v[4] = q.x; v[5] = q.y; v[6] = q.z; v[7] = q.w;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = mat[(int64_t)(k + e) * a.r + j];
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = 0.0f;
-      }
-      const u32x4 bb = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                        pack_bf16x2(v[6], v[7])};
-      acc = mfma16x16x32(xa, bb, acc);
+  if (k0 >= Ks || mat == nullptr) return;  // uniform over the workgroup
+  const int kn = min(KC, Ks - k0);           // a multiple of 32
+  const int r = a.r;
+  // stage the adapter chunk as bf16 [j][k]
+  if (!a.bside) {
+    const int q4 = kn / 4;
+    for (int idx = tid; idx < r * q4; idx += 256) {
+      const int j = idx / q4, k = (idx - j * q4) * 4;
+      const float4 v = *reinterpret_cast<const float4*>(mat + (int64_t)j * Ks + k0 + k);
+      *reinterpret_cast<uint2*>(Ms + j * MS_LD + k) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+    }
+  } else {
+    const float* src = mat + (int64_t)k0 * r;
+    for (int f = tid; f < kn * r; f += 256) {
+      const int k = f / r, j = f - k * r;
+      Ms[j * MS_LD + k] = f32_to_bf16(src[f]);
     }
   }
-  // acc[i] = C[row lg*4 + i][col lr]
-#pragma unroll
-  for (int i = 0; i < 4; ++i) red[wid][lg * 4 + i][lr] = acc[i];
   __syncthreads();
-  if (tid < 256) {
-    const int row = tid >> 4, col = tid & 15;
-    const float v = ((red[0][row][col] + red[1][row][col]) + red[2][row][col]) + red[3][row][col];
-    const int m = m0 + row, j = j0 + col;
-    if (m < a.M && j < a.r) a.U[(int64_t)m * a.ldu + sec * a.r + j] = a.scale * v;
+  const int m = blockIdx.x * 64 + wid * 16 + lr;
+  const uint16_t* xrow = a.X + (int64_t)min(m, a.M - 1) * a.ldx + a.xoff[sec] + k0;
+  const int jt_n = (r + 15) / 16;
+  f32x4 acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+  for (int st = 0; st < kn / 32; ++st) {
+    const int k = st * 32 + lg * 8;
+    u32x4 xa = *reinterpret_cast<const u32x4*>(xrow + k);
+    if (m >= a.M) xa = u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      if (jt >= jt_n) break;
+      const int j = jt * 16 + lr;
+      u32x4 bb = {0, 0, 0, 0};
+      if (j < r) bb = *reinterpret_cast<const u32x4*>(Ms + j * MS_LD + k);
+      acc[jt] = mfma16x16x32(xa, bb, acc[jt]);
+    }
+  }
+  float* out = a.part + (size_t)(sec * nch_max + c) * a.M * r;
+  const int mb = blockIdx.x * 64 + wid * 16 + lg * 4;
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+    if (jt >= jt_n) break;
+    const int j = jt * 16 + lr;
+    if (j >= r) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (mb + i < a.M) out[(size_t)(mb + i) * r + j] = acc[jt][i];
+  }
+}
+
+__global__ __launch_bounds__(256) void lora_down_reduce_kernel(LoraDown a, int nch_max) {
+  const int64_t total = (int64_t)a.M * a.nsec * a.r;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int j = (int)(i % a.r);
+    const int64_t rest = i / a.r;
+    const int sec = (int)(rest % a.nsec);
+    const int64_t t = rest / a.nsec;
+    float v = 0.0f;
+    if (a.mat[sec] != nullptr) {
+      const int nch = (sec_k(a, sec) + KC - 1) / KC;
+      const float* p = a.part + (size_t)sec * nch_max * a.M * a.r + (size_t)t * a.r + j;
+      for (int c = 0; c < nch; ++c) v += p[(size_t)c * a.M * a.r];
+    }
+    a.U[t * a.ldu + sec * a.r + j] = a.scale * v;
   }
 }
 
@@ -70,33 +106,84 @@ struct GradBatch {
   LoraGradSec s[3];
 };
 
+constexpr int PS_LD = 40;  // LDS row stride (bf16) of the transposed P chunk
+
 template <int R>
-__global__ __launch_bounds__(256) void lora_grad_kernel(GradBatch gb, int T) {
-  __shared__ float red[4][R][64];
+__global__ __launch_bounds__(256) void lora_grad_kernel(GradBatch gb, int T, int cpw) {
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[4][32 * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[4][R * PS_LD];
+  __shared__ float red[4][R][65];
   const LoraGradSec& g = gb.s[blockIdx.y];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int q = blockIdx.x * 64 + lane;
-  if (blockIdx.x * 64 >= g.nq) return;  // whole workgroup idle for this section
-  const bool live = q < g.nq;
-  float acc[R];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, lr = lane & 15, lg = lane >> 4;
+  const int k0 = blockIdx.x * 64;
+  if (k0 >= g.nq) return;  // uniform over the workgroup
+  constexpr int JT = R / 16 > 0 ? R / 16 : 1;
+  f32x4 acc[JT][4];
 #pragma unroll
-  for (int j = 0; j < R; ++j) acc[j] = 0.0f;
-  for (int t = wid; t < T; t += 4) {
-    const float qv = live ? bf16_to_f32(g.Q[(int64_t)t * g.ldq + g.qoff + q]) : 0.0f;
-    const float* prow = g.P + (int64_t)t * g.ldp + g.pcol0;
+  for (int a = 0; a < JT; ++a)
 #pragma unroll
-    for (int j = 0; j < R; ++j) acc[j] = fmaf(prow[j], qv, acc[j]);
-  }
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0, 0, 0, 0};
+  for (int ci = 0; ci < cpw; ++ci) {
+    const int t0 = (wid * cpw + ci) * 32;
+    // Q chunk: 32 tokens x 64 columns
 #pragma unroll
-  for (int j = 0; j < R; ++j) red[wid][j][lane] = acc[j];
-  __syncthreads();
-  if (wid == 0 && live) {
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const float v = ((red[0][j][lane] + red[1][j][lane]) + red[2][j][lane]) + red[3][j][lane];
-      float* dst = g.transposed ? g.out + (int64_t)q * R + j : g.out + (int64_t)j * g.nq + q;
-      *dst += g.scale * v;
+    for (int i = 0; i < 4; ++i) {
+      const int idx = lane + 64 * i;
+      const int row = idx >> 3, ch = idx & 7;
+      const int t = t0 + row, k = k0 + ch * 8;
+      u32x4 v = {0, 0, 0, 0};
+      if (t < T && k < g.nq) v = *reinterpret_cast<const u32x4*>(g.Q + (int64_t)t * g.ldq + g.qoff + k);
+      *reinterpret_cast<u32x4*>(Qs[wid] + off_r8(row, ch)) = v;
     }
+    // P chunk, transposed to [j][t] bf16
+    {
+      const int t = lane >> 1, jh = (lane & 1) * (R / 2);
+      const bool ok = t0 + t < T;
+      const float* prow = g.P + (int64_t)(t0 + t) * g.ldp + g.pcol0 + jh;
+#pragma unroll
+      for (int e = 0; e < R / 2; ++e) Ps[wid][(jh + e) * PS_LD + t] = f32_to_bf16(ok ? prow[e] : 0.0f);
+    }
+    __syncthreads();
+    u32x4 af[JT];
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt)
+      af[jt] = (jt * 16 + lr < R) ? *reinterpret_cast<const u32x4*>(Ps[wid] + (jt * 16 + lr) * PS_LD + lg * 8)
+                                  : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf) {
+      const int col = nf * 16 + lr;
+      uint32_t w[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int t = lg * 8 + 2 * p;
+        const uint32_t lo = Qs[wid][off_r8(t, col >> 3) + (col & 7)];
+        const uint32_t hi = Qs[wid][off_r8(t + 1, col >> 3) + (col & 7)];
+        w[p] = lo | (hi << 16);
+      }
+      const u32x4 bf = {w[0], w[1], w[2], w[3]};
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt) acc[jt][nf] = mfma16x16x32(af[jt], bf, acc[jt][nf]);
+    }
+    __syncthreads();
+  }
+  // acc[jt][nf][i] = partial Out[jt*16 + lg*4 + i][nf*16 + lr]
+#pragma unroll
+  for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = jt * 16 + lg * 4 + i;
+        if (j < R) red[wid][j][nf * 16 + lr] = acc[jt][nf][i];
+      }
+  __syncthreads();
+  for (int o = tid; o < R * 64; o += 256) {
+    const int j = o >> 6, kk = o & 63;
+    const int k = k0 + kk;
+    if (k >= g.nq) continue;
+    const float v = ((red[0][j][kk] + red[1][j][kk]) + red[2][j][kk]) + red[3][j][kk];
+    float* dst = g.transposed ? g.out + (int64_t)k * R + j : g.out + (int64_t)j * g.nq + k;
+    *dst += g.scale * v;
   }
 }
 
@@ -104,8 +191,15 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(GradBatch gb, int T) {
 
 hipError_t lora_down(const LoraDown& a, hipStream_t s) {
   if (a.M <= 0 || a.nsec <= 0) return hipSuccess;
-  dim3 grid((a.M + 15) / 16, a.nsec, (a.r + 15) / 16);
-  hipLaunchKernelGGL(lora_down_kernel, grid, dim3(256), 0, s, a);
+  if (a.r <= 0 || a.r > 64 || a.part == nullptr) return hipErrorInvalidValue;
+  int nch_max = 0;
+  for (int i = 0; i < a.nsec; ++i) nch_max = std::max(nch_max, (sec_k(a, i) + KC - 1) / KC);
+  if ((size_t)a.nsec * nch_max * a.M * a.r > a.part_floats) return hipErrorInvalidValue;
+  dim3 grid((a.M + 63) / 64, a.nsec * nch_max);
+  hipLaunchKernelGGL(lora_down_part_kernel, grid, dim3(256), 0, s, a, nch_max);
+  const int64_t total = (int64_t)a.M * a.nsec * a.r;
+  const int blocks = (int)std::min<int64_t>((total + 255) / 256, 2048);
+  hipLaunchKernelGGL(lora_down_reduce_kernel, dim3(blocks), dim3(256), 0, s, a, nch_max);
   return hipGetLastError();
 }
 
@@ -117,13 +211,15 @@ hipError_t lora_grad(const LoraGradSec* secs, int nsec, int T, int r, hipStream_
     gb.s[i] = secs[i];
     maxq = std::max(maxq, secs[i].nq);
   }
+  const int chunks = (T + 31) / 32;
+  const int cpw = (chunks + 3) / 4;  // 32-token chunks per wave
   dim3 grid((maxq + 63) / 64, nsec);
   switch (r) {
-    case 4: hipLaunchKernelGGL(lora_grad_kernel<4>, grid, dim3(256), 0, s, gb, T); break;
-    case 8: hipLaunchKernelGGL(lora_grad_kernel<8>, grid, dim3(256), 0, s, gb, T); break;
-    case 16: hipLaunchKernelGGL(lora_grad_kernel<16>, grid, dim3(256), 0, s, gb, T); break;
-    case 32: hipLaunchKernelGGL(lora_grad_kernel<32>, grid, dim3(256), 0, s, gb, T); break;
-    case 64: hipLaunchKernelGGL(lora_grad_kernel<64>, grid, dim3(256), 0, s, gb, T); break;
+    case 4: hipLaunchKernelGGL(lora_grad_kernel<4>, grid, dim3(256), 0, s, gb, T, cpw); break;
+    case 8: hipLaunchKernelGGL(lora_grad_kernel<8>, grid, dim3(256), 0, s, gb, T, cpw); break;
+    case 16: hipLaunchKernelGGL(lora_grad_kernel<16>, grid, dim3(256), 0, s, gb, T, cpw); break;
+    case 32: hipLaunchKernelGGL(lora_grad_kernel<32>, grid, dim3(256), 0, s, gb, T, cpw); break;
+    case 64: hipLaunchKernelGGL(lora_grad_kernel<64>, grid, dim3(256), 0, s, gb, T, cpw); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

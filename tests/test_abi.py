@@ -1,0 +1,120 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and its host-side calls (layouts, workspace sizes, argument
+validation, error reporting) behave as documented.  No kernel is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from layer_streamed_frozen_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lsf.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from layer_streamed_frozen_amd import build
+        build.build()
+    return B.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^LSF_API\s+[\w\s\*]*?(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_core_calls():
+    names = declared_functions()
+    for core in ("nf4_quantize", "layer_fwd", "layer_bwd", "stream_stack_step"):
+        assert core in names
+    assert len(names) >= 18
+
+
+def test_every_declared_function_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        assert hasattr(lib, n)
+
+
+def test_blob_layout_of_8b_layer(lib):
+    from layer_streamed_frozen_amd.store import LLAMA8B
+    lay = B.layer_blob_layout(LLAMA8B.cfg(1, 512), B.FMT_NF4)
+    # packed q|k|v, o, gate|up, down, then their fp32 absmax, then two bf16 norms
+    sizes = [6144 * 4096 // 2, 4096 * 4096 // 2, 28672 * 4096 // 2, 4096 * 14336 // 2,
+             6144 * 4096 // 16, 4096 * 4096 // 16, 28672 * 4096 // 16, 4096 * 14336 // 16, 8192, 8192]
+    assert list(lay.off) == [sum(sizes[:i]) for i in range(10)]
+    assert lay.bytes == sum(sizes) == 122699776
+    assert lay.stride == 122699776
+    bf = B.layer_blob_layout(LLAMA8B.cfg(1, 512), B.FMT_BF16)
+    assert bf.bytes == 2 * 218103808 + 2 * 8192
+
+
+def test_workspace_sizes(lib):
+    from layer_streamed_frozen_amd.store import LLAMA8B
+    w1 = B.layer_workspace_bytes(LLAMA8B.cfg(1, 512))
+    w4 = B.layer_workspace_bytes(LLAMA8B.cfg(4, 512))
+    assert 0 < w1 < w4 < 8 * w1
+    assert B.stack_workspace_bytes(LLAMA8B.cfg(1, 512), 128256) > w1
+    assert B.linear_workspace_bytes(64, 256, 256, 8) > 0
+    assert B.linear_workspace_bytes(0, 256, 256, 8) == 0
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_invalid_arguments_are_rejected_before_any_launch(lib):
+    L = lib
+    st = L.nf4_quantize(None, 100, 64, None, None, None)
+    assert st == B.LSF_ERR_SHAPE and b"multiple of 64" in L.lsf_last_error()
+    assert L.nf4_quantize(None, 128, 32, None, None, None) == B.LSF_ERR_SHAPE
+    assert L.nf4_quantize(None, 128, 64, None, None, None) == B.LSF_ERR_INVALID_ARG
+    assert L.nf4_quantize(None, 0, 64, None, None, None) == B.LSF_OK
+    assert L.nf4_dequantize(8, 8, 128, 64, 8, None) == B.LSF_ERR_ALIGN  # misaligned pointers
+    assert L.layer_fwd(None, None, None, None, None, None, 0, None) == B.LSF_ERR_INVALID_ARG
+    from layer_streamed_frozen_amd.store import LLAMA8B
+    cfg = LLAMA8B.cfg(1, 512)
+    cfg.head_dim = 64
+    assert L.layer_fwd(ctypes.byref(cfg), None, None, None, None, None, 0, None) == B.LSF_ERR_SHAPE
+    cfg = LLAMA8B.cfg(1, 512)
+    cfg.rank = 12
+    assert L.layer_fwd(ctypes.byref(cfg), None, None, None, None, None, 0, None) == B.LSF_ERR_SHAPE
+    cfg = LLAMA8B.cfg(0, 512)
+    assert L.layer_bwd(ctypes.byref(cfg), None, None, None, None, None, None, 0, None) == B.LSF_ERR_SHAPE
+    cfg = LLAMA8B.cfg(1, 512)
+    cfg.n_kv_heads = 5
+    assert L.layer_workspace_bytes(ctypes.byref(cfg)) == 0
+    w = B.LayerWeights()
+    assert L.layer_fwd(ctypes.byref(LLAMA8B.cfg(1, 512)), ctypes.byref(w), None, None, None, None, 0,
+                       None) == B.LSF_ERR_ALIGN
+    # stack descriptor checks that need no device
+    d = B.StackDesc()
+    d.n_layers = 0
+    h = ctypes.c_void_p()
+    assert L.stack_create(ctypes.byref(LLAMA8B.cfg(1, 512)), ctypes.byref(d), ctypes.byref(h)) == \
+        B.LSF_ERR_INVALID_ARG
+    d.n_layers = 2
+    d.format = B.FMT_NF4
+    d.blob_stride = 1000
+    assert L.stack_create(ctypes.byref(LLAMA8B.cfg(1, 512)), ctypes.byref(d), ctypes.byref(h)) == B.LSF_ERR_SHAPE
+    d.blob_stride = 122699776
+    assert L.stack_create(ctypes.byref(LLAMA8B.cfg(1, 512)), ctypes.byref(d), ctypes.byref(h)) == \
+        B.LSF_ERR_INVALID_ARG  # no device buffers
+    assert L.stream_stack_step(None, None) == B.LSF_ERR_INVALID_ARG
+    assert L.stack_destroy(None) == B.LSF_OK
+
+
+def test_binding_raises_with_message(lib):
+    with pytest.raises(B.LsfError) as e:
+        B.check(lib.nf4_quantize(None, 100, 64, None, None, None))
+    assert e.value.status == B.LSF_ERR_SHAPE
+    assert "LSF_ERR_SHAPE" in str(e.value)

@@ -126,19 +126,31 @@ def test_run_to_run_determinism(small):
     assert same(a, small.snapshot())
 
 
-def test_copy_accounting(small):
-    B.stack_reset_stats(small.stack.handle)
-    small.step(mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
-    st = small.stack.stats()
+def test_copy_accounting():
+    s = Setup(SMALL, 4, 512, 1, 48, "cnt")
+    L = s.L
+    s.step(mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+    st = s.stack.stats()
     assert st.steps == 1
-    assert st.copies == 2 * small.L - 2          # the two layers resident at the turn are reused
-    assert st.bytes == st.copies * small.store.blob_bytes()
-    B.stack_reset_stats(small.stack.handle)
-    small.step(mode=B.MODE_STREAMED | B.MODE_FWD_ONLY)
-    assert small.stack.stats().copies == small.L
-    B.stack_reset_stats(small.stack.handle)
-    small.step(mode=B.MODE_RESIDENT | B.MODE_ZERO_GRADS)
-    assert small.stack.stats().copies == 0
+    assert st.copies == 2 * L - 2                # the two layers resident at the turn are reused
+    assert st.bytes == st.copies * s.store.blob_bytes()
+    a = s.snapshot()
+    B.stack_reset_stats(s.stack.handle)
+    s.step(mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+    assert s.stack.stats().copies == 2 * L - 4   # layers 0 and 1 are still resident from the last step
+    assert same(a, s.snapshot())
+    B.stack_reset_stats(s.stack.handle)
+    s.step(mode=B.MODE_STREAMED | B.MODE_FWD_ONLY)
+    assert s.stack.stats().copies == L - 2
+    B.stack_reset_stats(s.stack.handle)
+    s.step(mode=B.MODE_RESIDENT | B.MODE_ZERO_GRADS)
+    assert s.stack.stats().copies == 0
+    assert same(a, s.snapshot())
+    # after a forward-only step the buffers hold layers L-2 and L-1: layer 0 must be copied again
+    B.stack_reset_stats(s.stack.handle)
+    s.step(mode=B.MODE_STREAMED | B.MODE_FWD_ONLY)
+    s.step(mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+    assert same(a, s.snapshot())
 
 
 def test_no_turn_reuse_and_timing_give_same_bits():
@@ -148,6 +160,8 @@ def test_no_turn_reuse_and_timing_give_same_bits():
     st = s.stack.stats()
     assert st.copies == 2 * s.L
     assert st.copy_ms > 0.0
+    assert st.kernel_launches[B.KERNELS.index("gate_up_fwd")] == 2 * s.L  # forward + recompute
+    assert st.kernel_launches[B.KERNELS.index("down_bwd")] == s.L
     a = s.snapshot()
     s.step(mode=B.MODE_RESIDENT | B.MODE_ZERO_GRADS)
     assert same(a, s.snapshot())
