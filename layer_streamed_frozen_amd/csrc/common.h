@@ -28,6 +28,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float a) {
   return (uint16_t)(pack_bf16x2(a, 0.0f) & 0xFFFFu);
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane s supplies the address of 4 consecutive bf16 values S[s][0..3]; lane i
+// receives O[i][k] = S[(i >> 2) + 4k][i & 3].  So if lane s points at row
+// base + (s >> 2), column cbase + 4 (s & 3) of a row-major tile, lane i gets
+// column cbase + i of rows base .. base + 3: an MFMA operand whose contraction
+// runs down the rows.
+typedef short lsf_v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr4(const uint16_t* base, int off) {
+  const lsf_v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) lsf_v4s*)(base + off));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);

@@ -12,23 +12,34 @@
 // rank-r activations U (already scaled) and the adapter matrix form a 64-wide
 // extension of A and W, so the scaled add happens inside the accumulator.
 //
-// Tiling: 256 threads = 4 waves (2 x 2), 128 x 128 C tile, 64-deep k tiles,
-// v_mfma_f32_16x16x32_bf16, LDS double-buffered (64 KB per workgroup, two
-// workgroups per CU).  Split-K over grid.z with a fixed-order reduction keeps
-// results deterministic.
+// Tiling: BM x 128 C tiles (BM = 128 or 256), 64-deep k tiles, waves of 64x64
+// (2 across N, BM/64 down M), v_mfma_f32_16x16x32_bf16, LDS double-buffered.
+// A 256-row tile decodes each weight once for twice the rows.  The forward
+// loop keeps two register stages (prefetch distance 2) and issues the decode
+// of the next tile between the MFMAs of the current one.  The input-gradient
+// GEMM reads its B operand with transposing LDS loads (ds_read_b64_tr_b16)
+// because its contraction runs down the weight's rows.  Split-K over grid.z
+// with a fixed-order reduction keeps results deterministic.
 #include "common.h"
 #include "kernels.h"
 
 namespace lsf {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64, NTHR = 256;
-constexpr int TILE_ELEMS = BM * BK;  // 8192 bf16 per operand tile
+constexpr int BN = 128, BK = 64;
+
+template <int BM>
+struct Cfg {
+  static constexpr int NTHR = BM * 2;            // one 64x64 wave tile per 64 rows x 64 columns
+  static constexpr int A_ELEMS = BM * BK;
+  static constexpr int STAGE = A_ELEMS + BK * BN;
+  static constexpr int UNIT = (BN * BK) / NTHR;  // weights each thread decodes per tile: 32 or 16
+  static constexpr int MIN_BLOCKS = 512 / NTHR;  // eight waves per CU
+};
 
 // LDS layouts (in bf16 elements).  R8: 64 bf16 per row (8 chunks of 16 B),
 // chunk' = chunk ^ (row & 7).  R16: 128 bf16 per row (16 chunks), chunk' =
-// chunk ^ swz16(row), which keeps both 16-B row reads and 2-B column gathers
-// (8 consecutive rows per lane group) free of bank conflicts.
+// chunk ^ swz16(row).
 __device__ __forceinline__ int swz16(int row) { return (row & 15) ^ (((row >> 4) & 1) << 2); }
 __device__ __forceinline__ int off_r8(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
 __device__ __forceinline__ int off_r16(int row, int chunk) { return row * 128 + ((chunk ^ swz16(row)) << 3); }
@@ -41,6 +52,7 @@ __device__ __forceinline__ void lds_write16(uint16_t* base, int off, const u32x4
 }
 
 __device__ __forceinline__ u32x4 gload16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x2 gload8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
 
 // Row of the weight that feeds physical tile column c (NT).
 __device__ __forceinline__ int64_t nt_wrow(const GemmArgs& g, int ntile, int c) {
@@ -49,15 +61,6 @@ __device__ __forceinline__ int64_t nt_wrow(const GemmArgs& g, int ntile, int c) 
     return ((c >> 4) & 1) ? (int64_t)g.pair_I + j : (int64_t)j;
   }
   return (int64_t)ntile * BN + c;
-}
-
-__device__ __forceinline__ void decode32(float absmax, const u32x4& q, u32x4 out[4]) {
-  const Nf4Table t = nf4_table(absmax);
-  uint32_t o[4];
-  nf4_decode8(t, q.x, o); out[0] = u32x4{o[0], o[1], o[2], o[3]};
-  nf4_decode8(t, q.y, o); out[1] = u32x4{o[0], o[1], o[2], o[3]};
-  nf4_decode8(t, q.z, o); out[2] = u32x4{o[0], o[1], o[2], o[3]};
-  nf4_decode8(t, q.w, o); out[3] = u32x4{o[0], o[1], o[2], o[3]};
 }
 
 // Absmax of the 64-block holding element e of an NF4_DQ weight: 8-bit code
@@ -78,83 +81,96 @@ struct Stage {
   float absmax;
 };
 
-template <bool NN, int FMT>
+template <int BM, bool NN, int FMT>
 __device__ __forceinline__ void load_main(const GemmArgs& g, int m0, int ntile, int k0, int tid, Stage& st) {
-  // A tile: 128 rows x 64 k, 4 chunks of 16 B per thread.
+  using C = Cfg<BM>;
+  // A tile: BM rows x 64 k, 4 chunks of 16 B per thread.
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int idx = tid + NTHR * i;
+    const int idx = tid + C::NTHR * i;
     const int row = idx >> 3, ch = idx & 7;
     const int gm = m0 + row;
     st.a[i] = (gm < g.M) ? gload16(g.A + (int64_t)gm * g.lda + k0 + ch * 8) : u32x4{0, 0, 0, 0};
   }
-  if constexpr (!NN) {
-    if constexpr (FMT == FMT_BF16) {
+  if constexpr (FMT == FMT_BF16) {
+    constexpr int PER = 1024 / C::NTHR;  // 16-byte chunks of the weight tile per thread
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int idx = tid + NTHR * i;
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + C::NTHR * i;
+      if constexpr (!NN) {
         const int row = idx >> 3, ch = idx & 7;
         st.b[i] = gload16(g.W.bf16 + nt_wrow(g, ntile, row) * g.W.ld + k0 + ch * 8);
+      } else {
+        const int row = idx >> 4, ch = idx & 15;
+        st.b[i] = gload16(g.W.bf16 + (int64_t)(k0 + row) * g.W.ld + ntile * BN + ch * 8);
       }
-    } else {
-      const int row = tid >> 1, h = tid & 1;
-      const int64_t e = nt_wrow(g, ntile, row) * g.W.ld + k0;
-      st.b[0] = gload16(g.W.packed + (e >> 1) + h * 16);
-      st.absmax = block_absmax(g.W, e);
     }
   } else {
-    const int n0 = ntile * BN;
-    if constexpr (FMT == FMT_BF16) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int idx = tid + NTHR * i;
-        const int row = idx >> 4, ch = idx & 15;
-        st.b[i] = gload16(g.W.bf16 + (int64_t)(k0 + row) * g.W.ld + n0 + ch * 8);
-      }
+    constexpr int U = C::UNIT;
+    int64_t e;
+    if constexpr (!NN) {
+      const int per_row = BK / U;  // units per weight row
+      const int row = tid / per_row, q = tid % per_row;
+      e = nt_wrow(g, ntile, row) * g.W.ld + k0 + q * U;
     } else {
-      const int row = tid >> 2, seg = tid & 3;
-      const int64_t e = (int64_t)(k0 + row) * g.W.ld + n0 + seg * 32;
-      st.b[0] = gload16(g.W.packed + (e >> 1));
-      st.absmax = block_absmax(g.W, e);
+      const int per_row = BN / U;
+      const int row = tid / per_row, q = tid % per_row;
+      e = (int64_t)(k0 + row) * g.W.ld + ntile * BN + q * U;
     }
+    if constexpr (U == 32) st.b[0] = gload16(g.W.packed + (e >> 1));
+    else {
+      const u32x2 v = gload8(g.W.packed + (e >> 1));
+      st.b[0] = u32x4{v.x, v.y, 0, 0};
+    }
+    st.absmax = block_absmax(g.W, e);
   }
 }
 
-template <bool NN, int FMT>
+template <int BM, bool NN, int FMT>
 __device__ __forceinline__ void store_main(const Stage& st, int tid, uint16_t* As, uint16_t* Bs) {
+  using C = Cfg<BM>;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int idx = tid + NTHR * i;
+    const int idx = tid + C::NTHR * i;
     lds_write16(As, off_r8(idx >> 3, idx & 7), st.a[i]);
   }
   if constexpr (FMT == FMT_BF16) {
+    constexpr int PER = 1024 / C::NTHR;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + NTHR * i;
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + C::NTHR * i;
       if constexpr (!NN) lds_write16(Bs, off_r8(idx >> 3, idx & 7), st.b[i]);
       else lds_write16(Bs, off_r16(idx >> 4, idx & 15), st.b[i]);
     }
   } else {
-    u32x4 d[4];
-    decode32(st.absmax, st.b[0], d);
-    if constexpr (!NN) {
-      const int row = tid >> 1, h = tid & 1;
+    constexpr int U = C::UNIT;
+    constexpr int NW = U / 8;  // packed dwords per thread
+    const Nf4Table t = nf4_table(st.absmax);
+    const uint32_t q[4] = {st.b[0].x, st.b[0].y, st.b[0].z, st.b[0].w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lds_write16(Bs, off_r8(row, h * 4 + i), d[i]);
-    } else {
-      const int row = tid >> 2, seg = tid & 3;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lds_write16(Bs, off_r16(row, seg * 4 + i), d[i]);
+    for (int i = 0; i < NW; ++i) {
+      uint32_t o[4];
+      nf4_decode8(t, q[i], o);
+      const u32x4 v = {o[0], o[1], o[2], o[3]};
+      if constexpr (!NN) {
+        const int per_row = BK / U;
+        const int row = tid / per_row, qq = tid % per_row;
+        lds_write16(Bs, off_r8(row, qq * NW + i), v);
+      } else {
+        const int per_row = BN / U;
+        const int row = tid / per_row, qq = tid % per_row;
+        lds_write16(Bs, off_r16(row, qq * NW + i), v);
+      }
     }
   }
 }
 
 // LoRA extension tile number `xt` written straight into LDS.
-template <bool NN>
+template <int BM, bool NN>
 __device__ void store_ext(const GemmArgs& g, int m0, int ntile, int xt, int tid, uint16_t* As, uint16_t* Bs) {
   const LoraExt& x = g.ext;
   const int jb = xt * BK;
-  {  // A: 128 rows x 64 columns of U, scaled, rounded to bf16
+  {  // A: BM rows x 64 columns of U, scaled, rounded to bf16
     const int row = tid >> 1, h = tid & 1;
     const int gm = m0 + row;
     uint32_t w[16];
@@ -172,6 +188,7 @@ __device__ void store_ext(const GemmArgs& g, int m0, int ntile, int xt, int tid,
     for (int i = 0; i < 4; ++i)
       lds_write16(As, off_r8(row, h * 4 + i), u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]});
   }
+  if (tid >= 256) return;
   if constexpr (!NN) {  // B: tile row c = weight row, column = U column j
     const int row = tid >> 1, h = tid & 1;
     const int64_t wr = nt_wrow(g, ntile, row);
@@ -232,23 +249,38 @@ __device__ __forceinline__ void compute_tile(const uint16_t* As, const uint16_t*
       if constexpr (!NN) {
         bf[nf] = lds_read16(Bs, off_r8(wn * 64 + nf * 16 + lr, s * 4 + lg));
       } else {
-        const int n = wn * 64 + nf * 16 + lr;
-        const int ch = n >> 3, e = n & 7;
-        uint32_t w[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int c0 = s * 32 + lg * 8 + 2 * p;
-          const uint32_t lo = Bs[off_r16(c0, ch) + e];
-          const uint32_t hi = Bs[off_r16(c0 + 1, ch) + e];
-          w[p] = lo | (hi << 16);
-        }
-        bf[nf] = u32x4{w[0], w[1], w[2], w[3]};
+        // Contraction runs down the tile rows: two transposing 8-byte reads
+        // give this lane (column nbase + lr) rows c..c+3 and c+4..c+7.
+        const int col = wn * 64 + nf * 16 + 4 * (lr & 3);
+        const int row = s * 32 + lg * 8 + (lr >> 2);
+        const u32x2 lo = lds_read_tr4(Bs, off_r16(row, col >> 3) + (col & 7));
+        const u32x2 hi = lds_read_tr4(Bs, off_r16(row + 4, col >> 3) + (col & 7));
+        bf[nf] = u32x4{lo.x, lo.y, hi.x, hi.y};
       }
     }
 #pragma unroll
     for (int mf = 0; mf < 4; ++mf)
 #pragma unroll
       for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mfma16x16x32(af[mf], bf[nf], acc[mf][nf]);
+  }
+}
+
+// One 64-deep k tile of MFMAs from (As, Bs) and, in the same basic block, the
+// decode + LDS store of the next tile (staged in st) into (An, Bn), so the
+// decode's VALU work issues between the MFMAs instead of after them.
+template <int BM, bool NN, int FMT>
+__device__ __forceinline__ void compute_and_stage(const uint16_t* As, const uint16_t* Bs, const Stage& st, int tid,
+                                                  uint16_t* An, uint16_t* Bn, int lane, int wm, int wn,
+                                                  f32x4 (&acc)[4][4]) {
+  compute_tile<NN>(As, Bs, lane, wm, wn, acc);
+  store_main<BM, NN, FMT>(st, tid, An, Bn);
+  if constexpr (FMT != FMT_BF16) {
+    constexpr int V = Cfg<BM>::UNIT == 32 ? 6 : 4;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, V, 0);  // then a few VALU
+    }
   }
 }
 
@@ -307,9 +339,10 @@ __device__ void epilogue(const GemmArgs& g, const EpiArgs& e, const f32x4 (&acc)
     }
 }
 
-template <bool NN, int FMT, int EPI>
-__global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs g, EpiArgs e) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2 * TILE_ELEMS];
+template <int BM, bool NN, int FMT, int EPI>
+__global__ __launch_bounds__(Cfg<BM>::NTHR, Cfg<BM>::MIN_BLOCKS) void gemm_kernel(GemmArgs g, EpiArgs e) {
+  using C = Cfg<BM>;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][C::STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
   const int mt = (g.M + BM - 1) / BM, nt = g.N / BN;
@@ -326,7 +359,6 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs g, EpiArgs e) {
   const int ke = min(kch, kb + per);
   const int nmain = max(0, ke - kb);
   const int next = (z == g.splits - 1 && g.ext.kx > 0) ? (g.ext.kx + BK - 1) / BK : 0;
-  const int iters = nmain + next;
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -334,62 +366,96 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs g, EpiArgs e) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
 
-  Stage st;
-  if (iters > 0) {
+  uint16_t* b0 = lds[0];
+  uint16_t* b1 = lds[1];
+  if constexpr (NN) {
+    // Input-gradient GEMM: one register stage.
+    Stage st;
     if (nmain > 0) {
-      load_main<NN, FMT>(g, m0, ntile, kb * BK, tid, st);
-      store_main<NN, FMT>(st, tid, lds[0], lds[0] + TILE_ELEMS);
-    } else {
-      store_ext<NN>(g, m0, ntile, 0, tid, lds[0], lds[0] + TILE_ELEMS);
+      load_main<BM, NN, FMT>(g, m0, ntile, kb * BK, tid, st);
+      store_main<BM, NN, FMT>(st, tid, b0, b0 + C::A_ELEMS);
+    }
+    __syncthreads();
+    for (int i = 0; i < nmain; ++i) {
+      const bool pre = i + 1 < nmain;
+      if (pre) load_main<BM, NN, FMT>(g, m0, ntile, (kb + i + 1) * BK, tid, st);
+      uint16_t* cur = lds[i & 1];
+      compute_tile<NN>(cur, cur + C::A_ELEMS, lane, wm, wn, acc);
+      if (pre) store_main<BM, NN, FMT>(st, tid, lds[(i + 1) & 1], lds[(i + 1) & 1] + C::A_ELEMS);
+      __syncthreads();
+    }
+  } else {
+    // Forward GEMM: two register stages and two LDS buffers.  Iteration i
+    // computes tile i from buffer i&1 while the decode of tile i+1 (loaded
+    // one iteration earlier) fills the other buffer and tile i+2 loads.
+    Stage s0, s1;
+    if (nmain > 0) load_main<BM, NN, FMT>(g, m0, ntile, kb * BK, tid, s0);
+    if (nmain > 1) load_main<BM, NN, FMT>(g, m0, ntile, (kb + 1) * BK, tid, s1);
+    if (nmain > 0) store_main<BM, NN, FMT>(s0, tid, b0, b0 + C::A_ELEMS);
+    __syncthreads();
+    int it = 0;
+    for (; it + 1 < nmain; it += 2) {
+      if (it + 2 < nmain) load_main<BM, NN, FMT>(g, m0, ntile, (kb + it + 2) * BK, tid, s0);
+      compute_and_stage<BM, NN, FMT>(b0, b0 + C::A_ELEMS, s1, tid, b1, b1 + C::A_ELEMS, lane, wm, wn, acc);
+      __syncthreads();
+      if (it + 2 < nmain) {
+        if (it + 3 < nmain) load_main<BM, NN, FMT>(g, m0, ntile, (kb + it + 3) * BK, tid, s1);
+        compute_and_stage<BM, NN, FMT>(b1, b1 + C::A_ELEMS, s0, tid, b0, b0 + C::A_ELEMS, lane, wm, wn, acc);
+      } else {
+        compute_tile<NN>(b1, b1 + C::A_ELEMS, lane, wm, wn, acc);
+      }
+      __syncthreads();
+    }
+    if (it < nmain) {  // odd tile count: the last tile sits in b0
+      compute_tile<NN>(b0, b0 + C::A_ELEMS, lane, wm, wn, acc);
+      __syncthreads();
     }
   }
-  __syncthreads();
-  for (int it = 0; it < iters; ++it) {
-    const int nx = it + 1;
-    const bool pre = nx < nmain;
-    if (pre) load_main<NN, FMT>(g, m0, ntile, (kb + nx) * BK, tid, st);
-    uint16_t* cur = lds[it & 1];
-    compute_tile<NN>(cur, cur + TILE_ELEMS, lane, wm, wn, acc);
-    if (nx < iters) {
-      uint16_t* nb = lds[nx & 1];
-      if (pre) store_main<NN, FMT>(st, tid, nb, nb + TILE_ELEMS);
-      else store_ext<NN>(g, m0, ntile, nx - nmain, tid, nb, nb + TILE_ELEMS);
-    }
+  // LoRA extension steps (last split only)
+  for (int xt = 0; xt < next; ++xt) {
+    store_ext<BM, NN>(g, m0, ntile, xt, tid, b0, b0 + C::A_ELEMS);
+    __syncthreads();
+    compute_tile<NN>(b0, b0 + C::A_ELEMS, lane, wm, wn, acc);
     __syncthreads();
   }
   epilogue<NN, EPI>(g, e, acc, m0, ntile, lane, wm, wn, z);
 }
 
-template <bool NN, int EPI>
+template <int BM, bool NN, int EPI>
 hipError_t launch_fmt(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
   const int mt = (g.M + BM - 1) / BM, nt = g.N / BN;
-  dim3 grid(mt * nt, 1, g.splits), block(NTHR);
+  dim3 grid(mt * nt, 1, g.splits), block(Cfg<BM>::NTHR);
   switch (g.W.fmt) {
-    case FMT_NF4: hipLaunchKernelGGL((gemm_kernel<NN, FMT_NF4, EPI>), grid, block, 0, s, g, e); break;
-    case FMT_BF16: hipLaunchKernelGGL((gemm_kernel<NN, FMT_BF16, EPI>), grid, block, 0, s, g, e); break;
-    case FMT_NF4_DQ: hipLaunchKernelGGL((gemm_kernel<NN, FMT_NF4_DQ, EPI>), grid, block, 0, s, g, e); break;
+    case FMT_NF4: hipLaunchKernelGGL((gemm_kernel<BM, NN, FMT_NF4, EPI>), grid, block, 0, s, g, e); break;
+    case FMT_BF16: hipLaunchKernelGGL((gemm_kernel<BM, NN, FMT_BF16, EPI>), grid, block, 0, s, g, e); break;
+    case FMT_NF4_DQ: hipLaunchKernelGGL((gemm_kernel<BM, NN, FMT_NF4_DQ, EPI>), grid, block, 0, s, g, e); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <bool NN>
-hipError_t launch(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
+template <int BM, bool NN>
+hipError_t launch_bm(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
   switch (e.kind) {
-    case EPI_F32: return launch_fmt<NN, EPI_F32>(g, e, s);
-    case EPI_BF16: return launch_fmt<NN, EPI_BF16>(g, e, s);
+    case EPI_F32: return launch_fmt<BM, NN, EPI_F32>(g, e, s);
+    case EPI_BF16: return launch_fmt<BM, NN, EPI_BF16>(g, e, s);
     case EPI_RESID_BF16:
-      if constexpr (!NN) return launch_fmt<NN, EPI_RESID_BF16>(g, e, s);
+      if constexpr (!NN) return launch_fmt<BM, NN, EPI_RESID_BF16>(g, e, s);
       break;
     case EPI_SWIGLU:
-      if constexpr (!NN) return launch_fmt<NN, EPI_SWIGLU>(g, e, s);
+      if constexpr (!NN) return launch_fmt<BM, NN, EPI_SWIGLU>(g, e, s);
       break;
     case EPI_SWIGLU_BWD:
-      if constexpr (NN) return launch_fmt<NN, EPI_SWIGLU_BWD>(g, e, s);
+      if constexpr (NN) return launch_fmt<BM, NN, EPI_SWIGLU_BWD>(g, e, s);
       break;
     default: break;
   }
   return hipErrorInvalidValue;
+}
+
+template <bool NN>
+hipError_t launch(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
+  return gemm_tile_rows(g.M, g.N, NN) == 256 ? launch_bm<256, NN>(g, e, s) : launch_bm<128, NN>(g, e, s);
 }
 
 __global__ void splitk_reduce_kernel(const float* part, int splits, int M, int N, EpiArgs e) {
@@ -419,6 +485,14 @@ __global__ void splitk_reduce_kernel(const float* part, int splits, int M, int N
 }
 
 }  // namespace
+
+// Measured on MI355X at 512 and 2048 tokens: 256-row tiles are faster for the
+// input-gradient GEMMs and for forward GEMMs with N <= 4096 (o, down); the
+// wide forward GEMMs (q|k|v, gate|up) are faster with 128-row tiles.
+int gemm_tile_rows(int M, int N, bool nn) {
+  if (M < 256) return 128;
+  return (nn || N <= 4096) ? 256 : 128;
+}
 
 hipError_t gemm_nt(const GemmArgs& g, const EpiArgs& e, hipStream_t s) { return launch<false>(g, e, s); }
 hipError_t gemm_nn(const GemmArgs& g, const EpiArgs& e, hipStream_t s) { return launch<true>(g, e, s); }

@@ -63,6 +63,8 @@ struct EpiArgs {
   int64_t ldgu = 0;
 };
 
+// Rows of the C tile (128 or 256) a GEMM of M x N uses; columns are 128.
+int gemm_tile_rows(int M, int N, bool nn);
 // C = A W^T (+ LoRA), W rows map to C columns.
 hipError_t gemm_nt(const GemmArgs& g, const EpiArgs& e, hipStream_t s);
 // C = A W (+ LoRA), contraction over W rows.

@@ -111,7 +111,8 @@ int choose_splits(int tiles, int K) {
 }
 
 hipError_t run_gemm(bool nn, GemmArgs g, const EpiArgs& e, float* part, size_t part_floats, hipStream_t s) {
-  const int tiles = ((g.M + 127) / 128) * (g.N / 128);
+  const int bm = gemm_tile_rows(g.M, g.N, nn);
+  const int tiles = ((g.M + bm - 1) / bm) * (g.N / 128);
   int splits = (e.kind == EPI_SWIGLU || part == nullptr) ? 1 : choose_splits(tiles, g.K);
   while (splits > 1 && (size_t)splits * g.M * g.N > part_floats) splits /= 2;
   g.splits = splits;
