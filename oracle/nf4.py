@@ -133,3 +133,70 @@ def nf4_dequantize_bf16(packed, absmax, blocksize=BLOCKSIZE):
 def nf4_dequantize(packed, absmax, shape, blocksize=BLOCKSIZE):
     """Dequantised weight as the fp32 values of its bf16 rounding, reshaped."""
     return bf16_to_f32(nf4_dequantize_bf16(packed, absmax, blocksize)).reshape(shape)
+
+
+# ------------------------------------------------------ double quantisation
+#
+# The pages' store and buffer sizes (3.60 GB over 32 layers, 113 MB per layer;
+# review "repodaily.xyz/zh/projects/2026-08-17/soup/", architecture section)
+# fit NF4 codes plus an 8-bit absmax, QLoRA's "double quantisation", but the
+# pages do not give the second-level code.  Reading taken here (plain affine
+# 8-bit, no codebook): the fp32 absmax values are grouped 256 at a time (in
+# block order); per group offset = min, scale = fp32((max - min) / 255);
+# code = clamp(rint(fp32(fp32(a - offset) / scale)), 0, 255) with
+# round-half-to-even (code 0 when scale is 0).  The stored absmax is
+# a' = fp32(fp32(code * scale) + offset).  NF4 codes are still chosen against
+# the exact absmax; only the scale that dequantisation multiplies by is a'.
+#
+# Parity: pinned (NF4 codes equal the single-level ones; brute-force nearest
+# of the 256 levels; group minimum reconstructs exactly; error bound scale/2).
+
+DQ_GROUP = 256
+
+
+def dq_encode_absmax(absmax):
+    """8-bit codes of the absmax values and the per-group (scale, offset).
+
+    Returns (codes uint8 [nb], scale2 fp32 [ngroups, 2]) with columns
+    (scale, offset)."""
+    a = np.ascontiguousarray(absmax, dtype=np.float32).reshape(-1)
+    ng = (a.size + DQ_GROUP - 1) // DQ_GROUP
+    codes = np.zeros(a.size, dtype=np.uint8)
+    s2 = np.zeros((ng, 2), dtype=np.float32)
+    for gi in range(ng):
+        grp = a[gi * DQ_GROUP:(gi + 1) * DQ_GROUP]
+        lo, hi = np.float32(grp.min()), np.float32(grp.max())
+        scale = np.float32((hi - lo) / np.float32(255.0))
+        if scale > 0:
+            q = np.rint(((grp - lo).astype(np.float32) / scale).astype(np.float32))
+            codes[gi * DQ_GROUP:gi * DQ_GROUP + grp.size] = np.clip(q, 0, 255).astype(np.uint8)
+        s2[gi] = (scale, lo)
+    return codes, s2
+
+
+def dq_decode_absmax(codes, scale2):
+    """a' = fp32(fp32(code * scale) + offset) for every block."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8).reshape(-1)
+    g = np.arange(c.size) // DQ_GROUP
+    scale = scale2[g, 0].astype(np.float32)
+    off = scale2[g, 1].astype(np.float32)
+    return ((c.astype(np.float32) * scale).astype(np.float32) + off).astype(np.float32)
+
+
+def nf4dq_quantize(w, blocksize=BLOCKSIZE):
+    """NF4 with a double-quantised absmax.
+
+    Returns (packed uint8 [n/2], absmax codes uint8 [n/bs], scale2 fp32
+    [ceil(n/bs/256), 2], exact absmax fp32 [n/bs])."""
+    codes, absmax = nf4_codes(w, blocksize)
+    aq, s2 = dq_encode_absmax(absmax)
+    return nf4_pack(codes), aq, s2, absmax
+
+
+def nf4dq_dequantize_bf16(packed, absq, scale2, blocksize=BLOCKSIZE):
+    """bf16 bits of c[code] * a' (flat)."""
+    return nf4_dequantize_bf16(packed, dq_decode_absmax(absq, scale2), blocksize)
+
+
+def nf4dq_dequantize(packed, absq, scale2, shape, blocksize=BLOCKSIZE):
+    return bf16_to_f32(nf4dq_dequantize_bf16(packed, absq, scale2, blocksize)).reshape(shape)

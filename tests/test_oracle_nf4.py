@@ -168,3 +168,55 @@ def test_blocks_follow_row_major_flattening():
 def test_rejects_ragged_size():
     with pytest.raises(ValueError):
         nf4.nf4_codes(np.zeros(100, np.float32))
+
+
+# ------------------------------------------------------ double quantisation
+
+def test_dq_keeps_single_level_codes():
+    w = _blocks(1000, seed=20)
+    p1, a1 = nf4.nf4_quantize(w)
+    p2, aq, s2, a2 = nf4.nf4dq_quantize(w)
+    assert np.array_equal(p1, p2) and np.array_equal(a1, a2)
+    assert aq.size == 1000 and s2.shape == (4, 2)   # 1000 blocks -> 4 groups, the last ragged
+
+
+def test_dq_code_is_nearest_of_256_levels():
+    a = np.abs(np.random.default_rng(21).standard_normal(256 * 3).astype(np.float32)) * 0.05
+    codes, s2 = nf4.dq_encode_absmax(a)
+    for gi in range(3):
+        scale, off = s2[gi].astype(np.float64)
+        levels = (np.arange(256, dtype=np.float32) * np.float32(s2[gi, 0])).astype(np.float32) + np.float32(s2[gi, 1])
+        grp = a[gi * 256:(gi + 1) * 256].astype(np.float64)
+        d = np.abs(grp[:, None] - levels[None, :].astype(np.float64))
+        best = np.argmin(d, axis=1)
+        gap = np.sort(d, axis=1)
+        clear = (gap[:, 1] - gap[:, 0]) > 1e-6 * scale   # skip near-ties
+        assert np.array_equal(codes[gi * 256:(gi + 1) * 256][clear], best[clear])
+
+
+def test_dq_group_minimum_exact_and_error_bound():
+    a = np.abs(np.random.default_rng(22).standard_normal(256 * 2 + 17).astype(np.float32)) * 0.03
+    codes, s2 = nf4.dq_encode_absmax(a)
+    ad = nf4.dq_decode_absmax(codes, s2)
+    for gi in range(3):
+        grp = slice(gi * 256, min(a.size, (gi + 1) * 256))
+        i = np.argmin(a[grp])
+        assert ad[grp][i] == a[grp][i]                       # the offset itself
+        assert codes[grp].max() == 255
+        scale = np.float64(s2[gi, 0])
+        assert np.all(np.abs(ad[grp].astype(np.float64) - a[grp]) <= scale / 2 * (1 + 1e-5) + 1e-9)
+
+
+def test_dq_constant_group():
+    a = np.full(300, 0.0421, np.float32)
+    codes, s2 = nf4.dq_encode_absmax(a)
+    assert np.all(codes == 0) and np.all(s2[:, 0] == 0)
+    assert np.array_equal(nf4.dq_decode_absmax(codes, s2), a)
+
+
+def test_dq_dequant_close_to_single_level():
+    w = _blocks(512, seed=23)
+    p, aq, s2, am = nf4.nf4dq_quantize(w)
+    d1 = nf4.nf4_dequantize_f32(p, am).astype(np.float64)
+    d2 = nf4.bf16_to_f32(nf4.nf4dq_dequantize_bf16(p, aq, s2)).astype(np.float64)
+    assert np.linalg.norm(d2 - d1) / np.linalg.norm(d1) < 1e-2
