@@ -57,6 +57,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", choices=["stack1", "stack4"], default="stack1")
     p.add_argument("--layers", type=int, default=32)
+    p.add_argument("--format", choices=["nf4", "nf4dq", "bf16"], default="nf4",
+                   help="frozen-base storage: NF4 with fp32 absmax, NF4 with 8-bit double-quantised absmax, "
+                        "or unquantised bf16")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-timing", action="store_true", help="skip the per-kernel event probes")
     return p.parse_args()
@@ -168,7 +171,18 @@ def main():
 
     t0 = time.time()
     log(f"building the NF4 store: {L} layers")
-    store = S.Store(shape, L, resident=False, pinned=True)
+    fmt = {"nf4": B.FMT_NF4, "nf4dq": B.FMT_NF4_DQ, "bf16": B.FMT_BF16}[args.format]
+    base_desc = {"nf4": "NF4 base (bs 64, fp32 absmax)", "nf4dq": "NF4 base (bs 64, 8-bit double-quantised absmax)",
+                 "bf16": "unquantised bf16 base"}[args.format]
+
+    def weights(i):
+        W = S.layer_weights_fp32(f"layer{i}", shape)
+        if fmt == B.FMT_BF16:
+            for n in S.PROJ:
+                W[n] = synth.bf16_exact(W[n])[0].reshape(W[n].shape)
+        return W
+
+    store = S.Store(shape, L, fmt=fmt, resident=False, pinned=True, weights_fn=weights)
     log(f"store built in {time.time() - t0:.1f}s: {store.stride * L / 1e9:.3f} GB pinned, "
         f"blob {store.blob_bytes()} B")
     lora = S.LoraSet(shape, L)
@@ -264,7 +278,7 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded random weights and token ids)",
-        "config": {"workload": (f"streamed {L}-layer Llama-3.1-8B-shaped stack, NF4 base (bs 64, fp32 absmax), "
+        "config": {"workload": (f"streamed {L}-layer Llama-3.1-8B-shaped stack, {base_desc}, "
                                 f"LoRA r16 on q,k,v,o,gate,up,down, vocab {V}, "
                                 f"batch {batch} x seq {seq}, accumulation {accum}"),
                    "global_batch": batch * accum, "seq_len": seq, "layers": L, "vocab": V,

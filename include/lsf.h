@@ -97,6 +97,21 @@ LSF_API lsf_status nf4_quantize(const float* w, int64_t n, int32_t blocksize,
 LSF_API lsf_status nf4_dequantize(const uint8_t* packed, const float* absmax, int64_t n,
                           int32_t blocksize, uint16_t* out, lsf_stream stream);
 
+/* Double-quantised NF4 ([REVIEW]: the pages' 113 MB per 8B layer fits NF4
+ * codes with an 8-bit absmax; the pages give no second-level code, so a plain
+ * affine one is used).  Codes are chosen exactly as nf4_quantize (against the
+ * fp32 absmax, also written to `absmax`, device fp32 [n/64]); then per group
+ * of 256 consecutive blocks offset = min, scale = (max - min) / 255 and each
+ * absmax becomes code = clamp(rint((a - offset) / scale), 0, 255) (ties to
+ * even; 0 when scale is 0) in `absq` (device uint8 [n/64]); `scale2` (device
+ * fp32 [2 * ceil(n/64/256)], 8-byte aligned) holds (scale, offset) pairs.
+ * The absmax used to dequantise is fp32(fp32(code * scale) + offset). */
+LSF_API lsf_status nf4dq_quantize(const float* w, int64_t n, int32_t blocksize, uint8_t* packed,
+                                  float* absmax, uint8_t* absq, float* scale2, lsf_stream stream);
+/* out[i] = bf16_rne(level[code[i]] * absmax'(block)), absmax' as above. */
+LSF_API lsf_status nf4dq_dequantize(const uint8_t* packed, const uint8_t* absq, const float* scale2,
+                                    int64_t n, int32_t blocksize, uint16_t* out, lsf_stream stream);
+
 /* --------------------------------------------------------- layer config -- */
 
 typedef struct {
@@ -117,8 +132,8 @@ typedef struct {
 #define LSF_FMT_NF4 0    /* data = packed codes [out*in/2], scale = fp32 absmax [out*in/64] */
 #define LSF_FMT_BF16 1   /* data = bf16 [out*in], scale = NULL (unquantised streamed base) */
 #define LSF_FMT_NF4_DQ 2 /* data = packed codes, scale = uint8 absmax codes [out*in/64],
-                            scale2 = fp32 [ceil(out*in/64/256)] second-level
-                            scales + offset (see nf4dq_quantize) */
+                            scale2 = fp32 (scale, offset) pairs [ceil(out*in/64/256)]
+                            (see nf4dq_quantize) */
 
 typedef struct {
   const void* data;

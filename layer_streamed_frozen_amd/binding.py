@@ -94,6 +94,8 @@ _PROTOS = {
     "lsf_version": (ctypes.c_char_p, []),
     "nf4_quantize": (c_int32, [c_void_p, c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
     "nf4_dequantize": (c_int32, [c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_void_p]),
+    "nf4dq_quantize": (c_int32, [c_void_p, c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "nf4dq_dequantize": (c_int32, [c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_void_p]),
     "linear_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
     "linear_fwd": (c_int32, [ctypes.POINTER(Weight), c_int32, c_int32, c_int32, c_void_p, c_void_p, c_int32,
                              c_float, c_void_p, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
@@ -172,6 +174,28 @@ def nf4_dequantize(packed, absmax, n, out=None, stream=None):
     if out is None:
         out = torch.empty(n, dtype=torch.bfloat16, device=packed.device)
     check(lib().nf4_dequantize(ptr(packed), ptr(absmax), n, 64, ptr(out), stream_ptr(stream)))
+    return out
+
+
+def nf4dq_quantize(w, packed=None, absmax=None, absq=None, scale2=None, stream=None):
+    """Double-quantised NF4: -> (packed uint8 [n/2], absmax fp32 [n/64], absq uint8 [n/64],
+    scale2 fp32 [ceil(n/64/256), 2])."""
+    n = w.numel()
+    nb = n // 64
+    dev = w.device
+    packed = torch.empty(n // 2, dtype=torch.uint8, device=dev) if packed is None else packed
+    absmax = torch.empty(nb, dtype=torch.float32, device=dev) if absmax is None else absmax
+    absq = torch.empty(nb, dtype=torch.uint8, device=dev) if absq is None else absq
+    scale2 = torch.empty(((nb + 255) // 256, 2), dtype=torch.float32, device=dev) if scale2 is None else scale2
+    check(lib().nf4dq_quantize(ptr(w), n, 64, ptr(packed), ptr(absmax), ptr(absq), ptr(scale2),
+                               stream_ptr(stream)))
+    return packed, absmax, absq, scale2
+
+
+def nf4dq_dequantize(packed, absq, scale2, n, out=None, stream=None):
+    if out is None:
+        out = torch.empty(n, dtype=torch.bfloat16, device=packed.device)
+    check(lib().nf4dq_dequantize(ptr(packed), ptr(absq), ptr(scale2), n, 64, ptr(out), stream_ptr(stream)))
     return out
 
 

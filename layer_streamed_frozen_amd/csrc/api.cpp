@@ -183,6 +183,33 @@ lsf_status nf4_dequantize(const uint8_t* packed, const float* absmax, int64_t n,
   return ok();
 }
 
+lsf_status nf4dq_quantize(const float* w, int64_t n, int32_t blocksize, uint8_t* packed, float* absmax,
+                          uint8_t* absq, float* scale2, lsf_stream stream) {
+  if (blocksize != 64) return fail(LSF_ERR_SHAPE, "blocksize must be 64");
+  if (n < 0 || n % 64) return fail(LSF_ERR_SHAPE, "n must be a non-negative multiple of 64 (got %lld)", (long long)n);
+  if (n == 0) return ok();
+  lsf_status s;
+  if ((s = check_dev(w, "w")) || (s = check_dev(packed, "packed")) || (s = check_dev(absmax, "absmax"))) return s;
+  if (absq == nullptr || scale2 == nullptr) return fail(LSF_ERR_INVALID_ARG, "absq or scale2 is NULL");
+  if (!aligned(scale2, 8)) return fail(LSF_ERR_ALIGN, "scale2 must be 8-byte aligned");
+  HIPCK(nf4_quantize_launch(w, n, packed, absmax, S(stream)));
+  HIPCK(dq_encode_launch(absmax, n / 64, absq, scale2, S(stream)));
+  return ok();
+}
+
+lsf_status nf4dq_dequantize(const uint8_t* packed, const uint8_t* absq, const float* scale2, int64_t n,
+                            int32_t blocksize, uint16_t* out, lsf_stream stream) {
+  if (blocksize != 64) return fail(LSF_ERR_SHAPE, "blocksize must be 64");
+  if (n < 0 || n % 64) return fail(LSF_ERR_SHAPE, "n must be a non-negative multiple of 64 (got %lld)", (long long)n);
+  if (n == 0) return ok();
+  lsf_status s;
+  if ((s = check_dev(packed, "packed")) || (s = check_dev(out, "out"))) return s;
+  if (absq == nullptr || scale2 == nullptr) return fail(LSF_ERR_INVALID_ARG, "absq or scale2 is NULL");
+  if (!aligned(scale2, 8)) return fail(LSF_ERR_ALIGN, "scale2 must be 8-byte aligned");
+  HIPCK(nf4dq_dequantize_launch(packed, absq, scale2, n, out, S(stream)));
+  return ok();
+}
+
 // ----------------------------------------------------------- single linear
 size_t linear_workspace_bytes(int32_t tokens, int32_t n_out, int32_t n_in, int32_t rank) {
   if (tokens <= 0 || n_out <= 0 || n_in <= 0) return 0;

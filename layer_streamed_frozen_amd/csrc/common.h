@@ -56,6 +56,14 @@ __device__ __forceinline__ float nf4_level(int i) {
   return L[i];
 }
 
+// Absmax of a block stored with an 8-bit code: fp32(fp32(code * scale) + offset),
+// two roundings, never contracted into an fma.
+__device__ __forceinline__ float dq_absmax_value(uint32_t code, float scale, float offset) {
+#pragma clang fp contract(off)
+  const float p = (float)code * scale;
+  return p + offset;
+}
+
 // Byte planes of one block's scaled table e_i = bf16(level_i * absmax):
 // lo[k] holds the low bytes of e_{4k..4k+3}, hi[k] the high bytes.  A code is
 // then looked up with byte permutes instead of a per-element multiply.

@@ -67,7 +67,7 @@ __device__ __forceinline__ int64_t nt_wrow(const GemmArgs& g, int ntile, int c) 
 // times the group's scale plus the group's offset (groups of 256 blocks).
 __device__ __forceinline__ float dq_absmax(const WeightRef& w, int64_t block) {
   const float2 so = reinterpret_cast<const float2*>(w.dq2)[block >> 8];
-  return (float)w.absq[block] * so.x + so.y;
+  return dq_absmax_value(w.absq[block], so.x, so.y);
 }
 
 __device__ __forceinline__ float block_absmax(const WeightRef& w, int64_t elem) {

@@ -76,6 +76,10 @@ hipError_t splitk_reduce(const float* part, int splits, int M, int N, const EpiA
 hipError_t nf4_quantize_launch(const float* w, int64_t n, uint8_t* packed, float* absmax, hipStream_t s);
 hipError_t nf4_dequantize_launch(const uint8_t* packed, const float* absmax, int64_t n, uint16_t* out,
                                  hipStream_t s);
+// Double quantisation: 8-bit absmax codes and (scale, offset) per 256 blocks.
+hipError_t dq_encode_launch(const float* absmax, int64_t nblocks, uint8_t* codes, float* scale2, hipStream_t s);
+hipError_t nf4dq_dequantize_launch(const uint8_t* packed, const uint8_t* absq, const float* scale2, int64_t n,
+                                   uint16_t* out, hipStream_t s);
 
 // LoRA side paths.
 //  down_fwd: U[m, sec*r + j] = scale * sum_k X[m, k] * A_sec[j, k]  (all sections read X)

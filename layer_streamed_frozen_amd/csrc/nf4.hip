@@ -77,7 +77,75 @@ __global__ __launch_bounds__(256) void nf4_dequantize_kernel(const uint8_t* __re
   }
 }
 
+// Second-level code of the absmax values: one workgroup per group of 256
+// blocks; offset = min, scale = (max - min) / 255 (IEEE division), code =
+// clamp(rint((a - min) / scale), 0, 255), ties to even.
+__global__ __launch_bounds__(256) void dq_encode_kernel(const float* __restrict__ absmax, int64_t nb,
+                                                        uint8_t* __restrict__ codes, float2* __restrict__ s2) {
+  __shared__ float red_lo[4], red_hi[4];
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool live = b < nb;
+  const float a = live ? absmax[b] : 0.0f;
+  float lo = live ? a : INFINITY, hi = live ? a : -INFINITY;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = fminf(lo, __shfl_xor(lo, o, 64));
+    hi = fmaxf(hi, __shfl_xor(hi, o, 64));
+  }
+  const int wid = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { red_lo[wid] = lo; red_hi[wid] = hi; }
+  __syncthreads();
+  lo = fminf(fminf(red_lo[0], red_lo[1]), fminf(red_lo[2], red_lo[3]));
+  hi = fmaxf(fmaxf(red_hi[0], red_hi[1]), fmaxf(red_hi[2], red_hi[3]));
+  const float scale = __fdiv_rn(__fsub_rn(hi, lo), 255.0f);
+  if (live) {
+    uint32_t c = 0;
+    if (scale > 0.0f) {
+      const float q = rintf(__fdiv_rn(__fsub_rn(a, lo), scale));
+      c = (uint32_t)fminf(fmaxf(q, 0.0f), 255.0f);
+    }
+    codes[b] = (uint8_t)c;
+  }
+  if (threadIdx.x == 0) s2[blockIdx.x] = make_float2(scale, lo);
+}
+
+__global__ __launch_bounds__(256) void nf4dq_dequantize_kernel(const uint8_t* __restrict__ packed,
+                                                               const uint8_t* __restrict__ absq,
+                                                               const float2* __restrict__ s2, int64_t nunits,
+                                                               uint16_t* __restrict__ out) {
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < nunits; u += (int64_t)gridDim.x * blockDim.x) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(packed + u * 16);
+    const int64_t blk = u >> 1;
+    const float2 so = s2[blk >> 8];
+    const Nf4Table t = nf4_table(dq_absmax_value(absq[blk], so.x, so.y));
+    uint32_t o[4];
+    u32x4* dst = reinterpret_cast<u32x4*>(out + u * 32);
+    nf4_decode8(t, q.x, o); dst[0] = u32x4{o[0], o[1], o[2], o[3]};
+    nf4_decode8(t, q.y, o); dst[1] = u32x4{o[0], o[1], o[2], o[3]};
+    nf4_decode8(t, q.z, o); dst[2] = u32x4{o[0], o[1], o[2], o[3]};
+    nf4_decode8(t, q.w, o); dst[3] = u32x4{o[0], o[1], o[2], o[3]};
+  }
+}
+
 }  // namespace
+
+hipError_t dq_encode_launch(const float* absmax, int64_t nblocks, uint8_t* codes, float* scale2, hipStream_t s) {
+  if (nblocks <= 0) return hipSuccess;
+  const int64_t groups = (nblocks + 255) / 256;
+  hipLaunchKernelGGL(dq_encode_kernel, dim3((unsigned)groups), dim3(256), 0, s, absmax, nblocks, codes,
+                     reinterpret_cast<float2*>(scale2));
+  return hipGetLastError();
+}
+
+hipError_t nf4dq_dequantize_launch(const uint8_t* packed, const uint8_t* absq, const float* scale2, int64_t n,
+                                   uint16_t* out, hipStream_t s) {
+  const int64_t units = n / 32;
+  if (units == 0) return hipSuccess;
+  const int grid = (int)std::min<int64_t>((units + 255) / 256, 65536);
+  hipLaunchKernelGGL(nf4dq_dequantize_kernel, dim3(grid), dim3(256), 0, s, packed, absq,
+                     reinterpret_cast<const float2*>(scale2), units, out);
+  return hipGetLastError();
+}
 
 hipError_t nf4_quantize_launch(const float* w, int64_t n, uint8_t* packed, float* absmax, hipStream_t s) {
   const int64_t nblocks = n / 64;

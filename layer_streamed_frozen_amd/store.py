@@ -89,8 +89,16 @@ def build_layer_blob(shape, W, fmt=B.FMT_NF4, device="cuda", out=None):
         elif fmt == B.FMT_BF16:
             bits = (wd.reshape(-1).view(torch.int32) >> 16).to(torch.int16)
             blob[lay.off[i]: lay.off[i] + 2 * n].view(torch.int16).copy_(bits)
+        elif fmt == B.FMT_NF4_DQ:
+            nb = n // 64
+            packed = blob[lay.off[i]: lay.off[i] + n // 2]
+            absq = blob[lay.off[4 + i]: lay.off[4 + i] + nb]
+            s2o = lay.off[4 + i] + (nb + 255) // 256 * 256
+            ng = (nb + 255) // 256
+            scale2 = blob[s2o: s2o + 8 * ng].view(torch.float32).view(ng, 2)
+            B.nf4dq_quantize(wd.reshape(-1), packed, None, absq, scale2)
         else:
-            raise ValueError("use nf4dq.build_layer_blob for the double-quantised format")
+            raise ValueError(f"unknown weight format {fmt}")
         del wd
     for k, sec in (("norm1", 8), ("norm2", 9)):
         nb = torch.from_numpy(np.ascontiguousarray(W[k]).view(np.int16)).to(device)

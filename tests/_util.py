@@ -40,3 +40,14 @@ def oracle_dense(W):
     """The oracle's own NF4 round trip of a fp32 weight: dense fp64 [out, in]."""
     p, a = onf4.nf4_quantize(W)
     return onf4.nf4_dequantize(p, a, W.shape).astype(np.float64)
+
+
+def oracle_dense_dq(W):
+    """The oracle's double-quantised NF4 round trip: dense fp64 [out, in]."""
+    p, aq, s2, _ = onf4.nf4dq_quantize(W)
+    return onf4.nf4dq_dequantize(p, aq, s2, W.shape).astype(np.float64)
+
+
+def oracle_dense_bf16(W):
+    """An unquantised bf16 weight (its values are already bf16-exact)."""
+    return np.asarray(W, dtype=np.float64)

@@ -8,7 +8,7 @@ from layer_streamed_frozen_amd import binding as B
 from layer_streamed_frozen_amd import store as S
 from oracle import model as M
 from oracle import nf4 as onf4
-from tests._util import TOL, bf16_input, bf16_tensor_to_np, oracle_dense, report
+from tests._util import TOL, bf16_input, bf16_tensor_to_np, oracle_dense, oracle_dense_bf16, oracle_dense_dq, report
 
 pytestmark = pytest.mark.gpu
 
@@ -16,8 +16,9 @@ SMALL = S.LayerShape(hidden=512, intermediate=1024, n_heads=4, n_kv_heads=2, hea
                      rope_theta=500000.0)
 
 
-def oracle_layer_weights(W):
-    d = {n: oracle_dense(W[n]) for n in S.PROJ}
+def oracle_layer_weights(W, fmt=B.FMT_NF4):
+    dense = {B.FMT_NF4: oracle_dense, B.FMT_NF4_DQ: oracle_dense_dq, B.FMT_BF16: oracle_dense_bf16}[fmt]
+    d = {n: dense(W[n]) for n in S.PROJ}
     d["norm1"] = onf4.bf16_to_f32(W["norm1"]).astype(np.float64)
     d["norm2"] = onf4.bf16_to_f32(W["norm2"]).astype(np.float64)
     return d
@@ -28,15 +29,26 @@ def oracle_shape(shape):
                         rms_eps=shape.rms_eps, rope_theta=shape.rope_theta, lora_scale=shape.lora_scale)
 
 
-def run_layer(shape, batch, seq, prefix, targets=S.PROJ, norms_random=True, enabled=True):
-    print(f"[layer] {prefix} H={shape.hidden} I={shape.intermediate} B={batch} S={seq} targets={targets}",
-          flush=True)
+def bf16_weights(W):
+    """Make the projections bfloat16-exact (the unquantised streamed base)."""
+    from layer_streamed_frozen_amd import synth
+    out = dict(W)
+    for n in S.PROJ:
+        out[n] = synth.bf16_exact(W[n])[0].reshape(W[n].shape)
+    return out
+
+
+def run_layer(shape, batch, seq, prefix, targets=S.PROJ, norms_random=True, enabled=True, fmt=B.FMT_NF4):
+    print(f"[layer] {prefix} H={shape.hidden} I={shape.intermediate} B={batch} S={seq} targets={targets} "
+          f"fmt={fmt}", flush=True)
     W = S.layer_weights_fp32(prefix, shape)
     if norms_random:
         W.update(S.random_norms(prefix, shape))
-    blob = S.build_layer_blob(shape, W)
+    if fmt == B.FMT_BF16:
+        W = bf16_weights(W)
+    blob = S.build_layer_blob(shape, W, fmt)
     cfg = shape.cfg(batch, seq)
-    lw = B.layer_weights_from_blob(cfg, B.FMT_NF4, blob.data_ptr())
+    lw = B.layer_weights_from_blob(cfg, fmt, blob.data_ptr())
     lora = S.LoraSet(shape, 1, targets=targets, prefix=prefix + ".lora")
     T, H = batch * seq, shape.hidden
     X, xg = bf16_input(prefix + ".x", (T, H))
@@ -49,7 +61,7 @@ def run_layer(shape, batch, seq, prefix, targets=S.PROJ, norms_random=True, enab
     B.layer_bwd(cfg, lw, ls, xg, dyg, dx, ws)
     torch.cuda.synchronize()
 
-    ow = oracle_layer_weights(W)
+    ow = oracle_layer_weights(W, fmt)
     oc = oracle_shape(shape)
     x64 = X.astype(np.float64).reshape(batch, seq, H)
     yr, cache = M.layer_fwd(x64, ow, lora.numpy(0, enabled), oc)
@@ -110,4 +122,19 @@ def test_layer_is_deterministic():
 
 def test_full_8b_layer_seq512():
     res, _ = run_layer(S.LLAMA8B, 1, 512, "l8b", norms_random=False)
+    _assert_all(res)
+
+
+def test_small_layer_double_quantised():
+    res, _ = run_layer(SMALL, 2, 90, "sldq", fmt=B.FMT_NF4_DQ)
+    _assert_all(res)
+
+
+def test_small_layer_unquantised_bf16_base():
+    res, _ = run_layer(SMALL, 1, 120, "slbf", fmt=B.FMT_BF16)
+    _assert_all(res)
+
+
+def test_full_8b_layer_double_quantised():
+    res, _ = run_layer(S.LLAMA8B, 1, 512, "l8bdq", norms_random=False, fmt=B.FMT_NF4_DQ)
     _assert_all(res)

@@ -80,3 +80,29 @@ def test_denormal_blocks():
     rng = np.random.default_rng(1)
     w = (rng.standard_normal(64 * 4) * 1e-39).astype(np.float32)
     _check(w, "denormal")
+
+
+def _check_dq(w, label):
+    print(f"[nf4dq] {label} n={w.size}", flush=True)
+    wd = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32).reshape(-1)).cuda()
+    packed, absmax, absq, s2 = B.nf4dq_quantize(wd)
+    deq = B.nf4dq_dequantize(packed, absq, s2, wd.numel())
+    torch.cuda.synchronize()
+    rp, raq, rs2, ra = onf4.nf4dq_quantize(w)
+    assert np.array_equal(absmax.cpu().numpy().view(np.uint32), ra.view(np.uint32)), label
+    assert np.array_equal(packed.cpu().numpy(), rp), label
+    assert np.array_equal(s2.cpu().numpy().view(np.uint32), rs2.view(np.uint32)), f"{label}: scale/offset differ"
+    bad = np.nonzero(absq.cpu().numpy() != raq)[0]
+    assert bad.size == 0, f"{label}: {bad.size} absmax codes differ, first {bad[:5]}"
+    rd = onf4.nf4dq_dequantize_bf16(rp, raq, rs2)
+    assert np.array_equal(deq.view(torch.int16).cpu().numpy().view(np.uint16), rd), label
+
+
+def test_dq_8b_o_projection_full():
+    _check_dq(synth.normal("nf4.o8b", (4096, 4096), 0.02), "4096x4096")
+
+
+def test_dq_ragged_groups_and_constant_group():
+    _check_dq(synth.normal("nf4dq.odd", (64 * 300,), 0.5), "300 blocks")
+    w = np.tile(np.linspace(-1, 1, 64, dtype=np.float32), 256)   # 256 identical blocks: scale 0
+    _check_dq(w, "constant group")

@@ -11,7 +11,7 @@ from layer_streamed_frozen_amd import synth
 from oracle import model as M
 from oracle import nf4 as onf4
 from tests._util import TOL, bf16_tensor_to_np, report
-from tests.test_gpu_layer import SMALL, oracle_layer_weights, oracle_shape
+from tests.test_gpu_layer import SMALL, bf16_weights, oracle_layer_weights, oracle_shape
 
 pytestmark = pytest.mark.gpu
 
@@ -23,7 +23,7 @@ def bf16_param(name, shape, std):
 
 class Setup:
     def __init__(self, shape, n_layers, vocab, batch, seq, prefix, resident=True, targets=S.PROJ, flags=0,
-                 pinned=True, random_norms=True):
+                 pinned=True, random_norms=True, fmt=B.FMT_NF4):
         print(f"[stack] {prefix} L={n_layers} V={vocab} B={batch} S={seq}", flush=True)
         self.shape, self.L, self.V, self.batch, self.seq = shape, n_layers, vocab, batch, seq
         self.prefix = prefix
@@ -32,10 +32,11 @@ class Setup:
             W = S.layer_weights_fp32(f"{prefix}.layer{i}", shape)
             if random_norms:
                 W.update(S.random_norms(f"{prefix}.layer{i}", shape))
-            return W
+            return bf16_weights(W) if fmt == B.FMT_BF16 else W
 
         self.wfn = wfn
-        self.store = S.Store(shape, n_layers, resident=resident, weights_fn=wfn, pinned=pinned)
+        self.fmt = fmt
+        self.store = S.Store(shape, n_layers, fmt=fmt, resident=resident, weights_fn=wfn, pinned=pinned)
         self.lora = S.LoraSet(shape, n_layers, targets=targets, prefix=prefix + ".lora")
         H = shape.hidden
         self.emb_np, self.emb = bf16_param(prefix + ".embed", (vocab, H), 1.0)
@@ -59,7 +60,7 @@ class Setup:
         return self.stack.logits.clone(), self.stack.loss.clone(), g
 
     def oracle(self, loss_scale=1.0, ids=None):
-        layers = [oracle_layer_weights(self.wfn(i)) for i in range(self.L)]
+        layers = [oracle_layer_weights(self.wfn(i), self.fmt) for i in range(self.L)]
         loras = [self.lora.numpy(i) for i in range(self.L)]
         return M.stack_step(self.ids_np if ids is None else ids, self.emb_np, layers, loras,
                             self.fnorm_np.astype(np.float64), self.head_np.astype(np.float64),
@@ -236,5 +237,22 @@ def test_full_8b_shapes_two_layers_match_oracle():
     for i in range(s.L):
         g = s.lora.grads_numpy(i)
         for n in S.PROJ:
+            assert report(f"L{i}.dA_{n}", g[n][0], ref["grads"][i][n][0]) < TOL
+            assert report(f"L{i}.dB_{n}", g[n][1], ref["grads"][i][n][1]) < TOL
+
+
+@pytest.mark.parametrize("fmt", [B.FMT_NF4_DQ, B.FMT_BF16])
+def test_other_base_formats_stream_bit_equal_and_match_oracle(fmt):
+    s = Setup(SMALL, 3, 512, 1, 72, f"fmt{fmt}", fmt=fmt)
+    s.step(mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+    a = s.snapshot()
+    s.step(mode=B.MODE_RESIDENT | B.MODE_ZERO_GRADS)
+    assert same(a, s.snapshot())
+    ref = s.oracle()
+    assert abs(float(s.stack.loss.item()) - ref["loss"]) / abs(ref["loss"]) < TOL
+    assert report("logits", s.stack.logits.double().cpu().numpy(), ref["logits"]) < TOL
+    for i in range(s.L):
+        g = s.lora.grads_numpy(i)
+        for n in ("q", "o", "gate", "down"):
             assert report(f"L{i}.dA_{n}", g[n][0], ref["grads"][i][n][0]) < TOL
             assert report(f"L{i}.dB_{n}", g[n][1], ref["grads"][i][n][1]) < TOL
