@@ -281,6 +281,33 @@ LSF_API size_t stack_workspace_bytes(const lsf_layer_cfg* cfg, int32_t vocab);
  * streamed recompute + backward, LoRA gradients accumulated. */
 LSF_API lsf_status stream_stack_step(lsf_stack* st, const lsf_stack_io* io);
 
+/* One DPO micro-batch ([README] paragraph on preference losses with layer
+ * streaming; [BLOG] section on DPO support): the reference model is the same
+ * frozen base with every adapter switched off, so it needs no second copy of
+ * the weights.  The batch holds P = batch/2 chosen sequences, then the P
+ * rejected ones (pair p = sequences p and P+p).  With l(s) the sum of the
+ * next-token log-probabilities of sequence s,
+ *   h_p = (l_pi(p) - l_ref(p)) - (l_pi(P+p) - l_ref(P+p)),
+ *   loss = mean_p softplus(-beta h_p)   (written to base.loss, unscaled),
+ * and only the adapters (policy) receive gradients, times base.loss_scale.
+ * fused_reference = 1 runs the reference forward of layer i in the same visit
+ * as the policy forward of layer i, so each layer is read once per forward
+ * (2L copies per step, as for SFT); 0 runs a separate reference pass over the
+ * stack first (3L copies).  Both give the same bits.  base.logits ends with the
+ * policy logits; base.ckpt holds the policy's layer inputs.  seq_logp (may be
+ * NULL): device fp32 [2, batch], policy log-probabilities then reference.
+ * Errors: LSF_ERR_SHAPE for an odd batch, LSF_ERR_INVALID_ARG for beta <= 0
+ * or non-finite, plus every error of stream_stack_step.  Workspace: the same
+ * stack_workspace_bytes. */
+typedef struct {
+  lsf_stack_io base;
+  float beta;               /* DPO temperature, e.g. 0.1 */
+  int32_t fused_reference;  /* 1: reference forward in the policy's layer visit */
+  float* seq_logp;          /* optional device fp32 [2, batch] */
+} lsf_dpo_io;
+
+LSF_API lsf_status dpo_stack_step(lsf_stack* st, const lsf_dpo_io* io);
+
 /* Kernel classes timed with HIP events under LSF_STACK_TIMING (index into
  * lsf_stack_stats.kernel_ms / kernel_launches).  A GEMM's time includes its
  * split-K reduction when it has one. */
@@ -292,7 +319,7 @@ enum {
 };
 
 typedef struct {
-  int64_t steps;       /* stream_stack_step calls since create / reset */
+  int64_t steps;       /* stream_stack_step and dpo_stack_step calls since create / reset */
   int64_t copies;      /* host-to-device layer copies enqueued */
   int64_t bytes;       /* bytes those copies moved */
   double copy_ms;      /* summed copy durations (LSF_STACK_TIMING only) */

@@ -79,6 +79,10 @@ class StackIO(ctypes.Structure):
                 ("mode", c_uint32)]
 
 
+class DpoIO(ctypes.Structure):
+    _fields_ = [("base", StackIO), ("beta", c_float), ("fused_reference", c_int32), ("seq_logp", c_void_p)]
+
+
 class StackStats(ctypes.Structure):
     _fields_ = [("steps", c_int64), ("copies", c_int64), ("bytes", c_int64), ("copy_ms", ctypes.c_double),
                 ("wait_ms", ctypes.c_double), ("kernel_ms", ctypes.c_double * 16),
@@ -114,6 +118,7 @@ _PROTOS = {
     "stack_destroy": (c_int32, [c_void_p]),
     "stack_workspace_bytes": (c_size_t, [ctypes.POINTER(LayerCfg), c_int32]),
     "stream_stack_step": (c_int32, [c_void_p, ctypes.POINTER(StackIO)]),
+    "dpo_stack_step": (c_int32, [c_void_p, ctypes.POINTER(DpoIO)]),
     "stack_stats": (c_int32, [c_void_p, ctypes.POINTER(StackStats)]),
     "stack_reset_stats": (c_int32, [c_void_p]),
 }
@@ -260,6 +265,10 @@ def stack_workspace_bytes(cfg, vocab):
 
 def stream_stack_step(h, io):
     check(lib().stream_stack_step(h, ctypes.byref(io)))
+
+
+def dpo_stack_step(h, io):
+    check(lib().dpo_stack_step(h, ctypes.byref(io)))
 
 
 def stack_stats(h):

@@ -3,6 +3,7 @@
 // two-buffer layer streamer with the stack step.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -509,8 +510,8 @@ lsf_status wait_ready(lsf_stack* st, int b) {
 
 struct StackWs {
   LayerWs layer;
-  uint16_t *hN, *dhN, *dlog, *dx[2];
-  float *rstdN, *row_loss, *part;
+  uint16_t *hN, *dhN, *dlog, *dx[2], *rx[2];
+  float *rstdN, *row_loss, *part, *lse, *lp, *coef;
   size_t part_floats;
 };
 
@@ -519,9 +520,10 @@ size_t head_part_floats(const lsf_layer_cfg& c) { return (size_t)8 * c.batch * c
 size_t stack_ws_bytes(const lsf_layer_cfg& c, int V) {
   const size_t T = (size_t)c.batch * c.seq, H = c.hidden;
   size_t b = LayerWs::bytes(c);
-  b += al256(T * H * 2) * 4;  // hN, dhN, dx[0], dx[1]
+  b += al256(T * H * 2) * 6;  // hN, dhN, dx[0], dx[1], rx[0], rx[1]
   b += al256(T * (size_t)V * 2);
-  b += al256(T * 4) * 2;
+  b += al256(T * 4) * 3;      // rstdN, row_loss, lse
+  b += al256((size_t)c.batch * 8) + al256((size_t)c.batch * 4);  // lp (policy, reference), coef
   b += al256(head_part_floats(c) * 4);
   return b + 512;
 }
@@ -540,12 +542,204 @@ StackWs carve_stack(const lsf_layer_cfg& c, int V, void* base) {
   w.dhN = (uint16_t*)take(T * H * 2);
   w.dx[0] = (uint16_t*)take(T * H * 2);
   w.dx[1] = (uint16_t*)take(T * H * 2);
+  w.rx[0] = (uint16_t*)take(T * H * 2);
+  w.rx[1] = (uint16_t*)take(T * H * 2);
   w.dlog = (uint16_t*)take(T * (size_t)V * 2);
   w.rstdN = (float*)take(T * 4);
   w.row_loss = (float*)take(T * 4);
+  w.lse = (float*)take(T * 4);
+  w.lp = (float*)take((size_t)c.batch * 8);
+  w.coef = (float*)take((size_t)c.batch * 4);
   w.part_floats = head_part_floats(c);
   w.part = (float*)take(w.part_floats * 4);
   return w;
+}
+
+// One walk over the stack: layers 0..L-1 (forward) or L-1..0.  Layer j
+// computes from buffer j % 2; once it is done the buffer is released and the
+// layer two further along is copied into it.  The first two layers of the walk
+// are taken as the buffers hold them when allow_reuse is set (the frozen store
+// never changes, so a buffer that holds layer j holds the right bytes).
+template <class Fn>
+lsf_status walk_layers(lsf_stack* st, bool resident, bool forward, bool allow_reuse, Fn&& fn) {
+  const int L = st->d.n_layers;
+  const int first = forward ? 0 : L - 1, dir = forward ? 1 : -1;
+  hipStream_t cs = S(st->d.compute);
+  lsf_status s;
+  if (!resident) {
+    if ((s = acquire(st, first, first & 1, allow_reuse))) return s;
+    if (L > 1 && (s = acquire(st, first + dir, (first + dir) & 1, allow_reuse))) return s;
+  }
+  for (int n = 0; n < L; ++n) {
+    const int j = first + n * dir, b = j & 1;
+    if (!resident && (s = wait_ready(st, b))) return s;
+    const void* blob = resident ? static_cast<const char*>(st->d.resident_store) + (uint64_t)j * st->d.blob_stride
+                                : st->d.dev_buf[b];
+    lsf_layer_weights lw;
+    weights_from_blob(st->cfg, st->d.format, blob, &lw);
+    HIPCK(fn(j, lw));
+    if (!resident) {
+      HIPCK(hipEventRecord(st->freed[b], cs));
+      st->used[b] = true;
+      const int nx = j + 2 * dir;
+      if (nx >= 0 && nx < L && (s = acquire(st, nx, b, false))) return s;
+    }
+  }
+  return LSF_OK;
+}
+
+// Final RMSNorm of x (into hN, rstdN) and the fp32 logits through lm_head.
+hipError_t head_logits(lsf_stack* st, const lsf_stack_io* io, const StackWs& w, const uint16_t* x, bool timing) {
+  const lsf_layer_cfg& c = st->cfg;
+  const int T = c.batch * c.seq, H = c.hidden;
+  hipStream_t cs = S(st->d.compute);
+  hipError_t e;
+  if ((e = rmsnorm_fwd(x, io->final_norm, T, H, c.rms_eps, w.hN, w.rstdN, cs)) != hipSuccess) return e;
+  GemmArgs g;
+  g.M = T; g.N = io->vocab; g.K = H; g.A = w.hN; g.lda = H;
+  g.W.fmt = FMT_BF16; g.W.bf16 = io->lm_head; g.W.ld = H;
+  EpiArgs ep; ep.kind = EPI_F32; ep.C = io->logits; ep.ldc = io->vocab;
+  if (timing && (e = st->probe.begin(LSF_K_HEAD_FWD, cs)) != hipSuccess) return e;
+  if ((e = gemm_nt(g, ep, cs)) != hipSuccess) return e;
+  if (timing && (e = st->probe.end(LSF_K_HEAD_FWD, cs)) != hipSuccess) return e;
+  return hipSuccess;
+}
+
+// dlogits (bf16, in w.dlog) back through lm_head and the final RMSNorm of x.
+hipError_t head_backward(lsf_stack* st, const lsf_stack_io* io, const StackWs& w, const uint16_t* x, uint16_t* dx,
+                         bool timing) {
+  const lsf_layer_cfg& c = st->cfg;
+  const int T = c.batch * c.seq, H = c.hidden;
+  hipStream_t cs = S(st->d.compute);
+  hipError_t e;
+  GemmArgs g;
+  g.M = T; g.N = H; g.K = io->vocab; g.A = w.dlog; g.lda = io->vocab;
+  g.W.fmt = FMT_BF16; g.W.bf16 = io->lm_head; g.W.ld = H;
+  EpiArgs ep; ep.kind = EPI_BF16; ep.C = w.dhN; ep.ldc = H;
+  if (timing && (e = st->probe.begin(LSF_K_HEAD_BWD, cs)) != hipSuccess) return e;
+  if ((e = run_gemm(true, g, ep, w.part, w.part_floats, cs)) != hipSuccess) return e;
+  if (timing && (e = st->probe.end(LSF_K_HEAD_BWD, cs)) != hipSuccess) return e;
+  return rmsnorm_bwd(w.dhN, x, io->final_norm, w.rstdN, nullptr, T, H, dx, cs);
+}
+
+// One micro-batch: SFT (dpo == NULL) or DPO with the adapters-off reference.
+lsf_status run_step(lsf_stack* st, const lsf_stack_io* io, const lsf_dpo_io* dpo) {
+  if (st == nullptr) return fail(LSF_ERR_INVALID_ARG, "stack or io is NULL");
+  const lsf_layer_cfg& c = st->cfg;
+  const int L = st->d.n_layers;
+  const int V = io->vocab;
+  const int T = c.batch * c.seq, H = c.hidden;
+  lsf_status s;
+  if (V < 128 || V % 128) return fail(LSF_ERR_SHAPE, "vocab must be a positive multiple of 128 (got %d)", V);
+  if ((s = check_dev(io->ids, "ids")) || (s = check_dev(io->embed, "embed")) ||
+      (s = check_dev(io->final_norm, "final_norm")) || (s = check_dev(io->lm_head, "lm_head")) ||
+      (s = check_dev(io->ckpt, "ckpt")) || (s = check_dev(io->logits, "logits")) || (s = check_dev(io->loss, "loss")))
+    return s;
+  if (io->lora == nullptr) return fail(LSF_ERR_INVALID_ARG, "lora array is NULL");
+  for (int i = 0; i < L; ++i)
+    if ((s = check_lora(&io->lora[i]))) return s;
+  const bool resident = io->mode & LSF_MODE_RESIDENT;
+  if (resident && st->d.resident_store == nullptr) return fail(LSF_ERR_INVALID_ARG, "RESIDENT mode needs a resident store");
+  if (!resident && st->d.host_store == nullptr) return fail(LSF_ERR_INVALID_ARG, "STREAMED mode needs a host store");
+  if (io->ws == nullptr || io->ws_bytes < stack_ws_bytes(c, V))
+    return fail(LSF_ERR_WORKSPACE, "workspace too small (need %zu bytes)", stack_ws_bytes(c, V));
+  if (dpo != nullptr) {
+    if (c.batch < 2 || c.batch % 2)
+      return fail(LSF_ERR_SHAPE, "DPO needs an even batch (chosen, then rejected sequences); got %d", c.batch);
+    if (!(dpo->beta > 0.0f) || !std::isfinite(dpo->beta))
+      return fail(LSF_ERR_INVALID_ARG, "DPO beta must be positive and finite");
+    if (dpo->seq_logp != nullptr && !aligned(dpo->seq_logp, 4)) return fail(LSF_ERR_ALIGN, "seq_logp is not aligned");
+  }
+
+  hipStream_t cs = S(st->d.compute);
+  StackWs w = carve_stack(c, V, io->ws);
+  const bool timing = st->d.flags & LSF_STACK_TIMING;
+  if (timing) {
+    st->probe.pool = &st->events;
+    w.layer.probe = &st->probe;
+    HIPCK(harvest_all(st, false));  // recycle the events of work that has finished
+  }
+  const size_t act = (size_t)T * H;
+  st->stats.steps += 1;
+
+  if (io->mode & LSF_MODE_ZERO_GRADS) {
+    const int64_t Dq = (int64_t)c.n_heads * c.head_dim, Dk = (int64_t)c.n_kv_heads * c.head_dim;
+    const int64_t in[7] = {c.hidden, c.hidden, c.hidden, Dq, c.hidden, c.hidden, c.intermediate};
+    const int64_t outd[7] = {Dq, Dk, Dk, c.hidden, c.intermediate, c.intermediate, c.hidden};
+    for (int i = 0; i < L; ++i) {
+      const lsf_lora_proj* p = &io->lora[i].q;
+      for (int k = 0; k < 7; ++k) {
+        if (p[k].A == nullptr) continue;
+        if (p[k].dA) HIPCK(zero_f32(p[k].dA, (int64_t)c.rank * in[k], cs));
+        if (p[k].dB) HIPCK(zero_f32(p[k].dB, (int64_t)c.rank * outd[k], cs));
+      }
+    }
+  }
+
+  HIPCK(rope_table(c.seq, c.head_dim, c.rope_theta, w.layer.rope, cs));
+  HIPCK(embed_gather(io->ids, io->embed, T, H, V, io->ckpt, cs));
+
+  // Policy forward of layer i: ckpt[i] -> ckpt[i+1] (kept for the backward).
+  auto policy_fwd = [&](int i, const lsf_layer_weights& lw) {
+    return layer_forward(c, lw, &io->lora[i], io->ckpt + (size_t)i * act, io->ckpt + (size_t)(i + 1) * act, w.layer,
+                         false, true, cs);
+  };
+  // Reference (adapters off) forward of layer i, through the rx ping-pong:
+  // input rx[i % 2] (the embeddings for layer 0), output rx[(i + 1) % 2].
+  auto reference_fwd = [&](int i, const lsf_layer_weights& lw) {
+    const uint16_t* x = i == 0 ? io->ckpt : w.rx[i & 1];
+    return layer_forward(c, lw, nullptr, x, w.rx[(i + 1) & 1], w.layer, false, true, cs);
+  };
+  float* lp_pi = w.lp;
+  float* lp_ref = w.lp + c.batch;
+  auto reference_head = [&]() -> hipError_t {
+    hipError_t e;
+    if ((e = head_logits(st, io, w, w.rx[L & 1], timing)) != hipSuccess) return e;
+    return seq_logprobs(io->logits, io->ids, c.batch, c.seq, V, w.lse, w.row_loss, lp_ref, cs);
+  };
+
+  // ---- forward.  A full step ends with layers 1 and 0 in buffers 1 and 0,
+  // which is what the next forward reads first: they are reused unless
+  // LSF_STACK_NO_TURN_REUSE asks for every copy.
+  const bool reuse = !(st->d.flags & LSF_STACK_NO_TURN_REUSE);
+  if (dpo != nullptr && !dpo->fused_reference) {
+    if ((s = walk_layers(st, resident, true, reuse, reference_fwd))) return s;
+    HIPCK(reference_head());
+  }
+  if (dpo != nullptr && dpo->fused_reference) {
+    auto both = [&](int i, const lsf_layer_weights& lw) {
+      const hipError_t e = policy_fwd(i, lw);
+      return e != hipSuccess ? e : reference_fwd(i, lw);
+    };
+    if ((s = walk_layers(st, resident, true, reuse, both))) return s;
+    HIPCK(reference_head());
+  } else if ((s = walk_layers(st, resident, true, reuse, policy_fwd))) {
+    return s;
+  }
+
+  // ---- head: final norm, lm_head, loss and dlogits
+  const uint16_t* xL = io->ckpt + (size_t)L * act;
+  const bool fwd_only = io->mode & LSF_MODE_FWD_ONLY;
+  HIPCK(head_logits(st, io, w, xL, timing));
+  if (dpo == nullptr) {
+    HIPCK(cross_entropy(io->logits, io->ids, c.batch, c.seq, V, io->loss_scale, w.dlog, w.row_loss, io->loss, cs));
+  } else {
+    HIPCK(seq_logprobs(io->logits, io->ids, c.batch, c.seq, V, w.lse, w.row_loss, lp_pi, cs));
+    HIPCK(dpo_head_grad(io->logits, io->ids, w.lse, lp_pi, lp_ref, c.batch, c.seq, V, dpo->beta, io->loss_scale,
+                        w.coef, io->loss, fwd_only ? nullptr : w.dlog, cs));
+    if (dpo->seq_logp != nullptr)
+      HIPCK(hipMemcpyAsync(dpo->seq_logp, w.lp, (size_t)c.batch * 8, hipMemcpyDeviceToDevice, cs));
+  }
+  if (fwd_only) return ok();
+  HIPCK(head_backward(st, io, w, xL, w.dx[L & 1], timing));
+
+  // ---- backward: layers L-1 .. 0, each read again and recomputed
+  auto policy_bwd = [&](int j, const lsf_layer_weights& lw) {
+    return layer_backward(c, lw, &io->lora[j], io->ckpt + (size_t)j * act, w.dx[(j + 1) & 1], w.dx[j & 1], w.layer,
+                          true, cs);
+  };
+  if ((s = walk_layers(st, resident, false, reuse, policy_bwd))) return s;
+  return ok();
 }
 
 }  // namespace
@@ -617,130 +811,13 @@ size_t stack_workspace_bytes(const lsf_layer_cfg* cfg, int32_t vocab) {
 }
 
 lsf_status stream_stack_step(lsf_stack* st, const lsf_stack_io* io) {
-  if (st == nullptr || io == nullptr) return fail(LSF_ERR_INVALID_ARG, "stack or io is NULL");
-  const lsf_layer_cfg& c = st->cfg;
-  const int L = st->d.n_layers;
-  const int V = io->vocab;
-  const int T = c.batch * c.seq, H = c.hidden;
-  lsf_status s;
-  if (V < 128 || V % 128) return fail(LSF_ERR_SHAPE, "vocab must be a positive multiple of 128 (got %d)", V);
-  if ((s = check_dev(io->ids, "ids")) || (s = check_dev(io->embed, "embed")) ||
-      (s = check_dev(io->final_norm, "final_norm")) || (s = check_dev(io->lm_head, "lm_head")) ||
-      (s = check_dev(io->ckpt, "ckpt")) || (s = check_dev(io->logits, "logits")) || (s = check_dev(io->loss, "loss")))
-    return s;
-  if (io->lora == nullptr) return fail(LSF_ERR_INVALID_ARG, "lora array is NULL");
-  for (int i = 0; i < L; ++i)
-    if ((s = check_lora(&io->lora[i]))) return s;
-  const bool resident = io->mode & LSF_MODE_RESIDENT;
-  if (resident && st->d.resident_store == nullptr) return fail(LSF_ERR_INVALID_ARG, "RESIDENT mode needs a resident store");
-  if (!resident && st->d.host_store == nullptr) return fail(LSF_ERR_INVALID_ARG, "STREAMED mode needs a host store");
-  if (io->ws == nullptr || io->ws_bytes < stack_ws_bytes(c, V))
-    return fail(LSF_ERR_WORKSPACE, "workspace too small (need %zu bytes)", stack_ws_bytes(c, V));
+  if (io == nullptr) return fail(LSF_ERR_INVALID_ARG, "stack or io is NULL");
+  return run_step(st, io, nullptr);
+}
 
-  hipStream_t cs = S(st->d.compute);
-  StackWs w = carve_stack(c, V, io->ws);
-  const bool timing = st->d.flags & LSF_STACK_TIMING;
-  if (timing) {
-    st->probe.pool = &st->events;
-    w.layer.probe = &st->probe;
-    HIPCK(harvest_all(st, false));  // recycle the events of work that has finished
-  }
-  const size_t act = (size_t)T * H;
-  st->stats.steps += 1;
-
-  if (io->mode & LSF_MODE_ZERO_GRADS) {
-    for (int i = 0; i < L; ++i) {
-      const lsf_layer_lora& l = io->lora[i];
-      const lsf_lora_proj* p = &l.q;
-      const lsf_layer_cfg& cc = c;
-      const int64_t H_ = cc.hidden, I_ = cc.intermediate, Dq = (int64_t)cc.n_heads * cc.head_dim,
-                    Dk = (int64_t)cc.n_kv_heads * cc.head_dim;
-      const int64_t in[7] = {H_, H_, H_, Dq, H_, H_, I_};
-      const int64_t outd[7] = {Dq, Dk, Dk, H_, I_, I_, H_};
-      for (int k = 0; k < 7; ++k) {
-        if (p[k].A == nullptr) continue;
-        if (p[k].dA) HIPCK(zero_f32(p[k].dA, (int64_t)cc.rank * in[k], cs));
-        if (p[k].dB) HIPCK(zero_f32(p[k].dB, (int64_t)cc.rank * outd[k], cs));
-      }
-    }
-  }
-
-  HIPCK(rope_table(c.seq, c.head_dim, c.rope_theta, w.layer.rope, cs));
-  HIPCK(embed_gather(io->ids, io->embed, T, H, V, io->ckpt, cs));
-
-  auto weights_of = [&](int j, int b) {
-    lsf_layer_weights lw;
-    const void* blob = resident ? static_cast<const char*>(st->d.resident_store) + (uint64_t)j * st->d.blob_stride
-                                : st->d.dev_buf[b];
-    weights_from_blob(c, st->d.format, blob, &lw);
-    return lw;
-  };
-
-  // ---- forward: layer i computes from buffer i % 2 while i + 1 loads.  A
-  // full step ends with layers 1 and 0 in buffers 1 and 0, which is what the
-  // next forward reads first: the frozen store never changes, so they are
-  // reused unless LSF_STACK_NO_TURN_REUSE asks for every copy.
-  const bool reuse = !(st->d.flags & LSF_STACK_NO_TURN_REUSE);
-  if (!resident) {
-    if ((s = acquire(st, 0, 0, reuse))) return s;
-    if (L > 1 && (s = acquire(st, 1, 1, reuse))) return s;
-  }
-  for (int i = 0; i < L; ++i) {
-    const int b = i & 1;
-    if (!resident && (s = wait_ready(st, b))) return s;
-    const lsf_layer_weights lw = weights_of(i, b);
-    HIPCK(layer_forward(c, lw, &io->lora[i], io->ckpt + (size_t)i * act, io->ckpt + (size_t)(i + 1) * act, w.layer,
-                        false, true, cs));
-    if (!resident) {
-      HIPCK(hipEventRecord(st->freed[b], cs));
-      st->used[b] = true;
-      if (i + 2 < L && (s = acquire(st, i + 2, b, false))) return s;
-    }
-  }
-
-  // ---- head: final norm, lm_head, cross-entropy, lm_head input gradient
-  const uint16_t* xL = io->ckpt + (size_t)L * act;
-  HIPCK(rmsnorm_fwd(xL, io->final_norm, T, H, c.rms_eps, w.hN, w.rstdN, cs));
-  {
-    GemmArgs g;
-    g.M = T; g.N = V; g.K = H; g.A = w.hN; g.lda = H;
-    g.W.fmt = FMT_BF16; g.W.bf16 = io->lm_head; g.W.ld = H;
-    EpiArgs e; e.kind = EPI_F32; e.C = io->logits; e.ldc = V;
-    if (timing) HIPCK(st->probe.begin(LSF_K_HEAD_FWD, cs));
-    HIPCK(gemm_nt(g, e, cs));
-    if (timing) HIPCK(st->probe.end(LSF_K_HEAD_FWD, cs));
-  }
-  HIPCK(cross_entropy(io->logits, io->ids, c.batch, c.seq, V, io->loss_scale, w.dlog, w.row_loss, io->loss, cs));
-  if (io->mode & LSF_MODE_FWD_ONLY) return ok();
-  {
-    GemmArgs g;
-    g.M = T; g.N = H; g.K = V; g.A = w.dlog; g.lda = V;
-    g.W.fmt = FMT_BF16; g.W.bf16 = io->lm_head; g.W.ld = H;
-    EpiArgs e; e.kind = EPI_BF16; e.C = w.dhN; e.ldc = H;
-    if (timing) HIPCK(st->probe.begin(LSF_K_HEAD_BWD, cs));
-    HIPCK(run_gemm(true, g, e, w.part, w.part_floats, cs));
-    if (timing) HIPCK(st->probe.end(LSF_K_HEAD_BWD, cs));
-  }
-  HIPCK(rmsnorm_bwd(w.dhN, xL, io->final_norm, w.rstdN, nullptr, T, H, w.dx[L & 1], cs));
-
-  // ---- backward: layers L-1 .. 0, layer j again from buffer j % 2
-  if (!resident) {
-    if ((s = acquire(st, L - 1, (L - 1) & 1, reuse))) return s;
-    if (L > 1 && (s = acquire(st, L - 2, (L - 2) & 1, reuse))) return s;
-  }
-  for (int j = L - 1; j >= 0; --j) {
-    const int b = j & 1;
-    if (!resident && (s = wait_ready(st, b))) return s;
-    const lsf_layer_weights lw = weights_of(j, b);
-    HIPCK(layer_backward(c, lw, &io->lora[j], io->ckpt + (size_t)j * act, w.dx[(j + 1) & 1], w.dx[j & 1], w.layer,
-                         true, cs));
-    if (!resident) {
-      HIPCK(hipEventRecord(st->freed[b], cs));
-      st->used[b] = true;
-      if (j - 2 >= 0 && (s = acquire(st, j - 2, b, false))) return s;
-    }
-  }
-  return ok();
+lsf_status dpo_stack_step(lsf_stack* st, const lsf_dpo_io* io) {
+  if (io == nullptr) return fail(LSF_ERR_INVALID_ARG, "stack or io is NULL");
+  return run_step(st, &io->base, io);
 }
 
 lsf_status stack_stats(lsf_stack* st, lsf_stack_stats* out) {

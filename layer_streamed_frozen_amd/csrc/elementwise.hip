@@ -138,17 +138,10 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
   for (int i = threadIdx.x; i < H / 8; i += 256) dst[i] = src[i];
 }
 
-// One workgroup per row of logits.  Pass 1: running (max, sum of exp) per
-// thread, merged in a fixed order; pass 2: softmax minus one-hot, scaled.
-__global__ __launch_bounds__(256) void ce_row_kernel(const float* __restrict__ logits, const int32_t* __restrict__ ids,
-                                                     int seq, int V, float coef, uint16_t* __restrict__ dlogits,
-                                                     float* __restrict__ row_loss) {
+// Log-sum-exp of one row of V logits over a 256-thread workgroup: a running
+// (max, sum of exp) per thread, merged lane -> wave -> workgroup in a fixed order.
+__device__ __forceinline__ float row_lse(const float* __restrict__ z, int V) {
   __shared__ float sm[4], ss[4];
-  const int64_t t = blockIdx.x;
-  const float* z = logits + t * V;
-  const bool valid = (t % seq) < seq - 1;
-  int label = valid ? ids[t + 1] : 0;
-  label = label < 0 ? 0 : (label >= V ? V - 1 : label);
   float m = -INFINITY, s = 0.0f;
   for (int v = threadIdx.x; v < V; v += 256) {
     const float x = z[v];
@@ -159,7 +152,6 @@ __global__ __launch_bounds__(256) void ce_row_kernel(const float* __restrict__ l
       s += __expf(x - m);
     }
   }
-  // merge within the wave
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
@@ -170,16 +162,101 @@ __global__ __launch_bounds__(256) void ce_row_kernel(const float* __restrict__ l
   const int wid = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) { sm[wid] = m; ss[wid] = s; }
   __syncthreads();
-  float M = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+  const float M = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
   float S = 0.0f;
 #pragma unroll
   for (int w = 0; w < 4; ++w) S += ss[w] * __expf(sm[w] - M);
-  const float lse = M + __logf(S);
+  return M + __logf(S);
+}
+
+// Next-token label of row t (the id one position on) and whether row t has
+// one: the last position of each sequence is unlabelled.
+__device__ __forceinline__ int row_label(const int32_t* __restrict__ ids, int64_t t, int seq, int V, bool& valid) {
+  valid = (t % seq) < seq - 1;
+  int label = valid ? ids[t + 1] : 0;
+  return label < 0 ? 0 : (label >= V ? V - 1 : label);
+}
+
+// One workgroup per row of logits: the loss term and softmax minus one-hot, scaled.
+__global__ __launch_bounds__(256) void ce_row_kernel(const float* __restrict__ logits, const int32_t* __restrict__ ids,
+                                                     int seq, int V, float coef, uint16_t* __restrict__ dlogits,
+                                                     float* __restrict__ row_loss) {
+  const int64_t t = blockIdx.x;
+  const float* z = logits + t * V;
+  bool valid;
+  const int label = row_label(ids, t, seq, V, valid);
+  const float lse = row_lse(z, V);
   if (threadIdx.x == 0) row_loss[t] = valid ? (lse - z[label]) : 0.0f;
   uint16_t* d = dlogits + t * V;
   for (int v = threadIdx.x; v < V; v += 256) {
     float g = 0.0f;
     if (valid) g = (__expf(z[v] - lse) - (v == label ? 1.0f : 0.0f)) * coef;
+    d[v] = f32_to_bf16(g);
+  }
+}
+
+// Row statistics for sequence log-probabilities: lse[t] and the log-probability
+// of row t's label (0 for unlabelled rows).
+__global__ __launch_bounds__(256) void ce_stats_kernel(const float* __restrict__ logits,
+                                                       const int32_t* __restrict__ ids, int seq, int V,
+                                                       float* __restrict__ lse_out, float* __restrict__ row_logp) {
+  const int64_t t = blockIdx.x;
+  const float* z = logits + t * V;
+  bool valid;
+  const int label = row_label(ids, t, seq, V, valid);
+  const float lse = row_lse(z, V);
+  if (threadIdx.x == 0) {
+    lse_out[t] = lse;
+    row_logp[t] = valid ? (z[label] - lse) : 0.0f;
+  }
+}
+
+// One workgroup per sequence: the sum of its seq row values, fixed order.
+__global__ __launch_bounds__(256) void seq_sum_kernel(const float* __restrict__ x, int seq, float* __restrict__ out) {
+  __shared__ float red[4];
+  const float* r = x + (int64_t)blockIdx.x * seq;
+  float s = 0.0f;
+  for (int i = threadIdx.x; i < seq; i += 256) s += r[i];
+  s = block_sum(s, red);
+  if (threadIdx.x == 0) out[blockIdx.x] = s;
+}
+
+// DPO over P pairs (sequences 0..P-1 chosen, P..2P-1 rejected):
+// h_p = (lp[p] - ref[p]) - (lp[P+p] - ref[P+p]), loss = mean_p softplus(-beta h_p).
+// coef[s] is -dloss/dlp[s] times loss_scale, the factor on (softmax - onehot)
+// in the rows of sequence s.  One thread, pairs summed in order.
+__global__ void dpo_coef_kernel(const float* __restrict__ lp, const float* __restrict__ ref, int P, float beta,
+                                float loss_scale, float* __restrict__ coef, float* __restrict__ loss) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  float acc = 0.0f;
+  for (int p = 0; p < P; ++p) {
+    const float h = (lp[p] - ref[p]) - (lp[P + p] - ref[P + p]);
+    const float x = -beta * h;
+    acc += fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x)));  // softplus(x)
+    const float sig = 1.0f / (1.0f + expf(beta * h));  // sigmoid(-beta h)
+    const float c = beta * sig / (float)P * loss_scale;
+    coef[p] = c;
+    coef[P + p] = -c;
+  }
+  *loss = acc / (float)P;
+}
+
+// dlogits of a sequence-level loss: coef[sequence] (softmax - onehot) on labelled rows.
+__global__ __launch_bounds__(256) void ce_grad_kernel(const float* __restrict__ logits,
+                                                      const int32_t* __restrict__ ids,
+                                                      const float* __restrict__ lse_in,
+                                                      const float* __restrict__ coef, int seq, int V,
+                                                      uint16_t* __restrict__ dlogits) {
+  const int64_t t = blockIdx.x;
+  const float* z = logits + t * V;
+  bool valid;
+  const int label = row_label(ids, t, seq, V, valid);
+  const float lse = lse_in[t];
+  const float c = coef[t / seq];
+  uint16_t* d = dlogits + t * V;
+  for (int v = threadIdx.x; v < V; v += 256) {
+    float g = 0.0f;
+    if (valid) g = (__expf(z[v] - lse) - (v == label ? 1.0f : 0.0f)) * c;
     d[v] = f32_to_bf16(g);
   }
 }
@@ -243,6 +320,25 @@ hipError_t cross_entropy(const float* logits, const int32_t* ids, int batch, int
   hipLaunchKernelGGL(ce_row_kernel, dim3(T), dim3(256), 0, s, logits, ids, seq, V, coef, dlogits, row_loss);
   hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(256), 0, s, row_loss, T, count > 0 ? 1.0f / (float)count : 0.0f,
                      loss);
+  return hipGetLastError();
+}
+
+hipError_t seq_logprobs(const float* logits, const int32_t* ids, int batch, int seq, int V, float* lse,
+                        float* row_logp, float* lp, hipStream_t s) {
+  const int T = batch * seq;
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(ce_stats_kernel, dim3(T), dim3(256), 0, s, logits, ids, seq, V, lse, row_logp);
+  hipLaunchKernelGGL(seq_sum_kernel, dim3(batch), dim3(256), 0, s, row_logp, seq, lp);
+  return hipGetLastError();
+}
+
+hipError_t dpo_head_grad(const float* logits, const int32_t* ids, const float* lse, const float* lp_pi,
+                         const float* lp_ref, int batch, int seq, int V, float beta, float loss_scale, float* coef,
+                         float* loss, uint16_t* dlogits, hipStream_t s) {
+  const int P = batch / 2;
+  hipLaunchKernelGGL(dpo_coef_kernel, dim3(1), dim3(64), 0, s, lp_pi, lp_ref, P, beta, loss_scale, coef, loss);
+  if (dlogits != nullptr)
+    hipLaunchKernelGGL(ce_grad_kernel, dim3(batch * seq), dim3(256), 0, s, logits, ids, lse, coef, seq, V, dlogits);
   return hipGetLastError();
 }
 

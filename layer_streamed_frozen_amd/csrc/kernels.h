@@ -130,6 +130,15 @@ hipError_t embed_gather(const int32_t* ids, const uint16_t* E, int T, int H, int
 // CE over next-token labels; writes per-row loss terms, dlogits (bf16) and the mean loss.
 hipError_t cross_entropy(const float* logits, const int32_t* ids, int batch, int seq, int V, float loss_scale,
                          uint16_t* dlogits, float* row_loss, float* loss, hipStream_t s);
+// Per-sequence sums of next-token log-probabilities: lse [T], row_logp [T]
+// (label log-probability, 0 on unlabelled rows) and lp [batch].
+hipError_t seq_logprobs(const float* logits, const int32_t* ids, int batch, int seq, int V, float* lse,
+                        float* row_logp, float* lp, hipStream_t s);
+// DPO loss over batch/2 pairs (chosen sequences first) and, if dlogits is not
+// NULL, its logits gradient times loss_scale; coef [batch] is scratch.
+hipError_t dpo_head_grad(const float* logits, const int32_t* ids, const float* lse, const float* lp_pi,
+                         const float* lp_ref, int batch, int seq, int V, float beta, float loss_scale, float* coef,
+                         float* loss, uint16_t* dlogits, hipStream_t s);
 
 // Attention (head_dim 128, causal, GQA).  qkv: [T, ldqkv] with q heads, then
 // k heads, then v heads; o: [T, nq*128]; lse: [batch, nq, seq].

@@ -222,8 +222,9 @@ class Stack:
         self.ckpt = torch.empty((store.n_layers + 1, T, H), dtype=torch.bfloat16, device=device)
         self.logits = torch.empty((T, vocab), dtype=torch.float32, device=device)
         self.loss = torch.zeros(1, dtype=torch.float32, device=device)
+        self.seq_logp = torch.zeros((2, batch), dtype=torch.float32, device=device)  # DPO: policy, reference
 
-    def step(self, ids, embed, final_norm, lm_head, lora_arr, mode=B.MODE_STREAMED, loss_scale=1.0):
+    def _io(self, ids, embed, final_norm, lm_head, lora_arr, mode, loss_scale):
         io = B.StackIO()
         io.ids = ids.data_ptr()
         io.embed = embed.data_ptr()
@@ -238,7 +239,22 @@ class Stack:
         io.ws_bytes = self.ws.numel()
         io.loss_scale = loss_scale
         io.mode = mode
-        B.stream_stack_step(self.handle, io)
+        return io
+
+    def step(self, ids, embed, final_norm, lm_head, lora_arr, mode=B.MODE_STREAMED, loss_scale=1.0):
+        """One SFT micro-batch (cross-entropy on next tokens)."""
+        B.stream_stack_step(self.handle, self._io(ids, embed, final_norm, lm_head, lora_arr, mode, loss_scale))
+
+    def dpo_step(self, ids, embed, final_norm, lm_head, lora_arr, beta=0.1, fused=True, mode=B.MODE_STREAMED,
+                 loss_scale=1.0):
+        """One DPO micro-batch: ids holds the chosen sequences, then the
+        rejected ones.  Fills self.seq_logp [2, batch] (policy, reference)."""
+        io = B.DpoIO()
+        io.base = self._io(ids, embed, final_norm, lm_head, lora_arr, mode, loss_scale)
+        io.beta = beta
+        io.fused_reference = 1 if fused else 0
+        io.seq_logp = self.seq_logp.data_ptr()
+        B.dpo_stack_step(self.handle, io)
 
     def stats(self):
         return B.stack_stats(self.handle)

@@ -68,6 +68,17 @@ def token_ids(name, shape, vocab, seed=SEED):
     return g.integers(0, vocab, size=shape, dtype=np.int64).astype(np.int32)
 
 
+def preference_pairs(name, pairs, seq, vocab, prompt_len, seed=SEED):
+    """int32 ids [2 * pairs, seq] for preference training: rows 0..pairs-1 are
+    the chosen sequences, rows pairs..2*pairs-1 the rejected ones; pair p
+    shares its first prompt_len tokens (the prompt) and draws the two
+    responses independently."""
+    prompt = token_ids(name + ".prompt", (pairs, prompt_len), vocab, seed)
+    resp = token_ids(name + ".response", (2 * pairs, seq - prompt_len), vocab, seed)
+    ids = np.concatenate([np.concatenate([prompt, prompt]), resp], axis=1)
+    return np.ascontiguousarray(ids, dtype=np.int32)
+
+
 def bf16_exact(x):
     """Clear the low 16 bits: returns (fp32 values, uint16 bfloat16 bits)."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32) & np.uint32(0xFFFF0000)
