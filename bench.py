@@ -1,6 +1,6 @@
 """Throughput of the streamed NF4 + LoRA training step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload stack1|stack4]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload stack1|stack4|dpo|dpo-unfused]
 
 Workload (default "stack1"): 32 Llama-3.1-8B-shaped decoder layers (hidden
 4096, intermediate 14336, 32 query / 8 kv heads of 128, RoPE theta 500000),
@@ -10,7 +10,12 @@ v, o, gate, up, down; resident untied bf16 embedding and lm_head over a
 128256-token vocabulary; one sequence of 512 random token ids per step;
 cross-entropy loss; forward, head, and recomputing backward (all LoRA
 gradients).  "stack4" is 4 sequences of 512 per micro-batch and 4 micro-batches
-(gradient accumulation) per step.  Inputs and weights are seeded synthetic data.
+(gradient accumulation) per step.  "dpo" is the preference-loss step: 2
+chosen/rejected pairs of 512 tokens (4 sequences, pair p sharing a 256-token
+prompt), DPO with beta 0.1, the reference log-probabilities from the same
+streamed base with the adapters off, computed in the policy's layer visit
+("dpo-unfused": in a separate pass over the stack).  Inputs and weights are
+seeded synthetic data.
 
 Prints one JSON line.  ``value`` is tokens per second over the timed steps,
 with every input already resident (the frozen store in pinned host memory is
@@ -55,7 +60,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", choices=["stack1", "stack4"], default="stack1")
+    p.add_argument("--workload", choices=["stack1", "stack4", "dpo", "dpo-unfused"], default="stack1")
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--format", choices=["nf4", "nf4dq", "bf16"], default="nf4",
                    help="frozen-base storage: NF4 with fp32 absmax, NF4 with 8-bit double-quantised absmax, "
@@ -166,7 +171,8 @@ def main():
     torch.cuda.set_device(0)
     shape = S.LLAMA8B
     L, V, seq = args.layers, 128256, 512
-    batch, accum = (1, 1) if args.workload == "stack1" else (4, 4)
+    batch, accum = {"stack1": (1, 1), "stack4": (4, 4), "dpo": (4, 1), "dpo-unfused": (4, 1)}[args.workload]
+    dpo = args.workload.startswith("dpo")
     T = batch * seq
 
     t0 = time.time()
@@ -192,13 +198,20 @@ def main():
     head = torch.from_numpy(synth.bf16_exact(synth.normal("lm_head", (V, H), 0.02))[1].view(np.int16)) \
         .view(torch.bfloat16).cuda()
     fnorm = torch.ones(H, dtype=torch.bfloat16, device="cuda")
-    ids = [torch.from_numpy(synth.token_ids(f"ids{m}", (batch, seq), V)).cuda() for m in range(accum)]
+    if dpo:
+        ids = [torch.from_numpy(synth.preference_pairs("pairs", batch // 2, seq, V, seq // 2)).cuda()]
+    else:
+        ids = [torch.from_numpy(synth.token_ids(f"ids{m}", (batch, seq), V)).cuda() for m in range(accum)]
     flags = 0 if args.no_timing else B.STACK_TIMING
     stack = S.Stack(shape, store, batch, seq, V, flags=flags)
     arr = lora.array()
     torch.cuda.synchronize()
 
     def step():
+        if dpo:
+            stack.dpo_step(ids[0], emb, fnorm, head, arr, beta=0.1, fused=args.workload == "dpo",
+                           mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+            return
         for m in range(accum):
             mode = B.MODE_STREAMED | (B.MODE_ZERO_GRADS if m == 0 else 0)
             stack.step(ids[m], emb, fnorm, head, arr, mode=mode, loss_scale=1.0 / accum)
@@ -280,7 +293,11 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded random weights and token ids)",
         "config": {"workload": (f"streamed {L}-layer Llama-3.1-8B-shaped stack, {base_desc}, "
                                 f"LoRA r16 on q,k,v,o,gate,up,down, vocab {V}, "
-                                f"batch {batch} x seq {seq}, accumulation {accum}"),
+                                + (f"DPO beta 0.1 over {batch // 2} chosen/rejected pairs x seq {seq}, "
+                                   f"reference = adapters off, "
+                                   + ("fused into the policy's layer visit" if args.workload == "dpo"
+                                      else "separate reference pass") if dpo else
+                                   f"batch {batch} x seq {seq}, accumulation {accum}")),
                    "global_batch": batch * accum, "seq_len": seq, "layers": L, "vocab": V,
                    "parallelism": "single GPU"},
         "h2d": h2d, "roofline": roof, "layer_gemms": layer_gemms, "kernels": kernels,
