@@ -308,6 +308,37 @@ typedef struct {
 
 LSF_API lsf_status dpo_stack_step(lsf_stack* st, const lsf_dpo_io* io);
 
+/* ------------------------------------------------------------ optimizer --
+ * [TUTORIAL] "step 2: one YAML" trains the adapters with an Adam-family
+ * optimizer with decoupled weight decay at lr 2e-4; [NEWS] keeps the adapters,
+ * their gradients and the optimizer state on the GPU.  AdamW (fp32 state; the
+ * pages' 8-bit paged state is not built) over ONE flat fp32 array of n values:
+ * a caller that lays every adapter A and B of the stack end to end (and their
+ * gradients likewise) updates all of them with one call.  For step t >= 1:
+ *   g <- g * min(1, max_grad_norm / (||g||_2 + 1e-6))   when max_grad_norm > 0
+ *   p <- p - lr*weight_decay*p
+ *   m <- beta1 m + (1 - beta1) g;   v <- beta2 v + (1 - beta2) g^2
+ *   p <- p - lr/(1 - beta1^t) * m / (sqrt(v)/sqrt(1 - beta2^t) + eps)
+ * The norm is summed in a fixed order (deterministic).  grad is not modified. */
+typedef struct {
+  float lr;             /* learning rate, >= 0 */
+  float beta1, beta2;   /* in [0, 1), e.g. 0.9, 0.999 */
+  float eps;            /* > 0, e.g. 1e-8 */
+  float weight_decay;   /* decoupled decay, >= 0 (0 = none) */
+  float max_grad_norm;  /* > 0: clip by the global L2 norm first; 0 = no clipping */
+  int32_t step;         /* t >= 1: updates made so far, this one included */
+} lsf_adamw_cfg;
+
+/* Device workspace adamw_step needs (a few KiB, independent of n). */
+LSF_API size_t adamw_workspace_bytes(void);
+/* param, m, v: device fp32 [n], updated in place; grad: device fp32 [n].  All
+ * four 16-byte aligned (LSF_ERR_ALIGN).  grad_norm (optional, device fp32 [1])
+ * receives ||grad||_2 before clipping.  n >= 0 (0 enqueues nothing).  Bad
+ * hyper-parameters give LSF_ERR_INVALID_ARG. */
+LSF_API lsf_status adamw_step(float* param, const float* grad, float* m, float* v, int64_t n,
+                              const lsf_adamw_cfg* cfg, float* grad_norm, void* ws, size_t ws_bytes,
+                              lsf_stream stream);
+
 /* Kernel classes timed with HIP events under LSF_STACK_TIMING (index into
  * lsf_stack_stats.kernel_ms / kernel_launches).  A GEMM's time includes its
  * split-K reduction when it has one. */

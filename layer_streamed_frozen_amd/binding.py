@@ -83,6 +83,11 @@ class DpoIO(ctypes.Structure):
     _fields_ = [("base", StackIO), ("beta", c_float), ("fused_reference", c_int32), ("seq_logp", c_void_p)]
 
 
+class AdamwCfg(ctypes.Structure):
+    _fields_ = [("lr", c_float), ("beta1", c_float), ("beta2", c_float), ("eps", c_float),
+                ("weight_decay", c_float), ("max_grad_norm", c_float), ("step", c_int32)]
+
+
 class StackStats(ctypes.Structure):
     _fields_ = [("steps", c_int64), ("copies", c_int64), ("bytes", c_int64), ("copy_ms", ctypes.c_double),
                 ("wait_ms", ctypes.c_double), ("kernel_ms", ctypes.c_double * 16),
@@ -121,6 +126,9 @@ _PROTOS = {
     "dpo_stack_step": (c_int32, [c_void_p, ctypes.POINTER(DpoIO)]),
     "stack_stats": (c_int32, [c_void_p, ctypes.POINTER(StackStats)]),
     "stack_reset_stats": (c_int32, [c_void_p]),
+    "adamw_workspace_bytes": (c_size_t, []),
+    "adamw_step": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, ctypes.POINTER(AdamwCfg), c_void_p,
+                             c_void_p, c_size_t, c_void_p]),
 }
 
 _LIB = None
@@ -279,3 +287,15 @@ def stack_stats(h):
 
 def stack_reset_stats(h):
     check(lib().stack_reset_stats(h))
+
+
+def adamw_workspace_bytes():
+    return lib().adamw_workspace_bytes()
+
+
+def adamw_step(param, grad, m, v, cfg, grad_norm, ws, n=None, stream=None):
+    """AdamW over flat fp32 device tensors (n defaults to param.numel())."""
+    n = param.numel() if n is None else n
+    check(lib().adamw_step(ptr(param), ptr(grad), ptr(m), ptr(v), n, ctypes.byref(cfg),
+                           ptr(grad_norm) if grad_norm is not None else None, ptr(ws),
+                           ws.numel() * ws.element_size(), stream_ptr(stream)))

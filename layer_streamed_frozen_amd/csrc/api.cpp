@@ -820,6 +820,35 @@ lsf_status dpo_stack_step(lsf_stack* st, const lsf_dpo_io* io) {
   return run_step(st, &io->base, io);
 }
 
+size_t adamw_workspace_bytes(void) { return adamw_ws_bytes(); }
+
+lsf_status adamw_step(float* param, const float* grad, float* m, float* v, int64_t n, const lsf_adamw_cfg* cfg,
+                      float* grad_norm, void* ws, size_t ws_bytes, lsf_stream stream) {
+  if (cfg == nullptr) return fail(LSF_ERR_INVALID_ARG, "cfg is NULL");
+  if (n < 0) return fail(LSF_ERR_INVALID_ARG, "n must be >= 0");
+  const lsf_adamw_cfg& c = *cfg;
+  if (!(c.lr >= 0.0f) || !std::isfinite(c.lr)) return fail(LSF_ERR_INVALID_ARG, "lr must be finite and >= 0");
+  if (!(c.beta1 >= 0.0f && c.beta1 < 1.0f) || !(c.beta2 >= 0.0f && c.beta2 < 1.0f))
+    return fail(LSF_ERR_INVALID_ARG, "beta1 and beta2 must lie in [0, 1)");
+  if (!(c.eps > 0.0f) || !std::isfinite(c.eps)) return fail(LSF_ERR_INVALID_ARG, "eps must be positive");
+  if (!(c.weight_decay >= 0.0f) || !std::isfinite(c.weight_decay))
+    return fail(LSF_ERR_INVALID_ARG, "weight_decay must be finite and >= 0");
+  if (!(c.max_grad_norm >= 0.0f) || !std::isfinite(c.max_grad_norm))
+    return fail(LSF_ERR_INVALID_ARG, "max_grad_norm must be finite and >= 0");
+  if (c.step < 1) return fail(LSF_ERR_INVALID_ARG, "step must be >= 1 (got %d)", c.step);
+  if (n == 0) return ok();
+  lsf_status s;
+  if ((s = check_dev(param, "param")) || (s = check_dev(grad, "grad")) || (s = check_dev(m, "m")) ||
+      (s = check_dev(v, "v")))
+    return s;
+  if (grad_norm != nullptr && !aligned(grad_norm, 4)) return fail(LSF_ERR_ALIGN, "grad_norm is not aligned");
+  if (ws == nullptr || ws_bytes < adamw_ws_bytes() || !aligned(ws, 16))
+    return fail(LSF_ERR_WORKSPACE, "workspace too small or unaligned (need %zu bytes)", adamw_ws_bytes());
+  HIPCK(adamw_update(param, grad, m, v, n, c.lr, c.beta1, c.beta2, c.eps, c.weight_decay, c.max_grad_norm, c.step,
+                     grad_norm, static_cast<float*>(ws), S(stream)));
+  return ok();
+}
+
 lsf_status stack_stats(lsf_stack* st, lsf_stack_stats* out) {
   if (st == nullptr || out == nullptr) return fail(LSF_ERR_INVALID_ARG, "stack or out is NULL");
   HIPCK(harvest_all(st, true));

@@ -140,6 +140,14 @@ hipError_t dpo_head_grad(const float* logits, const int32_t* ids, const float* l
                          const float* lp_ref, int batch, int seq, int V, float beta, float loss_scale, float* coef,
                          float* loss, uint16_t* dlogits, hipStream_t s);
 
+// AdamW over n fp32 values (16-byte aligned arrays), moments m, v; t = step >= 1.
+// Clips the gradient to max_grad_norm (> 0) by its global L2 norm first; writes
+// that norm to grad_norm when it is not NULL.  ws: adamw_ws_bytes() of device memory.
+size_t adamw_ws_bytes();
+hipError_t adamw_update(float* p, const float* g, float* m, float* v, int64_t n, float lr, float beta1, float beta2,
+                        float eps, float weight_decay, float max_grad_norm, int step, float* grad_norm, float* ws,
+                        hipStream_t s);
+
 // Attention (head_dim 128, causal, GQA).  qkv: [T, ldqkv] with q heads, then
 // k heads, then v heads; o: [T, nq*128]; lse: [batch, nq, seq].
 struct AttnArgs {

@@ -135,27 +135,45 @@ class Store:
 
 class LoraSet:
     """Trainable adapters of a stack: fp32 A [r, in], B [out, r] and their
-    gradients, per layer and projection (``targets`` picks the projections)."""
+    gradients, per layer and projection (``targets`` picks the projections).
+
+    Every A and B lives in one flat fp32 arena (``params``), and every dA, dB
+    at the same offsets in a second one (``grads``), each tensor starting on a
+    256-byte boundary with zero padding between, so one optimizer call updates
+    the whole set."""
+
+    ALIGN = 64  # elements (256 bytes)
 
     def __init__(self, shape, n_layers, targets=PROJ, device="cuda", prefix="lora", b_zero=False):
         self.shape, self.n_layers, self.targets = shape, n_layers, tuple(targets)
         self.A, self.B, self.dA, self.dB = [], [], [], []
         r = shape.rank
+        slots, total = [], 0
         for i in range(n_layers):
-            a, b, da, db = {}, {}, {}, {}
             for n, (o, inn) in shape.proj_shapes().items():
                 if n not in self.targets:
                     continue
-                lim = 1.0 / np.sqrt(inn)
-                a[n] = torch.from_numpy(synth.uniform(f"{prefix}{i}.{n}.A", (r, inn), -lim, lim)).to(device)
-                bb = synth.normal(f"{prefix}{i}.{n}.B", (o, r), 0.01)
-                b[n] = torch.from_numpy(np.zeros_like(bb) if b_zero else bb).to(device)
-                da[n] = torch.zeros((r, inn), dtype=torch.float32, device=device)
-                db[n] = torch.zeros((o, r), dtype=torch.float32, device=device)
-            self.A.append(a)
-            self.B.append(b)
-            self.dA.append(da)
-            self.dB.append(db)
+                for which, shp in (("A", (r, inn)), ("B", (o, r))):
+                    slots.append((i, n, which, shp, total))
+                    total += -(-shp[0] * shp[1] // self.ALIGN) * self.ALIGN
+        self.params = torch.zeros(max(total, self.ALIGN), dtype=torch.float32, device=device)
+        self.grads = torch.zeros_like(self.params)
+        for i in range(n_layers):
+            for lst in (self.A, self.B, self.dA, self.dB):
+                lst.append({})
+        for i, n, which, shp, off in slots:
+            cnt = shp[0] * shp[1]
+            if which == "A":
+                lim = 1.0 / np.sqrt(shp[1])
+                vals = synth.uniform(f"{prefix}{i}.{n}.A", shp, -lim, lim)
+            else:
+                vals = synth.normal(f"{prefix}{i}.{n}.B", shp, 0.01)
+                if b_zero:
+                    vals = np.zeros_like(vals)
+            view = self.params[off:off + cnt].view(shp)
+            view.copy_(torch.from_numpy(np.ascontiguousarray(vals, dtype=np.float32)))
+            (self.A if which == "A" else self.B)[i][n] = view
+            (self.dA if which == "A" else self.dB)[i][n] = self.grads[off:off + cnt].view(shp)
         self._arr = None
 
     def struct(self, i, enabled=True, grads=True):
@@ -177,10 +195,7 @@ class LoraSet:
         return arr
 
     def zero_grads(self):
-        for i in range(self.n_layers):
-            for n in self.targets:
-                self.dA[i][n].zero_()
-                self.dB[i][n].zero_()
+        self.grads.zero_()
 
     def numpy(self, i, enabled=True):
         """LoRA dict in the oracle's form (fp64 numpy), None where absent."""
@@ -192,6 +207,25 @@ class LoraSet:
     def grads_numpy(self, i):
         return {n: (self.dA[i][n].double().cpu().numpy(), self.dB[i][n].double().cpu().numpy())
                 for n in self.targets}
+
+
+class AdamW:
+    """AdamW (fp32 moments) over a LoraSet's flat parameter arena, one launch
+    per update."""
+
+    def __init__(self, lora, lr=2e-4, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0, max_grad_norm=0.0):
+        self.lora = lora
+        self.cfg = B.AdamwCfg(lr=lr, beta1=betas[0], beta2=betas[1], eps=eps, weight_decay=weight_decay,
+                              max_grad_norm=max_grad_norm, step=0)
+        self.m = torch.zeros_like(lora.params)
+        self.v = torch.zeros_like(lora.params)
+        self.ws = torch.empty(B.adamw_workspace_bytes(), dtype=torch.uint8, device=lora.params.device)
+        self.grad_norm = torch.zeros(1, dtype=torch.float32, device=lora.params.device)
+
+    def step(self, stream=None):
+        self.cfg.step += 1
+        B.adamw_step(self.lora.params, self.lora.grads, self.m, self.v, self.cfg, self.grad_norm, self.ws,
+                     stream=stream)
 
 
 class Stack:
