@@ -22,6 +22,7 @@
 // with a fixed-order reduction keeps results deterministic.
 #include "common.h"
 #include "kernels.h"
+#include "weight_decode.h"
 
 namespace lsf {
 namespace {
@@ -61,18 +62,6 @@ __device__ __forceinline__ int64_t nt_wrow(const GemmArgs& g, int ntile, int c) 
     return ((c >> 4) & 1) ? (int64_t)g.pair_I + j : (int64_t)j;
   }
   return (int64_t)ntile * BN + c;
-}
-
-// Absmax of the 64-block holding element e of an NF4_DQ weight: 8-bit code
-// times the group's scale plus the group's offset (groups of 256 blocks).
-__device__ __forceinline__ float dq_absmax(const WeightRef& w, int64_t block) {
-  const float2 so = reinterpret_cast<const float2*>(w.dq2)[block >> 8];
-  return dq_absmax_value(w.absq[block], so.x, so.y);
-}
-
-__device__ __forceinline__ float block_absmax(const WeightRef& w, int64_t elem) {
-  const int64_t b = elem >> 6;
-  return (w.fmt == FMT_NF4_DQ) ? dq_absmax(w, b) : w.absmax[b];
 }
 
 struct Stage {
@@ -122,7 +111,7 @@ __device__ __forceinline__ void load_main(const GemmArgs& g, int m0, int ntile, 
       const u32x2 v = gload8(g.W.packed + (e >> 1));
       st.b[0] = u32x4{v.x, v.y, 0, 0};
     }
-    st.absmax = block_absmax(g.W, e);
+    st.absmax = block_absmax_t<FMT>(g.W, e);
   }
 }
 
