@@ -35,11 +35,11 @@ HBM_PEAK_GBPS = 8000.0
 PCIE5_X16_GBPS = 63.0            # theoretical per direction after 128b/130b encoding
 
 # HBM bytes per launch of the gate|up forward GEMM from two rocprofv3 --pmc passes
-# (profiles/pmc_traffic_layer8b_seq512.md): FETCH_SIZE 68693.4 KiB scaled by 1.99975
-# (the calibration kernel's ratio) + WRITE_SIZE 28675.2 KiB scaled by 1.0.  Valid only
+# (profiles/pmc_traffic_layer8b_seq512.md): FETCH_SIZE 73131.2 KiB scaled by 1.99975
+# (the calibration kernel's ratio) + WRITE_SIZE 28674.3 KiB scaled by 1.0.  Valid only
 # for the GEMM sources they were taken on (hash below); otherwise traffic is null.
-GATE_UP_TRAFFIC_BYTES = (68693.4 * 1.99975 + 28675.2 * 1.0) * 1024
-GATE_UP_TRAFFIC_SRC = "76924095fd4dc99c"
+GATE_UP_TRAFFIC_BYTES = (73131.2 * 1.99975 + 28674.3 * 1.0) * 1024
+GATE_UP_TRAFFIC_SRC = "dd4730dcf2e65007"
 # Algorithmic bytes of one such launch: NF4 codes 58.72 MB + absmax 7.34 MB + x 4.19 MB +
 # LoRA (U, B) 1.9 MB read; a 14.7 MB (forward) or a, g, u 44.0 MB (recompute) written.
 GATE_UP_ALGO_BYTES = (58.72 + 7.34 + 4.19 + 1.9 + (14.68 + 44.04) / 2) * 1e6
@@ -49,7 +49,7 @@ def gemm_src_hash():
     import hashlib
     here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "layer_streamed_frozen_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.h", "kernels.h"):
+    for f in ("gemm.hip", "common.h", "kernels.h", "weight_decode.h"):
         with open(os.path.join(here, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -130,7 +130,7 @@ def cpu_baseline(shape, T_layer=512):
     x = synth.normal("cpu.x", (1, T_layer, shape.hidden)).astype(np.float64)
     dy = synth.normal("cpu.dy", (1, T_layer, shape.hidden)).astype(np.float64)
     reps, spent = 0, 0.0
-    while reps < 2 or (spent < 10.0 and reps < 12):   # about 10 s of CPU work
+    while reps < 2 or (spent < 15.0 and reps < 40):   # about 15 s of CPU work
         t0 = time.perf_counter()
         y, cache = M.layer_fwd(x, dense, ldict, oc)
         M.layer_bwd(dy, dense, ldict, oc, cache)
