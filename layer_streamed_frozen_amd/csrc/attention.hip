@@ -1,19 +1,29 @@
 // Causal grouped-query attention, head_dim 128, on gfx950 MFMA.
 //
+// Every product whose output feeds another product is computed transposed, so
+// that its C fragments are already the B operand of the next MFMA and P and
+// dS never leave the registers: a 16x16 C fragment gives lane l the column
+// l % 16 at rows 4 (l / 16) + 0..3; two of them (rows 32c .. 32c + 31) make
+// the 8 contraction values of lane group l / 16 in the order
+// {32c + 4g + 0..3, 32c + 16 + 4g + 0..3}.  The matching A operand is read
+// from a row-major LDS tile with two transposing loads (ds_read_b64_tr_b16)
+// at those row groups.
+//
 // Forward: one workgroup per (64-query block, query head, sequence); four
-// waves own 16 query rows each.  Key/value blocks of 64 rows are staged in
-// LDS; S = Q K^T and O += P V run on v_mfma_f32_16x16x32_bf16 with an online
-// (running max / running sum) softmax in fp32.  The log-sum-exp of every row
-// is kept for the backward pass.
+// waves own 16 query rows each.  Key/value blocks of 64 rows are prefetched
+// into registers and double-buffered in LDS.  S^T = K Q^T, online softmax in
+// fp32 per query (column), O^T += V^T P^T.  The log-sum-exp of every row is
+// kept for the backward pass.
 //
 // Backward (recomputes P from Q, K and the saved log-sum-exp):
 //   pass 0: Dsum[q] = sum_d dO[q, d] O[q, d]
-//   pass 1: per (64-key block, query head): dV_h = P^T dO, dK_h = dS^T Q,
-//           written as fp32 partials per query head;
-//   pass 2: per (64-query block, query head): dQ = dS K;
+//   pass 1: per (64-key block, query head): S = Q K^T, dP = dO V^T,
+//           dV_h^T = dO^T P, dK_h^T = Q^T dS, written as fp32 partials per
+//           query head;
+//   pass 2: per (64-query block, query head): S^T, dP^T, dQ^T = K^T dS^T;
 //   pass 3: dK, dV of a kv head = the sum of its query heads' partials,
 //           in a fixed order (no atomics).
-// with dS = P (dP - Dsum), dP = dO V^T, and the 1/sqrt(d) scale.
+// with dS = P (dP - Dsum), and the 1/sqrt(d) scale.
 #include "common.h"
 #include "kernels.h"
 
@@ -25,36 +35,52 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 __device__ __forceinline__ int swz16(int row) { return (row & 15) ^ (((row >> 4) & 1) << 2); }
 __device__ __forceinline__ int off_r16(int row, int chunk) { return row * 128 + ((chunk ^ swz16(row)) << 3); }
-__device__ __forceinline__ int off_r8(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
 
-// Stage rows [r0, r0 + 64) of a [rows, ld] bf16 matrix (columns col0 .. col0+127)
-// into a 64 x 128 LDS tile; rows at or past `rows` are zero.
-__device__ __forceinline__ void load_tile(const uint16_t* src, int64_t ld, int64_t col0, int r0, int rows,
-                                          uint16_t* lds, int tid) {
+// A 64 x 128 bf16 tile (rows r0 .. r0 + 63 of a [rows, ld] matrix; zeros at or
+// past `rows`) held as four 16-byte chunks per thread between its global load
+// and its LDS store.
+struct TileRegs {
+  u32x4 v[4];
+};
+
+__device__ __forceinline__ void tile_load(const uint16_t* src, int64_t ld, int r0, int rows, int tid, TileRegs& t) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int idx = tid + NTHR * i;
     const int row = idx >> 4, ch = idx & 15;
-    u32x4 v = {0, 0, 0, 0};
-    if (r0 + row < rows) v = *reinterpret_cast<const u32x4*>(src + (int64_t)(r0 + row) * ld + col0 + ch * 8);
-    *reinterpret_cast<u32x4*>(lds + off_r16(row, ch)) = v;
+    t.v[i] = (r0 + row < rows) ? *reinterpret_cast<const u32x4*>(src + (int64_t)(r0 + row) * ld + ch * 8)
+                               : u32x4{0, 0, 0, 0};
   }
 }
 
+__device__ __forceinline__ void tile_store(const TileRegs& t, uint16_t* lds, int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + NTHR * i;
+    *reinterpret_cast<u32x4*>(lds + off_r16(idx >> 4, idx & 15)) = t.v[i];
+  }
+}
+
+// Row fragment of an LDS tile: row `row`, 8 values of chunk `chunk`.
 __device__ __forceinline__ u32x4 frag_row(const uint16_t* lds, int row, int chunk) {
   return *reinterpret_cast<const u32x4*>(lds + off_r16(row, chunk));
 }
-// Operand whose contraction runs down the tile rows: rows row0..row0+7 of column col.
-__device__ __forceinline__ u32x4 frag_gather(const uint16_t* lds, int col, int row0) {
-  const int ch = col >> 3, e = col & 7;
-  uint32_t w[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t lo = lds[off_r16(row0 + 2 * p, ch) + e];
-    const uint32_t hi = lds[off_r16(row0 + 2 * p + 1, ch) + e];
-    w[p] = lo | (hi << 16);
-  }
-  return u32x4{w[0], w[1], w[2], w[3]};
+
+// Operand whose contraction runs down the tile rows: lane l gets column
+// col0 + l % 16 at rows r0 + 4g + 0..3 and r0 + 16 + 4g + 0..3, g = l / 16.
+__device__ __forceinline__ u32x4 frag_tr(const uint16_t* lds, int col0, int r0, int lane) {
+  const int lr = lane & 15, lg = lane >> 4;
+  const int col = col0 + 4 * (lr & 3);
+  const int row = r0 + lg * 4 + (lr >> 2);
+  const u32x2 lo = lds_read_tr4(lds, off_r16(row, col >> 3) + (col & 7));
+  const u32x2 hi = lds_read_tr4(lds, off_r16(row + 16, col >> 3) + (col & 7));
+  return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+
+// B operand from two C fragments (contraction rows 32c .. 32c + 31).
+__device__ __forceinline__ u32x4 c_to_b(const f32x4& f0, const f32x4& f1) {
+  return u32x4{pack_bf16x2(f0[0], f0[1]), pack_bf16x2(f0[2], f0[3]), pack_bf16x2(f1[0], f1[1]),
+               pack_bf16x2(f1[2], f1[3])};
 }
 
 // Global row fragment: row `row` (or zeros past `rows`), dims s*32 + lg*8 .. +8.
@@ -63,109 +89,102 @@ __device__ __forceinline__ u32x4 gfrag(const uint16_t* base, int64_t ld, int row
   return *reinterpret_cast<const u32x4*>(base + (int64_t)row * ld + s * 32 + lg * 8);
 }
 
-// Write a wave's 16 x 64 C-layout fragment set as bf16 into a row-major
-// (R8-swizzled) 16 x 64 LDS block.
-__device__ __forceinline__ void store_c16x64(uint16_t* lds, const f32x4 (&v)[4], int lr, int lg) {
-#pragma unroll
-  for (int nf = 0; nf < 4; ++nf)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = lg * 4 + i, col = nf * 16 + lr;
-      lds[off_r8(row, col >> 3) + (col & 7)] = f32_to_bf16(v[nf][i]);
-    }
-}
-
 __global__ __launch_bounds__(NTHR) void attn_fwd_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BLK * HD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[BLK * HD];
-  __shared__ __attribute__((aligned(16))) uint16_t Ps[4][16 * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BLK * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BLK * HD];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, lr = lane & 15, lg = lane >> 4;
-  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int kvh = h / (a.nq / a.nkv);
   const int seq = a.seq;
+  const int nqb = (seq + BLK - 1) / BLK;
+  const int qb = nqb - 1 - (int)blockIdx.x;  // the longest rows first
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int kvh = h / (a.nq / a.nkv);
   const int64_t rowbase = (int64_t)b * seq;
   const uint16_t* Qg = a.qkv + rowbase * a.ldqkv + (int64_t)h * HD;
   const uint16_t* Kg = a.qkv + rowbase * a.ldqkv + (int64_t)(a.nq + kvh) * HD;
   const uint16_t* Vg = a.qkv + rowbase * a.ldqkv + (int64_t)(a.nq + a.nkv + kvh) * HD;
   const int qw = qb * BLK + wid * 16;
+  const int q = qw + lr;  // this lane's query (its softmax column)
   const float c = LOG2E / sqrtf((float)HD);
 
   u32x4 qf[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) qf[s] = gfrag(Qg, a.ldqkv, qw + lr, seq, s, lg);
+  for (int s = 0; s < 4; ++s) qf[s] = gfrag(Qg, a.ldqkv, q, seq, s, lg);
 
-  f32x4 o[8];
+  f32x4 o[8];  // O^T: o[n][i] = O[q][16 n + 4 lg + i]
 #pragma unroll
   for (int n = 0; n < 8; ++n) o[n] = f32x4{0, 0, 0, 0};
-  float mrow[4], lrow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { mrow[i] = -INFINITY; lrow[i] = 0.0f; }
+  float mrow = -INFINITY, lrow = 0.0f;
 
-  const int nkb = min(qb + 1, (seq + BLK - 1) / BLK);
+  const int nkb = min(qb + 1, nqb);
+  TileRegs kr, vr;
+  tile_load(Kg, a.ldqkv, 0, seq, tid, kr);
+  tile_load(Vg, a.ldqkv, 0, seq, tid, vr);
+  tile_store(kr, Ks[0], tid);
+  tile_store(vr, Vs[0], tid);
+  __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
-    load_tile(Kg, a.ldqkv, 0, kb * BLK, seq, Ks, tid);
-    load_tile(Vg, a.ldqkv, 0, kb * BLK, seq, Vs, tid);
-    __syncthreads();
-    f32x4 S[4];
+    const int cur = kb & 1;
+    const bool pre = kb + 1 < nkb;
+    if (pre) {
+      tile_load(Kg, a.ldqkv, (kb + 1) * BLK, seq, tid, kr);
+      tile_load(Vg, a.ldqkv, (kb + 1) * BLK, seq, tid, vr);
+    }
+    f32x4 st[4];  // S^T: st[nf][i] = S[q][kb*64 + 16 nf + 4 lg + i]
 #pragma unroll
     for (int nf = 0; nf < 4; ++nf) {
-      S[nf] = f32x4{0, 0, 0, 0};
+      st[nf] = f32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) S[nf] = mfma16x16x32(qf[s], frag_row(Ks, nf * 16 + lr, s * 4 + lg), S[nf]);
+      for (int s = 0; s < 4; ++s) st[nf] = mfma16x16x32(frag_row(Ks[cur], nf * 16 + lr, s * 4 + lg), qf[s], st[nf]);
     }
-    float mloc[4];
+    float mloc = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = qw + lg * 4 + i;
-      mloc[i] = -INFINITY;
+    for (int nf = 0; nf < 4; ++nf)
 #pragma unroll
-      for (int nf = 0; nf < 4; ++nf) {
-        const int kv = kb * BLK + nf * 16 + lr;
-        const float v = (kv <= q && kv < seq) ? S[nf][i] * c : -INFINITY;
-        S[nf][i] = v;
-        mloc[i] = fmaxf(mloc[i], v);
+      for (int i = 0; i < 4; ++i) {
+        const int kv = kb * BLK + nf * 16 + lg * 4 + i;
+        const float v = (kv <= q && kv < seq) ? st[nf][i] * c : -INFINITY;
+        st[nf][i] = v;
+        mloc = fmaxf(mloc, v);
       }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float mn = fmaxf(mrow, mloc);
+    const float alpha = (mrow == -INFINITY) ? 0.0f : exp2f(mrow - mn);
+    float rs = 0.0f;
 #pragma unroll
-      for (int off = 1; off < 16; off <<= 1) mloc[i] = fmaxf(mloc[i], __shfl_xor(mloc[i], off, 64));
-    }
+    for (int nf = 0; nf < 4; ++nf)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float mn = fmaxf(mrow[i], mloc[i]);
-      const float alpha = (mrow[i] == -INFINITY) ? 0.0f : exp2f(mrow[i] - mn);
-      float rs = 0.0f;
-#pragma unroll
-      for (int nf = 0; nf < 4; ++nf) {
-        const float p = (S[nf][i] == -INFINITY) ? 0.0f : exp2f(S[nf][i] - mn);
-        S[nf][i] = p;
+      for (int i = 0; i < 4; ++i) {
+        const float p = (st[nf][i] == -INFINITY) ? 0.0f : exp2f(st[nf][i] - mn);
+        st[nf][i] = p;
         rs += p;
       }
+    rs += __shfl_xor(rs, 16, 64);
+    rs += __shfl_xor(rs, 32, 64);
+    lrow = lrow * alpha + rs;
+    mrow = mn;
 #pragma unroll
-      for (int off = 1; off < 16; off <<= 1) rs += __shfl_xor(rs, off, 64);
-      lrow[i] = lrow[i] * alpha + rs;
-      mrow[i] = mn;
+    for (int n = 0; n < 8; ++n) o[n] *= alpha;
+    const u32x4 pb0 = c_to_b(st[0], st[1]), pb1 = c_to_b(st[2], st[3]);
 #pragma unroll
-      for (int n = 0; n < 8; ++n) o[n][i] *= alpha;
+    for (int n = 0; n < 8; ++n) {
+      o[n] = mfma16x16x32(frag_tr(Vs[cur], n * 16, 0, lane), pb0, o[n]);
+      o[n] = mfma16x16x32(frag_tr(Vs[cur], n * 16, 32, lane), pb1, o[n]);
     }
-    store_c16x64(Ps[wid], S, lr, lg);
-    __syncthreads();
-    u32x4 pa[2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) pa[s2] = *reinterpret_cast<const u32x4*>(Ps[wid] + off_r8(lr, s2 * 4 + lg));
-#pragma unroll
-    for (int n = 0; n < 8; ++n)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) o[n] = mfma16x16x32(pa[s2], frag_gather(Vs, n * 16 + lr, s2 * 32 + lg * 8), o[n]);
+    if (pre) {
+      tile_store(kr, Ks[cur ^ 1], tid);
+      tile_store(vr, Vs[cur ^ 1], tid);
+    }
     __syncthreads();
   }
-  uint16_t* Og = a.o + rowbase * ((int64_t)a.nq * HD) + (int64_t)h * HD;
+  if (q < seq) {
+    uint16_t* Og = a.o + (rowbase + q) * ((int64_t)a.nq * HD) + (int64_t)h * HD;
+    const float inv = 1.0f / lrow;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = qw + lg * 4 + i;
-    if (q >= seq) continue;
-    const float inv = 1.0f / lrow[i];
-#pragma unroll
-    for (int n = 0; n < 8; ++n) Og[(int64_t)q * a.nq * HD + n * 16 + lr] = f32_to_bf16(o[n][i] * inv);
-    if (lr == 0) a.lse[((int64_t)b * a.nq + h) * seq + q] = (mrow[i] + log2f(lrow[i])) / LOG2E;
+    for (int n = 0; n < 8; ++n)
+      *reinterpret_cast<u32x2*>(Og + n * 16 + lg * 4) =
+          u32x2{pack_bf16x2(o[n][0] * inv, o[n][1] * inv), pack_bf16x2(o[n][2] * inv, o[n][3] * inv)};
+    if (lg == 0) a.lse[((int64_t)b * a.nq + h) * seq + q] = (mrow + log2f(lrow)) / LOG2E;
   }
 }
 
@@ -194,11 +213,9 @@ struct BwdScratch {
 };
 
 __global__ __launch_bounds__(NTHR) void attn_bwd_kv_kernel(AttnArgs a, BwdScratch sc) {
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[BLK * HD];
-  __shared__ __attribute__((aligned(16))) uint16_t dOs[BLK * HD];
-  __shared__ __attribute__((aligned(16))) uint16_t Pt[4][16 * 64];
-  __shared__ __attribute__((aligned(16))) uint16_t Dt[4][16 * 64];
-  __shared__ float lse_s[BLK], ds_s[BLK];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BLK * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t dOs[2][BLK * HD];
+  __shared__ float lse_s[2][BLK], ds_s[2][BLK];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, lr = lane & 15, lg = lane >> 4;
   const int kb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int kvh = h / (a.nq / a.nkv);
@@ -212,165 +229,173 @@ __global__ __launch_bounds__(NTHR) void attn_bwd_kv_kernel(AttnArgs a, BwdScratc
   const float* lse = a.lse + ((int64_t)b * a.nq + h) * seq;
   const float* Ds = a.Dsum + ((int64_t)b * a.nq + h) * seq;
   const int kw = kb * BLK + wid * 16;
+  const int kv = kw + lr;  // this lane's key (column of S, dP)
   const float c = LOG2E / sqrtf((float)HD);
 
   u32x4 kf[4], vf[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    kf[s] = gfrag(Kg, a.ldqkv, kw + lr, seq, s, lg);
-    vf[s] = gfrag(Vg, a.ldqkv, kw + lr, seq, s, lg);
+    kf[s] = gfrag(Kg, a.ldqkv, kv, seq, s, lg);
+    vf[s] = gfrag(Vg, a.ldqkv, kv, seq, s, lg);
   }
-  f32x4 dk[8], dv[8];
+  f32x4 dk[8], dv[8];  // dK^T, dV^T: dk[n][i] = dK[kv][16 n + 4 lg + i]
 #pragma unroll
   for (int n = 0; n < 8; ++n) { dk[n] = f32x4{0, 0, 0, 0}; dv[n] = f32x4{0, 0, 0, 0}; }
 
   const int nqb = (seq + BLK - 1) / BLK;
-  for (int qb = kb; qb < nqb; ++qb) {
-    load_tile(Qg, a.ldqkv, 0, qb * BLK, seq, Qs, tid);
-    load_tile(dOg, ldo, 0, qb * BLK, seq, dOs, tid);
+  TileRegs qr, orr;
+  auto stage_scalars = [&](int qb, int buf) {
     if (tid < BLK) {
-      const int q = qb * BLK + tid;
-      lse_s[tid] = (q < seq) ? lse[q] * LOG2E : 0.0f;
-      ds_s[tid] = (q < seq) ? Ds[q] : 0.0f;
+      const int qq = qb * BLK + tid;
+      lse_s[buf][tid] = (qq < seq) ? lse[qq] * LOG2E : 0.0f;
+      ds_s[buf][tid] = (qq < seq) ? Ds[qq] : 0.0f;
     }
-    __syncthreads();
-    f32x4 St[4], dPt[4];
+  };
+  tile_load(Qg, a.ldqkv, kb * BLK, seq, tid, qr);
+  tile_load(dOg, ldo, kb * BLK, seq, tid, orr);
+  tile_store(qr, Qs[0], tid);
+  tile_store(orr, dOs[0], tid);
+  stage_scalars(kb, 0);
+  __syncthreads();
+  for (int qb = kb; qb < nqb; ++qb) {
+    const int cur = (qb - kb) & 1;
+    const bool pre = qb + 1 < nqb;
+    if (pre) {
+      tile_load(Qg, a.ldqkv, (qb + 1) * BLK, seq, tid, qr);
+      tile_load(dOg, ldo, (qb + 1) * BLK, seq, tid, orr);
+    }
+    f32x4 st[4], dpt[4];  // S, dP: st[nf][i] = S[qb*64 + 16 nf + 4 lg + i][kv]
 #pragma unroll
     for (int nf = 0; nf < 4; ++nf) {
-      St[nf] = f32x4{0, 0, 0, 0};
-      dPt[nf] = f32x4{0, 0, 0, 0};
+      st[nf] = f32x4{0, 0, 0, 0};
+      dpt[nf] = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        St[nf] = mfma16x16x32(kf[s], frag_row(Qs, nf * 16 + lr, s * 4 + lg), St[nf]);
-        dPt[nf] = mfma16x16x32(vf[s], frag_row(dOs, nf * 16 + lr, s * 4 + lg), dPt[nf]);
+        st[nf] = mfma16x16x32(frag_row(Qs[cur], nf * 16 + lr, s * 4 + lg), kf[s], st[nf]);
+        dpt[nf] = mfma16x16x32(frag_row(dOs[cur], nf * 16 + lr, s * 4 + lg), vf[s], dpt[nf]);
       }
     }
 #pragma unroll
-    for (int nf = 0; nf < 4; ++nf) {
-      const int ql = nf * 16 + lr;
-      const int q = qb * BLK + ql;
+    for (int nf = 0; nf < 4; ++nf)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int kv = kw + lg * 4 + i;
-        const bool ok = kv <= q && q < seq && kv < seq;
-        const float p = ok ? exp2f(St[nf][i] * c - lse_s[ql]) : 0.0f;
-        St[nf][i] = p;
-        dPt[nf][i] = p * (dPt[nf][i] - ds_s[ql]);
+        const int ql = nf * 16 + lg * 4 + i;
+        const int qq = qb * BLK + ql;
+        const bool ok = kv <= qq && qq < seq && kv < seq;
+        const float p = ok ? exp2f(st[nf][i] * c - lse_s[cur][ql]) : 0.0f;
+        st[nf][i] = p;
+        dpt[nf][i] = p * (dpt[nf][i] - ds_s[cur][ql]);
       }
+    const u32x4 pb0 = c_to_b(st[0], st[1]), pb1 = c_to_b(st[2], st[3]);
+    const u32x4 db0 = c_to_b(dpt[0], dpt[1]), db1 = c_to_b(dpt[2], dpt[3]);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      dv[n] = mfma16x16x32(frag_tr(dOs[cur], n * 16, 0, lane), pb0, dv[n]);
+      dv[n] = mfma16x16x32(frag_tr(dOs[cur], n * 16, 32, lane), pb1, dv[n]);
+      dk[n] = mfma16x16x32(frag_tr(Qs[cur], n * 16, 0, lane), db0, dk[n]);
+      dk[n] = mfma16x16x32(frag_tr(Qs[cur], n * 16, 32, lane), db1, dk[n]);
     }
-    store_c16x64(Pt[wid], St, lr, lg);
-    store_c16x64(Dt[wid], dPt, lr, lg);
-    __syncthreads();
-    u32x4 pa[2], da[2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      pa[s2] = *reinterpret_cast<const u32x4*>(Pt[wid] + off_r8(lr, s2 * 4 + lg));
-      da[s2] = *reinterpret_cast<const u32x4*>(Dt[wid] + off_r8(lr, s2 * 4 + lg));
+    if (pre) {
+      tile_store(qr, Qs[cur ^ 1], tid);
+      tile_store(orr, dOs[cur ^ 1], tid);
+      stage_scalars(qb + 1, cur ^ 1);
     }
-#pragma unroll
-    for (int n = 0; n < 8; ++n)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        dv[n] = mfma16x16x32(pa[s2], frag_gather(dOs, n * 16 + lr, s2 * 32 + lg * 8), dv[n]);
-        dk[n] = mfma16x16x32(da[s2], frag_gather(Qs, n * 16 + lr, s2 * 32 + lg * 8), dk[n]);
-      }
     __syncthreads();
   }
-  const float scale = 1.0f / sqrtf((float)HD);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int kv = kw + lg * 4 + i;
-    if (kv >= seq) continue;
+  if (kv < seq) {
+    const float scale = 1.0f / sqrtf((float)HD);
     const int64_t base = ((rowbase + kv) * a.nq + h) * HD;
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
-      sc.dkp[base + n * 16 + lr] = dk[n][i] * scale;
-      sc.dvp[base + n * 16 + lr] = dv[n][i];
+      *reinterpret_cast<f32x4*>(sc.dkp + base + n * 16 + lg * 4) = dk[n] * scale;
+      *reinterpret_cast<f32x4*>(sc.dvp + base + n * 16 + lg * 4) = dv[n];
     }
   }
 }
 
 __global__ __launch_bounds__(NTHR) void attn_bwd_q_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BLK * HD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[BLK * HD];
-  __shared__ __attribute__((aligned(16))) uint16_t Dt[4][16 * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BLK * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BLK * HD];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, lr = lane & 15, lg = lane >> 4;
-  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int kvh = h / (a.nq / a.nkv);
   const int seq = a.seq;
+  const int nqb = (seq + BLK - 1) / BLK;
+  const int qb = nqb - 1 - (int)blockIdx.x;  // the longest rows first
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int kvh = h / (a.nq / a.nkv);
   const int64_t rowbase = (int64_t)b * seq;
   const int64_t ldo = (int64_t)a.nq * HD;
   const uint16_t* Qg = a.qkv + rowbase * a.ldqkv + (int64_t)h * HD;
   const uint16_t* Kg = a.qkv + rowbase * a.ldqkv + (int64_t)(a.nq + kvh) * HD;
   const uint16_t* Vg = a.qkv + rowbase * a.ldqkv + (int64_t)(a.nq + a.nkv + kvh) * HD;
   const uint16_t* dOg = a.dout + rowbase * ldo + (int64_t)h * HD;
-  const float* lse = a.lse + ((int64_t)b * a.nq + h) * seq;
-  const float* Ds = a.Dsum + ((int64_t)b * a.nq + h) * seq;
   const int qw = qb * BLK + wid * 16;
+  const int q = qw + lr;  // this lane's query (column of S^T, dP^T)
   const float c = LOG2E / sqrtf((float)HD);
 
   u32x4 qf[4], of[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    qf[s] = gfrag(Qg, a.ldqkv, qw + lr, seq, s, lg);
-    of[s] = gfrag(dOg, ldo, qw + lr, seq, s, lg);
+    qf[s] = gfrag(Qg, a.ldqkv, q, seq, s, lg);
+    of[s] = gfrag(dOg, ldo, q, seq, s, lg);
   }
-  float l2[4], dd[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = qw + lg * 4 + i;
-    l2[i] = (q < seq) ? lse[q] * LOG2E : 0.0f;
-    dd[i] = (q < seq) ? Ds[q] : 0.0f;
-  }
-  f32x4 dq[8];
+  const float l2 = (q < seq) ? a.lse[((int64_t)b * a.nq + h) * seq + q] * LOG2E : 0.0f;
+  const float dd = (q < seq) ? a.Dsum[((int64_t)b * a.nq + h) * seq + q] : 0.0f;
+  f32x4 dq[8];  // dQ^T: dq[n][i] = dQ[q][16 n + 4 lg + i]
 #pragma unroll
   for (int n = 0; n < 8; ++n) dq[n] = f32x4{0, 0, 0, 0};
-  const int nkb = min(qb + 1, (seq + BLK - 1) / BLK);
+  const int nkb = min(qb + 1, nqb);
+  TileRegs kr, vr;
+  tile_load(Kg, a.ldqkv, 0, seq, tid, kr);
+  tile_load(Vg, a.ldqkv, 0, seq, tid, vr);
+  tile_store(kr, Ks[0], tid);
+  tile_store(vr, Vs[0], tid);
+  __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
-    load_tile(Kg, a.ldqkv, 0, kb * BLK, seq, Ks, tid);
-    load_tile(Vg, a.ldqkv, 0, kb * BLK, seq, Vs, tid);
-    __syncthreads();
-    f32x4 S[4], dP[4];
+    const int cur = kb & 1;
+    const bool pre = kb + 1 < nkb;
+    if (pre) {
+      tile_load(Kg, a.ldqkv, (kb + 1) * BLK, seq, tid, kr);
+      tile_load(Vg, a.ldqkv, (kb + 1) * BLK, seq, tid, vr);
+    }
+    f32x4 st[4], dpt[4];  // S^T, dP^T: st[nf][i] = S[q][kb*64 + 16 nf + 4 lg + i]
 #pragma unroll
     for (int nf = 0; nf < 4; ++nf) {
-      S[nf] = f32x4{0, 0, 0, 0};
-      dP[nf] = f32x4{0, 0, 0, 0};
+      st[nf] = f32x4{0, 0, 0, 0};
+      dpt[nf] = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        S[nf] = mfma16x16x32(qf[s], frag_row(Ks, nf * 16 + lr, s * 4 + lg), S[nf]);
-        dP[nf] = mfma16x16x32(of[s], frag_row(Vs, nf * 16 + lr, s * 4 + lg), dP[nf]);
+        st[nf] = mfma16x16x32(frag_row(Ks[cur], nf * 16 + lr, s * 4 + lg), qf[s], st[nf]);
+        dpt[nf] = mfma16x16x32(frag_row(Vs[cur], nf * 16 + lr, s * 4 + lg), of[s], dpt[nf]);
       }
     }
 #pragma unroll
-    for (int nf = 0; nf < 4; ++nf) {
-      const int kv = kb * BLK + nf * 16 + lr;
+    for (int nf = 0; nf < 4; ++nf)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int q = qw + lg * 4 + i;
+        const int kv = kb * BLK + nf * 16 + lg * 4 + i;
         const bool ok = kv <= q && q < seq && kv < seq;
-        const float p = ok ? exp2f(S[nf][i] * c - l2[i]) : 0.0f;
-        dP[nf][i] = p * (dP[nf][i] - dd[i]);
+        const float p = ok ? exp2f(st[nf][i] * c - l2) : 0.0f;
+        dpt[nf][i] = p * (dpt[nf][i] - dd);
       }
+    const u32x4 db0 = c_to_b(dpt[0], dpt[1]), db1 = c_to_b(dpt[2], dpt[3]);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      dq[n] = mfma16x16x32(frag_tr(Ks[cur], n * 16, 0, lane), db0, dq[n]);
+      dq[n] = mfma16x16x32(frag_tr(Ks[cur], n * 16, 32, lane), db1, dq[n]);
     }
-    store_c16x64(Dt[wid], dP, lr, lg);
-    __syncthreads();
-    u32x4 da[2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) da[s2] = *reinterpret_cast<const u32x4*>(Dt[wid] + off_r8(lr, s2 * 4 + lg));
-#pragma unroll
-    for (int n = 0; n < 8; ++n)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) dq[n] = mfma16x16x32(da[s2], frag_gather(Ks, n * 16 + lr, s2 * 32 + lg * 8), dq[n]);
+    if (pre) {
+      tile_store(kr, Ks[cur ^ 1], tid);
+      tile_store(vr, Vs[cur ^ 1], tid);
+    }
     __syncthreads();
   }
-  const float scale = 1.0f / sqrtf((float)HD);
-  uint16_t* dQg = a.dqkv + rowbase * a.ldqkv + (int64_t)h * HD;
+  if (q < seq) {
+    const float scale = 1.0f / sqrtf((float)HD);
+    uint16_t* dQg = a.dqkv + (rowbase + q) * a.ldqkv + (int64_t)h * HD;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = qw + lg * 4 + i;
-    if (q >= seq) continue;
-#pragma unroll
-    for (int n = 0; n < 8; ++n) dQg[(int64_t)q * a.ldqkv + n * 16 + lr] = f32_to_bf16(dq[n][i] * scale);
+    for (int n = 0; n < 8; ++n)
+      *reinterpret_cast<u32x2*>(dQg + n * 16 + lg * 4) = u32x2{pack_bf16x2(dq[n][0] * scale, dq[n][1] * scale),
+                                                              pack_bf16x2(dq[n][2] * scale, dq[n][3] * scale)};
   }
 }
 
@@ -403,12 +428,11 @@ hipError_t attention_fwd(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Scratch: the caller passes it through a.Dsum's neighbour: dK/dV partials
-// live right after Dsum (see attention_bwd_scratch_floats).
+// Scratch: the dK / dV partials live right after Dsum, at a 64-float boundary.
 hipError_t attention_bwd(const AttnArgs& a, hipStream_t s) {
   const int64_t T = (int64_t)a.batch * a.seq;
   BwdScratch sc;
-  sc.dkp = a.Dsum + (int64_t)a.batch * a.nq * a.seq;
+  sc.dkp = a.Dsum + attention_dsum_floats(a.batch, a.nq, a.seq);
   sc.dvp = sc.dkp + T * a.nq * HD;
   {
     const int64_t waves = T * a.nq;

@@ -158,11 +158,15 @@ struct AttnArgs {
   float* lse = nullptr;
   // backward
   const uint16_t* dout = nullptr;
-  float* Dsum = nullptr;   // [batch, nq, seq]
+  float* Dsum = nullptr;   // [batch, nq, seq], then the dK / dV partials (see below)
   uint16_t* dqkv = nullptr;  // same layout as qkv
 };
 hipError_t attention_fwd(const AttnArgs& a, hipStream_t s);
+// a.Dsum points at attention_dsum_floats(batch, nq, seq) + 2 * batch*seq * nq * 128
+// floats of device scratch (16-byte aligned): Dsum, then the per-query-head dK
+// and dV partials.
 hipError_t attention_bwd(const AttnArgs& a, hipStream_t s);
+inline int64_t attention_dsum_floats(int64_t batch, int64_t nq, int64_t seq) { return (batch * nq * seq + 63) / 64 * 64; }
 
 hipError_t zero_f32(float* p, int64_t n, hipStream_t s);
 

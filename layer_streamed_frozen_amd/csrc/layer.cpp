@@ -43,7 +43,7 @@ size_t LayerWs::bytes(const lsf_layer_cfg& c) {
   b += up(z.T * 3 * z.r * 4) + up(z.T * z.r * 4) * 2 + up(z.T * 2 * z.r * 4);  // U's
   b += up(z.T * 3 * z.r * 4);                 // dU
   b += up(z.seq * (c.head_dim / 2) * 8);      // rope table
-  b += up((z.batch * z.nq * z.seq + 2 * z.T * z.nq * 128) * 4);  // attention backward scratch
+  b += up((attention_dsum_floats(z.batch, z.nq, z.seq) + 2 * z.T * z.nq * 128) * 4);  // attention bwd scratch
   b += up((size_t)8 * z.T * z.maxN() * 4);    // split-K partials
   return b + AL;
 }
@@ -81,7 +81,7 @@ LayerWs LayerWs::carve(const lsf_layer_cfg& c, void* base) {
   w.Ugu = (float*)take(z.T * 2 * z.r * 4);
   w.dU = (float*)take(z.T * 3 * z.r * 4);
   w.rope = (float2*)take(z.seq * (c.head_dim / 2) * 8);
-  w.attn_scratch = (float*)take((z.batch * z.nq * z.seq + 2 * z.T * z.nq * 128) * 4);
+  w.attn_scratch = (float*)take((attention_dsum_floats(z.batch, z.nq, z.seq) + 2 * z.T * z.nq * 128) * 4);
   w.part_floats = (size_t)8 * z.T * z.maxN();
   w.part = (float*)take(w.part_floats * 4);
   return w;
