@@ -237,7 +237,11 @@ typedef struct lsf_stack lsf_stack;
 
 #define LSF_STACK_ALLOW_PAGEABLE 0x1u /* accept a pageable host store (slow fallback, [TUTORIAL] item 2) */
 #define LSF_STACK_NO_TURN_REUSE 0x2u  /* copy every layer twice per micro-batch */
-#define LSF_STACK_TIMING 0x4u         /* record copy-busy and compute-wait events for stack_stats */
+#define LSF_STACK_TIMING 0x4u         /* record copy, compute-wait and kernel events for stack_stats */
+#define LSF_STACK_KERNEL_TIMING 0x8u  /* record only the kernel events (leaves the copy stream untouched) */
+/* Record only kernel class k (an LSF_K_* value; several may be or-ed), for a
+ * measurement that must disturb the step as little as possible. */
+#define LSF_STACK_TIME_KERNEL(k) (0x100u << (k))
 
 typedef struct {
   int32_t n_layers;
@@ -339,7 +343,8 @@ LSF_API lsf_status adamw_step(float* param, const float* grad, float* m, float* 
                               const lsf_adamw_cfg* cfg, float* grad_norm, void* ws, size_t ws_bytes,
                               lsf_stream stream);
 
-/* Kernel classes timed with HIP events under LSF_STACK_TIMING (index into
+/* Kernel classes timed with HIP events under LSF_STACK_TIMING or
+ * LSF_STACK_KERNEL_TIMING (index into
  * lsf_stack_stats.kernel_ms / kernel_launches).  A GEMM's time includes its
  * split-K reduction when it has one. */
 enum {
@@ -355,8 +360,8 @@ typedef struct {
   int64_t bytes;       /* bytes those copies moved */
   double copy_ms;      /* summed copy durations (LSF_STACK_TIMING only) */
   double wait_ms;      /* summed compute-stream stalls on copies (LSF_STACK_TIMING only) */
-  double kernel_ms[16];        /* summed durations per LSF_K_* class (LSF_STACK_TIMING only) */
-  int64_t kernel_launches[16]; /* launches per class (LSF_STACK_TIMING only) */
+  double kernel_ms[16];        /* summed durations per LSF_K_* class (either timing flag) */
+  int64_t kernel_launches[16]; /* launches per class (either timing flag) */
 } lsf_stack_stats;
 /* Counters and event timings since the last reset (or create).  Waits for the
  * recorded events, so it synchronises with the work they bracket. */

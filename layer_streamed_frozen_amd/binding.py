@@ -23,7 +23,12 @@ STATUS_NAMES = ["LSF_OK", "LSF_ERR_INVALID_ARG", "LSF_ERR_SHAPE", "LSF_ERR_ALIGN
 
 FMT_NF4, FMT_BF16, FMT_NF4_DQ = 0, 1, 2
 
-STACK_ALLOW_PAGEABLE, STACK_NO_TURN_REUSE, STACK_TIMING = 0x1, 0x2, 0x4
+STACK_ALLOW_PAGEABLE, STACK_NO_TURN_REUSE, STACK_TIMING, STACK_KERNEL_TIMING = 0x1, 0x2, 0x4, 0x8
+
+
+def STACK_TIME_KERNEL(k):
+    """Flag that times only kernel class k (an index into KERNELS)."""
+    return 0x100 << k
 MODE_STREAMED, MODE_RESIDENT, MODE_FWD_ONLY, MODE_ZERO_GRADS = 0x0, 0x1, 0x2, 0x4
 
 c_void_p, c_int32, c_int64, c_uint32, c_uint64, c_float, c_size_t = (

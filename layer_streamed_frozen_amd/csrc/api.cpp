@@ -378,8 +378,10 @@ struct EventPool {
       free.pop_back();
       return e;
     }
+    // Timing-only events: no system-scope fence (no cache writeback and
+    // invalidate on record), so measuring does not slow the work measured.
     hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     all.push_back(e);
     return e;
   }
@@ -416,14 +418,17 @@ hipError_t harvest(EventPool& pool, EvPairs& v, double& ms_sum, int64_t* count, 
 // Brackets the big kernels of every layer call with events (LSF_STACK_TIMING).
 struct KernelProbe : Probe {
   EventPool* pool = nullptr;
+  uint32_t mask = 0;  // bit k: kernel class k is timed
   hipEvent_t open[LSF_K_COUNT] = {};
   EvPairs ev[LSF_K_COUNT];
   hipError_t begin(int kind, hipStream_t s) override {
+    if (!((mask >> kind) & 1u)) return hipSuccess;
     open[kind] = pool->get();
     if (open[kind] == nullptr) return hipErrorOutOfMemory;
     return hipEventRecord(open[kind], s);
   }
   hipError_t end(int kind, hipStream_t s) override {
+    if (!((mask >> kind) & 1u)) return hipSuccess;
     hipEvent_t e = pool->get();
     if (e == nullptr) return hipErrorOutOfMemory;
     hipError_t r = hipEventRecord(e, s);
@@ -653,8 +658,13 @@ lsf_status run_step(lsf_stack* st, const lsf_stack_io* io, const lsf_dpo_io* dpo
 
   hipStream_t cs = S(st->d.compute);
   StackWs w = carve_stack(c, V, io->ws);
-  const bool timing = st->d.flags & LSF_STACK_TIMING;
+  const uint32_t all_classes = (1u << LSF_K_COUNT) - 1u;
+  const uint32_t class_mask = (st->d.flags & (LSF_STACK_TIMING | LSF_STACK_KERNEL_TIMING))
+                                  ? all_classes
+                                  : (st->d.flags / LSF_STACK_TIME_KERNEL(0)) & all_classes;
+  const bool timing = class_mask != 0;
   if (timing) {
+    st->probe.mask = class_mask;
     st->probe.pool = &st->events;
     w.layer.probe = &st->probe;
     HIPCK(harvest_all(st, false));  // recycle the events of work that has finished
@@ -752,6 +762,11 @@ lsf_status stack_create(const lsf_layer_cfg* cfg, const lsf_stack_desc* desc, ls
   if (desc == nullptr || out == nullptr) return fail(LSF_ERR_INVALID_ARG, "desc or out is NULL");
   *out = nullptr;
   if (desc->n_layers < 1) return fail(LSF_ERR_INVALID_ARG, "n_layers must be >= 1");
+  {
+    const uint32_t known = LSF_STACK_ALLOW_PAGEABLE | LSF_STACK_NO_TURN_REUSE | LSF_STACK_TIMING |
+                           LSF_STACK_KERNEL_TIMING | LSF_STACK_TIME_KERNEL(0) * ((1u << LSF_K_COUNT) - 1u);
+    if (desc->flags & ~known) return fail(LSF_ERR_INVALID_ARG, "unknown stack flags 0x%x", desc->flags & ~known);
+  }
   if (desc->format != LSF_FMT_NF4 && desc->format != LSF_FMT_BF16 && desc->format != LSF_FMT_NF4_DQ)
     return fail(LSF_ERR_INVALID_ARG, "unknown weight format %d", desc->format);
   const Blob b = blob_layout(*cfg, desc->format);

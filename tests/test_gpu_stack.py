@@ -256,3 +256,17 @@ def test_other_base_formats_stream_bit_equal_and_match_oracle(fmt):
         for n in ("q", "o", "gate", "down"):
             assert report(f"L{i}.dA_{n}", g[n][0], ref["grads"][i][n][0]) < TOL
             assert report(f"L{i}.dB_{n}", g[n][1], ref["grads"][i][n][1]) < TOL
+
+
+def test_single_kernel_class_timing_and_unknown_flags():
+    k = B.KERNELS.index("gate_up_fwd")
+    s = Setup(SMALL, 2, 512, 1, 48, "tk", flags=B.STACK_TIME_KERNEL(k))
+    B.stack_reset_stats(s.stack.handle)
+    s.step(mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+    st = s.stack.stats()
+    assert st.kernel_launches[k] == 2 * s.L      # forward + recompute
+    assert all(st.kernel_launches[i] == 0 for i in range(len(B.KERNELS)) if i != k)
+    assert st.copy_ms == 0.0 and st.wait_ms == 0.0
+    with pytest.raises(B.LsfError) as e:
+        S.Stack(SMALL, s.store, 1, 48, 512, flags=1 << 30)
+    assert e.value.status == B.LSF_ERR_INVALID_ARG
