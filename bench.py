@@ -75,6 +75,9 @@ def parse():
     p.add_argument("--timing", choices=["dominant", "all"], default="dominant",
                    help="events in the timed steps: around the gate|up forward GEMM only, or around every "
                         "kernel class and copy")
+    p.add_argument("--keep-activations", action="store_true",
+                   help="keep every layer's forward intermediates in HBM and skip the recompute in the backward "
+                        "walk (each layer is still read twice)")
     p.add_argument("--diag-steps", type=int, default=5,
                    help="steps of the diagnostic pass that times every kernel class and copy (0: none)")
     return p.parse_args()
@@ -222,7 +225,7 @@ def main():
         flags = B.STACK_TIMING
     else:
         flags = B.STACK_TIME_KERNEL(dom_k)
-    stack = S.Stack(shape, store, batch, seq, V, flags=flags)
+    stack = S.Stack(shape, store, batch, seq, V, flags=flags, keep_activations=args.keep_activations)
     arr = lora.array()
     opt = S.AdamW(lora, lr=2e-4)
     torch.cuda.synchronize()
@@ -286,7 +289,7 @@ def main():
         stack.close()
         del stack
         log(f"diagnostic pass: {diag_steps} steps with every kernel and copy timed")
-        diag = S.Stack(shape, store, batch, seq, V, flags=B.STACK_TIMING)
+        diag = S.Stack(shape, store, batch, seq, V, flags=B.STACK_TIMING, keep_activations=args.keep_activations)
         step(diag)
         torch.cuda.synchronize()
         B.stack_reset_stats(diag.handle)
@@ -344,6 +347,8 @@ def main():
                                    f"batch {batch} x seq {seq}, accumulation {accum}")),
                    "global_batch": batch * accum, "seq_len": seq, "layers": L, "vocab": V,
                    "optimizer": "AdamW lr 2e-4, fp32 moments, once per step",
+                   "backward": ("forward intermediates kept in HBM, no recompute" if args.keep_activations
+                                else "per-layer recompute from the checkpoint"),
                    "parallelism": "single GPU"},
         "h2d": h2d, "roofline": roof, "layer_gemms": layer_gemms, "kernels": kernels,
         "peak_device_GB": round(peak_gb, 3),

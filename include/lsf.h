@@ -262,6 +262,11 @@ LSF_API lsf_status stack_destroy(lsf_stack* st);
 #define LSF_MODE_RESIDENT 0x1u   /* weights read in place from resident_store */
 #define LSF_MODE_FWD_ONLY 0x2u   /* stop after the loss (no backward) */
 #define LSF_MODE_ZERO_GRADS 0x4u /* zero every dA/dB before accumulating */
+/* Keep every layer's forward intermediates in io->act and skip the recompute
+ * in the backward walk.  Each layer is still read twice (the input gradient
+ * needs the frozen weight); the recompute is traded for
+ * stack_activation_bytes() of device memory.  Same bits as the default. */
+#define LSF_MODE_KEEP_ACTIVATIONS 0x8u
 
 typedef struct {
   const int32_t* ids;          /* device [batch, seq] token ids in [0, vocab) */
@@ -277,9 +282,13 @@ typedef struct {
   size_t ws_bytes;             /* >= stack_workspace_bytes(cfg, vocab) */
   float loss_scale;            /* multiplies dL/dlogits (e.g. 1/accumulation) */
   uint32_t mode;               /* LSF_MODE_* */
+  void* act;                   /* LSF_MODE_KEEP_ACTIVATIONS: device, 256-B aligned; else ignored */
+  size_t act_bytes;            /* >= stack_activation_bytes(cfg, n_layers) */
 } lsf_stack_io;
 
 LSF_API size_t stack_workspace_bytes(const lsf_layer_cfg* cfg, int32_t vocab);
+/* Device bytes LSF_MODE_KEEP_ACTIVATIONS needs for n_layers layers. */
+LSF_API size_t stack_activation_bytes(const lsf_layer_cfg* cfg, int32_t n_layers);
 /* One SFT micro-batch: embedding gather, streamed forward, final RMSNorm,
  * lm_head, cross-entropy over next-token labels, lm_head input gradient,
  * streamed recompute + backward, LoRA gradients accumulated. */

@@ -29,7 +29,7 @@ STACK_ALLOW_PAGEABLE, STACK_NO_TURN_REUSE, STACK_TIMING, STACK_KERNEL_TIMING = 0
 def STACK_TIME_KERNEL(k):
     """Flag that times only kernel class k (an index into KERNELS)."""
     return 0x100 << k
-MODE_STREAMED, MODE_RESIDENT, MODE_FWD_ONLY, MODE_ZERO_GRADS = 0x0, 0x1, 0x2, 0x4
+MODE_STREAMED, MODE_RESIDENT, MODE_FWD_ONLY, MODE_ZERO_GRADS, MODE_KEEP_ACTIVATIONS = 0x0, 0x1, 0x2, 0x4, 0x8
 
 c_void_p, c_int32, c_int64, c_uint32, c_uint64, c_float, c_size_t = (
     ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_float,
@@ -81,7 +81,7 @@ class StackIO(ctypes.Structure):
     _fields_ = [("ids", c_void_p), ("embed", c_void_p), ("final_norm", c_void_p), ("lm_head", c_void_p),
                 ("vocab", c_int32), ("lora", ctypes.POINTER(LayerLora)), ("ckpt", c_void_p), ("logits", c_void_p),
                 ("loss", c_void_p), ("ws", c_void_p), ("ws_bytes", c_size_t), ("loss_scale", c_float),
-                ("mode", c_uint32)]
+                ("mode", c_uint32), ("act", c_void_p), ("act_bytes", c_size_t)]
 
 
 class DpoIO(ctypes.Structure):
@@ -131,6 +131,7 @@ _PROTOS = {
     "dpo_stack_step": (c_int32, [c_void_p, ctypes.POINTER(DpoIO)]),
     "stack_stats": (c_int32, [c_void_p, ctypes.POINTER(StackStats)]),
     "stack_reset_stats": (c_int32, [c_void_p]),
+    "stack_activation_bytes": (c_size_t, [c_void_p, c_int32]),
     "adamw_workspace_bytes": (c_size_t, []),
     "adamw_step": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, ctypes.POINTER(AdamwCfg), c_void_p,
                              c_void_p, c_size_t, c_void_p]),
@@ -304,3 +305,7 @@ def adamw_step(param, grad, m, v, cfg, grad_norm, ws, n=None, stream=None):
     check(lib().adamw_step(ptr(param), ptr(grad), ptr(m), ptr(v), n, ctypes.byref(cfg),
                            ptr(grad_norm) if grad_norm is not None else None, ptr(ws),
                            ws.numel() * ws.element_size(), stream_ptr(stream)))
+
+
+def stack_activation_bytes(cfg, n_layers):
+    return lib().stack_activation_bytes(ctypes.byref(cfg), n_layers)

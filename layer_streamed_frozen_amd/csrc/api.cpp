@@ -648,6 +648,13 @@ lsf_status run_step(lsf_stack* st, const lsf_stack_io* io, const lsf_dpo_io* dpo
   if (!resident && st->d.host_store == nullptr) return fail(LSF_ERR_INVALID_ARG, "STREAMED mode needs a host store");
   if (io->ws == nullptr || io->ws_bytes < stack_ws_bytes(c, V))
     return fail(LSF_ERR_WORKSPACE, "workspace too small (need %zu bytes)", stack_ws_bytes(c, V));
+  const bool keep = io->mode & LSF_MODE_KEEP_ACTIVATIONS;
+  const size_t saved = LayerWs::saved_bytes(c);
+  if (keep) {
+    if (io->act == nullptr || io->act_bytes < saved * L)
+      return fail(LSF_ERR_WORKSPACE, "activation arena too small (need %zu bytes)", saved * L);
+    if (!aligned(io->act, 256)) return fail(LSF_ERR_ALIGN, "activation arena must be 256-byte aligned");
+  }
   if (dpo != nullptr) {
     if (c.batch < 2 || c.batch % 2)
       return fail(LSF_ERR_SHAPE, "DPO needs an even batch (chosen, then rejected sequences); got %d", c.batch);
@@ -689,10 +696,12 @@ lsf_status run_step(lsf_stack* st, const lsf_stack_io* io, const lsf_dpo_io* dpo
   HIPCK(rope_table(c.seq, c.head_dim, c.rope_theta, w.layer.rope, cs));
   HIPCK(embed_gather(io->ids, io->embed, T, H, V, io->ckpt, cs));
 
+  // Layer i's saved intermediates (LSF_MODE_KEEP_ACTIVATIONS).
+  auto kept = [&](int i) { return w.layer.with_saved(c, static_cast<char*>(io->act) + (size_t)i * saved); };
   // Policy forward of layer i: ckpt[i] -> ckpt[i+1] (kept for the backward).
   auto policy_fwd = [&](int i, const lsf_layer_weights& lw) {
-    return layer_forward(c, lw, &io->lora[i], io->ckpt + (size_t)i * act, io->ckpt + (size_t)(i + 1) * act, w.layer,
-                         false, true, cs);
+    return layer_forward(c, lw, &io->lora[i], io->ckpt + (size_t)i * act, io->ckpt + (size_t)(i + 1) * act,
+                         keep ? kept(i) : w.layer, keep, true, cs);
   };
   // Reference (adapters off) forward of layer i, through the rx ping-pong:
   // input rx[i % 2] (the embeddings for layer 0), output rx[(i + 1) % 2].
@@ -745,8 +754,8 @@ lsf_status run_step(lsf_stack* st, const lsf_stack_io* io, const lsf_dpo_io* dpo
 
   // ---- backward: layers L-1 .. 0, each read again and recomputed
   auto policy_bwd = [&](int j, const lsf_layer_weights& lw) {
-    return layer_backward(c, lw, &io->lora[j], io->ckpt + (size_t)j * act, w.dx[(j + 1) & 1], w.dx[j & 1], w.layer,
-                          true, cs);
+    return layer_backward(c, lw, &io->lora[j], io->ckpt + (size_t)j * act, w.dx[(j + 1) & 1], w.dx[j & 1],
+                          keep ? kept(j) : w.layer, true, cs, !keep);
   };
   if ((s = walk_layers(st, resident, false, reuse, policy_bwd))) return s;
   return ok();
@@ -818,6 +827,11 @@ lsf_status stack_destroy(lsf_stack* st) {
   for (hipEvent_t e : st->events.all) (void)hipEventDestroy(e);
   delete st;
   return ok();
+}
+
+size_t stack_activation_bytes(const lsf_layer_cfg* cfg, int32_t n_layers) {
+  if (check_cfg(cfg) != LSF_OK || n_layers <= 0) return 0;
+  return LayerWs::saved_bytes(*cfg) * (size_t)n_layers;
 }
 
 size_t stack_workspace_bytes(const lsf_layer_cfg* cfg, int32_t vocab) {

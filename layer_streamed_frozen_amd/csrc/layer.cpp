@@ -87,6 +87,43 @@ LayerWs LayerWs::carve(const lsf_layer_cfg& c, void* base) {
   return w;
 }
 
+size_t LayerWs::saved_bytes(const lsf_layer_cfg& c) {
+  Sizes z(c);
+  size_t b = up(z.T * z.H * 2) * 3;                 // h1, x2, h2
+  b += up(z.T * z.Nqkv * 2) + up(z.T * z.Dq * 2);    // qkv (rotated), att
+  b += up(z.T * z.I * 2) * 3;                        // g, u, a
+  b += up(z.batch * z.nq * z.seq * 4) + up(z.T * 4) * 2;  // lse, rstd1, rstd2
+  b += up(z.T * 3 * z.r * 4) + up(z.T * z.r * 4) * 2 + up(z.T * 2 * z.r * 4);  // U's
+  return b;
+}
+
+LayerWs LayerWs::with_saved(const lsf_layer_cfg& c, void* base) const {
+  Sizes z(c);
+  uintptr_t p = (uintptr_t)base;
+  auto take = [&](size_t n) {
+    void* r = (void*)p;
+    p += up(n);
+    return r;
+  };
+  LayerWs w = *this;
+  w.h1 = (uint16_t*)take(z.T * z.H * 2);
+  w.x2 = (uint16_t*)take(z.T * z.H * 2);
+  w.h2 = (uint16_t*)take(z.T * z.H * 2);
+  w.qkv = (uint16_t*)take(z.T * z.Nqkv * 2);
+  w.att = (uint16_t*)take(z.T * z.Dq * 2);
+  w.g = (uint16_t*)take(z.T * z.I * 2);
+  w.u = (uint16_t*)take(z.T * z.I * 2);
+  w.a = (uint16_t*)take(z.T * z.I * 2);
+  w.lse = (float*)take(z.batch * z.nq * z.seq * 4);
+  w.rstd1 = (float*)take(z.T * 4);
+  w.rstd2 = (float*)take(z.T * 4);
+  w.Uqkv = (float*)take(z.T * 3 * z.r * 4);
+  w.Uo = (float*)take(z.T * z.r * 4);
+  w.Ud = (float*)take(z.T * z.r * 4);
+  w.Ugu = (float*)take(z.T * 2 * z.r * 4);
+  return w;
+}
+
 WeightRef weight_ref(const lsf_weight& w, int fmt, int64_t ld) {
   WeightRef r;
   r.fmt = fmt;
@@ -293,13 +330,14 @@ hipError_t lora_grads(int T, int r, float sc, int nsec, const lsf_lora_proj* con
 
 hipError_t layer_backward(const lsf_layer_cfg& c, const lsf_layer_weights& w, const lsf_layer_lora* lora,
                           const uint16_t* x, const uint16_t* dy, uint16_t* dx, const LayerWs& ws, bool rope_ready,
-                          hipStream_t s) {
+                          hipStream_t s, bool recompute) {
   Sizes z(c);
   const int T = (int)z.T, H = (int)z.H, I = (int)z.I, r = (int)z.r;
   const int fmt = w.format;
   const float sc = c.lora_scale;
   // Recompute the forward from the checkpoint, keeping what the backward reads.
-  CK(layer_forward(c, w, lora, x, nullptr, ws, true, rope_ready, s));
+  if (recompute) CK(layer_forward(c, w, lora, x, nullptr, ws, true, rope_ready, s));
+  else if (!rope_ready) CK(rope_table(c.seq, c.head_dim, c.rope_theta, ws.rope, s));
 
   // down projection: dA = dY W_down (+ LoRA), then SwiGLU backward in the epilogue
   {

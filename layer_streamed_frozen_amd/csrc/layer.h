@@ -25,6 +25,11 @@ struct LayerWs {
   Probe* probe = nullptr;
   static size_t bytes(const lsf_layer_cfg& c);
   static LayerWs carve(const lsf_layer_cfg& c, void* base);
+  // The tensors a forward with save = true leaves for the backward (h1, qkv,
+  // att, lse, x2, h2, g, u, a, rstd1, rstd2 and the LoRA activations), laid
+  // out from `base`: this workspace with those pointers moved there.
+  static size_t saved_bytes(const lsf_layer_cfg& c);
+  LayerWs with_saved(const lsf_layer_cfg& c, void* base) const;
 };
 
 WeightRef weight_ref(const lsf_weight& w, int fmt, int64_t ld);
@@ -35,9 +40,11 @@ WeightRef weight_ref(const lsf_weight& w, int fmt, int64_t ld);
 hipError_t layer_forward(const lsf_layer_cfg& c, const lsf_layer_weights& w, const lsf_layer_lora* lora,
                          const uint16_t* x, uint16_t* y, const LayerWs& ws, bool save, bool rope_ready,
                          hipStream_t s);
+// recompute = false: ws already holds what layer_forward(save = true) of the
+// same x left (LayerWs::with_saved), and the forward is not run again.
 hipError_t layer_backward(const lsf_layer_cfg& c, const lsf_layer_weights& w, const lsf_layer_lora* lora,
                           const uint16_t* x, const uint16_t* dy, uint16_t* dx, const LayerWs& ws, bool rope_ready,
-                          hipStream_t s);
+                          hipStream_t s, bool recompute = true);
 
 // Split count for a GEMM with `tiles` output tiles and contraction K.
 int choose_splits(int tiles, int K);

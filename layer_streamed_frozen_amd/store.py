@@ -231,7 +231,7 @@ class AdamW:
 class Stack:
     """A streamed stack: store + two device buffers + streams + handle."""
 
-    def __init__(self, shape, store, batch, seq, vocab, flags=0, device="cuda"):
+    def __init__(self, shape, store, batch, seq, vocab, flags=0, device="cuda", keep_activations=False):
         self.shape, self.store, self.batch, self.seq, self.vocab = shape, store, batch, seq, vocab
         self.cfg = shape.cfg(batch, seq)
         nbytes = store.layout.bytes
@@ -257,6 +257,11 @@ class Stack:
         self.logits = torch.empty((T, vocab), dtype=torch.float32, device=device)
         self.loss = torch.zeros(1, dtype=torch.float32, device=device)
         self.seq_logp = torch.zeros((2, batch), dtype=torch.float32, device=device)  # DPO: policy, reference
+        # every layer's forward intermediates, when the backward skips the recompute
+        self.act = None
+        if keep_activations:
+            self.act = torch.empty(B.stack_activation_bytes(self.cfg, store.n_layers), dtype=torch.uint8,
+                                   device=device)
 
     def _io(self, ids, embed, final_norm, lm_head, lora_arr, mode, loss_scale):
         io = B.StackIO()
@@ -273,6 +278,10 @@ class Stack:
         io.ws_bytes = self.ws.numel()
         io.loss_scale = loss_scale
         io.mode = mode
+        if self.act is not None:
+            io.mode |= B.MODE_KEEP_ACTIVATIONS
+            io.act = self.act.data_ptr()
+            io.act_bytes = self.act.numel()
         return io
 
     def step(self, ids, embed, final_norm, lm_head, lora_arr, mode=B.MODE_STREAMED, loss_scale=1.0):

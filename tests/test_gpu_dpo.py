@@ -157,3 +157,18 @@ def test_dpo_bad_arguments():
         odd.dpo_step(ids, s.emb, s.fnorm, s.head, s.lora.array())
     assert e.value.status == B.LSF_ERR_SHAPE
     odd.close()
+
+
+def test_dpo_with_kept_activations_gives_the_same_bits(pair):
+    pair.dpo()
+    a = pair.snapshot()
+    kept = S.Stack(SMALL, pair.store, 4, 96, 1024, keep_activations=True)
+    for fused in (True, False):
+        kept.dpo_step(pair.ids, pair.emb, pair.fnorm, pair.head, pair.lora.array(), beta=BETA, fused=fused,
+                      mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+        torch.cuda.synchronize()
+        got = (kept.logits.clone(), kept.loss.clone(),
+               [{n: (pair.lora.dA[i][n].clone(), pair.lora.dB[i][n].clone()) for n in pair.lora.targets}
+                for i in range(pair.L)], kept.seq_logp.clone())
+        assert same(a, got)
+    kept.close()

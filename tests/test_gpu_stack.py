@@ -270,3 +270,29 @@ def test_single_kernel_class_timing_and_unknown_flags():
     with pytest.raises(B.LsfError) as e:
         S.Stack(SMALL, s.store, 1, 48, 512, flags=1 << 30)
     assert e.value.status == B.LSF_ERR_INVALID_ARG
+
+
+def test_kept_activations_give_the_same_bits():
+    s = Setup(SMALL, 3, 512, 2, 64, "keep")
+    s.step(mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+    a = s.snapshot()
+    kept = S.Stack(SMALL, s.store, 2, 64, 512, keep_activations=True)
+    for mode in (B.MODE_STREAMED, B.MODE_RESIDENT):
+        kept.step(s.ids, s.emb, s.fnorm, s.head, s.lora.array(), mode=mode | B.MODE_ZERO_GRADS)
+        torch.cuda.synchronize()
+        got = (kept.logits.clone(), kept.loss.clone(),
+               [{n: (s.lora.dA[i][n].clone(), s.lora.dB[i][n].clone()) for n in s.lora.targets}
+                for i in range(s.L)])
+        assert same(a, got)
+    # the layers are still read twice per micro-batch
+    B.stack_reset_stats(kept.handle)
+    kept.step(s.ids, s.emb, s.fnorm, s.head, s.lora.array(), mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+    torch.cuda.synchronize()
+    assert kept.stats().copies == 2 * s.L - 4
+    # an arena that is too small is refused before anything runs
+    io = kept._io(s.ids, s.emb, s.fnorm, s.head, s.lora.array(), B.MODE_STREAMED, 1.0)
+    io.act_bytes = kept.act.numel() - 256
+    with pytest.raises(B.LsfError) as e:
+        B.stream_stack_step(kept.handle, io)
+    assert e.value.status == B.LSF_ERR_WORKSPACE
+    kept.close()
