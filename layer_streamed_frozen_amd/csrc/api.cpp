@@ -304,8 +304,8 @@ lsf_status linear_bwd(const lsf_weight* w, int32_t format, int32_t n_out, int32_
     ga.P = l.dU; ga.ldp = rank; ga.Q = x; ga.ldq = n_in; ga.nq = n_in; ga.out = dA; ga.scale = 1.0f;
     gb.P = l.U; gb.ldp = rank; gb.Q = dy; gb.ldq = n_out; gb.nq = n_out; gb.out = dB; gb.transposed = true;
     gb.scale = scale;
-    if (dA) HIPCK(lora_grad(&ga, 1, tokens, rank, S(stream)));
-    if (dB) HIPCK(lora_grad(&gb, 1, tokens, rank, S(stream)));
+    if (dA) HIPCK(lora_grad(&ga, 1, tokens, rank, l.part, l.part_floats, S(stream)));
+    if (dB) HIPCK(lora_grad(&gb, 1, tokens, rank, l.part, l.part_floats, S(stream)));
   }
   return ok();
 }

@@ -78,8 +78,10 @@ __device__ __forceinline__ void load_main(const GemmArgs& g, int m0, int ntile, 
   for (int i = 0; i < 4; ++i) {
     const int idx = tid + C::NTHR * i;
     const int row = idx >> 3, ch = idx & 7;
-    const int gm = m0 + row;
-    st.a[i] = (gm < g.M) ? gload16(g.A + (int64_t)gm * g.lda + k0 + ch * 8) : u32x4{0, 0, 0, 0};
+    // Rows past M read row M-1: each C row depends on its own A row only and
+    // rows past M are never stored, so the load needs no branch.
+    const int gm = min(m0 + row, g.M - 1);
+    st.a[i] = gload16(g.A + (int64_t)gm * g.lda + k0 + ch * 8);
   }
   if constexpr (FMT == FMT_BF16) {
     constexpr int PER = 1024 / C::NTHR;  // 16-byte chunks of the weight tile per thread
@@ -450,8 +452,13 @@ hipError_t launch(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
 __global__ void splitk_reduce_kernel(const float* part, int splits, int M, int N, EpiArgs e) {
   const int64_t MN = (int64_t)M * N;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < MN; i += (int64_t)gridDim.x * blockDim.x) {
-    float v = part[i];
-    for (int zz = 1; zz < splits; ++zz) v += part[zz * MN + i];
+    float q[8];
+#pragma unroll
+    for (int zz = 0; zz < 8; ++zz) q[zz] = (zz < splits) ? part[zz * MN + i] : 0.0f;  // splits <= 8
+    float v = q[0];
+#pragma unroll
+    for (int zz = 1; zz < 8; ++zz)
+      if (zz < splits) v += q[zz];
     const int64_t m = i / N, n = i - m * N;
     switch (e.kind) {
       case EPI_F32: static_cast<float*>(e.C)[m * e.ldc + n] = v; break;
@@ -487,6 +494,7 @@ hipError_t gemm_nt(const GemmArgs& g, const EpiArgs& e, hipStream_t s) { return 
 hipError_t gemm_nn(const GemmArgs& g, const EpiArgs& e, hipStream_t s) { return launch<true>(g, e, s); }
 
 hipError_t splitk_reduce(const float* part, int splits, int M, int N, const EpiArgs& e, hipStream_t s) {
+  if (splits < 1 || splits > 8) return hipErrorInvalidValue;
   const int64_t MN = (int64_t)M * N;
   const int blocks = (int)std::min<int64_t>((MN + 255) / 256, 4096);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, part, splits, M, N, e);

@@ -69,7 +69,7 @@ int gemm_tile_rows(int M, int N, bool nn);
 hipError_t gemm_nt(const GemmArgs& g, const EpiArgs& e, hipStream_t s);
 // C = A W (+ LoRA), contraction over W rows.
 hipError_t gemm_nn(const GemmArgs& g, const EpiArgs& e, hipStream_t s);
-// Sum `splits` fp32 partials [splits, M, N] in fixed order and apply e.
+// Sum `splits` (1..8) fp32 partials [splits, M, N] in fixed order and apply e.
 hipError_t splitk_reduce(const float* part, int splits, int M, int N, const EpiArgs& e, hipStream_t s);
 
 // NF4
@@ -114,7 +114,10 @@ struct LoraGradSec {
   bool transposed = false;
   float scale = 1.0f;
 };
-hipError_t lora_grad(const LoraGradSec* secs, int nsec, int T, int r, hipStream_t s);
+// part (part_floats floats of scratch, may be NULL) holds per-token-split
+// partials when the token range is split across workgroups.
+hipError_t lora_grad(const LoraGradSec* secs, int nsec, int T, int r, float* part, size_t part_floats,
+                     hipStream_t s);
 
 // Elementwise / normalisation.
 hipError_t rmsnorm_fwd(const uint16_t* x, const uint16_t* w, int T, int H, float eps, uint16_t* y, float* rstd,

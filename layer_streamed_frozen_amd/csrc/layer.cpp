@@ -306,7 +306,7 @@ hipError_t lora_dU(const uint16_t* dY, int64_t ld, int T, int r, float sc, int n
 // dA_sec += dU_sec^T X  and  dB_sec += s dY_sec^T U_sec.
 hipError_t lora_grads(int T, int r, float sc, int nsec, const lsf_lora_proj* const* p, const float* dU,
                       const uint16_t* X, int64_t ldx, int nx, const float* U, const uint16_t* dY, int64_t ldy,
-                      const int* yoff, const int* ny, hipStream_t s) {
+                      const int* yoff, const int* ny, const LayerWs& ws, hipStream_t s) {
   LoraGradSec ga[3], gb[3];
   int na = 0, nb = 0;
   for (int i = 0; i < nsec; ++i) {
@@ -322,8 +322,8 @@ hipError_t lora_grads(int T, int r, float sc, int nsec, const lsf_lora_proj* con
       q.out = p[i]->dB; q.transposed = true; q.scale = sc;
     }
   }
-  CK(lora_grad(ga, na, T, r, s));
-  return lora_grad(gb, nb, T, r, s);
+  CK(lora_grad(ga, na, T, r, ws.part, ws.part_floats, s));
+  return lora_grad(gb, nb, T, r, ws.part, ws.part_floats, s);
 }
 
 }  // namespace
@@ -353,7 +353,7 @@ hipError_t layer_backward(const lsf_layer_cfg& c, const lsf_layer_weights& w, co
     CK(timed_gemm(ws, LSF_K_DOWN_BWD, true, g, e, s));
     if (p[0]) {
       const int yo[1] = {0}, ny[1] = {H};
-      CK(lora_grads(T, r, sc, 1, p, ws.dU, ws.a, I, I, ws.Ud, dy, H, yo, ny, s));
+      CK(lora_grads(T, r, sc, 1, p, ws.dU, ws.a, I, I, ws.Ud, dy, H, yo, ny, ws, s));
     }
   }
   // gate|up: dh2 = dG W_gate + dU W_up (+ LoRA)
@@ -373,7 +373,7 @@ hipError_t layer_backward(const lsf_layer_cfg& c, const lsf_layer_weights& w, co
     CK(timed_gemm(ws, LSF_K_GATEUP_BWD, true, g, e, s));
     if (any) {
       const int yo[2] = {0, I}, ny[2] = {I, I};
-      CK(lora_grads(T, r, sc, 2, p, ws.dU, ws.h2, H, H, ws.Ugu, ws.dgu, 2 * (int64_t)I, yo, ny, s));
+      CK(lora_grads(T, r, sc, 2, p, ws.dU, ws.h2, H, H, ws.Ugu, ws.dgu, 2 * (int64_t)I, yo, ny, ws, s));
     }
   }
   CK(rmsnorm_bwd(ws.dh, ws.x2, w.norm2, ws.rstd2, dy, T, H, ws.dx2, s));
@@ -391,7 +391,7 @@ hipError_t layer_backward(const lsf_layer_cfg& c, const lsf_layer_weights& w, co
     CK(timed_gemm(ws, LSF_K_O_BWD, true, g, e, s));
     if (p[0]) {
       const int yo[1] = {0}, ny[1] = {H};
-      CK(lora_grads(T, r, sc, 1, p, ws.dU, ws.att, z.Dq, (int)z.Dq, ws.Uo, ws.dx2, H, yo, ny, s));
+      CK(lora_grads(T, r, sc, 1, p, ws.dU, ws.att, z.Dq, (int)z.Dq, ws.Uo, ws.dx2, H, yo, ny, ws, s));
     }
   }
   // attention
@@ -423,7 +423,7 @@ hipError_t layer_backward(const lsf_layer_cfg& c, const lsf_layer_weights& w, co
     CK(timed_gemm(ws, LSF_K_QKV_BWD, true, g, e, s));
     if (any) {
       const int ny[3] = {qd, kd, kd};
-      CK(lora_grads(T, r, sc, 3, p, ws.dU, ws.h1, H, H, ws.Uqkv, ws.dqkv, z.Nqkv, xo, ny, s));
+      CK(lora_grads(T, r, sc, 3, p, ws.dU, ws.h1, H, H, ws.Uqkv, ws.dqkv, z.Nqkv, xo, ny, ws, s));
     }
   }
   return rmsnorm_bwd(ws.dh, x, w.norm1, ws.rstd1, ws.dx2, T, H, dx, s);

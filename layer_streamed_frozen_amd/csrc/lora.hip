@@ -9,10 +9,12 @@
 //
 // lora_grad: the adapter gradients dA = dU^T X and dB = s dY^T U, reductions
 // over the tokens: Out[j, k] += scale * sum_t P[t, j] Q[t, k].  A workgroup
-// owns 64 columns k and all r rows j; each wave takes a quarter of the tokens
-// in 32-row chunks, staged in LDS so the MFMA operands can run along the token
-// axis (P transposed, Q gathered down its rows).  The four partial tiles are
-// summed in a fixed order and added (+=) into the fp32 gradient.  No atomics:
+// owns 64 columns k, all r rows j and one share of the tokens; each wave takes
+// a quarter of that share in 32-row chunks, staged in LDS so the MFMA operands
+// can run along the token axis (P transposed, Q read down its rows with
+// transposing loads).  The four wave tiles are summed in a fixed order; the
+// token shares, when there are several, are summed in order by a second
+// kernel, and the result is added (+=) into the fp32 gradient.  No atomics:
 // the same inputs give the same bits on every run.
 #include "common.h"
 #include "kernels.h"
@@ -95,8 +97,17 @@ __global__ __launch_bounds__(256) void lora_down_reduce_kernel(LoraDown a, int n
     float v = 0.0f;
     if (a.mat[sec] != nullptr) {
       const int nch = (sec_k(a, sec) + KC - 1) / KC;
-      const float* p = a.part + (size_t)sec * nch_max * a.M * a.r + (size_t)t * a.r + j;
-      for (int c = 0; c < nch; ++c) v += p[(size_t)c * a.M * a.r];
+      const size_t stride = (size_t)a.M * a.r;
+      const float* p = a.part + (size_t)sec * nch_max * stride + (size_t)t * a.r + j;
+      // eight loads in flight, then the adds in chunk order
+      for (int c0 = 0; c0 < nch; c0 += 8) {
+        float q[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) q[u] = (c0 + u < nch) ? p[(size_t)(c0 + u) * stride] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (c0 + u < nch) v += q[u];
+      }
     }
     a.U[t * a.ldu + sec * a.r + j] = a.scale * v;
   }
@@ -108,8 +119,12 @@ struct GradBatch {
 
 constexpr int PS_LD = 40;  // LDS row stride (bf16) of the transposed P chunk
 
+// Workgroup (column tile, section, token split z): tokens
+// [z * 4 * cpw * 32, (z + 1) * 4 * cpw * 32).  With one split the result is
+// added into the gradient directly; with several, each split writes its
+// partial [z][section][R][maxq] and lora_grad_reduce_kernel adds their sum.
 template <int R>
-__global__ __launch_bounds__(256) void lora_grad_kernel(GradBatch gb, int T, int cpw) {
+__global__ __launch_bounds__(256) void lora_grad_kernel(GradBatch gb, int T, int cpw, float* part, int maxq) {
   __shared__ __attribute__((aligned(16))) uint16_t Qs[4][32 * 64];
   __shared__ __attribute__((aligned(16))) uint16_t Ps[4][R * PS_LD];
   __shared__ float red[4][R][65];
@@ -124,7 +139,7 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(GradBatch gb, int T, int
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0, 0, 0, 0};
   for (int ci = 0; ci < cpw; ++ci) {
-    const int t0 = (wid * cpw + ci) * 32;
+    const int t0 = (((int)blockIdx.z * 4 + wid) * cpw + ci) * 32;
     // Q chunk: 32 tokens x 64 columns
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -151,16 +166,12 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(GradBatch gb, int T, int
                                   : u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int nf = 0; nf < 4; ++nf) {
-      const int col = nf * 16 + lr;
-      uint32_t w[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int t = lg * 8 + 2 * p;
-        const uint32_t lo = Qs[wid][off_r8(t, col >> 3) + (col & 7)];
-        const uint32_t hi = Qs[wid][off_r8(t + 1, col >> 3) + (col & 7)];
-        w[p] = lo | (hi << 16);
-      }
-      const u32x4 bf = {w[0], w[1], w[2], w[3]};
+      // column nf*16 + lr, tokens lg*8 .. lg*8 + 7: two transposing reads
+      const int col = nf * 16 + 4 * (lr & 3);
+      const int row = lg * 8 + (lr >> 2);
+      const u32x2 lo = lds_read_tr4(Qs[wid], off_r8(row, col >> 3) + (col & 7));
+      const u32x2 hi = lds_read_tr4(Qs[wid], off_r8(row + 4, col >> 3) + (col & 7));
+      const u32x4 bf = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt) acc[jt][nf] = mfma16x16x32(af[jt], bf, acc[jt][nf]);
     }
@@ -182,6 +193,36 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(GradBatch gb, int T, int
     const int k = k0 + kk;
     if (k >= g.nq) continue;
     const float v = ((red[0][j][kk] + red[1][j][kk]) + red[2][j][kk]) + red[3][j][kk];
+    if (part != nullptr) {
+      part[(((size_t)blockIdx.z * gridDim.y + blockIdx.y) * R + j) * maxq + k] = v;
+    } else {
+      float* dst = g.transposed ? g.out + (int64_t)k * R + j : g.out + (int64_t)j * g.nq + k;
+      *dst += g.scale * v;
+    }
+  }
+}
+
+// Out += scale * (sum over the token splits, in order) of the partials.
+template <int R>
+__global__ __launch_bounds__(256) void lora_grad_reduce_kernel(GradBatch gb, int nsec, int nz, const float* part,
+                                                               int maxq) {
+  const int64_t total = (int64_t)nsec * R * maxq;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int k = (int)(i % maxq);
+    const int64_t rest = i / maxq;
+    const int j = (int)(rest % R);
+    const int sec = (int)(rest / R);
+    const LoraGradSec& g = gb.s[sec];
+    if (k >= g.nq) continue;
+    const size_t stride = (size_t)nsec * R * maxq;
+    const float* p = part + ((size_t)sec * R + j) * maxq + k;
+    float q[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) q[u] = (u < nz) ? p[u * stride] : 0.0f;  // nz <= 8 loads in flight
+    float v = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u < nz) v += q[u];
     float* dst = g.transposed ? g.out + (int64_t)k * R + j : g.out + (int64_t)j * g.nq + k;
     *dst += g.scale * v;
   }
@@ -203,7 +244,29 @@ hipError_t lora_down(const LoraDown& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t lora_grad(const LoraGradSec* secs, int nsec, int T, int r, hipStream_t s) {
+template <int R>
+hipError_t launch_grad(const GradBatch& gb, int nsec, int T, int maxq, float* part, size_t part_floats,
+                       hipStream_t s) {
+  const int tiles = (maxq + 63) / 64;
+  const int chunks = (T + 31) / 32;
+  // token splits: enough workgroups to fill the chip, at least two 32-token
+  // chunks per wave, and partials that fit the scratch
+  int nz = std::max(1, std::min(std::min(8, (512 + tiles * nsec - 1) / (tiles * nsec)), chunks / 8));
+  while (nz > 1 && (part == nullptr || (size_t)nz * nsec * R * maxq > part_floats)) --nz;
+  const int cpw = (chunks + 4 * nz - 1) / (4 * nz);
+  nz = (chunks + 4 * cpw - 1) / (4 * cpw);
+  dim3 grid(tiles, nsec, nz);
+  hipLaunchKernelGGL(lora_grad_kernel<R>, grid, dim3(256), 0, s, gb, T, cpw, nz > 1 ? part : nullptr, maxq);
+  if (nz > 1) {
+    const int64_t total = (int64_t)nsec * R * maxq;
+    const int blocks = (int)std::min<int64_t>((total + 255) / 256, 2048);
+    hipLaunchKernelGGL(lora_grad_reduce_kernel<R>, dim3(blocks), dim3(256), 0, s, gb, nsec, nz, part, maxq);
+  }
+  return hipGetLastError();
+}
+
+hipError_t lora_grad(const LoraGradSec* secs, int nsec, int T, int r, float* part, size_t part_floats,
+                     hipStream_t s) {
   if (nsec <= 0 || T <= 0) return hipSuccess;
   GradBatch gb{};
   int maxq = 0;
@@ -211,18 +274,14 @@ hipError_t lora_grad(const LoraGradSec* secs, int nsec, int T, int r, hipStream_
     gb.s[i] = secs[i];
     maxq = std::max(maxq, secs[i].nq);
   }
-  const int chunks = (T + 31) / 32;
-  const int cpw = (chunks + 3) / 4;  // 32-token chunks per wave
-  dim3 grid((maxq + 63) / 64, nsec);
   switch (r) {
-    case 4: hipLaunchKernelGGL(lora_grad_kernel<4>, grid, dim3(256), 0, s, gb, T, cpw); break;
-    case 8: hipLaunchKernelGGL(lora_grad_kernel<8>, grid, dim3(256), 0, s, gb, T, cpw); break;
-    case 16: hipLaunchKernelGGL(lora_grad_kernel<16>, grid, dim3(256), 0, s, gb, T, cpw); break;
-    case 32: hipLaunchKernelGGL(lora_grad_kernel<32>, grid, dim3(256), 0, s, gb, T, cpw); break;
-    case 64: hipLaunchKernelGGL(lora_grad_kernel<64>, grid, dim3(256), 0, s, gb, T, cpw); break;
+    case 4: return launch_grad<4>(gb, nsec, T, maxq, part, part_floats, s);
+    case 8: return launch_grad<8>(gb, nsec, T, maxq, part, part_floats, s);
+    case 16: return launch_grad<16>(gb, nsec, T, maxq, part, part_floats, s);
+    case 32: return launch_grad<32>(gb, nsec, T, maxq, part, part_floats, s);
+    case 64: return launch_grad<64>(gb, nsec, T, maxq, part, part_floats, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace lsf
