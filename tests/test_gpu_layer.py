@@ -138,3 +138,28 @@ def test_small_layer_unquantised_bf16_base():
 def test_full_8b_layer_double_quantised():
     res, _ = run_layer(S.LLAMA8B, 1, 512, "l8bdq", norms_random=False, fmt=B.FMT_NF4_DQ)
     _assert_all(res)
+
+
+def _shape(**kw):
+    base = dict(hidden=512, intermediate=1024, n_heads=4, n_kv_heads=2, head_dim=128, rank=16, alpha=16.0,
+                rope_theta=500000.0)
+    base.update(kw)
+    return S.LayerShape(**base)
+
+
+def test_small_layer_multi_head_attention():
+    # one kv head per query head (nkv = nq)
+    res, _ = run_layer(_shape(n_kv_heads=4), 1, 70, "slmha")
+    _assert_all(res)
+
+
+def test_small_layer_four_query_heads_per_kv_head_long_rows():
+    # the 8B model's grouping (4 query heads per kv head) and ten 64-key blocks, the last one ragged
+    res, _ = run_layer(_shape(hidden=1024, n_heads=8, n_kv_heads=2), 1, 600, "slgqa4")
+    _assert_all(res)
+
+
+@pytest.mark.parametrize("rank", [4, 8, 32, 64])
+def test_small_layer_other_ranks(rank):
+    res, _ = run_layer(_shape(rank=rank, alpha=2.0 * rank), 2, 80, f"slr{rank}")
+    _assert_all(res)
