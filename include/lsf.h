@@ -239,6 +239,9 @@ typedef struct lsf_stack lsf_stack;
 #define LSF_STACK_NO_TURN_REUSE 0x2u  /* copy every layer twice per micro-batch */
 #define LSF_STACK_TIMING 0x4u         /* record copy, compute-wait and kernel events for stack_stats */
 #define LSF_STACK_KERNEL_TIMING 0x8u  /* record only the kernel events (leaves the copy stream untouched) */
+/* The host store is a file on disk ([TUTORIAL] item 4: the NVMe tier used when
+ * RAM is short).  Not built: stack_create returns LSF_ERR_UNSUPPORTED. */
+#define LSF_STACK_SOURCE_DISK 0x10u
 /* Record only kernel class k (an LSF_K_* value; several may be or-ed), for a
  * measurement that must disturb the step as little as possible. */
 #define LSF_STACK_TIME_KERNEL(k) (0x100u << (k))

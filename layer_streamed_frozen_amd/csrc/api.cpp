@@ -773,8 +773,11 @@ lsf_status stack_create(const lsf_layer_cfg* cfg, const lsf_stack_desc* desc, ls
   if (desc->n_layers < 1) return fail(LSF_ERR_INVALID_ARG, "n_layers must be >= 1");
   {
     const uint32_t known = LSF_STACK_ALLOW_PAGEABLE | LSF_STACK_NO_TURN_REUSE | LSF_STACK_TIMING |
-                           LSF_STACK_KERNEL_TIMING | LSF_STACK_TIME_KERNEL(0) * ((1u << LSF_K_COUNT) - 1u);
+                           LSF_STACK_KERNEL_TIMING | LSF_STACK_SOURCE_DISK |
+                           LSF_STACK_TIME_KERNEL(0) * ((1u << LSF_K_COUNT) - 1u);
     if (desc->flags & ~known) return fail(LSF_ERR_INVALID_ARG, "unknown stack flags 0x%x", desc->flags & ~known);
+    if (desc->flags & LSF_STACK_SOURCE_DISK)
+      return fail(LSF_ERR_UNSUPPORTED, "a disk-backed store (the NVMe tier) is not built; load it into RAM");
   }
   if (desc->format != LSF_FMT_NF4 && desc->format != LSF_FMT_BF16 && desc->format != LSF_FMT_NF4_DQ)
     return fail(LSF_ERR_INVALID_ARG, "unknown weight format %d", desc->format);

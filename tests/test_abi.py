@@ -103,6 +103,13 @@ def test_invalid_arguments_are_rejected_before_any_launch(lib):
     assert L.stack_create(ctypes.byref(LLAMA8B.cfg(1, 512)), ctypes.byref(d), ctypes.byref(h)) == \
         B.LSF_ERR_INVALID_ARG
     d.n_layers = 2
+    d.flags = 1 << 31  # unknown flag
+    assert L.stack_create(ctypes.byref(LLAMA8B.cfg(1, 512)), ctypes.byref(d), ctypes.byref(h)) == \
+        B.LSF_ERR_INVALID_ARG
+    d.flags = B.STACK_SOURCE_DISK  # the disk tier is not built
+    assert L.stack_create(ctypes.byref(LLAMA8B.cfg(1, 512)), ctypes.byref(d), ctypes.byref(h)) == \
+        B.LSF_ERR_UNSUPPORTED
+    d.flags = 0
     d.format = B.FMT_NF4
     d.blob_stride = 1000
     assert L.stack_create(ctypes.byref(LLAMA8B.cfg(1, 512)), ctypes.byref(d), ctypes.byref(h)) == B.LSF_ERR_SHAPE
