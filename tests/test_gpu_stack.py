@@ -296,3 +296,47 @@ def test_kept_activations_give_the_same_bits():
         B.stream_stack_step(kept.handle, io)
     assert e.value.status == B.LSF_ERR_WORKSPACE
     kept.close()
+
+
+def test_bench_configuration_32_layers_full_vocabulary():
+    # The configuration bench.py times: 32 Llama-3.1-8B-shaped layers (the same
+    # seeded weights), vocabulary 128256, one sequence of 512 tokens.  At this
+    # size the oracle checks the first layer's output (from the embedding and
+    # layer 0's weights alone); the whole step is checked by the bit-equality of
+    # the streamed and the resident runs and by the copy count.
+    shape = S.LLAMA8B
+    L, V, seq = 32, 128256, 512
+    print(f"[stack] bench configuration L={L} V={V} seq={seq}", flush=True)
+    store = S.Store(shape, L, resident=True, pinned=True, weights_fn=lambda i: S.layer_weights_fp32(f"layer{i}", shape))
+    lora = S.LoraSet(shape, L)
+    H = shape.hidden
+    emb_np, emb = bf16_param("embed", (V, H), 1.0)
+    head_np, head = bf16_param("lm_head", (V, H), 0.02)
+    fnorm = torch.ones(H, dtype=torch.bfloat16, device="cuda")
+    ids_np = synth.token_ids("ids0", (1, seq), V)
+    ids = torch.from_numpy(ids_np).cuda()
+    stack = S.Stack(shape, store, 1, seq, V)
+    arr = lora.array()
+
+    def run(mode):
+        stack.step(ids, emb, fnorm, head, arr, mode=mode | B.MODE_ZERO_GRADS)
+        torch.cuda.synchronize()
+        return (stack.logits.clone(), stack.loss.clone(),
+                [{n: (lora.dA[i][n].clone(), lora.dB[i][n].clone()) for n in lora.targets} for i in range(L)])
+
+    a = run(B.MODE_STREAMED)
+    layer1 = stack.ckpt[1].clone()
+    B.stack_reset_stats(stack.handle)
+    a2 = run(B.MODE_STREAMED)
+    assert stack.stats().copies == 2 * L - 4
+    assert same(a, a2)
+    assert same(a, run(B.MODE_RESIDENT))
+    loss = float(a[1].item())
+    print(f"  loss {loss:.4f} (ln V = {np.log(V):.4f})", flush=True)
+    assert np.isfinite(loss) and abs(loss - np.log(V)) < 1.0
+    # layer 0 against the oracle, from the ids and the embedding
+    x = emb_np.astype(np.float64)[ids_np]
+    W0 = oracle_layer_weights(S.layer_weights_fp32("layer0", shape))
+    y, _ = M.layer_fwd(x, W0, lora.numpy(0), oracle_shape(shape))
+    assert report("layer0.y", bf16_tensor_to_np(layer1).reshape(1, seq, H), y) < TOL
+    stack.close()
