@@ -43,8 +43,8 @@ PCIE5_X16_GBPS = 63.0            # theoretical per direction after 128b/130b enc
 # (profiles/pmc_traffic_layer8b_seq512.md): FETCH_SIZE 66768.1 KiB scaled by 1.99975
 # (the calibration kernel's ratio) + WRITE_SIZE 28677.2 KiB scaled by 1.0.  Valid only
 # for the GEMM sources they were taken on (hash below); otherwise traffic is null.
-GATE_UP_TRAFFIC_BYTES = (66768.1 * 1.99975 + 28677.2 * 1.0) * 1024
-GATE_UP_TRAFFIC_SRC = "f272b47a3e2c758d"
+GATE_UP_TRAFFIC_BYTES = (66792.1 * 1.99974 + 28676.0 * 1.0) * 1024
+GATE_UP_TRAFFIC_SRC = "0eaa6a194cae9439"
 # Algorithmic bytes of one such launch: NF4 codes 58.72 MB + absmax 7.34 MB + x 4.19 MB +
 # LoRA (U, B) 1.9 MB read; a 14.7 MB (forward) or a, g, u 44.0 MB (recompute) written.
 GATE_UP_ALGO_BYTES = (58.72 + 7.34 + 4.19 + 1.9 + (14.68 + 44.04) / 2) * 1e6

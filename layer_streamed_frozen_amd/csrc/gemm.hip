@@ -476,12 +476,15 @@ __global__ void splitk_reduce_kernel(const float* part, int splits, int M, int N
 }  // namespace
 
 // Measured on MI355X at 512 and 2048 tokens: 256-row tiles are faster for the
-// input-gradient GEMMs, for forward GEMMs with N <= 4096 (o, down) and for the
-// very wide gate|up (N = 28672: 6% less time, each weight tile decoded once per
-// 256 rows); q|k|v (N = 6144) is faster with 128-row tiles.
+// input-gradient GEMMs with N <= 4096 (q|k|v, o, gate|up), for forward GEMMs
+// with N <= 4096 (o, down) and for the very wide forward gate|up (N = 28672: 6%
+// less time, each weight tile decoded once per 256 rows); the forward q|k|v
+// (N = 6144) and the input gradient of down (N = 14336: 6% less time) are
+// faster with 128-row tiles.
 int gemm_tile_rows(int M, int N, bool nn) {
   if (M < 256) return 128;
-  return (nn || N <= 4096 || N >= 16384) ? 256 : 128;
+  if (nn) return N >= 8192 ? 128 : 256;
+  return (N <= 4096 || N >= 16384) ? 256 : 128;
 }
 
 hipError_t gemm_nt(const GemmArgs& g, const EpiArgs& e, hipStream_t s) { return launch<false>(g, e, s); }
