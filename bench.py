@@ -40,11 +40,11 @@ HBM_PEAK_GBPS = 8000.0
 PCIE5_X16_GBPS = 63.0            # theoretical per direction after 128b/130b encoding
 
 # HBM bytes per launch of the gate|up forward GEMM from two rocprofv3 --pmc passes
-# (profiles/pmc_traffic_layer8b_seq512.md): FETCH_SIZE 66768.1 KiB scaled by 1.99975
-# (the calibration kernel's ratio) + WRITE_SIZE 28677.2 KiB scaled by 1.0.  Valid only
+# (profiles/pmc_traffic_layer8b_seq512.md): FETCH_SIZE 50047.0 KiB scaled by 1.99974
+# (the calibration kernel's ratio) + WRITE_SIZE 28691.4 KiB scaled by 1.0.  Valid only
 # for the GEMM sources they were taken on (hash below); otherwise traffic is null.
-GATE_UP_TRAFFIC_BYTES = (66792.1 * 1.99974 + 28676.0 * 1.0) * 1024
-GATE_UP_TRAFFIC_SRC = "0eaa6a194cae9439"
+GATE_UP_TRAFFIC_BYTES = (50047.0 * 1.99974 + 28691.4 * 1.0) * 1024
+GATE_UP_TRAFFIC_SRC = "8a590657d0c5cc93"
 # Algorithmic bytes of one such launch: NF4 codes 58.72 MB + absmax 7.34 MB + x 4.19 MB +
 # LoRA (U, B) 1.9 MB read; a 14.7 MB (forward) or a, g, u 44.0 MB (recompute) written.
 GATE_UP_ALGO_BYTES = (58.72 + 7.34 + 4.19 + 1.9 + (14.68 + 44.04) / 2) * 1e6
@@ -54,7 +54,7 @@ def gemm_src_hash():
     import hashlib
     here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "layer_streamed_frozen_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.h", "kernels.h", "weight_decode.h"):
+    for f in ("gemm.hip", "gemm_wide.hip", "common.h", "kernels.h", "weight_decode.h"):
         with open(os.path.join(here, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -272,13 +272,17 @@ def main():
     if st.kernel_launches[dom_k] > 0:
         avg = st.kernel_ms[dom_k] / st.kernel_launches[dom_k] * 1e-3
         ach = flops["gate_up"] / avg / 1e12
+        # The counters and the algorithmic bytes belong to the configuration they
+        # were taken on: NF4 with fp32 absmax, 512 tokens, recomputing backward.
+        measured_cfg = args.format == "nf4" and T == 512 and not args.keep_activations
         same_src = gemm_src_hash() == GATE_UP_TRAFFIC_SRC
+        base = {"nf4": "NF4", "nf4dq": "double-quantised NF4", "bf16": "bf16"}[args.format]
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": round(GATE_UP_TRAFFIC_BYTES) if same_src else None,
-                "traffic_unit": "HBM bytes per launch (FETCH_SIZE x1.99975 + WRITE_SIZE x1.000)",
-                "algorithmic_bytes": round(GATE_UP_ALGO_BYTES),
-                "kernel": f"fused NF4 gate|up GEMM + SwiGLU epilogue, {T}x{2 * shape.intermediate}x{H}",
+                "traffic": round(GATE_UP_TRAFFIC_BYTES) if (same_src and measured_cfg) else None,
+                "traffic_unit": "HBM bytes per launch (FETCH_SIZE x1.99974 + WRITE_SIZE x1.000)",
+                "algorithmic_bytes": round(GATE_UP_ALGO_BYTES) if measured_cfg else None,
+                "kernel": f"fused {base} gate|up GEMM + SwiGLU epilogue, {T}x{2 * shape.intermediate}x{H}",
                 "flop_per_launch": flops["gate_up"], "avg_launch_us": round(avg * 1e6, 2),
                 "launches": int(st.kernel_launches[dom_k])}
 

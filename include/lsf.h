@@ -77,6 +77,16 @@ LSF_API const char* lsf_last_error(void);
 /* Library version string. */
 LSF_API const char* lsf_version(void);
 
+/* Diagnostics: the kernel that runs wide forward NF4 GEMMs (fp32 absmax,
+ * N >= 16384 with whole 256-column tiles, at least 256 tokens, no split-K:
+ * the gate|up projection of an 8B-shaped layer).  enable = 1 (the default):
+ * the 256 x 256 ping-pong kernel; 0: the general 128-column kernel.  Both
+ * compute the same contraction in the same order and give bitwise-identical
+ * results; the switch lets tests and profiles compare them.  Process-wide;
+ * GEMMs already enqueued are not affected.  enable must be 0 or 1
+ * (LSF_ERR_INVALID_ARG). */
+LSF_API lsf_status gemm_set_wide(int32_t enable);
+
 /* ------------------------------------------------------------------ NF4 --
  * [TUTORIAL] item 1: the decoder's Linear weights are stored offline as QLoRA
  * NF4; compute runs in higher precision.  Blocks of `blocksize` (= 64)

@@ -106,6 +106,7 @@ KERNELS = ["qkv_fwd", "o_fwd", "gate_up_fwd", "down_fwd", "qkv_bwd", "o_bwd", "g
 _PROTOS = {
     "lsf_last_error": (ctypes.c_char_p, []),
     "lsf_version": (ctypes.c_char_p, []),
+    "gemm_set_wide": (ctypes.c_int, [ctypes.c_int32]),
     "nf4_quantize": (c_int32, [c_void_p, c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
     "nf4_dequantize": (c_int32, [c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_void_p]),
     "nf4dq_quantize": (c_int32, [c_void_p, c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
@@ -177,6 +178,13 @@ def layer_cfg(hidden, intermediate, n_heads, n_kv_heads, head_dim, rank, lora_sc
 
 
 # ----------------------------------------------------------------- calls
+
+def gemm_set_wide(enable):
+    """Select the kernel of the wide forward NF4 GEMMs (True: 256x256
+    ping-pong kernel, the default; False: the general kernel).  Results are
+    bitwise identical either way."""
+    check(lib().gemm_set_wide(1 if enable else 0))
+
 
 def nf4_quantize(w, packed=None, absmax=None, stream=None):
     """w: fp32 device tensor (numel % 64 == 0) -> (packed uint8 [n/2], absmax fp32 [n/64])."""

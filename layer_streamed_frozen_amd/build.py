@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "liblsf.so")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 
-SOURCES = ["nf4.hip", "gemm.hip", "lora.hip", "elementwise.hip", "attention.hip", "optim.hip", "layer.cpp", "api.cpp"]
+SOURCES = ["nf4.hip", "gemm.hip", "gemm_wide.hip", "lora.hip", "elementwise.hip", "attention.hip", "optim.hip", "layer.cpp", "api.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

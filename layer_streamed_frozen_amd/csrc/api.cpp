@@ -162,6 +162,12 @@ extern "C" {
 const char* lsf_last_error(void) { return g_err.c_str(); }
 const char* lsf_version(void) { return "lsf 0.1.0 (gfx950)"; }
 
+lsf_status gemm_set_wide(int32_t enable) {
+  if (enable != 0 && enable != 1) return fail(LSF_ERR_INVALID_ARG, "enable must be 0 or 1 (got %d)", (int)enable);
+  set_gemm_wide(enable != 0);
+  return ok();
+}
+
 lsf_status nf4_quantize(const float* w, int64_t n, int32_t blocksize, uint8_t* packed, float* absmax,
                         lsf_stream stream) {
   if (blocksize != 64) return fail(LSF_ERR_SHAPE, "blocksize must be 64");

@@ -24,6 +24,8 @@
 #include "kernels.h"
 #include "weight_decode.h"
 
+#include <atomic>
+
 namespace lsf {
 namespace {
 
@@ -487,7 +489,16 @@ int gemm_tile_rows(int M, int N, bool nn) {
   return (N <= 4096 || N >= 16384) ? 256 : 128;
 }
 
-hipError_t gemm_nt(const GemmArgs& g, const EpiArgs& e, hipStream_t s) { return launch<false>(g, e, s); }
+namespace {
+std::atomic<bool> g_wide_enabled{true};
+}  // namespace
+
+void set_gemm_wide(bool enable) { g_wide_enabled.store(enable, std::memory_order_relaxed); }
+
+hipError_t gemm_nt(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
+  if (g_wide_enabled.load(std::memory_order_relaxed) && gemm_wide_applies(g, e)) return gemm_nt_wide(g, e, s);
+  return launch<false>(g, e, s);
+}
 hipError_t gemm_nn(const GemmArgs& g, const EpiArgs& e, hipStream_t s) { return launch<true>(g, e, s); }
 
 hipError_t splitk_reduce(const float* part, int splits, int M, int N, const EpiArgs& e, hipStream_t s) {

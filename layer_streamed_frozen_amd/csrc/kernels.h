@@ -67,6 +67,11 @@ struct EpiArgs {
 int gemm_tile_rows(int M, int N, bool nn);
 // C = A W^T (+ LoRA), W rows map to C columns.
 hipError_t gemm_nt(const GemmArgs& g, const EpiArgs& e, hipStream_t s);
+// The 256 x 256 ping-pong kernel for wide forward GEMMs (gate|up); gemm_nt
+// uses it by itself where gemm_wide_applies.
+bool gemm_wide_applies(const GemmArgs& g, const EpiArgs& e);
+void set_gemm_wide(bool enable);  // process-wide; default on
+hipError_t gemm_nt_wide(const GemmArgs& g, const EpiArgs& e, hipStream_t s);
 // C = A W (+ LoRA), contraction over W rows.
 hipError_t gemm_nn(const GemmArgs& g, const EpiArgs& e, hipStream_t s);
 // Sum `splits` (1..8) fp32 partials [splits, M, N] in fixed order and apply e.

@@ -125,3 +125,10 @@ def test_binding_raises_with_message(lib):
         B.check(lib.nf4_quantize(None, 100, 64, None, None, None))
     assert e.value.status == B.LSF_ERR_SHAPE
     assert "LSF_ERR_SHAPE" in str(e.value)
+
+
+def test_gemm_schedule_switch_validates(lib):
+    B.gemm_set_wide(False)
+    B.gemm_set_wide(True)
+    assert lib.gemm_set_wide(2) == B.LSF_ERR_INVALID_ARG
+    assert "enable" in lib.lsf_last_error().decode()
