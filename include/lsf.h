@@ -78,14 +78,17 @@ LSF_API const char* lsf_last_error(void);
 LSF_API const char* lsf_version(void);
 
 /* Diagnostics: the kernel that runs wide forward NF4 GEMMs (fp32 absmax,
- * N >= 16384 with whole 256-column tiles, at least 256 tokens, no split-K:
- * the gate|up projection of an 8B-shaped layer).  enable = 1 (the default):
+ * N >= 16384 with whole 256-column tiles, K >= 2048, at least 256 tokens,
+ * no split-K: the gate|up projection of an 8B-shaped layer).  enable = 1 (the default):
  * the 256 x 256 ping-pong kernel; 0: the general 128-column kernel.  Both
  * compute the same contraction in the same order and give bitwise-identical
  * results; the switch lets tests and profiles compare them.  Process-wide;
  * GEMMs already enqueued are not affected.  enable must be 0 or 1
  * (LSF_ERR_INVALID_ARG). */
 LSF_API lsf_status gemm_set_wide(int32_t enable);
+/* Diagnostics: number of GEMMs launched on the wide kernel so far in this
+ * process (lets a test confirm which kernel ran). */
+LSF_API int64_t gemm_wide_launch_count(void);
 
 /* ------------------------------------------------------------------ NF4 --
  * [TUTORIAL] item 1: the decoder's Linear weights are stored offline as QLoRA

@@ -107,6 +107,7 @@ _PROTOS = {
     "lsf_last_error": (ctypes.c_char_p, []),
     "lsf_version": (ctypes.c_char_p, []),
     "gemm_set_wide": (ctypes.c_int, [ctypes.c_int32]),
+    "gemm_wide_launch_count": (ctypes.c_int64, []),
     "nf4_quantize": (c_int32, [c_void_p, c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
     "nf4_dequantize": (c_int32, [c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_void_p]),
     "nf4dq_quantize": (c_int32, [c_void_p, c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
@@ -184,6 +185,11 @@ def gemm_set_wide(enable):
     ping-pong kernel, the default; False: the general kernel).  Results are
     bitwise identical either way."""
     check(lib().gemm_set_wide(1 if enable else 0))
+
+
+def gemm_wide_launch_count():
+    """GEMMs launched on the wide kernel so far in this process."""
+    return int(lib().gemm_wide_launch_count())
 
 
 def nf4_quantize(w, packed=None, absmax=None, stream=None):

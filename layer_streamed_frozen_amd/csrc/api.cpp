@@ -168,6 +168,8 @@ lsf_status gemm_set_wide(int32_t enable) {
   return ok();
 }
 
+int64_t gemm_wide_launch_count(void) { return gemm_wide_launches(); }
+
 lsf_status nf4_quantize(const float* w, int64_t n, int32_t blocksize, uint8_t* packed, float* absmax,
                         lsf_stream stream) {
   if (blocksize != 64) return fail(LSF_ERR_SHAPE, "blocksize must be 64");

@@ -28,6 +28,8 @@
 #include "kernels.h"
 #include "weight_decode.h"
 
+#include <atomic>
+
 namespace lsf {
 namespace {
 
@@ -319,23 +321,32 @@ hipError_t launch_wide_fmt(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
 }  // namespace
 
 // The wide kernel needs whole 256-column tiles (and 128-row halves of them in
-// pair mode), 64-deep absmax blocks, at least six 32-deep k tiles, 16-byte
-// aligned A rows, 8-byte aligned codes, and no split-K.  It is chosen for N >= 16384, where
-// its 256 x 256 tiles still fill the 256 compute units.
+// pair mode), 64-deep absmax blocks, 16-byte aligned A rows, 8-byte aligned
+// codes, and no split-K.  It is chosen for N >= 16384, where its 256 x 256
+// tiles still fill the 256 compute units, and K >= 2048: with short
+// contractions its prologue dominates (measured 1.7x slower than the general
+// kernel at K = 512).
 bool gemm_wide_applies(const GemmArgs& g, const EpiArgs& e) {
   if (g.splits != 1 || g.M < 256 || g.N < 16384 || g.N % WBN != 0) return false;
   // fp32 absmax only: with the double-quantised absmax (two more loads in
   // flight per code set) the kernel no longer fits its 256 registers.
   if (g.W.fmt != FMT_NF4) return false;
-  if (g.K % 64 != 0 || g.K < 6 * WBK || g.W.ld != g.K || g.lda % 8 != 0) return false;
+  if (g.K % 64 != 0 || g.K < 2048 || g.W.ld != g.K || g.lda % 8 != 0) return false;
   if (((uintptr_t)g.A & 15) != 0 || ((uintptr_t)g.W.packed & 7) != 0) return false;
   if (g.pair_I > 0 && (g.pair_I * 2 != g.N || g.pair_I % (WBN / 2) != 0)) return false;
   if (e.kind == EPI_SWIGLU) return g.pair_I > 0;
   return e.kind == EPI_BF16 && g.pair_I == 0;
 }
 
+namespace {
+std::atomic<int64_t> g_wide_launches{0};
+}  // namespace
+
+int64_t gemm_wide_launches() { return g_wide_launches.load(std::memory_order_relaxed); }
+
 hipError_t gemm_nt_wide(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
   if (!gemm_wide_applies(g, e)) return hipErrorInvalidValue;
+  g_wide_launches.fetch_add(1, std::memory_order_relaxed);
   return launch_wide_fmt<FMT_NF4>(g, e, s);
 }
 

@@ -71,6 +71,7 @@ hipError_t gemm_nt(const GemmArgs& g, const EpiArgs& e, hipStream_t s);
 // uses it by itself where gemm_wide_applies.
 bool gemm_wide_applies(const GemmArgs& g, const EpiArgs& e);
 void set_gemm_wide(bool enable);  // process-wide; default on
+int64_t gemm_wide_launches();      // wide-kernel launches so far
 hipError_t gemm_nt_wide(const GemmArgs& g, const EpiArgs& e, hipStream_t s);
 // C = A W (+ LoRA), contraction over W rows.
 hipError_t gemm_nn(const GemmArgs& g, const EpiArgs& e, hipStream_t s);

@@ -132,3 +132,4 @@ def test_gemm_schedule_switch_validates(lib):
     B.gemm_set_wide(True)
     assert lib.gemm_set_wide(2) == B.LSF_ERR_INVALID_ARG
     assert "enable" in lib.lsf_last_error().decode()
+    assert B.gemm_wide_launch_count() >= 0

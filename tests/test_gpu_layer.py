@@ -167,18 +167,21 @@ def test_small_layer_other_ranks(rank):
 
 @pytest.mark.parametrize("rank", [16, 64])
 def test_wide_gate_up_kernel_matches_oracle_and_general_kernel(rank):
-    # intermediate 8192: the gate|up GEMM (N = 16384) runs on the 256x256
-    # ping-pong kernel; 300 tokens leave the second 256-row tile ragged, and
-    # rank 64 gives four 32-wide LoRA steps.  The general kernel must give the
-    # same bits.
-    shape = _shape(intermediate=8192, rank=rank, alpha=2.0 * rank)
+    # hidden 2048, intermediate 8192: the gate|up GEMM (N = 16384, K = 2048)
+    # runs on the 256x256 ping-pong kernel; 300 tokens leave the second
+    # 256-row tile ragged, and rank 64 gives four 32-wide LoRA steps.  The
+    # general kernel must give the same bits.
+    shape = _shape(hidden=2048, n_heads=16, n_kv_heads=4, intermediate=8192, rank=rank, alpha=2.0 * rank)
+    n0 = B.gemm_wide_launch_count()
     res, (y, dx, lora) = run_layer(shape, 1, 300, f"slwide{rank}")
+    assert B.gemm_wide_launch_count() == n0 + 2  # forward and the recompute
     _assert_all(res)
     B.gemm_set_wide(False)
     try:
         _, (y2, dx2, lora2) = run_layer(shape, 1, 300, f"slwide{rank}")
     finally:
         B.gemm_set_wide(True)
+    assert B.gemm_wide_launch_count() == n0 + 2
     assert torch.equal(y, y2) and torch.equal(dx, dx2)
     for n in S.PROJ:
         assert torch.equal(lora.dA[0][n], lora2.dA[0][n]) and torch.equal(lora.dB[0][n], lora2.dB[0][n])

@@ -69,17 +69,20 @@ def test_linear_long_contraction_split_k():
 
 
 def test_wide_forward_kernel_matches_oracle_and_general_kernel():
-    # 16384 outputs: the forward GEMM runs on the 256x256 ping-pong kernel
-    # (two 256-row tiles, the second ragged); the general kernel gives the
-    # same bits.
-    res = _run("linwide", 16384, 512, 300, 16, 16.0)
+    # 16384 outputs, 2048 inputs: the forward GEMM runs on the 256x256
+    # ping-pong kernel (two 256-row tiles, the second ragged); the general
+    # kernel gives the same bits.
+    n0 = B.gemm_wide_launch_count()
+    res = _run("linwide", 16384, 2048, 300, 16, 16.0)
+    assert B.gemm_wide_launch_count() == n0 + 1
     for k, (g, r) in res.items():
         assert report(k, g, r) < TOL, k
     B.gemm_set_wide(False)
     try:
-        res2 = _run("linwide", 16384, 512, 300, 16, 16.0)
+        res2 = _run("linwide", 16384, 2048, 300, 16, 16.0)
     finally:
         B.gemm_set_wide(True)
+    assert B.gemm_wide_launch_count() == n0 + 1
     for k in res:
         assert np.array_equal(res[k][0], res2[k][0]), k
 

@@ -324,7 +324,10 @@ def test_bench_configuration_32_layers_full_vocabulary():
         return (stack.logits.clone(), stack.loss.clone(),
                 [{n: (lora.dA[i][n].clone(), lora.dB[i][n].clone()) for n in lora.targets} for i in range(L)])
 
+    n0 = B.gemm_wide_launch_count()
     a = run(B.MODE_STREAMED)
+    # gate|up forward and recompute of every layer on the 256x256 kernel
+    assert B.gemm_wide_launch_count() - n0 == 2 * L
     layer1 = stack.ckpt[1].clone()
     B.stack_reset_stats(stack.handle)
     a2 = run(B.MODE_STREAMED)
