@@ -44,7 +44,7 @@ PCIE5_X16_GBPS = 63.0            # theoretical per direction after 128b/130b enc
 # (the calibration kernel's ratio) + WRITE_SIZE 28691.4 KiB scaled by 1.0.  Valid only
 # for the GEMM sources they were taken on (hash below); otherwise traffic is null.
 GATE_UP_TRAFFIC_BYTES = (50047.0 * 1.99974 + 28691.4 * 1.0) * 1024
-GATE_UP_TRAFFIC_SRC = "105cdfe97d987c96"
+GATE_UP_TRAFFIC_SRC = "d5e9b6610efd7129"
 # Algorithmic bytes of one such launch: NF4 codes 58.72 MB + absmax 7.34 MB + x 4.19 MB +
 # LoRA (U, B) 1.9 MB read; a 14.7 MB (forward) or a, g, u 44.0 MB (recompute) written.
 GATE_UP_ALGO_BYTES = (58.72 + 7.34 + 4.19 + 1.9 + (14.68 + 44.04) / 2) * 1e6

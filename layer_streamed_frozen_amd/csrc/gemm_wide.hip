@@ -19,11 +19,15 @@
 //   registers, decode its half of the weight tile three ahead into LDS, and
 //   read its own fragments of the current tile.  A workgroup barrier between
 //   the phases swaps the roles.
-// * Every memory phase issues the same number of vector-memory operations
-//   (past the last tile the loads repeat it into a stage nobody reads again),
-//   so one fixed `s_waitcnt vmcnt(n)` at the start of a phase is exactly "the
-//   operations of two phases ago have landed".  Barriers carry no memory-model
-//   fence: a release fence would wait for every LDS-DMA in flight.
+// * Every memory phase issues the same vector-memory operations, the two
+//   LDS-DMA first (past the last tile they repeat it into a stage nobody reads
+//   again), then the code and absmax loads.  Loads complete in issue order, so
+//   `s_waitcnt vmcnt(4)` at the start of a phase means "the LDS-DMA of two
+//   phases ago has landed"; it stays safe if the compiler emits more loads
+//   per phase (it then waits longer) or merges the two register loads into
+//   one (the last operation of the older phase is still a register load).
+//   Barriers carry no memory-model fence: a release fence would wait for
+//   every LDS-DMA in flight.
 #include "common.h"
 #include "kernels.h"
 #include "weight_decode.h"
