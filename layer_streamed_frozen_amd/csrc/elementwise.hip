@@ -26,24 +26,47 @@ __device__ __forceinline__ u32x4 pack8(const float f[8]) {
   return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
 }
 
+// Rows of up to kRowRegs * 2048 elements stay in registers between the two
+// passes (sum of squares or dot product, then the output), so every input
+// byte is read from memory once; longer rows are read twice.
+constexpr int kRowRegs = 4;
+
 __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ w, int H, float eps,
                                                           uint16_t* __restrict__ y, float* __restrict__ rstd) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
   const uint16_t* xr = x + row * H;
+  const bool keep = H <= 256 * 8 * kRowRegs;
+  u32x4 xs[kRowRegs];
   float ss = 0.0f;
-  for (int i = threadIdx.x * 8; i < H; i += 256 * 8) {
+  int it = 0;
+  for (int i = threadIdx.x * 8; i < H; i += 256 * 8, ++it) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(xr + i);
+    if (keep) {
+#pragma unroll
+      for (int j = 0; j < kRowRegs; ++j)
+        if (j == it) xs[j] = q;
+    }
     float f[8];
-    unpack8(*reinterpret_cast<const u32x4*>(xr + i), f);
+    unpack8(q, f);
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
   }
   ss = block_sum(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)H + eps);
-  for (int i = threadIdx.x * 8; i < H; i += 256 * 8) {
+  it = 0;
+  for (int i = threadIdx.x * 8; i < H; i += 256 * 8, ++it) {
+    u32x4 q;
+    if (keep) {
+#pragma unroll
+      for (int j = 0; j < kRowRegs; ++j)
+        if (j == it) q = xs[j];
+    } else {
+      q = *reinterpret_cast<const u32x4*>(xr + i);
+    }
     float f[8], g[8];
-    unpack8(*reinterpret_cast<const u32x4*>(xr + i), f);
+    unpack8(q, f);
     unpack8(*reinterpret_cast<const u32x4*>(w + i), g);
 #pragma unroll
     for (int e = 0; e < 8; ++e) f[e] = f[e] * r * g[e];
@@ -61,23 +84,43 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const uint16_t* __rest
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
   const int64_t base = row * H;
+  const bool keep = H <= 256 * 8 * kRowRegs;
+  u32x4 as[kRowRegs], cs[kRowRegs];
   float dot = 0.0f;
-  for (int i = threadIdx.x * 8; i < H; i += 256 * 8) {
+  int it = 0;
+  for (int i = threadIdx.x * 8; i < H; i += 256 * 8, ++it) {
+    const u32x4 qa = *reinterpret_cast<const u32x4*>(dy + base + i);
+    const u32x4 qc = *reinterpret_cast<const u32x4*>(x + base + i);
+    if (keep) {
+#pragma unroll
+      for (int j = 0; j < kRowRegs; ++j)
+        if (j == it) { as[j] = qa; cs[j] = qc; }
+    }
     float a[8], b[8], c[8];
-    unpack8(*reinterpret_cast<const u32x4*>(dy + base + i), a);
+    unpack8(qa, a);
     unpack8(*reinterpret_cast<const u32x4*>(w + i), b);
-    unpack8(*reinterpret_cast<const u32x4*>(x + base + i), c);
+    unpack8(qc, c);
 #pragma unroll
     for (int e = 0; e < 8; ++e) dot = fmaf(a[e] * b[e], c[e], dot);
   }
   dot = block_sum(dot, red);
   const float r = rstd[row];
   const float k = r * r * r * dot / (float)H;
-  for (int i = threadIdx.x * 8; i < H; i += 256 * 8) {
+  it = 0;
+  for (int i = threadIdx.x * 8; i < H; i += 256 * 8, ++it) {
+    u32x4 qa, qc;
+    if (keep) {
+#pragma unroll
+      for (int j = 0; j < kRowRegs; ++j)
+        if (j == it) { qa = as[j]; qc = cs[j]; }
+    } else {
+      qa = *reinterpret_cast<const u32x4*>(dy + base + i);
+      qc = *reinterpret_cast<const u32x4*>(x + base + i);
+    }
     float a[8], b[8], c[8], o[8];
-    unpack8(*reinterpret_cast<const u32x4*>(dy + base + i), a);
+    unpack8(qa, a);
     unpack8(*reinterpret_cast<const u32x4*>(w + i), b);
-    unpack8(*reinterpret_cast<const u32x4*>(x + base + i), c);
+    unpack8(qc, c);
     if (resid != nullptr) unpack8(*reinterpret_cast<const u32x4*>(resid + base + i), o);
     else {
 #pragma unroll
@@ -138,19 +181,38 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
   for (int i = threadIdx.x; i < H / 8; i += 256) dst[i] = src[i];
 }
 
-// Log-sum-exp of one row of V logits over a 256-thread workgroup: a running
-// (max, sum of exp) per thread, merged lane -> wave -> workgroup in a fixed order.
+// Cross-entropy rows: one 1024-thread workgroup per row of V fp32 logits (16
+// waves per row keep enough loads in flight; a row of the 128256-entry
+// vocabulary is 501 KB), 16-byte loads when the row is 16-byte aligned.
+constexpr int kCeThreads = 1024;
+
+__device__ __forceinline__ void lse_push(float x, float& m, float& s) {
+  if (x > m) {
+    s = s * __expf(m - x) + 1.0f;
+    m = x;
+  } else {
+    s += __expf(x - m);
+  }
+}
+
+// Log-sum-exp of one row: a running (max, sum of exp) per thread, merged
+// lane -> wave -> workgroup in a fixed order.
 __device__ __forceinline__ float row_lse(const float* __restrict__ z, int V) {
-  __shared__ float sm[4], ss[4];
+  __shared__ float sm[kCeThreads / 64], ss[kCeThreads / 64];
   float m = -INFINITY, s = 0.0f;
-  for (int v = threadIdx.x; v < V; v += 256) {
-    const float x = z[v];
-    if (x > m) {
-      s = s * __expf(m - x) + 1.0f;
-      m = x;
-    } else {
-      s += __expf(x - m);
+  if ((V & 3) == 0 && (reinterpret_cast<uintptr_t>(z) & 15) == 0) {
+    const float4* z4 = reinterpret_cast<const float4*>(z);
+    for (int v = threadIdx.x; v < V / 4; v += kCeThreads) {
+      const float4 x = z4[v];
+      const float mx = fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w));
+      if (mx > m) {
+        s *= __expf(m - mx);
+        m = mx;
+      }
+      s += (__expf(x.x - m) + __expf(x.y - m)) + (__expf(x.z - m) + __expf(x.w - m));
     }
+  } else {
+    for (int v = threadIdx.x; v < V; v += kCeThreads) lse_push(z[v], m, s);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -162,11 +224,39 @@ __device__ __forceinline__ float row_lse(const float* __restrict__ z, int V) {
   const int wid = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) { sm[wid] = m; ss[wid] = s; }
   __syncthreads();
-  const float M = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+  float M = sm[0];
+#pragma unroll
+  for (int w = 1; w < kCeThreads / 64; ++w) M = fmaxf(M, sm[w]);
   float S = 0.0f;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) S += ss[w] * __expf(sm[w] - M);
+  for (int w = 0; w < kCeThreads / 64; ++w) S += ss[w] * __expf(sm[w] - M);
   return M + __logf(S);
+}
+
+// d[v] = bf16(c * (exp(z[v] - lse) - [v == label])) over one row, or zeros
+// when the row has no label; 8-byte stores when the rows are aligned.
+__device__ __forceinline__ void grad_row(const float* __restrict__ z, int V, float lse, int label, bool valid,
+                                         float c, uint16_t* __restrict__ d) {
+  if ((V & 3) == 0 && (reinterpret_cast<uintptr_t>(z) & 15) == 0 && (reinterpret_cast<uintptr_t>(d) & 7) == 0) {
+    const float4* z4 = reinterpret_cast<const float4*>(z);
+    u32x2* d4 = reinterpret_cast<u32x2*>(d);
+    for (int v = threadIdx.x; v < V / 4; v += kCeThreads) {
+      float g[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (valid) {
+        const float4 x = z4[v];
+        const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) g[e] = (__expf(xs[e] - lse) - (4 * v + e == label ? 1.0f : 0.0f)) * c;
+      }
+      d4[v] = u32x2{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
+    }
+  } else {
+    for (int v = threadIdx.x; v < V; v += kCeThreads) {
+      float g = 0.0f;
+      if (valid) g = (__expf(z[v] - lse) - (v == label ? 1.0f : 0.0f)) * c;
+      d[v] = f32_to_bf16(g);
+    }
+  }
 }
 
 // Next-token label of row t (the id one position on) and whether row t has
@@ -178,26 +268,22 @@ __device__ __forceinline__ int row_label(const int32_t* __restrict__ ids, int64_
 }
 
 // One workgroup per row of logits: the loss term and softmax minus one-hot, scaled.
-__global__ __launch_bounds__(256) void ce_row_kernel(const float* __restrict__ logits, const int32_t* __restrict__ ids,
-                                                     int seq, int V, float coef, uint16_t* __restrict__ dlogits,
-                                                     float* __restrict__ row_loss) {
+__global__ __launch_bounds__(kCeThreads) void ce_row_kernel(const float* __restrict__ logits,
+                                                            const int32_t* __restrict__ ids, int seq, int V,
+                                                            float coef, uint16_t* __restrict__ dlogits,
+                                                            float* __restrict__ row_loss) {
   const int64_t t = blockIdx.x;
   const float* z = logits + t * V;
   bool valid;
   const int label = row_label(ids, t, seq, V, valid);
   const float lse = row_lse(z, V);
   if (threadIdx.x == 0) row_loss[t] = valid ? (lse - z[label]) : 0.0f;
-  uint16_t* d = dlogits + t * V;
-  for (int v = threadIdx.x; v < V; v += 256) {
-    float g = 0.0f;
-    if (valid) g = (__expf(z[v] - lse) - (v == label ? 1.0f : 0.0f)) * coef;
-    d[v] = f32_to_bf16(g);
-  }
+  grad_row(z, V, lse, label, valid, coef, dlogits + t * V);
 }
 
 // Row statistics for sequence log-probabilities: lse[t] and the log-probability
 // of row t's label (0 for unlabelled rows).
-__global__ __launch_bounds__(256) void ce_stats_kernel(const float* __restrict__ logits,
+__global__ __launch_bounds__(kCeThreads) void ce_stats_kernel(const float* __restrict__ logits,
                                                        const int32_t* __restrict__ ids, int seq, int V,
                                                        float* __restrict__ lse_out, float* __restrict__ row_logp) {
   const int64_t t = blockIdx.x;
@@ -242,23 +328,15 @@ __global__ void dpo_coef_kernel(const float* __restrict__ lp, const float* __res
 }
 
 // dlogits of a sequence-level loss: coef[sequence] (softmax - onehot) on labelled rows.
-__global__ __launch_bounds__(256) void ce_grad_kernel(const float* __restrict__ logits,
-                                                      const int32_t* __restrict__ ids,
-                                                      const float* __restrict__ lse_in,
-                                                      const float* __restrict__ coef, int seq, int V,
-                                                      uint16_t* __restrict__ dlogits) {
+__global__ __launch_bounds__(kCeThreads) void ce_grad_kernel(const float* __restrict__ logits,
+                                                             const int32_t* __restrict__ ids,
+                                                             const float* __restrict__ lse_in,
+                                                             const float* __restrict__ coef, int seq, int V,
+                                                             uint16_t* __restrict__ dlogits) {
   const int64_t t = blockIdx.x;
-  const float* z = logits + t * V;
   bool valid;
   const int label = row_label(ids, t, seq, V, valid);
-  const float lse = lse_in[t];
-  const float c = coef[t / seq];
-  uint16_t* d = dlogits + t * V;
-  for (int v = threadIdx.x; v < V; v += 256) {
-    float g = 0.0f;
-    if (valid) g = (__expf(z[v] - lse) - (v == label ? 1.0f : 0.0f)) * c;
-    d[v] = f32_to_bf16(g);
-  }
+  grad_row(logits + t * V, V, lse_in[t], label, valid, coef[t / seq], dlogits + t * V);
 }
 
 __global__ __launch_bounds__(256) void mean_kernel(const float* __restrict__ x, int n, float inv, float* out) {
@@ -317,7 +395,7 @@ hipError_t cross_entropy(const float* logits, const int32_t* ids, int batch, int
   const int T = batch * seq;
   const int count = batch * (seq - 1);
   const float coef = count > 0 ? loss_scale / (float)count : 0.0f;
-  hipLaunchKernelGGL(ce_row_kernel, dim3(T), dim3(256), 0, s, logits, ids, seq, V, coef, dlogits, row_loss);
+  hipLaunchKernelGGL(ce_row_kernel, dim3(T), dim3(kCeThreads), 0, s, logits, ids, seq, V, coef, dlogits, row_loss);
   hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(256), 0, s, row_loss, T, count > 0 ? 1.0f / (float)count : 0.0f,
                      loss);
   return hipGetLastError();
@@ -327,7 +405,7 @@ hipError_t seq_logprobs(const float* logits, const int32_t* ids, int batch, int 
                         float* row_logp, float* lp, hipStream_t s) {
   const int T = batch * seq;
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(ce_stats_kernel, dim3(T), dim3(256), 0, s, logits, ids, seq, V, lse, row_logp);
+  hipLaunchKernelGGL(ce_stats_kernel, dim3(T), dim3(kCeThreads), 0, s, logits, ids, seq, V, lse, row_logp);
   hipLaunchKernelGGL(seq_sum_kernel, dim3(batch), dim3(256), 0, s, row_logp, seq, lp);
   return hipGetLastError();
 }
@@ -338,7 +416,8 @@ hipError_t dpo_head_grad(const float* logits, const int32_t* ids, const float* l
   const int P = batch / 2;
   hipLaunchKernelGGL(dpo_coef_kernel, dim3(1), dim3(64), 0, s, lp_pi, lp_ref, P, beta, loss_scale, coef, loss);
   if (dlogits != nullptr)
-    hipLaunchKernelGGL(ce_grad_kernel, dim3(batch * seq), dim3(256), 0, s, logits, ids, lse, coef, seq, V, dlogits);
+    hipLaunchKernelGGL(ce_grad_kernel, dim3(batch * seq), dim3(kCeThreads), 0, s, logits, ids, lse, coef, seq, V,
+                       dlogits);
   return hipGetLastError();
 }
 

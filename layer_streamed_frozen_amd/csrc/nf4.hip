@@ -9,6 +9,8 @@
 // Dequantise: a thread owns 32 consecutive elements (16 packed bytes, one
 // absmax) and decodes them with the same table routine the GEMMs use, so the
 // bytes this kernel writes are exactly the bf16 weights the GEMMs multiply.
+// The output goes through LDS so that every store instruction of a wave
+// writes 1 KB of contiguous memory.
 #include "common.h"
 #include "kernels.h"
 
@@ -62,18 +64,42 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const float* __restri
   }
 }
 
+// A thread decodes 32 weights (64 output bytes) into LDS; the wave then writes
+// its 4 KB of output with four fully contiguous 16-byte-per-lane stores.
+__device__ __forceinline__ void stage_and_store(const uint32_t (&o)[16], bool live, int64_t base, int64_t nunits,
+                                                u32x4* __restrict__ out16, u32x4* stage) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (live) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) stage[tid * 4 + k] = u32x4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = k * 64 + lane;             // 16-byte chunk of this wave's output
+    const int64_t unit = base + wv * 64 + (c >> 2);
+    if (unit < nunits) out16[(base + wv * 64) * 4 + c] = stage[wv * 256 + c];
+  }
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(256) void nf4_dequantize_kernel(const uint8_t* __restrict__ packed,
                                                              const float* __restrict__ absmax, int64_t nunits,
                                                              uint16_t* __restrict__ out) {
-  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < nunits; u += (int64_t)gridDim.x * blockDim.x) {
-    const u32x4 q = *reinterpret_cast<const u32x4*>(packed + u * 16);
-    const Nf4Table t = nf4_table(absmax[u >> 1]);
-    uint32_t o[4];
-    u32x4* dst = reinterpret_cast<u32x4*>(out + u * 32);
-    nf4_decode8(t, q.x, o); dst[0] = u32x4{o[0], o[1], o[2], o[3]};
-    nf4_decode8(t, q.y, o); dst[1] = u32x4{o[0], o[1], o[2], o[3]};
-    nf4_decode8(t, q.z, o); dst[2] = u32x4{o[0], o[1], o[2], o[3]};
-    nf4_decode8(t, q.w, o); dst[3] = u32x4{o[0], o[1], o[2], o[3]};
+  __shared__ u32x4 stage[256 * 4];
+  for (int64_t base = (int64_t)blockIdx.x * 256; base < nunits; base += (int64_t)gridDim.x * 256) {
+    const int64_t u = base + threadIdx.x;
+    const bool live = u < nunits;
+    uint32_t o[16] = {};
+    if (live) {
+      const u32x4 q = *reinterpret_cast<const u32x4*>(packed + u * 16);
+      const Nf4Table t = nf4_table(absmax[u >> 1]);
+      nf4_decode8(t, q.x, reinterpret_cast<uint32_t(&)[4]>(o[0]));
+      nf4_decode8(t, q.y, reinterpret_cast<uint32_t(&)[4]>(o[4]));
+      nf4_decode8(t, q.z, reinterpret_cast<uint32_t(&)[4]>(o[8]));
+      nf4_decode8(t, q.w, reinterpret_cast<uint32_t(&)[4]>(o[12]));
+    }
+    stage_and_store(o, live, base, nunits, reinterpret_cast<u32x4*>(out), stage);
   }
 }
 
@@ -113,17 +139,22 @@ __global__ __launch_bounds__(256) void nf4dq_dequantize_kernel(const uint8_t* __
                                                                const uint8_t* __restrict__ absq,
                                                                const float2* __restrict__ s2, int64_t nunits,
                                                                uint16_t* __restrict__ out) {
-  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < nunits; u += (int64_t)gridDim.x * blockDim.x) {
-    const u32x4 q = *reinterpret_cast<const u32x4*>(packed + u * 16);
-    const int64_t blk = u >> 1;
-    const float2 so = s2[blk >> 8];
-    const Nf4Table t = nf4_table(dq_absmax_value(absq[blk], so.x, so.y));
-    uint32_t o[4];
-    u32x4* dst = reinterpret_cast<u32x4*>(out + u * 32);
-    nf4_decode8(t, q.x, o); dst[0] = u32x4{o[0], o[1], o[2], o[3]};
-    nf4_decode8(t, q.y, o); dst[1] = u32x4{o[0], o[1], o[2], o[3]};
-    nf4_decode8(t, q.z, o); dst[2] = u32x4{o[0], o[1], o[2], o[3]};
-    nf4_decode8(t, q.w, o); dst[3] = u32x4{o[0], o[1], o[2], o[3]};
+  __shared__ u32x4 stage[256 * 4];
+  for (int64_t base = (int64_t)blockIdx.x * 256; base < nunits; base += (int64_t)gridDim.x * 256) {
+    const int64_t u = base + threadIdx.x;
+    const bool live = u < nunits;
+    uint32_t o[16] = {};
+    if (live) {
+      const u32x4 q = *reinterpret_cast<const u32x4*>(packed + u * 16);
+      const int64_t blk = u >> 1;
+      const float2 so = s2[blk >> 8];
+      const Nf4Table t = nf4_table(dq_absmax_value(absq[blk], so.x, so.y));
+      nf4_decode8(t, q.x, reinterpret_cast<uint32_t(&)[4]>(o[0]));
+      nf4_decode8(t, q.y, reinterpret_cast<uint32_t(&)[4]>(o[4]));
+      nf4_decode8(t, q.z, reinterpret_cast<uint32_t(&)[4]>(o[8]));
+      nf4_decode8(t, q.w, reinterpret_cast<uint32_t(&)[4]>(o[12]));
+    }
+    stage_and_store(o, live, base, nunits, reinterpret_cast<u32x4*>(out), stage);
   }
 }
 
