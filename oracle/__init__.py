@@ -16,7 +16,8 @@ obviously in NumPy:
                forward and hand-derived backward, fp64 by default.
 * ``dpo``    - the preference loss whose reference model is the same frozen
                base with the adapters switched off.
-* ``adamw``  - the AdamW update of the trainable LoRA tensors.
+* ``optim``  - the AdamW update of the trainable LoRA tensors (fp32 state).
+* ``optim8`` - the same update with 8-bit block-wise quantised moment states.
 
 Streaming and per-layer recomputation change where the frozen weights live,
 never what is computed (news article "aizxs.com/ai-learning/13312.html",
