@@ -1,6 +1,7 @@
 """Throughput of the streamed NF4 + LoRA training step on one MI355X.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload stack1|stack4|dpo|dpo-unfused]
+                    [--format nf4|nf4dq|bf16] [--optimizer adamw|adamw8] [--lora-targets all|qv]
 
 Workload (default "stack1"): 32 Llama-3.1-8B-shaped decoder layers (hidden
 4096, intermediate 14336, 32 query / 8 kv heads of 128, RoPE theta 500000),
@@ -75,6 +76,10 @@ def parse():
     p.add_argument("--timing", choices=["dominant", "all"], default="dominant",
                    help="events in the timed steps: around the gate|up forward GEMM only, or around every "
                         "kernel class and copy")
+    p.add_argument("--optimizer", choices=["adamw", "adamw8"], default="adamw",
+                   help="adamw8: AdamW with 8-bit block-wise moment states (the pages' paged_adamw_8bit)")
+    p.add_argument("--lora-targets", choices=["all", "qv"], default="all",
+                   help="qv: adapters on q and v only (the pages' published configuration)")
     p.add_argument("--keep-activations", action="store_true",
                    help="keep every layer's forward intermediates in HBM and skip the recompute in the backward "
                         "walk (each layer is still read twice)")
@@ -204,7 +209,8 @@ def main():
     store = S.Store(shape, L, fmt=fmt, resident=False, pinned=True, weights_fn=weights)
     log(f"store built in {time.time() - t0:.1f}s: {store.stride * L / 1e9:.3f} GB pinned, "
         f"blob {store.blob_bytes()} B")
-    lora = S.LoraSet(shape, L)
+    targets = S.PROJ if args.lora_targets == "all" else ("q", "v")
+    lora = S.LoraSet(shape, L, targets=targets)
     H = shape.hidden
     emb = torch.from_numpy(synth.bf16_exact(synth.normal("embed", (V, H), 1.0))[1].view(np.int16)) \
         .view(torch.bfloat16).cuda()
@@ -227,7 +233,7 @@ def main():
         flags = B.STACK_TIME_KERNEL(dom_k)
     stack = S.Stack(shape, store, batch, seq, V, flags=flags, keep_activations=args.keep_activations)
     arr = lora.array()
-    opt = S.AdamW(lora, lr=2e-4)
+    opt = (S.AdamW8 if args.optimizer == "adamw8" else S.AdamW)(lora, lr=2e-4)
     torch.cuda.synchronize()
 
     def step(stk):
@@ -274,7 +280,8 @@ def main():
         ach = flops["gate_up"] / avg / 1e12
         # The counters and the algorithmic bytes belong to the configuration they
         # were taken on: NF4 with fp32 absmax, 512 tokens, recomputing backward.
-        measured_cfg = args.format == "nf4" and T == 512 and not args.keep_activations
+        measured_cfg = (args.format == "nf4" and T == 512 and not args.keep_activations
+                        and args.lora_targets == "all")
         same_src = gemm_src_hash() == GATE_UP_TRAFFIC_SRC
         base = {"nf4": "NF4", "nf4dq": "double-quantised NF4", "bf16": "bf16"}[args.format]
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -343,14 +350,16 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded random weights and token ids)",
         "config": {"workload": (f"streamed {L}-layer Llama-3.1-8B-shaped stack, {base_desc}, "
-                                f"LoRA r16 on q,k,v,o,gate,up,down, vocab {V}, "
+                                f"LoRA r16 on {','.join(targets)}, vocab {V}, "
                                 + (f"DPO beta 0.1 over {batch // 2} chosen/rejected pairs x seq {seq}, "
                                    f"reference = adapters off, "
                                    + ("fused into the policy's layer visit" if args.workload == "dpo"
                                       else "separate reference pass") if dpo else
                                    f"batch {batch} x seq {seq}, accumulation {accum}")),
                    "global_batch": batch * accum, "seq_len": seq, "layers": L, "vocab": V,
-                   "optimizer": "AdamW lr 2e-4, fp32 moments, once per step",
+                   "optimizer": ("AdamW lr 2e-4, fp32 moments, once per step" if args.optimizer == "adamw" else
+                                 "AdamW lr 2e-4, 8-bit block-wise moments (blocks of 2048, dynamic code), "
+                                 "once per step"),
                    "backward": ("forward intermediates kept in HBM, no recompute" if args.keep_activations
                                 else "per-layer recompute from the checkpoint"),
                    "parallelism": "single GPU"},

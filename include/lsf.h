@@ -340,8 +340,8 @@ LSF_API lsf_status dpo_stack_step(lsf_stack* st, const lsf_dpo_io* io);
 /* ------------------------------------------------------------ optimizer --
  * [TUTORIAL] "step 2: one YAML" trains the adapters with an Adam-family
  * optimizer with decoupled weight decay at lr 2e-4; [NEWS] keeps the adapters,
- * their gradients and the optimizer state on the GPU.  AdamW (fp32 state; the
- * pages' 8-bit paged state is not built) over ONE flat fp32 array of n values:
+ * their gradients and the optimizer state on the GPU.  AdamW (fp32 state here;
+ * adamw8_step below keeps the moments in 8 bits) over ONE flat fp32 array of n values:
  * a caller that lays every adapter A and B of the stack end to end (and their
  * gradients likewise) updates all of them with one call.  For step t >= 1:
  *   g <- g * min(1, max_grad_norm / (||g||_2 + 1e-6))   when max_grad_norm > 0
@@ -367,6 +367,31 @@ LSF_API size_t adamw_workspace_bytes(void);
 LSF_API lsf_status adamw_step(float* param, const float* grad, float* m, float* v, int64_t n,
                               const lsf_adamw_cfg* cfg, float* grad_norm, void* ws, size_t ws_bytes,
                               lsf_stream stream);
+
+/* [TUTORIAL] "step 2: one YAML" names the optimizer paged_adamw_8bit.  The
+ * same AdamW update with the two moments stored between steps in 8 bits, as in
+ * the published block-wise 8-bit optimizer method: blocks of 2048 consecutive
+ * values, one fp32 absmax per block and moment, and each value stored as the
+ * nearest entry (a tie to the smaller) of a fixed code after division by the
+ * absmax.  Code values: 0 and +-(0.1 + 0.9 (j + 1) / 2^F) / 10^E, where E is
+ * the number of zero bits after the sign, then an indicator bit, then F
+ * fraction bits holding j; m uses 7 magnitude bits (F = 6 - E, 255 values,
+ * stored as int8: the entry's position relative to 0 in the sorted code), v
+ * uses 8 (F = 7 - E, 256 values, stored as uint8: the position in the sorted
+ * code).  Each step dequantises, updates in fp32 exactly as adamw_step
+ * (every operation rounded, no fused multiply-add; beta^t by repeated
+ * multiplication), then re-quantises with the new block maxima.  Zeroed codes
+ * and absmax are the zero state.  "Paged" (spilling state to host memory under
+ * memory pressure) has no counterpart: the state is resident.
+ * param, grad: device fp32 [n], 16-byte aligned; m_codes, v_codes: device [n],
+ * 8-byte aligned; m_absmax, v_absmax: device fp32 [adamw8_state_blocks(n)];
+ * all updated in place except grad.  grad_norm, cfg, ws and errors as
+ * adamw_step (ws: adamw8_workspace_bytes()). */
+LSF_API int64_t adamw8_state_blocks(int64_t n);
+LSF_API size_t adamw8_workspace_bytes(void);
+LSF_API lsf_status adamw8_step(float* param, const float* grad, int8_t* m_codes, uint8_t* v_codes,
+                               float* m_absmax, float* v_absmax, int64_t n, const lsf_adamw_cfg* cfg,
+                               float* grad_norm, void* ws, size_t ws_bytes, lsf_stream stream);
 
 /* Kernel classes timed with HIP events under LSF_STACK_TIMING or
  * LSF_STACK_KERNEL_TIMING (index into

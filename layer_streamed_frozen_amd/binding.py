@@ -137,6 +137,10 @@ _PROTOS = {
     "adamw_workspace_bytes": (c_size_t, []),
     "adamw_step": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, ctypes.POINTER(AdamwCfg), c_void_p,
                              c_void_p, c_size_t, c_void_p]),
+    "adamw8_state_blocks": (c_int64, [c_int64]),
+    "adamw8_workspace_bytes": (c_size_t, []),
+    "adamw8_step": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
+                              ctypes.POINTER(AdamwCfg), c_void_p, c_void_p, c_size_t, c_void_p]),
 }
 
 _LIB = None
@@ -319,6 +323,24 @@ def adamw_step(param, grad, m, v, cfg, grad_norm, ws, n=None, stream=None):
     check(lib().adamw_step(ptr(param), ptr(grad), ptr(m), ptr(v), n, ctypes.byref(cfg),
                            ptr(grad_norm) if grad_norm is not None else None, ptr(ws),
                            ws.numel() * ws.element_size(), stream_ptr(stream)))
+
+
+def adamw8_state_blocks(n):
+    return int(lib().adamw8_state_blocks(n))
+
+
+def adamw8_workspace_bytes():
+    return lib().adamw8_workspace_bytes()
+
+
+def adamw8_step(param, grad, m_codes, v_codes, m_absmax, v_absmax, cfg, grad_norm, ws, n=None, stream=None):
+    """AdamW with 8-bit moment states over flat device tensors: param, grad
+    fp32 [n]; m_codes int8 [n]; v_codes uint8 [n]; m_absmax, v_absmax fp32
+    [adamw8_state_blocks(n)]."""
+    n = param.numel() if n is None else n
+    check(lib().adamw8_step(ptr(param), ptr(grad), ptr(m_codes), ptr(v_codes), ptr(m_absmax), ptr(v_absmax), n,
+                            ctypes.byref(cfg), ptr(grad_norm) if grad_norm is not None else None, ptr(ws),
+                            ws.numel() * ws.element_size(), stream_ptr(stream)))
 
 
 def stack_activation_bytes(cfg, n_layers):

@@ -862,8 +862,8 @@ lsf_status dpo_stack_step(lsf_stack* st, const lsf_dpo_io* io) {
 
 size_t adamw_workspace_bytes(void) { return adamw_ws_bytes(); }
 
-lsf_status adamw_step(float* param, const float* grad, float* m, float* v, int64_t n, const lsf_adamw_cfg* cfg,
-                      float* grad_norm, void* ws, size_t ws_bytes, lsf_stream stream) {
+namespace {
+lsf_status check_adamw_cfg(const lsf_adamw_cfg* cfg, int64_t n) {
   if (cfg == nullptr) return fail(LSF_ERR_INVALID_ARG, "cfg is NULL");
   if (n < 0) return fail(LSF_ERR_INVALID_ARG, "n must be >= 0");
   const lsf_adamw_cfg& c = *cfg;
@@ -876,6 +876,15 @@ lsf_status adamw_step(float* param, const float* grad, float* m, float* v, int64
   if (!(c.max_grad_norm >= 0.0f) || !std::isfinite(c.max_grad_norm))
     return fail(LSF_ERR_INVALID_ARG, "max_grad_norm must be finite and >= 0");
   if (c.step < 1) return fail(LSF_ERR_INVALID_ARG, "step must be >= 1 (got %d)", c.step);
+  return LSF_OK;
+}
+}  // namespace
+
+lsf_status adamw_step(float* param, const float* grad, float* m, float* v, int64_t n, const lsf_adamw_cfg* cfg,
+                      float* grad_norm, void* ws, size_t ws_bytes, lsf_stream stream) {
+  lsf_status cs = check_adamw_cfg(cfg, n);
+  if (cs != LSF_OK) return cs;
+  const lsf_adamw_cfg& c = *cfg;
   if (n == 0) return ok();
   lsf_status s;
   if ((s = check_dev(param, "param")) || (s = check_dev(grad, "grad")) || (s = check_dev(m, "m")) ||
@@ -886,6 +895,30 @@ lsf_status adamw_step(float* param, const float* grad, float* m, float* v, int64
     return fail(LSF_ERR_WORKSPACE, "workspace too small or unaligned (need %zu bytes)", adamw_ws_bytes());
   HIPCK(adamw_update(param, grad, m, v, n, c.lr, c.beta1, c.beta2, c.eps, c.weight_decay, c.max_grad_norm, c.step,
                      grad_norm, static_cast<float*>(ws), S(stream)));
+  return ok();
+}
+
+int64_t adamw8_state_blocks(int64_t n) { return n > 0 ? adamw8_blocks(n) : 0; }
+size_t adamw8_workspace_bytes(void) { return adamw8_ws_bytes(); }
+
+lsf_status adamw8_step(float* param, const float* grad, int8_t* m_codes, uint8_t* v_codes, float* m_absmax,
+                       float* v_absmax, int64_t n, const lsf_adamw_cfg* cfg, float* grad_norm, void* ws,
+                       size_t ws_bytes, lsf_stream stream) {
+  lsf_status cs = check_adamw_cfg(cfg, n);
+  if (cs != LSF_OK) return cs;
+  const lsf_adamw_cfg& c = *cfg;
+  if (n == 0) return ok();
+  lsf_status s;
+  if ((s = check_dev(param, "param")) || (s = check_dev(grad, "grad"))) return s;
+  if (m_codes == nullptr || v_codes == nullptr || m_absmax == nullptr || v_absmax == nullptr)
+    return fail(LSF_ERR_INVALID_ARG, "state pointer is NULL");
+  if (!aligned(m_codes, 8) || !aligned(v_codes, 8) || !aligned(m_absmax, 4) || !aligned(v_absmax, 4))
+    return fail(LSF_ERR_ALIGN, "codes must be 8-byte and absmax 4-byte aligned");
+  if (grad_norm != nullptr && !aligned(grad_norm, 4)) return fail(LSF_ERR_ALIGN, "grad_norm is not aligned");
+  if (ws == nullptr || ws_bytes < adamw8_ws_bytes() || !aligned(ws, 16))
+    return fail(LSF_ERR_WORKSPACE, "workspace too small or unaligned (need %zu bytes)", adamw8_ws_bytes());
+  HIPCK(adamw8_update(param, grad, m_codes, v_codes, m_absmax, v_absmax, n, c.lr, c.beta1, c.beta2, c.eps,
+                      c.weight_decay, c.max_grad_norm, c.step, grad_norm, static_cast<float*>(ws), S(stream)));
   return ok();
 }
 

@@ -153,6 +153,13 @@ hipError_t dpo_head_grad(const float* logits, const int32_t* ids, const float* l
 // Clips the gradient to max_grad_norm (> 0) by its global L2 norm first; writes
 // that norm to grad_norm when it is not NULL.  ws: adamw_ws_bytes() of device memory.
 size_t adamw_ws_bytes();
+// The same update with 8-bit moment states: int8 codes qm, uint8 codes qv and
+// one fp32 absmax per 2048 values for each (adamw8_blocks(n) entries).
+size_t adamw8_ws_bytes();
+int64_t adamw8_blocks(int64_t n);
+hipError_t adamw8_update(float* p, const float* g, int8_t* qm, uint8_t* qv, float* am, float* av, int64_t n,
+                         float lr, float beta1, float beta2, float eps, float weight_decay, float max_grad_norm,
+                         int step, float* grad_norm, float* ws, hipStream_t s);
 hipError_t adamw_update(float* p, const float* g, float* m, float* v, int64_t n, float lr, float beta1, float beta2,
                         float eps, float weight_decay, float max_grad_norm, int step, float* grad_norm, float* ws,
                         hipStream_t s);

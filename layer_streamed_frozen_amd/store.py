@@ -228,6 +228,30 @@ class AdamW:
                      stream=stream)
 
 
+class AdamW8:
+    """AdamW with 8-bit block-wise quantised moments (the pages'
+    paged_adamw_8bit, resident) over a LoraSet's flat parameter arena."""
+
+    def __init__(self, lora, lr=2e-4, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0, max_grad_norm=0.0):
+        self.lora = lora
+        self.cfg = B.AdamwCfg(lr=lr, beta1=betas[0], beta2=betas[1], eps=eps, weight_decay=weight_decay,
+                              max_grad_norm=max_grad_norm, step=0)
+        n = lora.params.numel()
+        dev = lora.params.device
+        nb = B.adamw8_state_blocks(n)
+        self.m_codes = torch.zeros(n, dtype=torch.int8, device=dev)
+        self.v_codes = torch.zeros(n, dtype=torch.uint8, device=dev)
+        self.m_absmax = torch.zeros(nb, dtype=torch.float32, device=dev)
+        self.v_absmax = torch.zeros(nb, dtype=torch.float32, device=dev)
+        self.ws = torch.empty(B.adamw8_workspace_bytes(), dtype=torch.uint8, device=dev)
+        self.grad_norm = torch.zeros(1, dtype=torch.float32, device=dev)
+
+    def step(self, stream=None):
+        self.cfg.step += 1
+        B.adamw8_step(self.lora.params, self.lora.grads, self.m_codes, self.v_codes, self.m_absmax, self.v_absmax,
+                      self.cfg, self.grad_norm, self.ws, stream=stream)
+
+
 class Stack:
     """A streamed stack: store + two device buffers + streams + handle."""
 
