@@ -277,7 +277,7 @@ LSF_API lsf_status stack_destroy(lsf_stack* st);
 #define LSF_MODE_STREAMED 0x0u   /* weights come through the two buffers */
 #define LSF_MODE_RESIDENT 0x1u   /* weights read in place from resident_store */
 #define LSF_MODE_FWD_ONLY 0x2u   /* stop after the loss (no backward) */
-#define LSF_MODE_ZERO_GRADS 0x4u /* zero every dA/dB before accumulating */
+#define LSF_MODE_ZERO_GRADS 0x4u /* zero every dA/dB before accumulating (the first write of each stores) */
 /* Keep every layer's forward intermediates in io->act and skip the recompute
  * in the backward walk.  Each layer is still read twice (the input gradient
  * needs the frozen weight); the recompute is traded for

@@ -9,6 +9,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <algorithm>
 #include <vector>
 
 #include "../../include/lsf.h"
@@ -687,11 +688,33 @@ lsf_status run_step(lsf_stack* st, const lsf_stack_io* io, const lsf_dpo_io* dpo
   const size_t act = (size_t)T * H;
   st->stats.steps += 1;
 
-  if (io->mode & LSF_MODE_ZERO_GRADS) {
+  // LSF_MODE_ZERO_GRADS: the backward of every enabled layer stores its dA, dB
+  // (overwrite) instead of adding to them; only gradients no backward will
+  // write (forward-only calls, disabled layers) are zeroed here.
+  // Gradient arrays shared between layers (tied adapters) accumulate over
+  // the step, so they take the zero-then-add path.
+  const bool zero_grads = (io->mode & LSF_MODE_ZERO_GRADS) != 0;
+  bool overwrite = zero_grads && (io->mode & LSF_MODE_FWD_ONLY) == 0;
+  if (overwrite) {
+    std::vector<const float*> seen;
+    for (int i = 0; i < L; ++i) {
+      const lsf_lora_proj* p = &io->lora[i].q;
+      for (int k = 0; k < 7; ++k) {
+        if (p[k].A == nullptr) continue;
+        if (p[k].dA) seen.push_back(p[k].dA);
+        if (p[k].dB) seen.push_back(p[k].dB);
+      }
+    }
+    std::sort(seen.begin(), seen.end());
+    overwrite = std::adjacent_find(seen.begin(), seen.end()) == seen.end();
+  }
+  w.layer.grads_overwrite = overwrite;
+  if (zero_grads) {
     const int64_t Dq = (int64_t)c.n_heads * c.head_dim, Dk = (int64_t)c.n_kv_heads * c.head_dim;
     const int64_t in[7] = {c.hidden, c.hidden, c.hidden, Dq, c.hidden, c.hidden, c.intermediate};
     const int64_t outd[7] = {Dq, Dk, Dk, c.hidden, c.intermediate, c.intermediate, c.hidden};
     for (int i = 0; i < L; ++i) {
+      if (overwrite && io->lora[i].enabled) continue;
       const lsf_lora_proj* p = &io->lora[i].q;
       for (int k = 0; k < 7; ++k) {
         if (p[k].A == nullptr) continue;

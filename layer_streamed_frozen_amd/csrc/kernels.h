@@ -119,6 +119,7 @@ struct LoraGradSec {
   float* out = nullptr;
   bool transposed = false;
   float scale = 1.0f;
+  bool overwrite = false;  // out = ... instead of out += ... (the first accumulation)
 };
 // part (part_floats floats of scratch, may be NULL) holds per-token-split
 // partials when the token range is split across workgroups.

@@ -314,12 +314,12 @@ hipError_t lora_grads(int T, int r, float sc, int nsec, const lsf_lora_proj* con
     if (p[i]->dA) {
       LoraGradSec& q = ga[na++];
       q.P = dU; q.ldp = nsec * r; q.pcol0 = i * r; q.Q = X; q.ldq = ldx; q.qoff = 0; q.nq = nx;
-      q.out = p[i]->dA; q.transposed = false; q.scale = 1.0f;
+      q.out = p[i]->dA; q.transposed = false; q.scale = 1.0f; q.overwrite = ws.grads_overwrite;
     }
     if (p[i]->dB) {
       LoraGradSec& q = gb[nb++];
       q.P = U; q.ldp = nsec * r; q.pcol0 = i * r; q.Q = dY; q.ldq = ldy; q.qoff = yoff[i]; q.nq = ny[i];
-      q.out = p[i]->dB; q.transposed = true; q.scale = sc;
+      q.out = p[i]->dB; q.transposed = true; q.scale = sc; q.overwrite = ws.grads_overwrite;
     }
   }
   CK(lora_grad(ga, na, T, r, ws.part, ws.part_floats, s));

@@ -23,6 +23,7 @@ struct LayerWs {
   float *dU, *attn_scratch, *part;
   size_t part_floats;
   Probe* probe = nullptr;
+  bool grads_overwrite = false;  // the backward stores dA, dB instead of adding to them
   static size_t bytes(const lsf_layer_cfg& c);
   static LayerWs carve(const lsf_layer_cfg& c, void* base);
   // The tensors a forward with save = true leaves for the backward (h1, qkv,

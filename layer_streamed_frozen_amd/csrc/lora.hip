@@ -8,7 +8,8 @@
 // partial products are then summed in a fixed order by a second kernel.
 //
 // lora_grad: the adapter gradients dA = dU^T X and dB = s dY^T U, reductions
-// over the tokens: Out[j, k] += scale * sum_t P[t, j] Q[t, k].  A workgroup
+// over the tokens: Out[j, k] += scale * sum_t P[t, j] Q[t, k] (or = when the
+// section asks to overwrite: the first accumulation of a step).  A workgroup
 // owns 64 columns k, all r rows j and one share of the tokens; each wave takes
 // a quarter of that share in 32-row chunks, staged in LDS so the MFMA operands
 // can run along the token axis (P transposed, Q read down its rows with
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(GradBatch gb, int T, int
       part[(((size_t)blockIdx.z * gridDim.y + blockIdx.y) * R + j) * maxq + k] = v;
     } else {
       float* dst = g.transposed ? g.out + (int64_t)k * R + j : g.out + (int64_t)j * g.nq + k;
-      *dst += g.scale * v;
+      *dst = (g.overwrite ? 0.0f : *dst) + g.scale * v;
     }
   }
 }
@@ -224,7 +225,7 @@ __global__ __launch_bounds__(256) void lora_grad_reduce_kernel(GradBatch gb, int
     for (int u = 0; u < 8; ++u)
       if (u < nz) v += q[u];
     float* dst = g.transposed ? g.out + (int64_t)k * R + j : g.out + (int64_t)j * g.nq + k;
-    *dst += g.scale * v;
+    *dst = (g.overwrite ? 0.0f : *dst) + g.scale * v;
   }
 }
 
