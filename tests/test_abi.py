@@ -133,3 +133,27 @@ def test_gemm_schedule_switch_validates(lib):
     assert lib.gemm_set_wide(2) == B.LSF_ERR_INVALID_ARG
     assert "enable" in lib.lsf_last_error().decode()
     assert B.gemm_wide_launch_count() >= 0
+
+
+def test_optimizer_arguments_are_rejected_before_any_launch(lib):
+    L = lib
+    good = dict(lr=2e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, max_grad_norm=0.0, step=1)
+    for fn, extra in ((L.adamw_step, (None, None)), (L.adamw8_step, (None, None, None, None))):
+        def call(cfg, n=16, ws=None, ws_bytes=0):
+            args = (None, None) + extra + (n, ctypes.byref(cfg) if cfg is not None else None, None, ws, ws_bytes,
+                                           None)
+            return fn(*args)
+        assert call(None) == B.LSF_ERR_INVALID_ARG
+        for field, bad in (("lr", -1.0), ("beta1", 1.0), ("beta2", -0.1), ("eps", 0.0), ("weight_decay", -1.0),
+                           ("max_grad_norm", float("inf")), ("step", 0)):
+            cfg = B.AdamwCfg(**dict(good, **{field: bad}))
+            assert call(cfg) == B.LSF_ERR_INVALID_ARG, field
+        assert call(B.AdamwCfg(**good), n=-1) == B.LSF_ERR_INVALID_ARG
+        assert call(B.AdamwCfg(**good), n=0) == B.LSF_OK  # nothing to do
+        assert call(B.AdamwCfg(**good)) == B.LSF_ERR_INVALID_ARG  # NULL tensors
+    # 8-bit states: misaligned codes, and a workspace that is too small
+    st = L.adamw8_step(16, 16, 3, 16, 16, 16, 16, ctypes.byref(B.AdamwCfg(**good)), None, 16, 64, None)
+    assert st == B.LSF_ERR_ALIGN
+    st = L.adamw8_step(16, 16, 16, 16, 16, 16, 16, ctypes.byref(B.AdamwCfg(**good)), None, 16, 64, None)
+    assert st == B.LSF_ERR_WORKSPACE
+    assert B.adamw8_state_blocks(4097) == 3 and B.adamw8_workspace_bytes() > B.adamw_workspace_bytes()
