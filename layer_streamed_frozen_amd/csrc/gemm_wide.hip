@@ -13,19 +13,22 @@
 //   columns q*64..+64 (8 x 4 fragments of v_mfma_f32_16x16x32_bf16).
 // * 32-deep k tiles in a ring of four LDS stages (32 KB each).  The groups run
 //   half a tile apart (ping-pong): while one group issues its 32 MFMAs, the
-//   other runs its memory phase: wait for the LDS-DMA issued two phases ago,
-//   issue the LDS-DMA of A three tiles ahead (global_load_lds_dwordx4, no
-//   register round trip), load the packed codes of the tile five ahead into
-//   registers, decode its half of the weight tile three ahead into LDS, and
-//   read its own fragments of the current tile.  A workgroup barrier between
-//   the phases swaps the roles.
+//   other runs its memory phase: read its own fragments of the current tile,
+//   wait for the LDS-DMA issued two phases ago, issue the LDS-DMA of A three
+//   tiles ahead (global_load_lds_dwordx4, no register round trip), load the
+//   packed codes of the tile five ahead into registers, and decode its half
+//   of the weight tile three ahead into LDS; the fragment reads complete
+//   meanwhile instead of ending the phase.  A workgroup barrier between the
+//   phases swaps the roles.
 // * Every memory phase issues the same vector-memory operations, the two
 //   LDS-DMA first (past the last tile they repeat it into a stage nobody reads
 //   again), then the code and absmax loads.  Loads complete in issue order, so
-//   `s_waitcnt vmcnt(4)` at the start of a phase means "the LDS-DMA of two
-//   phases ago has landed"; it stays safe if the compiler emits more loads
+//   `s_waitcnt vmcnt(4)` before this phase's own loads means "the LDS-DMA of
+//   two phases ago has landed"; it stays safe if the compiler emits more loads
 //   per phase (it then waits longer) or merges the two register loads into
 //   one (the last operation of the older phase is still a register load).
+//   The fragment reads of tile t may precede that wait: the DMA of tile t was
+//   waited for one phase earlier and two barriers have passed since.
 //   Barriers carry no memory-model fence: a release fence would wait for
 //   every LDS-DMA in flight.
 #include "common.h"
@@ -176,12 +179,9 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g, EpiArgs e
   // The codes of tile t+3 are in `cdec`; tile t+5 loads into `cld`.
   auto step = [&](int t, CodeSet<FMT>& cdec, CodeSet<FMT>& cld) {
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm<phase_vm_ops<FMT>()>();
-    issue_a(min(t + 3, nk - 1), t + 3);
-    __builtin_amdgcn_sched_barrier(0);  // the LDS-DMA goes out before the register loads
-    cld = load_codes<FMT>(g.W, cp, e0, min(t + 5, nk - 1));
-    if (((t + 3) & 1) == 0) tb = nf4_table(cdec.am);  // first half of a 64-block
-    decode_b(t + 3, cdec.c, tb);
+    // Fragment reads first: tile t landed two phases ago, and their LDS
+    // latency then overlaps the loads and the decode instead of ending the
+    // phase (this order also keeps the kernel within 256 registers).
     u32x4 af[8], bf[4];
     {
       const uint16_t* st = lds + (t & 3) * WSTAGE;
@@ -192,6 +192,14 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g, EpiArgs e
       for (int nf = 0; nf < 4; ++nf)
         bf[nf] = *reinterpret_cast<const u32x4*>(st + WTILE + woff(q * 64 + nf * 16 + lr, lg));
     }
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<phase_vm_ops<FMT>()>();
+    issue_a(min(t + 3, nk - 1), t + 3);
+    __builtin_amdgcn_sched_barrier(0);  // the LDS-DMA goes out before the register loads
+    cld = load_codes<FMT>(g.W, cp, e0, min(t + 5, nk - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    if (((t + 3) & 1) == 0) tb = nf4_table(cdec.am);  // first half of a 64-block
+    decode_b(t + 3, cdec.c, tb);
     __builtin_amdgcn_sched_barrier(0);
     wbar();
     __builtin_amdgcn_sched_barrier(0);
