@@ -41,11 +41,11 @@ HBM_PEAK_GBPS = 8000.0
 PCIE5_X16_GBPS = 63.0            # theoretical per direction after 128b/130b encoding
 
 # HBM bytes per launch of the gate|up forward GEMM from two rocprofv3 --pmc passes
-# (profiles/pmc_traffic_layer8b_seq512.md): FETCH_SIZE 50046.9 KiB scaled by 1.99975
-# (the calibration kernel's ratio) + WRITE_SIZE 28692.9 KiB scaled by 1.0.  Valid only
-# for the GEMM sources they were taken on (hash below); otherwise traffic is null.
+# (profiles/pmc_traffic_layer8b_seq512.md): FETCH_SIZE 50047.97 KiB scaled by 1.99969
+# (the calibration kernel's ratio) + WRITE_SIZE 28691.80 KiB scaled by 1.0.  Valid only
+# for the sources of that kernel they were taken on (hash below); otherwise null.
 GATE_UP_TRAFFIC_BYTES = (50047.97 * 1.99969 + 28691.80 * 1.0) * 1024
-GATE_UP_TRAFFIC_SRC = "7bed207dabe040ff"
+GATE_UP_TRAFFIC_SRC = "590077a810cf546d"
 # Algorithmic bytes of one such launch: NF4 codes 58.72 MB + absmax 7.34 MB + x 4.19 MB +
 # LoRA (U, B) 1.9 MB read; a 14.7 MB (forward) or a, g, u 44.0 MB (recompute) written.
 GATE_UP_ALGO_BYTES = (58.72 + 7.34 + 4.19 + 1.9 + (14.68 + 44.04) / 2) * 1e6
@@ -55,7 +55,7 @@ def gemm_src_hash():
     import hashlib
     here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "layer_streamed_frozen_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("gemm.hip", "gemm_wide.hip", "common.h", "weight_decode.h"):
+    for f in ("gemm_wide.hip", "common.h", "weight_decode.h"):
         with open(os.path.join(here, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -354,8 +354,10 @@ __global__ __launch_bounds__(Cfg<BM>::NTHR, Cfg<BM>::MIN_BLOCKS) void gemm_kerne
 
   uint16_t* b0 = lds[0];
   uint16_t* b1 = lds[1];
-  if constexpr (NN) {
-    // Input-gradient GEMM: one register stage.
+  if constexpr (NN || FMT == FMT_BF16) {
+    // Input-gradient GEMM, and any GEMM over an unquantised bf16 weight (its
+    // tile arrives as 16-byte chunks, twice the registers of packed codes):
+    // one register stage.
     Stage st;
     if (nmain > 0) {
       load_main<BM, NN, FMT>(g, m0, ntile, kb * BK, tid, st);
