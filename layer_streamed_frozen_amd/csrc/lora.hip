@@ -11,9 +11,9 @@
 // over the tokens: Out[j, k] += scale * sum_t P[t, j] Q[t, k] (or = when the
 // section asks to overwrite: the first accumulation of a step).  A workgroup
 // owns 64 columns k, all r rows j and one share of the tokens; each wave takes
-// a quarter of that share in 32-row chunks, staged in LDS so the MFMA operands
-// can run along the token axis (P transposed, Q read down its rows with
-// transposing loads).  The four wave tiles are summed in a fixed order; the
+// a quarter of that share in 32-row chunks, staged in its own LDS region so the
+// MFMA operands can run along the token axis (P transposed, Q read down its
+// rows with transposing loads), loading chunk i+1 while it multiplies chunk i.  The four wave tiles are summed in a fixed order; the
 // token shares, when there are several, are summed in order by a second
 // kernel, and the result is added (+=) into the fp32 gradient.  No atomics:
 // the same inputs give the same bits on every run.
@@ -120,6 +120,15 @@ struct GradBatch {
 
 constexpr int PS_LD = 40;  // LDS row stride (bf16) of the transposed P chunk
 
+// This wave's LDS accesses so far are complete, and neither the compiler nor
+// the hardware moves later ones ahead of them.
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Workgroup (column tile, section, token split z): tokens
 // [z * 4 * cpw * 32, (z + 1) * 4 * cpw * 32).  With one split the result is
 // added into the gradient directly; with several, each split writes its
@@ -139,27 +148,43 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(GradBatch gb, int T, int
   for (int a = 0; a < JT; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0, 0, 0, 0};
-  for (int ci = 0; ci < cpw; ++ci) {
+  // Each wave works on its own 32-token chunks and its own LDS regions, so
+  // between staging and reading a chunk it only has to wait for its own LDS
+  // writes (LDS operations of one wave complete in order); the global loads of
+  // the next chunk are issued before the current one is read.
+  u32x4 qv[4];
+  float pv[R / 2];
+  auto load = [&](int ci) {
     const int t0 = (((int)blockIdx.z * 4 + wid) * cpw + ci) * 32;
-    // Q chunk: 32 tokens x 64 columns
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int idx = lane + 64 * i;
       const int row = idx >> 3, ch = idx & 7;
       const int t = t0 + row, k = k0 + ch * 8;
-      u32x4 v = {0, 0, 0, 0};
-      if (t < T && k < g.nq) v = *reinterpret_cast<const u32x4*>(g.Q + (int64_t)t * g.ldq + g.qoff + k);
-      *reinterpret_cast<u32x4*>(Qs[wid] + off_r8(row, ch)) = v;
+      qv[i] = u32x4{0, 0, 0, 0};
+      if (t < T && k < g.nq) qv[i] = *reinterpret_cast<const u32x4*>(g.Q + (int64_t)t * g.ldq + g.qoff + k);
     }
-    // P chunk, transposed to [j][t] bf16
+    const int t = lane >> 1, jh = (lane & 1) * (R / 2);
+    const bool ok = t0 + t < T;
+    const float* prow = g.P + (int64_t)(t0 + t) * g.ldp + g.pcol0 + jh;
+#pragma unroll
+    for (int e = 0; e < R / 2; ++e) pv[e] = ok ? prow[e] : 0.0f;
+  };
+  if (cpw > 0) load(0);
+  for (int ci = 0; ci < cpw; ++ci) {
+    // Q chunk: 32 tokens x 64 columns; P chunk transposed to [j][t] bf16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = lane + 64 * i;
+      *reinterpret_cast<u32x4*>(Qs[wid] + off_r8(idx >> 3, idx & 7)) = qv[i];
+    }
     {
       const int t = lane >> 1, jh = (lane & 1) * (R / 2);
-      const bool ok = t0 + t < T;
-      const float* prow = g.P + (int64_t)(t0 + t) * g.ldp + g.pcol0 + jh;
 #pragma unroll
-      for (int e = 0; e < R / 2; ++e) Ps[wid][(jh + e) * PS_LD + t] = f32_to_bf16(ok ? prow[e] : 0.0f);
+      for (int e = 0; e < R / 2; ++e) Ps[wid][(jh + e) * PS_LD + t] = f32_to_bf16(pv[e]);
     }
-    __syncthreads();
+    if (ci + 1 < cpw) load(ci + 1);
+    wave_lds_sync();
     u32x4 af[JT];
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt)
@@ -176,7 +201,7 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(GradBatch gb, int T, int
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt) acc[jt][nf] = mfma16x16x32(af[jt], bf, acc[jt][nf]);
     }
-    __syncthreads();
+    wave_lds_sync();  // this chunk's reads are done before the next one is staged
   }
   // acc[jt][nf][i] = partial Out[jt*16 + lg*4 + i][nf*16 + lr]
 #pragma unroll
