@@ -32,6 +32,7 @@ __host__ __device__ __forceinline__ int sec_k(const LoraDown& a, int sec) {
   return a.ksec[sec] > 0 ? a.ksec[sec] : a.K;
 }
 
+template <int R, bool BSIDE>
 __global__ __launch_bounds__(256) void lora_down_part_kernel(LoraDown a, int nch_max) {
   __shared__ __attribute__((aligned(16))) uint16_t Ms[64 * MS_LD];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, lr = lane & 15, lg = lane >> 4;
@@ -41,50 +42,77 @@ __global__ __launch_bounds__(256) void lora_down_part_kernel(LoraDown a, int nch
   const float* mat = a.mat[sec];
   if (k0 >= Ks || mat == nullptr) return;  // uniform over the workgroup
   const int kn = min(KC, Ks - k0);           // a multiple of 32
-  const int r = a.r;
-  // stage the adapter chunk as bf16 [j][k]
-  if (!a.bside) {
-    const int q4 = kn / 4;
-    for (int idx = tid; idx < r * q4; idx += 256) {
-      const int j = idx / q4, k = (idx - j * q4) * 4;
-      const float4 v = *reinterpret_cast<const float4*>(mat + (int64_t)j * Ks + k0 + k);
-      *reinterpret_cast<uint2*>(Ms + j * MS_LD + k) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+  // Load order: the adapter chunk (16-byte vectors), then this lane's X
+  // fragments, then the chunk is converted and stored, so the stores wait only
+  // for the adapter loads while the X loads are still in flight.  Addresses
+  // are clamped into range and unused values zeroed afterwards: loads under a
+  // branch would each be waited for on the spot.
+  constexpr int SMAX = (R * KC / 4 + 255) / 256;  // float4 per thread
+  const int n4 = R * kn / 4;
+  float4 sv[SMAX];
+#pragma unroll
+  for (int u = 0; u < SMAX; ++u) {
+    const int idx = min(tid + 256 * u, n4 - 1);
+    if constexpr (!BSIDE) {
+      const int q4 = kn / 4, j = idx / q4, k = (idx - j * q4) * 4;
+      sv[u] = *reinterpret_cast<const float4*>(mat + (int64_t)j * Ks + k0 + k);
+    } else {
+      sv[u] = reinterpret_cast<const float4*>(mat + (int64_t)k0 * R)[idx];
     }
-  } else {
-    const float* src = mat + (int64_t)k0 * r;
-    for (int f = tid; f < kn * r; f += 256) {
-      const int k = f / r, j = f - k * r;
-      Ms[j * MS_LD + k] = f32_to_bf16(src[f]);
+  }
+  const int m = blockIdx.x * 64 + wid * 16 + lr;
+  const uint16_t* xrow = a.X + (int64_t)min(m, a.M - 1) * a.ldx + a.xoff[sec] + k0 + lg * 8;
+  u32x4 xa[KC / 32];
+#pragma unroll
+  for (int st = 0; st < KC / 32; ++st) xa[st] = *reinterpret_cast<const u32x4*>(xrow + (st * 32 < kn ? st * 32 : 0));
+  // the chunk as bf16 [j][k] (B-side: element f of the chunk is B[k0 + f / R][f % R])
+#pragma unroll
+  for (int u = 0; u < SMAX; ++u) {
+    const int idx = tid + 256 * u;
+    if (idx < n4) {
+      if constexpr (!BSIDE) {
+        const int q4 = kn / 4, j = idx / q4, k = (idx - j * q4) * 4;
+        *reinterpret_cast<uint2*>(Ms + j * MS_LD + k) =
+            make_uint2(pack_bf16x2(sv[u].x, sv[u].y), pack_bf16x2(sv[u].z, sv[u].w));
+      } else {
+        const int k = (4 * idx) / R, j = 4 * idx - k * R;  // R is a multiple of 4: one row k
+        Ms[j * MS_LD + k] = f32_to_bf16(sv[u].x);
+        Ms[(j + 1) * MS_LD + k] = f32_to_bf16(sv[u].y);
+        Ms[(j + 2) * MS_LD + k] = f32_to_bf16(sv[u].z);
+        Ms[(j + 3) * MS_LD + k] = f32_to_bf16(sv[u].w);
+      }
     }
   }
   __syncthreads();
-  const int m = blockIdx.x * 64 + wid * 16 + lr;
-  const uint16_t* xrow = a.X + (int64_t)min(m, a.M - 1) * a.ldx + a.xoff[sec] + k0;
-  const int jt_n = (r + 15) / 16;
-  f32x4 acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
-  for (int st = 0; st < kn / 32; ++st) {
-    const int k = st * 32 + lg * 8;
-    u32x4 xa = *reinterpret_cast<const u32x4*>(xrow + k);
-    if (m >= a.M) xa = u32x4{0, 0, 0, 0};
+  // No branches around the MFMAs: steps past the chunk, rows past M and
+  // adapter rows past R multiply zeros.
+  constexpr int jt_n = (R + 15) / 16;
+  f32x4 acc[jt_n];
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      if (jt >= jt_n) break;
+  for (int jt = 0; jt < jt_n; ++jt) acc[jt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int st = 0; st < KC / 32; ++st) {
+    const uint32_t xkeep = (st * 32 < kn && m < a.M) ? 0xffffffffu : 0u;
+    const u32x4 x = {xa[st].x & xkeep, xa[st].y & xkeep, xa[st].z & xkeep, xa[st].w & xkeep};
+    const int k = (st * 32 < kn ? st * 32 : 0) + lg * 8;
+#pragma unroll
+    for (int jt = 0; jt < jt_n; ++jt) {
       const int j = jt * 16 + lr;
-      u32x4 bb = {0, 0, 0, 0};
-      if (j < r) bb = *reinterpret_cast<const u32x4*>(Ms + j * MS_LD + k);
-      acc[jt] = mfma16x16x32(xa, bb, acc[jt]);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(Ms + min(j, R - 1) * MS_LD + k);
+      const uint32_t keep = (j < R) ? 0xffffffffu : 0u;
+      const u32x4 bb = {v.x & keep, v.y & keep, v.z & keep, v.w & keep};
+      acc[jt] = mfma16x16x32(x, bb, acc[jt]);
     }
   }
-  float* out = a.part + (size_t)(sec * nch_max + c) * a.M * r;
+  float* out = a.part + (size_t)(sec * nch_max + c) * a.M * R;
   const int mb = blockIdx.x * 64 + wid * 16 + lg * 4;
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
-    if (jt >= jt_n) break;
+  for (int jt = 0; jt < jt_n; ++jt) {
     const int j = jt * 16 + lr;
-    if (j >= r) continue;
+    if (j >= R) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (mb + i < a.M) out[(size_t)(mb + i) * r + j] = acc[jt][i];
+      if (mb + i < a.M) out[(size_t)(mb + i) * R + j] = acc[jt][i];
   }
 }
 
@@ -254,16 +282,29 @@ __global__ __launch_bounds__(256) void lora_grad_reduce_kernel(GradBatch gb, int
   }
 }
 
+template <int R>
+void launch_down(const LoraDown& a, dim3 grid, int nch_max, hipStream_t s) {
+  if (a.bside) hipLaunchKernelGGL((lora_down_part_kernel<R, true>), grid, dim3(256), 0, s, a, nch_max);
+  else hipLaunchKernelGGL((lora_down_part_kernel<R, false>), grid, dim3(256), 0, s, a, nch_max);
+}
+
 }  // namespace
 
 hipError_t lora_down(const LoraDown& a, hipStream_t s) {
   if (a.M <= 0 || a.nsec <= 0) return hipSuccess;
-  if (a.r <= 0 || a.r > 64 || a.part == nullptr) return hipErrorInvalidValue;
+  if (a.r < 4 || a.r > 64 || (a.r & (a.r - 1)) != 0 || a.part == nullptr) return hipErrorInvalidValue;
   int nch_max = 0;
   for (int i = 0; i < a.nsec; ++i) nch_max = std::max(nch_max, (sec_k(a, i) + KC - 1) / KC);
   if ((size_t)a.nsec * nch_max * a.M * a.r > a.part_floats) return hipErrorInvalidValue;
   dim3 grid((a.M + 63) / 64, a.nsec * nch_max);
-  hipLaunchKernelGGL(lora_down_part_kernel, grid, dim3(256), 0, s, a, nch_max);
+  switch (a.r) {
+    case 4: launch_down<4>(a, grid, nch_max, s); break;
+    case 8: launch_down<8>(a, grid, nch_max, s); break;
+    case 16: launch_down<16>(a, grid, nch_max, s); break;
+    case 32: launch_down<32>(a, grid, nch_max, s); break;
+    case 64: launch_down<64>(a, grid, nch_max, s); break;
+    default: return hipErrorInvalidValue;
+  }
   const int64_t total = (int64_t)a.M * a.nsec * a.r;
   const int blocks = (int)std::min<int64_t>((total + 255) / 256, 2048);
   hipLaunchKernelGGL(lora_down_reduce_kernel, dim3(blocks), dim3(256), 0, s, a, nch_max);
