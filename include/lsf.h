@@ -133,7 +133,7 @@ typedef struct {
   int32_t n_heads;      /* query heads */
   int32_t n_kv_heads;   /* key/value heads; n_heads % n_kv_heads == 0 */
   int32_t head_dim;     /* 128 (the attention kernels are built for it) */
-  int32_t rank;         /* LoRA rank r of every adapter, 1..64 */
+  int32_t rank;         /* LoRA rank r of every adapter: 4, 8, 16, 32 or 64 (else LSF_ERR_SHAPE) */
   float lora_scale;     /* s = alpha / r */
   float rope_theta;     /* RoPE base, e.g. 500000 */
   float rms_eps;        /* RMSNorm epsilon, e.g. 1e-5 */
@@ -183,8 +183,8 @@ typedef struct {
 /* -------------------------------------------------------- one NF4 linear --
  * y = x W^T + s (x A^T) B^T   (LoRA on a frozen NF4 weight; [NEWS], [TUTORIAL]
  * item 3).  x: device bf16 [tokens, n_in]; y: device bf16 [tokens, n_out].
- * n_out % 128 == 0, n_in % 64 == 0, tokens >= 1, 1 <= rank <= 64.
- * A/B may be NULL (no adapter).  ws: device workspace of at least
+ * n_out % 128 == 0, n_in % 64 == 0, tokens >= 1; with an adapter, rank is one of
+ * 4, 8, 16, 32, 64 (else LSF_ERR_SHAPE).  A/B may be NULL (no adapter).  ws: device workspace of at least
  * linear_workspace_bytes() bytes. */
 LSF_API size_t linear_workspace_bytes(int32_t tokens, int32_t n_out, int32_t n_in, int32_t rank);
 LSF_API lsf_status linear_fwd(const lsf_weight* w, int32_t format, int32_t n_out, int32_t n_in,
