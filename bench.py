@@ -11,7 +11,9 @@ v, o, gate, up, down; resident untied bf16 embedding and lm_head over a
 128256-token vocabulary; one sequence of 512 random token ids per step;
 cross-entropy loss; forward, head, recomputing backward (all LoRA gradients)
 and one AdamW update of every adapter per step.  "stack4" is 4 sequences of 512 per micro-batch and 4 micro-batches
-(gradient accumulation) per step.  "dpo" is the preference-loss step: 2
+(gradient accumulation) per step, by default in one walk over the stack per direction
+(each layer copied once for all four micro-batches; ``--accum-order micro`` streams
+the stack once per micro-batch instead; both give the same bits).  "dpo" is the preference-loss step: 2
 chosen/rejected pairs of 512 tokens (4 sequences, pair p sharing a 256-token
 prompt), DPO with beta 0.1, the reference log-probabilities from the same
 streamed base with the adapters off, computed in the policy's layer visit
@@ -83,6 +85,9 @@ def parse():
     p.add_argument("--keep-activations", action="store_true",
                    help="keep every layer's forward intermediates in HBM and skip the recompute in the backward "
                         "walk (each layer is still read twice)")
+    p.add_argument("--accum-order", choices=["layer", "micro"], default="layer",
+                   help="gradient accumulation: every layer serves all micro-batches in one walk (layer) or "
+                        "the stack is walked once per micro-batch (micro)")
     p.add_argument("--diag-steps", type=int, default=5,
                    help="steps of the diagnostic pass that times every kernel class and copy (0: none)")
     return p.parse_args()
@@ -231,7 +236,9 @@ def main():
         flags = B.STACK_TIMING
     else:
         flags = B.STACK_TIME_KERNEL(dom_k)
-    stack = S.Stack(shape, store, batch, seq, V, flags=flags, keep_activations=args.keep_activations)
+    layer_major = accum > 1 and args.accum_order == "layer"
+    stack = S.Stack(shape, store, batch, seq, V, flags=flags, keep_activations=args.keep_activations,
+                    n_micro=accum if layer_major else 1)
     arr = lora.array()
     opt = (S.AdamW8 if args.optimizer == "adamw8" else S.AdamW)(lora, lr=2e-4)
     torch.cuda.synchronize()
@@ -240,6 +247,8 @@ def main():
         if dpo:
             stk.dpo_step(ids[0], emb, fnorm, head, arr, beta=0.1, fused=args.workload == "dpo",
                          mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+        elif layer_major:
+            stk.accum_step(ids, emb, fnorm, head, arr, mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
         else:
             for m in range(accum):
                 mode = B.MODE_STREAMED | (B.MODE_ZERO_GRADS if m == 0 else 0)
@@ -300,7 +309,8 @@ def main():
         stack.close()
         del stack
         log(f"diagnostic pass: {diag_steps} steps with every kernel and copy timed")
-        diag = S.Stack(shape, store, batch, seq, V, flags=B.STACK_TIMING, keep_activations=args.keep_activations)
+        diag = S.Stack(shape, store, batch, seq, V, flags=B.STACK_TIMING, keep_activations=args.keep_activations,
+                       n_micro=accum if layer_major else 1)
         step(diag)
         torch.cuda.synchronize()
         B.stack_reset_stats(diag.handle)
@@ -355,7 +365,10 @@ def main():
                                    f"reference = adapters off, "
                                    + ("fused into the policy's layer visit" if args.workload == "dpo"
                                       else "separate reference pass") if dpo else
-                                   f"batch {batch} x seq {seq}, accumulation {accum}")),
+                                   f"batch {batch} x seq {seq}, accumulation {accum}"
+                                   + ((", one walk over the stack per direction for all micro-batches"
+                                       if layer_major else ", the stack walked once per micro-batch")
+                                      if accum > 1 else ""))),
                    "global_batch": batch * accum, "seq_len": seq, "layers": L, "vocab": V,
                    "optimizer": ("AdamW lr 2e-4, fp32 moments, once per step" if args.optimizer == "adamw" else
                                  "AdamW lr 2e-4, 8-bit block-wise moments (blocks of 2048, dynamic code), "

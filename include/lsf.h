@@ -310,6 +310,24 @@ LSF_API size_t stack_activation_bytes(const lsf_layer_cfg* cfg, int32_t n_layers
  * streamed recompute + backward, LoRA gradients accumulated. */
 LSF_API lsf_status stream_stack_step(lsf_stack* st, const lsf_stack_io* io);
 
+/* Gradient accumulation over n_micro SFT micro-batches ([TUTORIAL] "step 2"
+ * configuration: accumulation 4) in one walk over the stack per direction:
+ * every layer copied in serves the forward (then the backward) of micro-batch
+ * 0, 1, ..., n_micro-1 before the next layer is read, so the stack is streamed
+ * twice per optimizer step instead of twice per micro-batch.  io points to
+ * n_micro descriptors; io[m] supplies micro-batch m's ids, ckpt, logits, loss
+ * and loss_scale (logits and loss may be shared), io[0] everything else
+ * (embed, vocab, final_norm, lm_head, lora, ws, act, mode).  All n_micro
+ * checkpoint arrays are live at once.  The result is that of n_micro
+ * stream_stack_step calls on io[0], io[1], ... in turn with
+ * LSF_MODE_ZERO_GRADS (if set) on the first only, bit for bit: each layer's
+ * gradients receive the micro-batches' contributions in the same order.
+ * ws: at least stack_accum_workspace_bytes(cfg, vocab, n_micro); act
+ * (LSF_MODE_KEEP_ACTIVATIONS): n_micro * stack_activation_bytes(cfg, n_layers).
+ * Errors: LSF_ERR_INVALID_ARG for n_micro < 1, plus those of stream_stack_step. */
+LSF_API size_t stack_accum_workspace_bytes(const lsf_layer_cfg* cfg, int32_t vocab, int32_t n_micro);
+LSF_API lsf_status stream_stack_accum_step(lsf_stack* st, const lsf_stack_io* io, int32_t n_micro);
+
 /* One DPO micro-batch ([README] paragraph on preference losses with layer
  * streaming; [BLOG] section on DPO support): the reference model is the same
  * frozen base with every adapter switched off, so it needs no second copy of
@@ -405,7 +423,7 @@ enum {
 };
 
 typedef struct {
-  int64_t steps;       /* stream_stack_step and dpo_stack_step calls since create / reset */
+  int64_t steps;       /* micro-batches since create / reset (n_micro per stream_stack_accum_step) */
   int64_t copies;      /* host-to-device layer copies enqueued */
   int64_t bytes;       /* bytes those copies moved */
   double copy_ms;      /* summed copy durations (LSF_STACK_TIMING only) */

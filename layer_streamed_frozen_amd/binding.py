@@ -130,6 +130,8 @@ _PROTOS = {
     "stack_destroy": (c_int32, [c_void_p]),
     "stack_workspace_bytes": (c_size_t, [ctypes.POINTER(LayerCfg), c_int32]),
     "stream_stack_step": (c_int32, [c_void_p, ctypes.POINTER(StackIO)]),
+    "stack_accum_workspace_bytes": (c_size_t, [ctypes.POINTER(LayerCfg), c_int32, c_int32]),
+    "stream_stack_accum_step": (c_int32, [c_void_p, ctypes.POINTER(StackIO), c_int32]),
     "dpo_stack_step": (c_int32, [c_void_p, ctypes.POINTER(DpoIO)]),
     "stack_stats": (c_int32, [c_void_p, ctypes.POINTER(StackStats)]),
     "stack_reset_stats": (c_int32, [c_void_p]),
@@ -297,6 +299,16 @@ def stack_workspace_bytes(cfg, vocab):
 
 def stream_stack_step(h, io):
     check(lib().stream_stack_step(h, ctypes.byref(io)))
+
+
+def stack_accum_workspace_bytes(cfg, vocab, n_micro):
+    return lib().stack_accum_workspace_bytes(ctypes.byref(cfg), vocab, n_micro)
+
+
+def stream_stack_accum_step(h, ios):
+    """ios: a sequence of StackIO, one per micro-batch."""
+    arr = (StackIO * len(ios))(*ios)
+    check(lib().stream_stack_accum_step(h, arr, len(ios)))
 
 
 def dpo_stack_step(h, io):

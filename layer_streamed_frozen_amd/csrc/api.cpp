@@ -527,6 +527,7 @@ struct StackWs {
   uint16_t *hN, *dhN, *dlog, *dx[2], *rx[2];
   float *rstdN, *row_loss, *part, *lse, *lp, *coef;
   size_t part_floats;
+  uint16_t* dx_more;  // micro-batches 1.. of an accumulated step: two [T, H] each
 };
 
 size_t head_part_floats(const lsf_layer_cfg& c) { return (size_t)8 * c.batch * c.seq * c.hidden; }
@@ -540,6 +541,13 @@ size_t stack_ws_bytes(const lsf_layer_cfg& c, int V) {
   b += al256((size_t)c.batch * 8) + al256((size_t)c.batch * 4);  // lp (policy, reference), coef
   b += al256(head_part_floats(c) * 4);
   return b + 512;
+}
+
+// With n micro-batches per walk, each keeps its own pair of gradient buffers
+// between the head and the backward walk.
+size_t stack_accum_ws_bytes(const lsf_layer_cfg& c, int V, int n) {
+  const size_t T = (size_t)c.batch * c.seq, H = c.hidden;
+  return n <= 1 ? stack_ws_bytes(c, V) : stack_ws_bytes(c, V) + 256 + (size_t)(n - 1) * 2 * al256(T * H * 2);
 }
 
 StackWs carve_stack(const lsf_layer_cfg& c, int V, void* base) {
@@ -566,7 +574,15 @@ StackWs carve_stack(const lsf_layer_cfg& c, int V, void* base) {
   w.coef = (float*)take((size_t)c.batch * 4);
   w.part_floats = head_part_floats(c);
   w.part = (float*)take(w.part_floats * 4);
+  w.dx_more = (uint16_t*)((p + 255) / 256 * 256);  // used only with the accumulated workspace size
   return w;
+}
+
+// Gradient buffer k (0, 1) of micro-batch m.
+uint16_t* dx_buf(const StackWs& w, const lsf_layer_cfg& c, int m, int k) {
+  if (m == 0) return w.dx[k];
+  const size_t TH = al256((size_t)c.batch * c.seq * c.hidden * 2);
+  return reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(w.dx_more) + ((size_t)(m - 1) * 2 + k) * TH);
 }
 
 // One walk over the stack: layers 0..L-1 (forward) or L-1..0.  Layer j
@@ -636,32 +652,43 @@ hipError_t head_backward(lsf_stack* st, const lsf_stack_io* io, const StackWs& w
   return rmsnorm_bwd(w.dhN, x, io->final_norm, w.rstdN, nullptr, T, H, dx, cs);
 }
 
-// One micro-batch: SFT (dpo == NULL) or DPO with the adapters-off reference.
-lsf_status run_step(lsf_stack* st, const lsf_stack_io* io, const lsf_dpo_io* dpo) {
-  if (st == nullptr) return fail(LSF_ERR_INVALID_ARG, "stack or io is NULL");
+// n micro-batches of SFT (dpo == NULL; io[0..n-1]) or one DPO micro-batch
+// with the adapters-off reference (n == 1).  Every layer visit serves all n
+// micro-batches in turn, so the stack is read once per direction however
+// many micro-batches there are; each layer's gradients receive the
+// micro-batches' contributions in the order 0, 1, ..., n-1.
+lsf_status run_step(lsf_stack* st, const lsf_stack_io* io_all, int n_micro, const lsf_dpo_io* dpo) {
+  if (st == nullptr || io_all == nullptr) return fail(LSF_ERR_INVALID_ARG, "stack or io is NULL");
+  if (n_micro < 1) return fail(LSF_ERR_INVALID_ARG, "n_micro must be >= 1 (got %d)", n_micro);
+  if (dpo != nullptr && n_micro != 1) return fail(LSF_ERR_INVALID_ARG, "DPO takes one micro-batch per call");
+  const lsf_stack_io* io = io_all;  // the shared fields come from io[0]
   const lsf_layer_cfg& c = st->cfg;
   const int L = st->d.n_layers;
   const int V = io->vocab;
   const int T = c.batch * c.seq, H = c.hidden;
   lsf_status s;
   if (V < 128 || V % 128) return fail(LSF_ERR_SHAPE, "vocab must be a positive multiple of 128 (got %d)", V);
-  if ((s = check_dev(io->ids, "ids")) || (s = check_dev(io->embed, "embed")) ||
-      (s = check_dev(io->final_norm, "final_norm")) || (s = check_dev(io->lm_head, "lm_head")) ||
-      (s = check_dev(io->ckpt, "ckpt")) || (s = check_dev(io->logits, "logits")) || (s = check_dev(io->loss, "loss")))
+  if ((s = check_dev(io->embed, "embed")) || (s = check_dev(io->final_norm, "final_norm")) ||
+      (s = check_dev(io->lm_head, "lm_head")))
     return s;
+  for (int m = 0; m < n_micro; ++m)
+    if ((s = check_dev(io_all[m].ids, "ids")) || (s = check_dev(io_all[m].ckpt, "ckpt")) ||
+        (s = check_dev(io_all[m].logits, "logits")) || (s = check_dev(io_all[m].loss, "loss")))
+      return s;
   if (io->lora == nullptr) return fail(LSF_ERR_INVALID_ARG, "lora array is NULL");
   for (int i = 0; i < L; ++i)
     if ((s = check_lora(&io->lora[i]))) return s;
   const bool resident = io->mode & LSF_MODE_RESIDENT;
   if (resident && st->d.resident_store == nullptr) return fail(LSF_ERR_INVALID_ARG, "RESIDENT mode needs a resident store");
   if (!resident && st->d.host_store == nullptr) return fail(LSF_ERR_INVALID_ARG, "STREAMED mode needs a host store");
-  if (io->ws == nullptr || io->ws_bytes < stack_ws_bytes(c, V))
-    return fail(LSF_ERR_WORKSPACE, "workspace too small (need %zu bytes)", stack_ws_bytes(c, V));
+  const size_t ws_need = stack_accum_ws_bytes(c, V, n_micro);
+  if (io->ws == nullptr || io->ws_bytes < ws_need) return fail(LSF_ERR_WORKSPACE, "workspace too small (need %zu bytes)", ws_need);
   const bool keep = io->mode & LSF_MODE_KEEP_ACTIVATIONS;
   const size_t saved = LayerWs::saved_bytes(c);
   if (keep) {
-    if (io->act == nullptr || io->act_bytes < saved * L)
-      return fail(LSF_ERR_WORKSPACE, "activation arena too small (need %zu bytes)", saved * L);
+    const size_t need = saved * L * (size_t)n_micro;
+    if (io->act == nullptr || io->act_bytes < need)
+      return fail(LSF_ERR_WORKSPACE, "activation arena too small (need %zu bytes)", need);
     if (!aligned(io->act, 256)) return fail(LSF_ERR_ALIGN, "activation arena must be 256-byte aligned");
   }
   if (dpo != nullptr) {
@@ -686,19 +713,33 @@ lsf_status run_step(lsf_stack* st, const lsf_stack_io* io, const lsf_dpo_io* dpo
     HIPCK(harvest_all(st, false));  // recycle the events of work that has finished
   }
   const size_t act = (size_t)T * H;
-  st->stats.steps += 1;
+  st->stats.steps += n_micro;
+
+  // Micro-batch m's descriptor: io[0] with m's own ids, checkpoints, logits,
+  // loss and loss scale.
+  auto io_of = [&](int m) {
+    lsf_stack_io r = *io;
+    r.ids = io_all[m].ids;
+    r.ckpt = io_all[m].ckpt;
+    r.logits = io_all[m].logits;
+    r.loss = io_all[m].loss;
+    r.loss_scale = io_all[m].loss_scale;
+    return r;
+  };
 
   // LSF_MODE_ZERO_GRADS: the backward of every enabled layer stores its dA, dB
   // (overwrite) instead of adding to them; only gradients no backward will
   // write (forward-only calls, disabled layers) are zeroed here.
   // Gradient arrays shared between layers (tied adapters) accumulate over
-  // the step, so they take the zero-then-add path.
+  // the step, so they take the zero-then-add path.  With several
+  // micro-batches only the first one's backward overwrites.
   const bool zero_grads = (io->mode & LSF_MODE_ZERO_GRADS) != 0;
   bool overwrite = zero_grads && (io->mode & LSF_MODE_FWD_ONLY) == 0;
   if (overwrite) {
     std::vector<const float*> seen;
     for (int i = 0; i < L; ++i) {
-      const lsf_lora_proj* p = &io->lora[i].q;
+      const lsf_layer_lora* li = &io->lora[i];
+      const lsf_lora_proj* p = &li->q;
       for (int k = 0; k < 7; ++k) {
         if (p[k].A == nullptr) continue;
         if (p[k].dA) seen.push_back(p[k].dA);
@@ -708,7 +749,6 @@ lsf_status run_step(lsf_stack* st, const lsf_stack_io* io, const lsf_dpo_io* dpo
     std::sort(seen.begin(), seen.end());
     overwrite = std::adjacent_find(seen.begin(), seen.end()) == seen.end();
   }
-  w.layer.grads_overwrite = overwrite;
   if (zero_grads) {
     const int64_t Dq = (int64_t)c.n_heads * c.head_dim, Dk = (int64_t)c.n_kv_heads * c.head_dim;
     const int64_t in[7] = {c.hidden, c.hidden, c.hidden, Dq, c.hidden, c.hidden, c.intermediate};
@@ -725,14 +765,24 @@ lsf_status run_step(lsf_stack* st, const lsf_stack_io* io, const lsf_dpo_io* dpo
   }
 
   HIPCK(rope_table(c.seq, c.head_dim, c.rope_theta, w.layer.rope, cs));
-  HIPCK(embed_gather(io->ids, io->embed, T, H, V, io->ckpt, cs));
+  for (int m = 0; m < n_micro; ++m) HIPCK(embed_gather(io_all[m].ids, io->embed, T, H, V, io_all[m].ckpt, cs));
 
-  // Layer i's saved intermediates (LSF_MODE_KEEP_ACTIVATIONS).
-  auto kept = [&](int i) { return w.layer.with_saved(c, static_cast<char*>(io->act) + (size_t)i * saved); };
-  // Policy forward of layer i: ckpt[i] -> ckpt[i+1] (kept for the backward).
-  auto policy_fwd = [&](int i, const lsf_layer_weights& lw) {
-    return layer_forward(c, lw, &io->lora[i], io->ckpt + (size_t)i * act, io->ckpt + (size_t)(i + 1) * act,
-                         keep ? kept(i) : w.layer, keep, true, cs);
+  // Layer i's saved intermediates for micro-batch m (LSF_MODE_KEEP_ACTIVATIONS).
+  auto kept = [&](int m, int i) {
+    return w.layer.with_saved(c, static_cast<char*>(io->act) + ((size_t)m * L + i) * saved);
+  };
+  // Policy forward of layer i for micro-batch m: ckpt[i] -> ckpt[i+1] (kept for the backward).
+  auto policy_fwd = [&](int m, int i, const lsf_layer_weights& lw) {
+    uint16_t* ck = io_all[m].ckpt;
+    return layer_forward(c, lw, &io->lora[i], ck + (size_t)i * act, ck + (size_t)(i + 1) * act,
+                         keep ? kept(m, i) : w.layer, keep, true, cs);
+  };
+  auto all_fwd = [&](int i, const lsf_layer_weights& lw) {
+    for (int m = 0; m < n_micro; ++m) {
+      const hipError_t e = policy_fwd(m, i, lw);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   };
   // Reference (adapters off) forward of layer i, through the rx ping-pong:
   // input rx[i % 2] (the embeddings for layer 0), output rx[(i + 1) % 2].
@@ -758,37 +808,46 @@ lsf_status run_step(lsf_stack* st, const lsf_stack_io* io, const lsf_dpo_io* dpo
   }
   if (dpo != nullptr && dpo->fused_reference) {
     auto both = [&](int i, const lsf_layer_weights& lw) {
-      const hipError_t e = policy_fwd(i, lw);
+      const hipError_t e = policy_fwd(0, i, lw);
       return e != hipSuccess ? e : reference_fwd(i, lw);
     };
     if ((s = walk_layers(st, resident, true, reuse, both))) return s;
     HIPCK(reference_head());
-  } else if ((s = walk_layers(st, resident, true, reuse, policy_fwd))) {
+  } else if ((s = walk_layers(st, resident, true, reuse, all_fwd))) {
     return s;
   }
 
-  // ---- head: final norm, lm_head, loss and dlogits
-  const uint16_t* xL = io->ckpt + (size_t)L * act;
+  // ---- heads: final norm, lm_head, loss and dlogits, lm_head input gradient
   const bool fwd_only = io->mode & LSF_MODE_FWD_ONLY;
-  HIPCK(head_logits(st, io, w, xL, timing));
-  if (dpo == nullptr) {
-    HIPCK(cross_entropy(io->logits, io->ids, c.batch, c.seq, V, io->loss_scale, w.dlog, w.row_loss, io->loss, cs));
-  } else {
-    HIPCK(seq_logprobs(io->logits, io->ids, c.batch, c.seq, V, w.lse, w.row_loss, lp_pi, cs));
-    HIPCK(dpo_head_grad(io->logits, io->ids, w.lse, lp_pi, lp_ref, c.batch, c.seq, V, dpo->beta, io->loss_scale,
-                        w.coef, io->loss, fwd_only ? nullptr : w.dlog, cs));
-    if (dpo->seq_logp != nullptr)
-      HIPCK(hipMemcpyAsync(dpo->seq_logp, w.lp, (size_t)c.batch * 8, hipMemcpyDeviceToDevice, cs));
+  for (int m = 0; m < n_micro; ++m) {
+    const lsf_stack_io iom = io_of(m);
+    const uint16_t* xL = iom.ckpt + (size_t)L * act;
+    HIPCK(head_logits(st, &iom, w, xL, timing));
+    if (dpo == nullptr) {
+      HIPCK(cross_entropy(iom.logits, iom.ids, c.batch, c.seq, V, iom.loss_scale, w.dlog, w.row_loss, iom.loss, cs));
+    } else {
+      HIPCK(seq_logprobs(iom.logits, iom.ids, c.batch, c.seq, V, w.lse, w.row_loss, lp_pi, cs));
+      HIPCK(dpo_head_grad(iom.logits, iom.ids, w.lse, lp_pi, lp_ref, c.batch, c.seq, V, dpo->beta, iom.loss_scale,
+                          w.coef, iom.loss, fwd_only ? nullptr : w.dlog, cs));
+      if (dpo->seq_logp != nullptr)
+        HIPCK(hipMemcpyAsync(dpo->seq_logp, w.lp, (size_t)c.batch * 8, hipMemcpyDeviceToDevice, cs));
+    }
+    if (!fwd_only) HIPCK(head_backward(st, &iom, w, xL, dx_buf(w, c, m, L & 1), timing));
   }
   if (fwd_only) return ok();
-  HIPCK(head_backward(st, io, w, xL, w.dx[L & 1], timing));
 
   // ---- backward: layers L-1 .. 0, each read again and recomputed
-  auto policy_bwd = [&](int j, const lsf_layer_weights& lw) {
-    return layer_backward(c, lw, &io->lora[j], io->ckpt + (size_t)j * act, w.dx[(j + 1) & 1], w.dx[j & 1],
-                          keep ? kept(j) : w.layer, true, cs, !keep);
+  auto all_bwd = [&](int j, const lsf_layer_weights& lw) {
+    for (int m = 0; m < n_micro; ++m) {
+      LayerWs lws = keep ? kept(m, j) : w.layer;
+      lws.grads_overwrite = overwrite && m == 0;
+      const hipError_t e = layer_backward(c, lw, &io->lora[j], io_all[m].ckpt + (size_t)j * act,
+                                          dx_buf(w, c, m, (j + 1) & 1), dx_buf(w, c, m, j & 1), lws, true, cs, !keep);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   };
-  if ((s = walk_layers(st, resident, false, reuse, policy_bwd))) return s;
+  if ((s = walk_layers(st, resident, false, reuse, all_bwd))) return s;
   return ok();
 }
 
@@ -873,14 +932,24 @@ size_t stack_workspace_bytes(const lsf_layer_cfg* cfg, int32_t vocab) {
   return stack_ws_bytes(*cfg, vocab);
 }
 
+size_t stack_accum_workspace_bytes(const lsf_layer_cfg* cfg, int32_t vocab, int32_t n_micro) {
+  if (check_cfg(cfg) != LSF_OK || vocab <= 0 || n_micro < 1) return 0;
+  return stack_accum_ws_bytes(*cfg, vocab, n_micro);
+}
+
 lsf_status stream_stack_step(lsf_stack* st, const lsf_stack_io* io) {
   if (io == nullptr) return fail(LSF_ERR_INVALID_ARG, "stack or io is NULL");
-  return run_step(st, io, nullptr);
+  return run_step(st, io, 1, nullptr);
+}
+
+lsf_status stream_stack_accum_step(lsf_stack* st, const lsf_stack_io* io, int32_t n_micro) {
+  if (io == nullptr) return fail(LSF_ERR_INVALID_ARG, "stack or io is NULL");
+  return run_step(st, io, n_micro, nullptr);
 }
 
 lsf_status dpo_stack_step(lsf_stack* st, const lsf_dpo_io* io) {
   if (io == nullptr) return fail(LSF_ERR_INVALID_ARG, "stack or io is NULL");
-  return run_step(st, &io->base, io);
+  return run_step(st, &io->base, 1, io);
 }
 
 size_t adamw_workspace_bytes(void) { return adamw_ws_bytes(); }

@@ -255,7 +255,7 @@ class AdamW8:
 class Stack:
     """A streamed stack: store + two device buffers + streams + handle."""
 
-    def __init__(self, shape, store, batch, seq, vocab, flags=0, device="cuda", keep_activations=False):
+    def __init__(self, shape, store, batch, seq, vocab, flags=0, device="cuda", keep_activations=False, n_micro=1):
         self.shape, self.store, self.batch, self.seq, self.vocab = shape, store, batch, seq, vocab
         self.cfg = shape.cfg(batch, seq)
         nbytes = store.layout.bytes
@@ -276,15 +276,20 @@ class Stack:
         self.handle = B.stack_create(self.cfg, d)
         T = batch * seq
         H = shape.hidden
-        self.ws = torch.empty(B.stack_workspace_bytes(self.cfg, vocab), dtype=torch.uint8, device=device)
-        self.ckpt = torch.empty((store.n_layers + 1, T, H), dtype=torch.bfloat16, device=device)
+        # n_micro > 1: accum_step keeps that many micro-batches' checkpoints
+        self.n_micro = n_micro
+        self.ws = torch.empty(B.stack_accum_workspace_bytes(self.cfg, vocab, n_micro), dtype=torch.uint8,
+                              device=device)
+        self.ckpts = [torch.empty((store.n_layers + 1, T, H), dtype=torch.bfloat16, device=device)
+                      for _ in range(n_micro)]
+        self.ckpt = self.ckpts[0]
         self.logits = torch.empty((T, vocab), dtype=torch.float32, device=device)
         self.loss = torch.zeros(1, dtype=torch.float32, device=device)
         self.seq_logp = torch.zeros((2, batch), dtype=torch.float32, device=device)  # DPO: policy, reference
         # every layer's forward intermediates, when the backward skips the recompute
         self.act = None
         if keep_activations:
-            self.act = torch.empty(B.stack_activation_bytes(self.cfg, store.n_layers), dtype=torch.uint8,
+            self.act = torch.empty(B.stack_activation_bytes(self.cfg, store.n_layers) * n_micro, dtype=torch.uint8,
                                    device=device)
 
     def _io(self, ids, embed, final_norm, lm_head, lora_arr, mode, loss_scale):
@@ -311,6 +316,21 @@ class Stack:
     def step(self, ids, embed, final_norm, lm_head, lora_arr, mode=B.MODE_STREAMED, loss_scale=1.0):
         """One SFT micro-batch (cross-entropy on next tokens)."""
         B.stream_stack_step(self.handle, self._io(ids, embed, final_norm, lm_head, lora_arr, mode, loss_scale))
+
+    def accum_step(self, ids_list, embed, final_norm, lm_head, lora_arr, mode=B.MODE_STREAMED, loss_scale=None):
+        """len(ids_list) SFT micro-batches in one walk over the stack per
+        direction (gradient accumulation); loss_scale defaults to 1/n.  The
+        loss of the last micro-batch ends in self.loss."""
+        n = len(ids_list)
+        if n > self.n_micro:
+            raise ValueError(f"this Stack holds checkpoints for {self.n_micro} micro-batches, not {n}")
+        scale = 1.0 / n if loss_scale is None else loss_scale
+        ios = []
+        for m, ids in enumerate(ids_list):
+            io = self._io(ids, embed, final_norm, lm_head, lora_arr, mode, scale)
+            io.ckpt = self.ckpts[m].data_ptr()
+            ios.append(io)
+        B.stream_stack_accum_step(self.handle, ios)
 
     def dpo_step(self, ids, embed, final_norm, lm_head, lora_arr, beta=0.1, fused=True, mode=B.MODE_STREAMED,
                  loss_scale=1.0):

@@ -182,6 +182,59 @@ def test_gradient_accumulation_matches_oracle():
             assert report(f"L{i}.dB_{n}", g[n][1], r1["grads"][i][n][1] + r2["grads"][i][n][1]) < TOL
 
 
+def test_accumulated_walk_equals_sequential_micro_batches():
+    # Three micro-batches: one stream_stack_accum_step (each layer copied once
+    # per direction for all three) against three stream_stack_step calls.
+    n = 3
+    s = Setup(SMALL, 4, 512, 2, 64, "accw")
+    ids = [torch.from_numpy(synth.token_ids(f"accw.ids{m}", (2, 64), 512)).cuda() for m in range(n)]
+    arr = s.lora.array()
+    for m in range(n):
+        mode = B.MODE_STREAMED | (B.MODE_ZERO_GRADS if m == 0 else 0)
+        s.stack.step(ids[m], s.emb, s.fnorm, s.head, arr, mode=mode, loss_scale=1.0 / n)
+    torch.cuda.synchronize()
+    ref = s.snapshot()
+    ref_ckpt = s.stack.ckpt.clone()
+
+    def run(mode, keep=False):
+        acc = S.Stack(SMALL, s.store, 2, 64, 512, n_micro=n, keep_activations=keep)
+        B.stack_reset_stats(acc.handle)
+        acc.accum_step(ids, s.emb, s.fnorm, s.head, arr, mode=mode)
+        torch.cuda.synchronize()
+        g = [{k: (s.lora.dA[i][k].clone(), s.lora.dB[i][k].clone()) for k in s.lora.targets} for i in range(s.L)]
+        out = (acc.logits.clone(), acc.loss.clone(), g)
+        st = acc.stats()
+        ck = acc.ckpts[n - 1].clone()
+        acc.close()
+        return out, st, ck
+
+    got, st, ck = run(B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+    assert st.steps == n
+    assert st.copies == 2 * s.L - 2       # once per direction, not once per micro-batch
+    assert same(ref, got)                 # last micro-batch's logits and loss, every gradient
+    assert torch.equal(ck, ref_ckpt)
+    got_r, st_r, _ = run(B.MODE_RESIDENT | B.MODE_ZERO_GRADS)
+    assert st_r.copies == 0 and same(ref, got_r)
+    got_k, _, _ = run(B.MODE_STREAMED | B.MODE_ZERO_GRADS, keep=True)
+    assert same(ref, got_k)
+
+
+def test_accumulated_walk_argument_errors():
+    s = Setup(SMALL, 2, 256, 1, 32, "accx")
+    arr = s.lora.array()
+    with pytest.raises(B.LsfError) as e:
+        B.stream_stack_accum_step(s.stack.handle, [])
+    assert e.value.status == B.LSF_ERR_INVALID_ARG
+    # a workspace sized for one micro-batch is too small for two
+    io = s.stack._io(s.ids, s.emb, s.fnorm, s.head, arr, B.MODE_STREAMED, 0.5)
+    with pytest.raises(B.LsfError) as e:
+        B.stream_stack_accum_step(s.stack.handle, [io, io])
+    assert e.value.status == B.LSF_ERR_WORKSPACE
+    assert B.stack_accum_workspace_bytes(s.stack.cfg, 256, 2) > B.stack_workspace_bytes(s.stack.cfg, 256)
+    assert B.stack_accum_workspace_bytes(s.stack.cfg, 256, 1) == B.stack_workspace_bytes(s.stack.cfg, 256)
+    assert B.stack_accum_workspace_bytes(s.stack.cfg, 256, 0) == 0
+
+
 def test_adapters_disabled_changes_only_through_lora():
     s = Setup(SMALL, 2, 512, 1, 48, "dis", targets=("q", "v"))
     s.step(mode=B.MODE_STREAMED | B.MODE_FWD_ONLY, enabled=False)
