@@ -396,3 +396,51 @@ def test_bench_configuration_32_layers_full_vocabulary():
     y, _ = M.layer_fwd(x, W0, lora.numpy(0), oracle_shape(shape))
     assert report("layer0.y", bf16_tensor_to_np(layer1).reshape(1, seq, H), y) < TOL
     stack.close()
+
+
+def test_accumulated_walk_at_8b_shapes_batch4():
+    # The stack4 bench configuration on four 8B-shaped layers: four micro-batches
+    # of 4 x 512 tokens, vocabulary 128256.  One accumulated walk gives the bits
+    # of four sequential micro-batch steps (every gradient, the last logits and
+    # loss) with 2L - 2 copies; micro-batch by micro-batch takes 2L - 2 for the
+    # first and 2L - 4 for each further one (layers 0 and 1 stay resident).
+    shape = S.LLAMA8B
+    L, V, batch, seq, n = 4, 128256, 4, 512, 4
+    print(f"[stack] accumulated walk L={L} V={V} {n} x {batch} x {seq}", flush=True)
+    store = S.Store(shape, L, resident=False, pinned=True,
+                    weights_fn=lambda i: S.layer_weights_fp32(f"acc8b.layer{i}", shape))
+    lora = S.LoraSet(shape, L, prefix="acc8b.lora")
+    H = shape.hidden
+    _, emb = bf16_param("acc8b.embed", (V, H), 1.0)
+    _, head = bf16_param("acc8b.head", (V, H), 0.02)
+    fnorm = torch.ones(H, dtype=torch.bfloat16, device="cuda")
+    ids = [torch.from_numpy(synth.token_ids(f"acc8b.ids{m}", (batch, seq), V)).cuda() for m in range(n)]
+    arr = lora.array()
+
+    def grads():
+        return [{k: (lora.dA[i][k].clone(), lora.dB[i][k].clone()) for k in lora.targets} for i in range(L)]
+
+    seq_stack = S.Stack(shape, store, batch, seq, V)
+    B.stack_reset_stats(seq_stack.handle)
+    for m in range(n):
+        mode = B.MODE_STREAMED | (B.MODE_ZERO_GRADS if m == 0 else 0)
+        seq_stack.step(ids[m], emb, fnorm, head, arr, mode=mode, loss_scale=1.0 / n)
+    torch.cuda.synchronize()
+    copies_seq = seq_stack.stats().copies
+    ref = (seq_stack.logits.clone(), seq_stack.loss.clone(), grads())
+    seq_stack.close()
+    del seq_stack
+    torch.cuda.empty_cache()
+
+    acc = S.Stack(shape, store, batch, seq, V, n_micro=n)
+    B.stack_reset_stats(acc.handle)
+    acc.accum_step(ids, emb, fnorm, head, arr, mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+    torch.cuda.synchronize()
+    st = acc.stats()
+    got = (acc.logits.clone(), acc.loss.clone(), grads())
+    acc.close()
+    print(f"  copies: {copies_seq} micro-batch by micro-batch, {st.copies} in one walk", flush=True)
+    assert st.copies == 2 * L - 2
+    assert copies_seq == (2 * L - 2) + (n - 1) * (2 * L - 4)
+    assert same(ref, got)
+    assert all(torch.isfinite(ref[2][i][k][0]).all() for i in range(L) for k in lora.targets)
