@@ -1,5 +1,6 @@
-// Wide forward NF4 GEMM for gfx950, used when N is large (the gate|up
-// projection):  C[M, N] = A[M, K] . deq(W)[N, K]^T  (+ LoRA, + epilogue).
+// Wide forward NF4 GEMM for gfx950, used when the output has many 256 x 256
+// tiles (the gate|up projection; q|k|v from 2048 tokens):
+// C[M, N] = A[M, K] . deq(W)[N, K]^T  (+ LoRA, + epilogue).
 //
 // Same arithmetic as the general kernel in gemm.hip (every weight decoded to
 // bf16_rne(level * absmax), bf16 MFMA with fp32 accumulation, the k order of
@@ -334,12 +335,14 @@ hipError_t launch_wide_fmt(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
 
 // The wide kernel needs whole 256-column tiles (and 128-row halves of them in
 // pair mode), 64-deep absmax blocks, 16-byte aligned A rows, 8-byte aligned
-// codes, and no split-K.  It is chosen for N >= 16384, where its 256 x 256
-// tiles still fill the 256 compute units, and K >= 2048: with short
-// contractions its prologue dominates (measured 1.7x slower than the general
-// kernel at K = 512).
+// codes, and no split-K.  It is chosen for N >= 16384 (gate|up), or when
+// there are at least 192 of its 256 x 256 tiles, three quarters of the 256
+// compute units (q|k|v from 2048 tokens: 144 vs 174 us there, measured), and
+// K >= 2048: with short contractions its prologue dominates (measured 1.7x
+// slower than the general kernel at K = 512).
 bool gemm_wide_applies(const GemmArgs& g, const EpiArgs& e) {
-  if (g.splits != 1 || g.M < 256 || g.N < 16384 || g.N % WBN != 0) return false;
+  if (g.splits != 1 || g.M < 256 || g.N % WBN != 0) return false;
+  if (g.N < 16384 && (int64_t)((g.M + WBM - 1) / WBM) * (g.N / WBN) < 192) return false;
   // fp32 absmax only: with the double-quantised absmax (two more loads in
   // flight per code set) the kernel no longer fits its 256 registers.
   if (g.W.fmt != FMT_NF4) return false;

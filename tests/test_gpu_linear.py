@@ -87,6 +87,28 @@ def test_wide_forward_kernel_matches_oracle_and_general_kernel():
         assert np.array_equal(res[k][0], res2[k][0]), k
 
 
+def test_wide_kernel_chosen_by_tile_count():
+    # 6144 outputs (the q|k|v width) over 2048 tokens: 8 x 24 = 192 tiles of
+    # 256 x 256, enough for the wide kernel; it matches the oracle and gives the
+    # general kernel's bits.
+    n0 = B.gemm_wide_launch_count()
+    res = _run("linwq", 6144, 2048, 2048, 16, 16.0)
+    assert B.gemm_wide_launch_count() == n0 + 1
+    for k, (g, r) in res.items():
+        assert report(k, g, r) < TOL, k
+    B.gemm_set_wide(False)
+    try:
+        res2 = _run("linwq", 6144, 2048, 2048, 16, 16.0)
+    finally:
+        B.gemm_set_wide(True)
+    for k in res:
+        assert np.array_equal(res[k][0], res2[k][0]), k
+    # 512 tokens of the same width: 48 tiles, the general kernel
+    n1 = B.gemm_wide_launch_count()
+    _run("linwq5", 6144, 2048, 512, 16, 16.0)
+    assert B.gemm_wide_launch_count() == n1
+
+
 def test_b_zero_reproduces_base_output_bitwise():
     a = _run("lin4", 256, 512, 96, 16, 16.0, b_zero=True)
     b = _run("lin4", 256, 512, 96, 16, 16.0, adapter=False)
