@@ -272,10 +272,86 @@ __device__ __forceinline__ void compute_and_stage(const uint16_t* As, const uint
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 
+// dg and du of one element from the input gradient v of a = silu(g) u.
+__device__ __forceinline__ void swiglu_grad(float v, float gv, float uv, float& dg, float& du) {
+  const float sg = 1.0f / (1.0f + __expf(-gv));
+  dg = v * uv * sg * (1.0f + gv * (1.0f - sg));
+  du = v * gv * sg;
+}
+
+// This wave's LDS accesses so far are complete, and neither the compiler nor
+// the hardware moves later ones ahead of them.
+__device__ __forceinline__ void wave_lds_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// SwiGLU backward with the accumulator tile passed through LDS.  Each wave
+// writes 32 rows of its 64 x 64 tile at a time into its own 8 KB of the stage
+// buffers (idle once the k loop has ended), then every lane takes 8
+// consecutive columns of one row, so the gate/up reads and the dg/du writes
+// are 16-byte accesses, 128 contiguous bytes per 8 lanes.  Rows past M load a
+// clamped row and store nothing.  Same arithmetic per element as the direct
+// form, so the same bits.
+__device__ void swiglu_bwd_staged(const GemmArgs& g, const EpiArgs& e, const f32x4 (&acc)[4][4], int m0, int ntile,
+                                  int lane, int wm, int wn, float* red) {
+  const int lr = lane & 15, lg = lane >> 4;
+  float* my = red + (wm * 2 + wn) * (32 * 64);
+  const int cq = (lane & 7) * 8;
+  const int n = ntile * BN + wn * 64 + cq;
+  uint16_t* C = static_cast<uint16_t*>(e.C);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int mf = 0; mf < 2; ++mf)
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) my[(mf * 16 + lg * 4 + i) * 64 + nf * 16 + lr] = acc[2 * h + mf][nf][i];
+    wave_lds_fence();
+    u32x4 gq[4], uq[4];
+    float4 v0[4], v1[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = p * 8 + (lane >> 3);
+      const int64_t m = min(m0 + wm * 64 + h * 32 + r, g.M - 1);
+      gq[p] = *reinterpret_cast<const u32x4*>(e.g + m * e.ldgu + n);
+      uq[p] = *reinterpret_cast<const u32x4*>(e.u + m * e.ldgu + n);
+      v0[p] = *reinterpret_cast<const float4*>(my + r * 64 + cq);
+      v1[p] = *reinterpret_cast<const float4*>(my + r * 64 + cq + 4);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int m = m0 + wm * 64 + h * 32 + p * 8 + (lane >> 3);
+      const float v[8] = {v0[p].x, v0[p].y, v0[p].z, v0[p].w, v1[p].x, v1[p].y, v1[p].z, v1[p].w};
+      u32x4 dgo, duo;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float dg0, du0, dg1, du1;
+        swiglu_grad(v[2 * q], bf16lo(gq[p][q]), bf16lo(uq[p][q]), dg0, du0);
+        swiglu_grad(v[2 * q + 1], bf16hi(gq[p][q]), bf16hi(uq[p][q]), dg1, du1);
+        dgo[q] = pack_bf16x2(dg0, dg1);
+        duo[q] = pack_bf16x2(du0, du1);
+      }
+      if (m < g.M) {
+        *reinterpret_cast<u32x4*>(C + (int64_t)m * e.ldc + n) = dgo;
+        *reinterpret_cast<u32x4*>(C + (int64_t)m * e.ldc + g.N + n) = duo;
+      }
+    }
+    wave_lds_fence();
+  }
+}
+
 template <bool NN, int EPI>
 __device__ void epilogue(const GemmArgs& g, const EpiArgs& e, const f32x4 (&acc)[4][4], int m0, int ntile,
-                         int lane, int wm, int wn, int z) {
+                         int lane, int wm, int wn, int z, uint16_t* lds_base) {
   const int lr = lane & 15, lg = lane >> 4;
+  if constexpr (NN && EPI == EPI_SWIGLU_BWD) {
+    swiglu_bwd_staged(g, e, acc, m0, ntile, lane, wm, wn, reinterpret_cast<float*>(lds_base));
+    return;
+  }
   if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
     for (int mf = 0; mf < 4; ++mf)
@@ -313,13 +389,6 @@ __device__ void epilogue(const GemmArgs& g, const EpiArgs& e, const f32x4 (&acc)
         } else if constexpr (EPI == EPI_RESID_BF16) {
           static_cast<uint16_t*>(e.C)[(int64_t)m * e.ldc + n] =
               f32_to_bf16(bf16_to_f32(e.R[(int64_t)m * e.ldr + n]) + v);
-        } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-          const float gv = bf16_to_f32(e.g[(int64_t)m * e.ldgu + n]);
-          const float uv = bf16_to_f32(e.u[(int64_t)m * e.ldgu + n]);
-          const float sg = 1.0f / (1.0f + __expf(-gv));
-          uint16_t* C = static_cast<uint16_t*>(e.C);
-          C[(int64_t)m * e.ldc + n] = f32_to_bf16(v * uv * sg * (1.0f + gv * (1.0f - sg)));
-          C[(int64_t)m * e.ldc + g.N + n] = f32_to_bf16(v * gv * sg);
         }
       }
     }
@@ -406,7 +475,7 @@ __global__ __launch_bounds__(Cfg<BM>::NTHR, Cfg<BM>::MIN_BLOCKS) void gemm_kerne
     compute_tile<NN>(b0, b0 + C::A_ELEMS, lane, wm, wn, acc);
     __syncthreads();
   }
-  epilogue<NN, EPI>(g, e, acc, m0, ntile, lane, wm, wn, z);
+  epilogue<NN, EPI>(g, e, acc, m0, ntile, lane, wm, wn, z, &lds[0][0]);
 }
 
 template <int BM, bool NN, int EPI>
@@ -434,7 +503,13 @@ hipError_t launch_bm(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
       if constexpr (!NN) return launch_fmt<BM, NN, EPI_SWIGLU>(g, e, s);
       break;
     case EPI_SWIGLU_BWD:
-      if constexpr (NN) return launch_fmt<BM, NN, EPI_SWIGLU_BWD>(g, e, s);
+      if constexpr (NN) {
+        // 16-byte accesses to g, u and both halves of C
+        const bool al = ((uintptr_t)e.C | (uintptr_t)e.g | (uintptr_t)e.u) % 16 == 0 && e.ldc % 8 == 0 &&
+                        e.ldgu % 8 == 0 && g.N % 8 == 0;
+        if (!al) return hipErrorInvalidValue;
+        return launch_fmt<BM, NN, EPI_SWIGLU_BWD>(g, e, s);
+      }
       break;
     default: break;
   }
