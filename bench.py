@@ -43,10 +43,10 @@ HBM_PEAK_GBPS = 8000.0
 PCIE5_X16_GBPS = 63.0            # theoretical per direction after 128b/130b encoding
 
 # HBM bytes per launch of the gate|up forward GEMM from two rocprofv3 --pmc passes
-# (profiles/pmc_traffic_layer8b_seq512.md): FETCH_SIZE 50048.06 KiB scaled by 1.99974
-# (the calibration kernel's ratio) + WRITE_SIZE 28691.52 KiB scaled by 1.0.  Valid only
+# (profiles/pmc_traffic_layer8b_seq512.md): FETCH_SIZE 50048.08 KiB scaled by 1.99975
+# (the calibration kernel's ratio) + WRITE_SIZE 28692.45 KiB scaled by 1.0.  Valid only
 # for the sources of that kernel they were taken on (hash below); otherwise null.
-GATE_UP_TRAFFIC_BYTES = (50048.06 * 1.99974 + 28691.52 * 1.0) * 1024
+GATE_UP_TRAFFIC_BYTES = (50048.08 * 1.99975 + 28692.45 * 1.0) * 1024
 GATE_UP_TRAFFIC_SRC = "9a733b284c9f0cb1"
 # Algorithmic bytes of one such launch: NF4 codes 58.72 MB + absmax 7.34 MB + x 4.19 MB +
 # LoRA (U, B) 1.9 MB read; a 14.7 MB (forward) or a, g, u 44.0 MB (recompute) written.
@@ -296,7 +296,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": round(GATE_UP_TRAFFIC_BYTES) if (same_src and measured_cfg) else None,
-                "traffic_unit": "HBM bytes per launch (FETCH_SIZE x1.99974 + WRITE_SIZE x1.000)",
+                "traffic_unit": "HBM bytes per launch (FETCH_SIZE x1.99975 + WRITE_SIZE x1.000)",
                 "algorithmic_bytes": round(GATE_UP_ALGO_BYTES) if measured_cfg else None,
                 "kernel": f"fused {base} gate|up GEMM + SwiGLU epilogue, {T}x{2 * shape.intermediate}x{H}",
                 "flop_per_launch": flops["gate_up"], "avg_launch_us": round(avg * 1e6, 2),
