@@ -138,7 +138,8 @@ typedef struct {
   float rope_theta;     /* RoPE base, e.g. 500000 */
   float rms_eps;        /* RMSNorm epsilon, e.g. 1e-5 */
   int32_t batch;        /* sequences per micro-batch (>= 1) */
-  int32_t seq;          /* tokens per sequence (>= 1); positions restart at 0 */
+  int32_t seq;          /* tokens per sequence (>= 1); positions restart at 0;
+                           batch * seq <= 2^20 (else LSF_ERR_SHAPE) */
 } lsf_layer_cfg;
 
 /* Weight storage formats of the frozen projections. */

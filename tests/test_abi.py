@@ -66,6 +66,9 @@ def test_workspace_sizes(lib):
     assert B.stack_workspace_bytes(LLAMA8B.cfg(1, 512), 128256) > w1
     assert B.linear_workspace_bytes(64, 256, 256, 8) > 0
     assert B.linear_workspace_bytes(0, 256, 256, 8) == 0
+    # at most 2^20 tokens per call: one more and the size query reports 0
+    assert B.layer_workspace_bytes(LLAMA8B.cfg(2048, 512)) > 0
+    assert B.layer_workspace_bytes(LLAMA8B.cfg(2049, 512)) == 0
 
 
 def _status(fn, *args):
@@ -90,6 +93,9 @@ def test_invalid_arguments_are_rejected_before_any_launch(lib):
     assert L.layer_fwd(ctypes.byref(cfg), None, None, None, None, None, 0, None) == B.LSF_ERR_SHAPE
     cfg = LLAMA8B.cfg(0, 512)
     assert L.layer_bwd(ctypes.byref(cfg), None, None, None, None, None, None, 0, None) == B.LSF_ERR_SHAPE
+    cfg = LLAMA8B.cfg(2049, 512)
+    assert L.layer_fwd(ctypes.byref(cfg), None, None, None, None, None, 0, None) == B.LSF_ERR_SHAPE
+    assert b"too many tokens" in L.lsf_last_error()
     cfg = LLAMA8B.cfg(1, 512)
     cfg.n_kv_heads = 5
     assert L.layer_workspace_bytes(ctypes.byref(cfg)) == 0
