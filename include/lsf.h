@@ -78,8 +78,10 @@ LSF_API const char* lsf_last_error(void);
 LSF_API const char* lsf_version(void);
 
 /* Diagnostics: the kernel that runs wide forward NF4 GEMMs (fp32 absmax,
- * N >= 16384 with whole 256-column tiles, K >= 2048, at least 256 tokens,
- * no split-K: the gate|up projection of an 8B-shaped layer).  enable = 1 (the default):
+ * whole 256-column tiles, K >= 2048, at least 256 tokens, no split-K, and
+ * either N >= 16384 or at least 192 tiles of 256 x 256: the gate|up
+ * projection of an 8B-shaped layer, and q|k|v from 2048 tokens on, with the
+ * bf16 or SwiGLU epilogue).  enable = 1 (the default):
  * the 256 x 256 ping-pong kernel; 0: the general 128-column kernel.  Both
  * compute the same contraction in the same order and give bitwise-identical
  * results; the switch lets tests and profiles compare them.  Process-wide;
