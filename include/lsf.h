@@ -186,9 +186,9 @@ typedef struct {
 /* -------------------------------------------------------- one NF4 linear --
  * y = x W^T + s (x A^T) B^T   (LoRA on a frozen NF4 weight; [NEWS], [TUTORIAL]
  * item 3).  x: device bf16 [tokens, n_in]; y: device bf16 [tokens, n_out].
- * n_out % 128 == 0, n_in % 64 == 0, tokens >= 1; with an adapter, rank is one of
- * 4, 8, 16, 32, 64 (else LSF_ERR_SHAPE).  A/B may be NULL (no adapter).  ws: device workspace of at least
- * linear_workspace_bytes() bytes. */
+ * n_out % 128 == 0, n_in % 128 == 0, tokens >= 1; with an adapter, rank is one
+ * of 4, 8, 16, 32, 64 (else LSF_ERR_SHAPE).  A/B may be NULL (no adapter).
+ * ws: device workspace of at least linear_workspace_bytes() bytes. */
 LSF_API size_t linear_workspace_bytes(int32_t tokens, int32_t n_out, int32_t n_in, int32_t rank);
 LSF_API lsf_status linear_fwd(const lsf_weight* w, int32_t format, int32_t n_out, int32_t n_in,
                       const float* A, const float* B, int32_t rank, float scale,
