@@ -33,6 +33,8 @@
  *     for the stack handle, which keeps the pointers given to stack_create
  *     until stack_destroy.  Device pointers must come from device memory
  *     (hipMalloc / torch); "host" pointers are host memory.
+ *   - No call allocates device memory: scratch space is a caller-provided
+ *     workspace whose size a *_workspace_bytes() query gives.
  *   - Work is enqueued on the given HIP stream (lsf_stream is a hipStream_t;
  *     NULL is the null stream) and the call returns without waiting; faults
  *     surface at the caller's next synchronisation.
