@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload stack1|stack4|dpo|dpo-unfused]
                     [--format nf4|nf4dq|bf16] [--optimizer adamw|adamw8] [--lora-targets all|qv]
+                    [--accum-order layer|micro] [--keep-activations] [--no-cpu-baseline]
 
 Workload (default "stack1"): 32 Llama-3.1-8B-shaped decoder layers (hidden
 4096, intermediate 14336, 32 query / 8 kv heads of 128, RoPE theta 500000),
