@@ -38,7 +38,10 @@ Backward formulas (dy is the incoming gradient):
 
 Parity: forward pinned by library routines (torch CPU scaled-dot-product
 attention, rms_norm, cross_entropy, silu; complex-number RoPE) and special
-cases; backward pinned by fp64 central finite differences on tiny shapes.
+cases; backward pinned by fp64 central finite differences on tiny shapes;
+``round_bf16`` pinned against torch's bf16 cast (random bit patterns and
+hand-built ties); a batch pinned to equal its sequences run one at a time
+(layer output, rotated q and k, input gradient, summed adapter gradients).
 """
 import numpy as np
 

@@ -286,3 +286,91 @@ def test_loss_scale_scales_gradients_only():
     b = M.stack_step(ids, emb, [W], [L], np.ones(cfg.hidden), head, cfg, loss_scale=0.25)
     assert a["loss"] == b["loss"]
     np.testing.assert_allclose(b["grads"][0]["up"][0], 0.25 * a["grads"][0]["up"][0], rtol=1e-12)
+
+
+# --------------------------------------------------- bf16 rounding, batches
+
+def test_round_bf16_matches_torch_cast():
+    """The layer-boundary rounding the stack oracle applies (the checkpoints
+    are bf16) is round-to-nearest-even: torch's bf16 cast on 10^5 values over
+    the whole fp32 range (normals, subnormals, signed zeros) and hand-built
+    ties.  A truncating rounding or a ties-away rule fails here."""
+    from oracle import nf4 as onf4
+    rng = np.random.default_rng(31)
+    bits = rng.integers(0, 2 ** 32, 100000, dtype=np.uint64).astype(np.uint32)
+    bits = bits[((bits >> 23) & 0xFF) != 0xFF]  # finite values only
+    x = np.concatenate([bits.view(np.float32),
+                        rng.standard_normal(20000).astype(np.float32),
+                        np.array([0.0, -0.0, 1e-45, -1e-45, 3.3895314e38], np.float32)])
+    got = M.round_bf16(x)
+    assert got.dtype == np.float32
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+    # the same bits as the NF4 module's own rounding (two independent writings)
+    np.testing.assert_array_equal(got.view(np.uint32) >> 16, onf4.bf16_round(x).astype(np.uint32))
+    # exact ties go to the even neighbour; one ulp above a tie rounds up
+    e = 2.0 ** -8  # half a bf16 ulp at 1.0
+    cases = [(1 + e, 0x3F80), (1 + 3 * e, 0x3F82), (-(1 + e), 0xBF80), (1 + e + 2 ** -23, 0x3F81),
+             (2 - e, 0x4000), (1 - e / 2, 0x3F80)]
+    for v, want in cases:
+        r = M.round_bf16(np.array([v], np.float32))
+        assert int(r.view(np.uint32)[0]) >> 16 == want, (v, hex(int(r.view(np.uint32)[0])))
+    # fp64 inputs are rounded through fp32, exactly as torch casts them
+    x64 = rng.standard_normal(5000) * 3.0
+    x64[:3] = [1 + e + 2 ** -40, -(1 + e + 2 ** -40), 1 + e]
+    ref64 = torch.from_numpy(x64).to(torch.bfloat16).to(torch.float64).numpy()
+    got64 = M.round_bf16(x64)
+    assert got64.dtype == np.float64
+    np.testing.assert_array_equal(got64, ref64)
+
+
+def test_batched_layer_equals_per_sequence_calls():
+    """A batch of sequences is a batch of independent sequences: RoPE
+    positions restart at 0 and no query attends to another sequence.  The
+    layer on a 3-sequence batch must equal three 1-sequence calls (output and
+    input gradient per sequence; adapter gradients as their sum), and so must
+    the rotated queries and keys it keeps.  Not bit for
+    bit: BLAS blocks a [3T, H] product differently from a [T, H] one, which
+    moves fp64 results by ~1e-14; a leaked position or cross-sequence
+    attention moves them by O(1)."""
+    cfg = _cfg()
+    rng = np.random.default_rng(32)
+    W, L = _weights(cfg, rng)
+    nb, T = 3, 9
+    x = rng.standard_normal((nb, T, cfg.hidden))
+    dy = rng.standard_normal((nb, T, cfg.hidden))
+    y, cache = M.layer_fwd(x, W, L, cfg)
+    dx, grads = M.layer_bwd(dy, W, L, cfg, cache)
+    gsum = {n: [np.zeros_like(a) for a in grads[n]] for n in grads}
+    for b in range(nb):
+        yb, cb = M.layer_fwd(x[b:b + 1], W, L, cfg)
+        dxb, gb = M.layer_bwd(dy[b:b + 1], W, L, cfg, cb)
+        # the rotated q and k themselves (attention scores depend only on
+        # position differences, so the outputs alone cannot show an offset)
+        np.testing.assert_allclose(cache["qr"][b], cb["qr"][0], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(cache["kr"][b], cb["kr"][0], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(y[b], yb[0], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dx[b], dxb[0], rtol=1e-12, atol=1e-12)
+        for n in gb:
+            for k in range(2):
+                gsum[n][k] += gb[n][k]
+    for n in grads:
+        for k in range(2):
+            np.testing.assert_allclose(grads[n][k], gsum[n][k], rtol=1e-11, atol=1e-12)
+    # the same holds for the whole stack step: two sequences = two steps,
+    # each with half the weight of the mean over labelled positions
+    V = 48
+    ids = rng.integers(0, V, (2, 7))
+    emb = rng.standard_normal((V, cfg.hidden))
+    head = rng.standard_normal((V, cfg.hidden)) * 0.1
+    fn = np.ones(cfg.hidden)
+    both = M.stack_step(ids, emb, [W], [L], fn, head, cfg)
+    parts = [M.stack_step(ids[b:b + 1], emb, [W], [L], fn, head, cfg, loss_scale=0.5) for b in range(2)]
+    np.testing.assert_allclose(both["logits"], np.concatenate([p["logits"] for p in parts]), rtol=1e-12,
+                               atol=1e-12)
+    assert abs(both["loss"] - 0.5 * (parts[0]["loss"] + parts[1]["loss"])) < 1e-12
+    for n in M.PROJ:
+        for k in range(2):
+            np.testing.assert_allclose(both["grads"][0][n][k],
+                                       parts[0]["grads"][0][n][k] + parts[1]["grads"][0][n][k],
+                                       rtol=1e-10, atol=1e-13)
