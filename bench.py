@@ -1,6 +1,7 @@
 """Throughput of the streamed NF4 + LoRA training step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload stack1|stack4|dpo|dpo-unfused]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--repeat 3]
+                    [--workload stack1|stack4|dpo|dpo-unfused|layer|linear]
                     [--format nf4|nf4dq|bf16] [--optimizer adamw|adamw8] [--lora-targets all|qv]
                     [--accum-order layer|micro] [--keep-activations] [--no-cpu-baseline]
 
@@ -18,8 +19,12 @@ the stack once per micro-batch instead; both give the same bits).  "dpo" is the 
 chosen/rejected pairs of 512 tokens (4 sequences, pair p sharing a 256-token
 prompt), DPO with beta 0.1, the reference log-probabilities from the same
 streamed base with the adapters off, computed in the policy's layer visit
-("dpo-unfused": in a separate pass over the stack).  Inputs and weights are
-seeded synthetic data.
+("dpo-unfused": in a separate pass over the stack).  "layer" is one 8B-shaped
+decoder layer at 512 tokens, resident: forward, then the backward that
+recomputes it (t_fwd, t_bwd, layer tokens/s, per-kernel MFMA fractions).
+"linear" is one 256 x 256 NF4 linear with a rank-8 LoRA adapter over 64
+tokens, forward + backward (latency; launch-bound, no roofline claim).  Inputs
+and weights are seeded synthetic data.
 
 Prints one JSON line.  ``value`` is tokens per second over the timed steps,
 with every input already resident (the frozen store in pinned host memory is
@@ -28,7 +33,9 @@ The timed steps carry HIP events around the gate|up forward GEMM only (the
 ``roofline`` kernel); a diagnostic pass of a few more steps afterwards times
 every kernel class and every copy (``kernels``, ``layer_gemms`` and the
 copy-engine figures in ``h2d``), since events on every kernel and copy slow
-the step by a few percent.
+the step by a few percent.  The timed region runs ``--repeat`` times (each
+``--steps`` steps); ``value`` is the mean, and ``repeat`` lists every run with
+the standard deviation.
 """
 import argparse
 import json
@@ -69,7 +76,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", choices=["stack1", "stack4", "dpo", "dpo-unfused"], default="stack1")
+    p.add_argument("--repeat", type=int, default=3, help="timed runs of --steps steps each (mean and sd)")
+    p.add_argument("--workload", choices=["stack1", "stack4", "dpo", "dpo-unfused", "layer", "linear"],
+                   default="stack1")
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--format", choices=["nf4", "nf4dq", "bf16"], default="nf4",
                    help="frozen-base storage: NF4 with fp32 absmax, NF4 with 8-bit double-quantised absmax, "
@@ -124,37 +133,129 @@ def measure_link_peak(torch, nbytes=1 << 30, reps=5):
     return best
 
 
-def cpu_baseline(shape, T_layer=512):
-    """The oracle (fp64 NumPy) on a bounded sample of the same workload: one
-    decoder layer forward + backward over 512 tokens, and the head over a
-    1/16 slice of the vocabulary; scaled to the full step."""
-    from layer_streamed_frozen_amd import store as S
-    from layer_streamed_frozen_amd import synth
-    from oracle import model as M
-    from oracle import nf4 as onf4
+def host_info():
+    """The CPU the oracle baseline runs on: core counts, the BLAS threads NumPy
+    uses, and the model name."""
     try:
         from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 0) for d in threadpool_info()] + [1])
+        blas = max([d.get("num_threads", 0) for d in threadpool_info()] + [0]) or None
     except Exception:
-        threads = os.cpu_count()
-    W = S.layer_weights_fp32("layer0", shape)
+        blas = None
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"os_cpu_count": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)), "blas_threads": blas,
+            "cpu_model": model}
+
+
+def _link_gbps(speed, width):
+    """Theoretical one-direction PCIe rate from sysfs strings ("32.0 GT/s PCIe", "16")."""
+    try:
+        gts = float(speed.split()[0])
+        lanes = int(width)
+    except (ValueError, IndexError, AttributeError):
+        return None
+    enc = 128.0 / 130.0 if gts >= 8.0 else 0.8
+    return round(gts * lanes * enc / 8.0, 2)
+
+
+def pcie_link(torch):
+    """The GPU's PCIe link as sysfs reports it: the device's own link and the
+    upstream ports between it and the root complex (speed, width, theoretical
+    GB/s)."""
+    props = torch.cuda.get_device_properties(0)
+    dom, bus, dev = (getattr(props, k, None) for k in ("pci_domain_id", "pci_bus_id", "pci_device_id"))
+    path = None
+    if bus is not None and dev is not None:
+        cand = f"/sys/bus/pci/devices/{(dom or 0):04x}:{bus:02x}:{dev:02x}.0"
+        if os.path.exists(cand):
+            path = cand
+    if path is None:
+        return {"found": False}
+    out = {"found": True, "bdf": os.path.basename(path), "hops": []}
+    p = os.path.realpath(path)
+    while os.path.basename(p).count(":") == 2:
+        def rd(name):
+            try:
+                with open(os.path.join(p, name)) as f:
+                    return f.read().strip()
+            except OSError:
+                return None
+        cs, cw, ms, mw = rd("current_link_speed"), rd("current_link_width"), rd("max_link_speed"), rd("max_link_width")
+        if cs is not None:
+            out["hops"].append({"bdf": os.path.basename(p), "current_speed": cs, "current_width": cw,
+                                "max_speed": ms, "max_width": mw, "current_GBps": _link_gbps(cs, cw)})
+        p = os.path.dirname(p)
+    if out["hops"]:
+        rates = [h["current_GBps"] for h in out["hops"] if h["current_GBps"]]
+        out["narrowest_GBps"] = min(rates) if rates else None
+    return out
+
+
+def _oracle_layer(shape, prefix, dtype):
+    """Dense oracle weights (the oracle's own NF4 round trip) and the adapters
+    LoraSet draws for layer 0, in dtype."""
+    from layer_streamed_frozen_amd import store as S
+    from layer_streamed_frozen_amd import synth
+    from oracle import nf4 as onf4
+    W = S.layer_weights_fp32(prefix, shape)
     dense = {}
     for n in S.PROJ:
         p, a = onf4.nf4_quantize(W[n])
-        dense[n] = onf4.nf4_dequantize(p, a, W[n].shape).astype(np.float64)
-    dense["norm1"] = np.ones(shape.hidden)
-    dense["norm2"] = np.ones(shape.hidden)
-    ldict = {}  # the same adapter values LoraSet draws for layer 0
+        dense[n] = onf4.nf4_dequantize(p, a, W[n].shape).astype(dtype)
+    dense["norm1"] = np.ones(shape.hidden, dtype)
+    dense["norm2"] = np.ones(shape.hidden, dtype)
+    ldict = {}
     for n, (o, inn) in shape.proj_shapes().items():
         lim = 1.0 / np.sqrt(inn)
-        ldict[n] = (synth.uniform(f"lora0.{n}.A", (shape.rank, inn), -lim, lim).astype(np.float64),
-                    synth.normal(f"lora0.{n}.B", (o, shape.rank), 0.01).astype(np.float64))
+        ldict[n] = (synth.uniform(f"lora0.{n}.A", (shape.rank, inn), -lim, lim).astype(dtype),
+                    synth.normal(f"lora0.{n}.B", (o, shape.rank), 0.01).astype(dtype))
+    return dense, ldict
+
+
+def cpu_baseline(shape, workload, T_layer=512, budget_s=15.0):
+    """The oracle (NumPy, fp32 arrays, multithreaded BLAS) on a bounded sample
+    of the workload, on this host's cores: one decoder layer forward + backward
+    over 512 tokens (repeated for about budget_s), and for the stack workloads
+    also the head over a 1/16 slice of the vocabulary; scaled to the unit of
+    the GPU line."""
+    from layer_streamed_frozen_amd import synth
+    from oracle import model as M
+    from oracle import nf4 as onf4
+    dt = np.float32
+    info = host_info()
+    cores = info["blas_threads"] or info["affinity_cpus"]
+    if workload == "linear":
+        W = synth.normal("cfg1.W", (256, 256), 0.02)
+        p, a = onf4.nf4_quantize(W)
+        Wd = onf4.nf4_dequantize(p, a, W.shape).astype(dt)
+        A = synth.uniform("cfg1.A", (8, 256), -1 / 16, 1 / 16).astype(dt)
+        Bm = synth.normal("cfg1.B", (256, 8), 0.01).astype(dt)
+        x = synth.bf16_exact(synth.normal("cfg1.X", (64, 256)))[0].astype(dt)
+        dy = synth.bf16_exact(synth.normal("cfg1.dY", (64, 256)))[0].astype(dt)
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < min(budget_s, 5.0):
+            y, u = M.lora_linear_fwd(x, Wd, A, Bm, 2.0)
+            M.lora_linear_bwd(dy, x, Wd, A, Bm, 2.0, u)
+            reps += 1
+        spent = time.perf_counter() - t0
+        return {"value": round(spent / reps * 1e6, 2), "unit": "us per fwd+bwd", "cores": int(cores),
+                "kind": "oracle", "dtype": "fp32", "host": info,
+                "sample": f"the same 256x256 NF4 linear + rank-8 LoRA over 64 tokens, {reps} fwd+bwd repetitions",
+                "seconds_measured": round(spent, 2)}
+    dense, ldict = _oracle_layer(shape, "layer0", dt)
     oc = M.LayerShape(shape.hidden, shape.intermediate, shape.n_heads, shape.n_kv_heads, shape.head_dim,
                       rms_eps=shape.rms_eps, rope_theta=shape.rope_theta, lora_scale=shape.lora_scale)
-    x = synth.normal("cpu.x", (1, T_layer, shape.hidden)).astype(np.float64)
-    dy = synth.normal("cpu.dy", (1, T_layer, shape.hidden)).astype(np.float64)
+    x = synth.normal("cpu.x", (1, T_layer, shape.hidden)).astype(dt)
+    dy = synth.normal("cpu.dy", (1, T_layer, shape.hidden)).astype(dt)
     reps, spent = 0, 0.0
-    while reps < 2 or (spent < 15.0 and reps < 40):   # about 15 s of CPU work
+    while reps < 2 or (spent < budget_s and reps < 40):
         t0 = time.perf_counter()
         y, cache = M.layer_fwd(x, dense, ldict, oc)
         M.layer_bwd(dy, dense, ldict, oc, cache)
@@ -162,22 +263,34 @@ def cpu_baseline(shape, T_layer=512):
         reps += 1
         del y, cache
     t_layer = spent / reps
+    if workload == "layer":
+        return {"value": round(T_layer / t_layer, 2), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+                "dtype": "fp32", "host": info,
+                "sample": (f"one 8B-shaped layer forward + backward on {T_layer} tokens, {reps} repetitions "
+                           f"averaging {t_layer:.2f} s"),
+                "seconds_measured": round(spent, 2)}
     V16 = 128256 // 16
-    head = synth.normal("cpu.head", (V16, shape.hidden), 0.02).astype(np.float64)
-    h = synth.normal("cpu.h", (T_layer, shape.hidden)).astype(np.float64)
+    head = synth.normal("cpu.head", (V16, shape.hidden), 0.02).astype(dt)
+    h = synth.normal("cpu.h", (T_layer, shape.hidden)).astype(dt)
     ids = synth.token_ids("cpu.ids", (1, T_layer), V16)
     t0 = time.perf_counter()
     logits = h @ head.T
     lab, val = M.shifted_labels(ids)
     _, dz = M.cross_entropy_fwd_bwd(logits, lab, val)
-    _ = dz @ head
+    _ = dz.astype(dt) @ head
     t_head = (time.perf_counter() - t0) * 16
     t_step = 32 * t_layer + t_head
-    return {"value": T_layer / t_step, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": round(T_layer / t_step, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "dtype": "fp32", "host": info,
             "sample": (f"one 8B-shaped layer fwd+bwd on {T_layer} tokens, {reps} repetitions averaging "
                        f"{t_layer:.2f} s (x32 layers), plus head fwd+CE+dX on a 1/16 vocabulary slice "
-                       f"({t_head / 16:.2f} s, x16); fp64 NumPy"),
+                       f"({t_head / 16:.2f} s, x16); per-token rate of a 512-token step"),
             "seconds_measured": round(spent + t_head / 16, 2)}
+
+
+def mean_sd(v):
+    a = np.asarray(v, dtype=np.float64)
+    return float(a.mean()), float(a.std(ddof=1)) if len(a) > 1 else 0.0
 
 
 def main():
@@ -194,6 +307,14 @@ def main():
     B.lib()  # fail loudly if the HIP library is missing
     torch.cuda.set_device(0)
     shape = S.LLAMA8B
+    if args.workload in ("linear", "layer"):
+        out = (run_linear if args.workload == "linear" else run_layer)(args, torch, B, S, synth)
+        out["pcie_link"] = pcie_link(torch)
+        if not args.no_cpu_baseline:
+            log("timing the CPU oracle on a bounded sample")
+            out["cpu_baseline"] = cpu_baseline(shape, args.workload)
+        print(json.dumps(out), flush=True)
+        return
     L, V, seq = args.layers, 128256, 512
     batch, accum = {"stack1": (1, 1), "stack4": (4, 4), "dpo": (4, 1), "dpo-unfused": (4, 1)}[args.workload]
     dpo = args.workload.startswith("dpo")
@@ -264,22 +385,27 @@ def main():
     torch.cuda.synchronize()
     B.stack_reset_stats(stack.handle)
     torch.cuda.reset_peak_memory_stats()
-    log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(stack)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    runs = []
+    for r in range(max(1, args.repeat)):
+        log(f"timing {args.steps} steps (run {r + 1} of {max(1, args.repeat)})")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(stack)
+        torch.cuda.synchronize()
+        runs.append(time.perf_counter() - t0)
+    n_timed = args.steps * len(runs)
+    elapsed = sum(runs)
     st = stack.stats()
     loss = float(stack.loss.item())
     peak_gb = torch.cuda.max_memory_allocated() / 1e9
     tokens = args.steps * accum * T
-    value = tokens / elapsed
-    ms_step = elapsed / args.steps * 1e3
-    log(f"{value:.1f} tok/s, {ms_step:.2f} ms/step, loss {loss:.4f}")
+    rates = [tokens / e for e in runs]
+    value, value_sd = mean_sd(rates)
+    ms_step = elapsed / n_timed * 1e3
+    log(f"{value:.1f} +- {value_sd:.1f} tok/s over {len(runs)} runs, {ms_step:.2f} ms/step, loss {loss:.4f}")
 
-    bytes_step = st.bytes / args.steps
+    bytes_step = st.bytes / n_timed
     h2d = {"bytes_per_step": int(bytes_step), "copies_per_step": st.copies / args.steps,
            "GBps_over_step": round(bytes_step / (ms_step * 1e-3) / 1e9, 2),
            "measured_link_peak_GBps": round(link_peak, 2), "pcie5_x16_theoretical_GBps": PCIE5_X16_GBPS}
@@ -358,6 +484,8 @@ def main():
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "repeat": {"n": len(runs), "tokens_per_s": [round(v, 2) for v in rates], "mean": round(value, 2),
+                   "sd": round(value_sd, 2)},
         "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded random weights and token ids)",
         "config": {"workload": (f"streamed {L}-layer Llama-3.1-8B-shaped stack, {base_desc}, "
@@ -377,14 +505,161 @@ def main():
                    "backward": ("forward intermediates kept in HBM, no recompute" if args.keep_activations
                                 else "per-layer recompute from the checkpoint"),
                    "parallelism": "single GPU"},
-        "h2d": h2d, "roofline": roof, "layer_gemms": layer_gemms, "kernels": kernels,
+        "h2d": h2d, "pcie_link": pcie_link(torch), "roofline": roof, "layer_gemms": layer_gemms,
+        "kernels": kernels,
         "peak_device_GB": round(peak_gb, 3),
         "loss": loss,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(shape)
+        out["cpu_baseline"] = cpu_baseline(shape, args.workload)
     print(json.dumps(out), flush=True)
+
+
+def _events(torch, fn, n):
+    """Average ms of fn() over n calls, by events on the current stream."""
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(n):
+        fn()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def run_linear(args, torch, B, S, synth):
+    """One 256 x 256 NF4 linear + rank-8 LoRA (alpha 16) over 64 tokens:
+    forward + backward latency."""
+    n_out = n_in = 256
+    T, r, scale = 64, 8, 2.0
+    W = synth.normal("cfg1.W", (n_out, n_in), 0.02)
+    packed, absmax = B.nf4_quantize(torch.from_numpy(W.reshape(-1)).cuda())
+    w = B.weight(packed, absmax)
+    A = torch.from_numpy(synth.uniform("cfg1.A", (r, n_in), -1 / 16, 1 / 16)).cuda()
+    Bm = torch.from_numpy(synth.normal("cfg1.B", (n_out, r), 0.01)).cuda()
+    bits = lambda name, shp: torch.from_numpy(synth.bf16_exact(synth.normal(name, shp))[1].view(np.int16)) \
+        .view(torch.bfloat16).cuda()
+    x, dy = bits("cfg1.X", (T, n_in)), bits("cfg1.dY", (T, n_out))
+    ws = torch.empty(B.linear_workspace_bytes(T, n_out, n_in, r), dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, n_out), dtype=torch.bfloat16, device="cuda")
+    dx = torch.empty((T, n_in), dtype=torch.bfloat16, device="cuda")
+    dA = torch.zeros((r, n_in), dtype=torch.float32, device="cuda")
+    dB = torch.zeros((n_out, r), dtype=torch.float32, device="cuda")
+    fwd = lambda: B.linear_fwd(w, B.FMT_NF4, n_out, n_in, A, Bm, r, scale, x, y, ws)
+    bwd = lambda: B.linear_bwd(w, B.FMT_NF4, n_out, n_in, A, Bm, r, scale, x, dy, dx, dA, dB, ws)
+    both = lambda: (fwd(), bwd())
+    for _ in range(args.warmup):
+        both()
+    torch.cuda.synchronize()
+    steps = max(args.steps, 200)
+    runs = [_events(torch, both, steps) * 1e3 for _ in range(max(1, args.repeat))]
+    t_f = _events(torch, fwd, steps) * 1e3
+    t_b = _events(torch, bwd, steps) * 1e3
+    value, sd = mean_sd(runs)
+    log(f"linear fwd+bwd {value:.2f} +- {sd:.2f} us (fwd {t_f:.2f}, bwd {t_b:.2f})")
+    return {"metric": "single NF4 linear + LoRA fwd+bwd latency (256x256, r 8, 64 tokens)", "value": round(value, 2),
+            "unit": "us", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+            "repeat": {"n": len(runs), "us": [round(v, 2) for v in runs], "mean": round(value, 2),
+                       "sd": round(sd, 2)},
+            "ms_per_step": round(value / 1e3, 5), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic (seeded)",
+            "config": {"workload": "one 256x256 NF4 linear (bs 64, fp32 absmax) + LoRA r 8 alpha 16, 64 tokens, "
+                                   "forward + backward (dx, dA, dB)", "parallelism": "single GPU"},
+            "t_fwd_us": round(t_f, 2), "t_bwd_us": round(t_b, 2),
+            "roofline": None, "roofline_note": "launch-bound (a few microseconds of kernels); no roofline claim"}
+
+
+def run_layer(args, torch, B, S, synth):
+    """One 8B-shaped NF4 decoder layer (LoRA r16 on all seven projections) at
+    512 tokens, resident: forward, then the recomputing backward."""
+    shape = S.LLAMA8B
+    T, H = 512, shape.hidden
+    W = S.layer_weights_fp32("layer0", shape)
+    blob = S.build_layer_blob(shape, W)
+    cfg = shape.cfg(1, T)
+    lw = B.layer_weights_from_blob(cfg, B.FMT_NF4, blob.data_ptr())
+    lora = S.LoraSet(shape, 1)
+    bits = lambda name: torch.from_numpy(synth.bf16_exact(synth.normal(name, (T, H)))[1].view(np.int16)) \
+        .view(torch.bfloat16).cuda()
+    x, dy = bits("layer.x"), bits("layer.dy")
+    ws = torch.empty(B.layer_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    ls = lora.struct(0)
+    fwd = lambda: B.layer_fwd(cfg, lw, ls, x, y, ws)
+    bwd = lambda: B.layer_bwd(cfg, lw, ls, x, dy, dx, ws)
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    steps = max(args.steps, 10)
+    t_f, t_b, rates = [], [], []
+    for _ in range(max(1, args.repeat)):
+        f = _events(torch, fwd, steps)
+        b = _events(torch, bwd, steps)
+        t_f.append(f)
+        t_b.append(b)
+        rates.append(T / ((f + b) * 1e-3))
+    value, sd = mean_sd(rates)
+    tf, tb = float(np.mean(t_f)), float(np.mean(t_b))
+    log(f"layer: fwd {tf:.3f} ms, bwd {tb:.3f} ms, {value:.1f} +- {sd:.1f} tok/s")
+    # per-kernel classes: the same layer as a one-layer resident stack with every kernel timed
+    store = S.Store(shape, 1, resident=True, pinned=True, weights_fn=lambda i: W)
+    V = 1024
+    stack = S.Stack(shape, store, 1, T, V, flags=B.STACK_TIMING)
+    emb = torch.from_numpy(synth.bf16_exact(synth.normal("layer.embed", (V, H), 1.0))[1].view(np.int16)) \
+        .view(torch.bfloat16).cuda()
+    head = torch.from_numpy(synth.bf16_exact(synth.normal("layer.head", (V, H), 0.02))[1].view(np.int16)) \
+        .view(torch.bfloat16).cuda()
+    fnorm = torch.ones(H, dtype=torch.bfloat16, device="cuda")
+    ids = torch.from_numpy(synth.token_ids("layer.ids", (1, T), V)).cuda()
+    arr = lora.array()
+    stack.step(ids, emb, fnorm, head, arr, mode=B.MODE_RESIDENT | B.MODE_ZERO_GRADS)
+    torch.cuda.synchronize()
+    B.stack_reset_stats(stack.handle)
+    n_diag = max(1, args.diag_steps)
+    for _ in range(n_diag):
+        stack.step(ids, emb, fnorm, head, arr, mode=B.MODE_RESIDENT | B.MODE_ZERO_GRADS)
+    torch.cuda.synchronize()
+    st = stack.stats()
+    stack.close()
+    flops = gemm_flops(T, shape)
+    kernels, gemm_ms, gemm_flop = {}, 0.0, 0.0
+    for k, name in enumerate(B.KERNELS):
+        n = st.kernel_launches[k]
+        base = name.rsplit("_", 1)[0]
+        if n == 0 or base not in flops:
+            continue
+        avg_ms = st.kernel_ms[k] / n
+        tf_s = flops[base] / (avg_ms * 1e-3) / 1e12
+        kernels[name] = {"launches_per_layer_pass": n / n_diag, "avg_us": round(avg_ms * 1e3, 2),
+                         "TFLOPs": round(tf_s, 1), "mfma_frac": round(tf_s / MFMA_BF16_PEAK_TFLOPS, 4)}
+        gemm_ms += st.kernel_ms[k]
+        gemm_flop += flops[base] * n
+    layer_gemms = None
+    if gemm_ms > 0:
+        tfl = gemm_flop / (gemm_ms * 1e-3) / 1e12
+        layer_gemms = {"TFLOPs": round(tfl, 1), "mfma_frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
+                       "ms_per_layer_pass": round(gemm_ms / n_diag, 3)}
+    dom = kernels.get("gate_up_fwd")
+    roof = None
+    if dom:
+        roof = {"bound": "mfma", "achieved": dom["TFLOPs"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": dom["mfma_frac"], "traffic": None,
+                "kernel": f"fused NF4 gate|up GEMM + SwiGLU epilogue, {T}x{2 * shape.intermediate}x{H}",
+                "avg_launch_us": dom["avg_us"]}
+    return {"metric": "one 8B-shape NF4+LoRA decoder layer fwd + recompute-bwd, tokens/s", "value": round(value, 2),
+            "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+            "repeat": {"n": len(rates), "tokens_per_s": [round(v, 2) for v in rates], "mean": round(value, 2),
+                       "sd": round(sd, 2)},
+            "ms_per_step": round(tf + tb, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic (seeded random weights and activations)",
+            "config": {"workload": "one Llama-3.1-8B-shaped decoder layer, NF4 base (bs 64, fp32 absmax), LoRA r16 on "
+                                   "q,k,v,o,gate,up,down, batch 1 x seq 512, resident, forward + recomputing backward",
+                       "parallelism": "single GPU"},
+            "t_fwd_ms": round(tf, 4), "t_bwd_ms": round(tb, 4),
+            "roofline": roof, "layer_gemms": layer_gemms, "kernels": kernels,
+            "kernels_from": f"the same layer as a one-layer resident stack, {n_diag} steps with every kernel timed"}
 
 
 if __name__ == "__main__":

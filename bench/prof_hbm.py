@@ -10,16 +10,19 @@ for the byte counters), then, ``--reps`` times each:
   16384 = 32 sequences of 512), large enough that RMSNorm, RoPE and the
   split-K reductions are no longer launch-bound.
 
-    python -m layer_streamed_frozen_amd.prof_hbm [--reps 3] [--tokens 16384]
+    python3 bench/prof_hbm.py [--reps 3] [--tokens 16384]
 """
 import argparse
+import os
+import sys
 
 import numpy as np
 import torch
 
-from . import binding as B
-from . import store as S
-from . import synth
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+from layer_streamed_frozen_amd import binding as B  # noqa: E402
+from layer_streamed_frozen_amd import store as S  # noqa: E402
+from layer_streamed_frozen_amd import synth  # noqa: E402
 
 
 def main():

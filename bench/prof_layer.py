@@ -5,16 +5,19 @@ for the byte counters), then one Llama-3.1-8B-shaped layer (NF4 base, LoRA
 rank 16 on all seven projections, 512 tokens): forward, and the backward that
 recomputes it, ``--reps`` times.
 
-    python -m layer_streamed_frozen_amd.prof_layer [--reps 2] [--tokens 512]
+    python3 bench/prof_layer.py [--reps 2] [--tokens 512]
 """
 import argparse
+import os
+import sys
 
 import numpy as np
 import torch
 
-from . import binding as B
-from . import store as S
-from . import synth
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+from layer_streamed_frozen_amd import binding as B  # noqa: E402
+from layer_streamed_frozen_amd import store as S  # noqa: E402
+from layer_streamed_frozen_amd import synth  # noqa: E402
 
 
 def main():

@@ -188,7 +188,8 @@ typedef struct {
 /* -------------------------------------------------------- one NF4 linear --
  * y = x W^T + s (x A^T) B^T   (LoRA on a frozen NF4 weight; [NEWS], [TUTORIAL]
  * item 3).  x: device bf16 [tokens, n_in]; y: device bf16 [tokens, n_out].
- * n_out % 128 == 0, n_in % 128 == 0, tokens >= 1; with an adapter, rank is one
+ * n_out % 128 == 0, n_in % 128 == 0, 1 <= tokens; tokens, n_out and n_in at
+ * most 2^20 (larger sizes: LSF_ERR_SHAPE, and a size query of 0); with an adapter, rank is one
  * of 4, 8, 16, 32, 64 (else LSF_ERR_SHAPE).  A/B may be NULL (no adapter).
  * ws: device workspace of at least linear_workspace_bytes() bytes. */
 LSF_API size_t linear_workspace_bytes(int32_t tokens, int32_t n_out, int32_t n_in, int32_t rank);
@@ -260,6 +261,18 @@ typedef struct lsf_stack lsf_stack;
 /* The host store is a file on disk ([TUTORIAL] item 4: the NVMe tier used when
  * RAM is short).  Not built: stack_create returns LSF_ERR_UNSUPPORTED. */
 #define LSF_STACK_SOURCE_DISK 0x10u
+/* Event-ordering stress modes ([BLOG] "correctness and bit-exactness": the
+ * streamed result must not depend on timing).  Both act on the copy stream
+ * only, between its wait for a buffer's release and the copy into it, and
+ * change no result of a correctly ordered stack:
+ *   DEBUG_POISON: fill the released buffer with 0xFF bytes (NaN as bf16 and
+ *   fp32) before the copy, so compute that read the buffer outside its
+ *   ready/freed window would see NaN;
+ *   DEBUG_COPY_DELAY: run a fixed-length delay kernel (a bounded number of
+ *   s_sleep iterations, about 0.2 ms) before the copy, so a compute stream
+ *   that did not wait for the copy would read the previous contents. */
+#define LSF_STACK_DEBUG_POISON 0x20u
+#define LSF_STACK_DEBUG_COPY_DELAY 0x40u
 /* Record only kernel class k (an LSF_K_* value; several may be or-ed), for a
  * measurement that must disturb the step as little as possible. */
 #define LSF_STACK_TIME_KERNEL(k) (0x100u << (k))
@@ -305,6 +318,14 @@ typedef struct {
   uint32_t mode;               /* LSF_MODE_* */
   void* act;                   /* LSF_MODE_KEEP_ACTIVATIONS: device, 256-B aligned; else ignored */
   size_t act_bytes;            /* >= stack_activation_bytes(cfg, n_layers) */
+  /* Optional device int32 [1] (4-byte aligned) or NULL.  Token ids live on the
+   * device, so they cannot be checked before the step is enqueued; instead the
+   * step sets *id_status = 1 when any id of this micro-batch lies outside
+   * [0, vocab), and never writes it otherwise (the caller zeroes it and reads
+   * it after synchronising).  A bad id's embedding row is zero and a bad
+   * next-token label leaves its position unlabelled (no loss term, zero
+   * gradient row), so no memory outside the tables is read. */
+  int32_t* id_status;
 } lsf_stack_io;
 
 LSF_API size_t stack_workspace_bytes(const lsf_layer_cfg* cfg, int32_t vocab);
@@ -321,7 +342,7 @@ LSF_API lsf_status stream_stack_step(lsf_stack* st, const lsf_stack_io* io);
  * 0, 1, ..., n_micro-1 before the next layer is read, so the stack is streamed
  * twice per optimizer step instead of twice per micro-batch.  io points to
  * n_micro descriptors; io[m] supplies micro-batch m's ids, ckpt, logits, loss
- * and loss_scale (logits and loss may be shared), io[0] everything else
+ * loss_scale and id_status (logits, loss and id_status may be shared), io[0] everything else
  * (embed, vocab, final_norm, lm_head, lora, ws, act, mode).  All n_micro
  * checkpoint arrays are live at once.  The result is that of n_micro
  * stream_stack_step calls on io[0], io[1], ... in turn with

@@ -14,7 +14,8 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liblsf.so")
+# LSF_LIB names another build of the same library (the host-sanitizer build).
+LIB_PATH = os.environ.get("LSF_LIB") or os.path.join(HERE, "liblsf.so")
 
 LSF_OK, LSF_ERR_INVALID_ARG, LSF_ERR_SHAPE, LSF_ERR_ALIGN, LSF_ERR_NOT_PINNED, LSF_ERR_UNSUPPORTED, \
     LSF_ERR_HIP, LSF_ERR_WORKSPACE = range(8)
@@ -24,6 +25,7 @@ STATUS_NAMES = ["LSF_OK", "LSF_ERR_INVALID_ARG", "LSF_ERR_SHAPE", "LSF_ERR_ALIGN
 FMT_NF4, FMT_BF16, FMT_NF4_DQ = 0, 1, 2
 
 STACK_ALLOW_PAGEABLE, STACK_NO_TURN_REUSE, STACK_TIMING, STACK_KERNEL_TIMING, STACK_SOURCE_DISK = 0x1, 0x2, 0x4, 0x8, 0x10
+STACK_DEBUG_POISON, STACK_DEBUG_COPY_DELAY = 0x20, 0x40
 
 
 def STACK_TIME_KERNEL(k):
@@ -81,7 +83,7 @@ class StackIO(ctypes.Structure):
     _fields_ = [("ids", c_void_p), ("embed", c_void_p), ("final_norm", c_void_p), ("lm_head", c_void_p),
                 ("vocab", c_int32), ("lora", ctypes.POINTER(LayerLora)), ("ckpt", c_void_p), ("logits", c_void_p),
                 ("loss", c_void_p), ("ws", c_void_p), ("ws_bytes", c_size_t), ("loss_scale", c_float),
-                ("mode", c_uint32), ("act", c_void_p), ("act_bytes", c_size_t)]
+                ("mode", c_uint32), ("act", c_void_p), ("act_bytes", c_size_t), ("id_status", c_void_p)]
 
 
 class DpoIO(ctypes.Structure):

@@ -1,6 +1,7 @@
 """Build liblsf.so (the gfx950 HIP library) in-tree with hipcc.
 
     python -m layer_streamed_frozen_amd.build        # or build() from Python
+    python -m layer_streamed_frozen_amd.build --asan # host AddressSanitizer build
 
 Every source is compiled for gfx950 only, without fast-math (the NF4 codes
 depend on IEEE fp32 division and comparisons), with packed-fp32 instructions
@@ -35,9 +36,24 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src, verbose):
-    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-side AddressSanitizer: instruments the host code of every source (the
+# C ABI, validation, layer composition, the streamer, the launchers) and
+# leaves the gfx950 device code as it is.
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+ASAN_DIR = os.path.join(ROOT, "_build", "asan")
+ASAN_OUT = os.path.join(ASAN_DIR, "liblsf.so")
+
+
+def asan_runtime():
+    """Path of the clang AddressSanitizer runtime that the host build links."""
+    import glob
+    cands = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return cands[-1] if cands else None
+
+
+def _compile(src, verbose, objdir=OBJDIR, extra=()):
+    obj = os.path.join(objdir, os.path.basename(src) + ".o")
+    cmd = [hipcc()] + FLAGS + list(extra) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -48,21 +64,28 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose=False):
-    """Compile every HIP source and link liblsf.so (always rebuilds)."""
-    os.makedirs(OBJDIR, exist_ok=True)
+def build(verbose=False, asan=False):
+    """Compile every HIP source and link liblsf.so (always rebuilds).  With
+    asan=True the host code is built with AddressSanitizer into
+    _build/asan/liblsf.so instead (load it through LSF_LIB with the runtime
+    preloaded; device code is unchanged)."""
+    objdir = os.path.join(ASAN_DIR, "obj") if asan else OBJDIR
+    out = ASAN_OUT if asan else OUT
+    extra = ASAN_FLAGS if asan else []
+    os.makedirs(objdir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = OUT + ".tmp"
-    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+        objs = list(ex.map(lambda s: _compile(s, verbose, objdir, extra), SOURCES))
+    tmp = out + ".tmp"
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + \
+        (["-Xarch_host", "-fsanitize=address", "-shared-libasan"] if asan else []) + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, asan="--asan" in sys.argv))

@@ -221,8 +221,13 @@ lsf_status nf4dq_dequantize(const uint8_t* packed, const uint8_t* absq, const fl
 }
 
 // ----------------------------------------------------------- single linear
+// Largest tokens, n_out and n_in a single linear call accepts (keeps every
+// size product far inside 64 bits).
+constexpr int32_t kLinearMaxDim = 1 << 20;
+
 size_t linear_workspace_bytes(int32_t tokens, int32_t n_out, int32_t n_in, int32_t rank) {
   if (tokens <= 0 || n_out <= 0 || n_in <= 0) return 0;
+  if (tokens > kLinearMaxDim || n_out > kLinearMaxDim || n_in > kLinearMaxDim) return 0;
   const size_t T = tokens, r = rank > 0 ? rank : 1;
   const size_t N = n_out > n_in ? n_out : n_in;
   return 3 * 256 + (T * r * 4 + 255) / 256 * 256 * 2 + (size_t)8 * T * N * 4;
@@ -236,6 +241,8 @@ static lsf_status linear_common(const lsf_weight* w, int32_t format, int32_t n_o
   if (n_out <= 0 || n_out % 128) return fail(LSF_ERR_SHAPE, "n_out must be a positive multiple of 128");
   if (n_in <= 0 || n_in % 128) return fail(LSF_ERR_SHAPE, "n_in must be a positive multiple of 128");
   if (tokens < 1) return fail(LSF_ERR_SHAPE, "tokens must be >= 1");
+  if (tokens > kLinearMaxDim || n_out > kLinearMaxDim || n_in > kLinearMaxDim)
+    return fail(LSF_ERR_SHAPE, "tokens, n_out and n_in must be at most %d", (int)kLinearMaxDim);
   if (A != nullptr && (B == nullptr || !valid_rank(rank)))
     return fail(LSF_ERR_SHAPE, "adapter needs B and a rank in {4, 8, 16, 32, 64}");
   if (A != nullptr && !aligned(A, 16)) return fail(LSF_ERR_ALIGN, "A not 16-byte aligned");
@@ -263,12 +270,10 @@ static LinWs lin_ws(void* ws, int32_t tokens, int32_t n_out, int32_t n_in, int32
   return l;
 }
 
-lsf_status linear_fwd(const lsf_weight* w, int32_t format, int32_t n_out, int32_t n_in, const float* A, const float* B,
-                      int32_t rank, float scale, const uint16_t* x, int32_t tokens, uint16_t* y, void* ws,
-                      size_t ws_bytes, lsf_stream stream) {
-  lsf_status s = linear_common(w, format, n_out, n_in, A, B, rank, tokens, ws, ws_bytes);
-  if (s) return s;
-  if ((s = check_dev(x, "x")) || (s = check_dev(y, "y"))) return s;
+// The forward of one NF4 linear on workspace ws (validated by the caller).
+static lsf_status linear_fwd_impl(const lsf_weight* w, int32_t format, int32_t n_out, int32_t n_in, const float* A,
+                                  const float* B, int32_t rank, float scale, const uint16_t* x, int32_t tokens,
+                                  uint16_t* y, void* ws, lsf_stream stream) {
   const LinWs l = lin_ws(ws, tokens, n_out, n_in, rank);
   GemmArgs g;
   g.M = tokens; g.N = n_out; g.K = n_in; g.A = x; g.lda = n_in; g.W = weight_ref(*w, format, n_in);
@@ -283,6 +288,15 @@ lsf_status linear_fwd(const lsf_weight* w, int32_t format, int32_t n_out, int32_
   EpiArgs e; e.kind = EPI_BF16; e.C = y; e.ldc = n_out;
   HIPCK(run_gemm(false, g, e, l.part, l.part_floats, S(stream)));
   return ok();
+}
+
+lsf_status linear_fwd(const lsf_weight* w, int32_t format, int32_t n_out, int32_t n_in, const float* A, const float* B,
+                      int32_t rank, float scale, const uint16_t* x, int32_t tokens, uint16_t* y, void* ws,
+                      size_t ws_bytes, lsf_stream stream) {
+  lsf_status s = linear_common(w, format, n_out, n_in, A, B, rank, tokens, ws, ws_bytes);
+  if (s) return s;
+  if ((s = check_dev(x, "x")) || (s = check_dev(y, "y"))) return s;
+  return linear_fwd_impl(w, format, n_out, n_in, A, B, rank, scale, x, tokens, y, ws, stream);
 }
 
 lsf_status linear_bwd(const lsf_weight* w, int32_t format, int32_t n_out, int32_t n_in, const float* A, const float* B,
@@ -477,11 +491,18 @@ hipError_t harvest_all(lsf_stack* st, bool wait) {
   return hipSuccess;
 }
 
+// Sleeps of the copy-delay stress mode (about 0.2 ms in all).
+constexpr int kDebugDelayIters = 64;
+
 // Make layer j resident in buffer b: copy unless the buffer already holds it.
 lsf_status acquire(lsf_stack* st, int j, int b, bool allow_reuse) {
   if (allow_reuse && st->slot_layer[b] == j) return LSF_OK;
   hipStream_t cs = S(st->d.copy);
   if (st->used[b]) HIPCK(hipStreamWaitEvent(cs, st->freed[b], 0));
+  // Stress modes: between the release and the copy the buffer holds NaN
+  // bytes, and the copy starts late.
+  if (st->d.flags & LSF_STACK_DEBUG_POISON) HIPCK(fill_pattern(st->d.dev_buf[b], (int64_t)st->blob.bytes, ~0u, cs));
+  if (st->d.flags & LSF_STACK_DEBUG_COPY_DELAY) HIPCK(delay(kDebugDelayIters, cs));
   const bool timing = st->d.flags & LSF_STACK_TIMING;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (timing) {
@@ -671,10 +692,13 @@ lsf_status run_step(lsf_stack* st, const lsf_stack_io* io_all, int n_micro, cons
   if ((s = check_dev(io->embed, "embed")) || (s = check_dev(io->final_norm, "final_norm")) ||
       (s = check_dev(io->lm_head, "lm_head")))
     return s;
-  for (int m = 0; m < n_micro; ++m)
+  for (int m = 0; m < n_micro; ++m) {
     if ((s = check_dev(io_all[m].ids, "ids")) || (s = check_dev(io_all[m].ckpt, "ckpt")) ||
         (s = check_dev(io_all[m].logits, "logits")) || (s = check_dev(io_all[m].loss, "loss")))
       return s;
+    if (io_all[m].id_status != nullptr && !aligned(io_all[m].id_status, 4))
+      return fail(LSF_ERR_ALIGN, "id_status is not 4-byte aligned");
+  }
   if (io->lora == nullptr) return fail(LSF_ERR_INVALID_ARG, "lora array is NULL");
   for (int i = 0; i < L; ++i)
     if ((s = check_lora(&io->lora[i]))) return s;
@@ -765,7 +789,8 @@ lsf_status run_step(lsf_stack* st, const lsf_stack_io* io_all, int n_micro, cons
   }
 
   HIPCK(rope_table(c.seq, c.head_dim, c.rope_theta, w.layer.rope, cs));
-  for (int m = 0; m < n_micro; ++m) HIPCK(embed_gather(io_all[m].ids, io->embed, T, H, V, io_all[m].ckpt, cs));
+  for (int m = 0; m < n_micro; ++m)
+    HIPCK(embed_gather(io_all[m].ids, io->embed, T, H, V, io_all[m].ckpt, io_all[m].id_status, cs));
 
   // Layer i's saved intermediates for micro-batch m (LSF_MODE_KEEP_ACTIVATIONS).
   auto kept = [&](int m, int i) {
@@ -863,7 +888,8 @@ lsf_status stack_create(const lsf_layer_cfg* cfg, const lsf_stack_desc* desc, ls
   if (desc->n_layers < 1) return fail(LSF_ERR_INVALID_ARG, "n_layers must be >= 1");
   {
     const uint32_t known = LSF_STACK_ALLOW_PAGEABLE | LSF_STACK_NO_TURN_REUSE | LSF_STACK_TIMING |
-                           LSF_STACK_KERNEL_TIMING | LSF_STACK_SOURCE_DISK |
+                           LSF_STACK_KERNEL_TIMING | LSF_STACK_SOURCE_DISK | LSF_STACK_DEBUG_POISON |
+                           LSF_STACK_DEBUG_COPY_DELAY |
                            LSF_STACK_TIME_KERNEL(0) * ((1u << LSF_K_COUNT) - 1u);
     if (desc->flags & ~known) return fail(LSF_ERR_INVALID_ARG, "unknown stack flags 0x%x", desc->flags & ~known);
     if (desc->flags & LSF_STACK_SOURCE_DISK)

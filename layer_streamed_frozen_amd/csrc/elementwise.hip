@@ -171,13 +171,20 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(uint16_t* __restrict__ 
   *reinterpret_cast<u32x4*>(p + half) = pack8(b);
 }
 
+// One row per workgroup.  An id outside [0, V) reads nothing: its row is
+// zero and *status (if given) is set to 1 (every writer stores the same value).
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ ids, const uint16_t* __restrict__ E,
-                                                    int H, int V, uint16_t* __restrict__ x) {
+                                                    int H, int V, uint16_t* __restrict__ x, int32_t* status) {
   const int64_t t = blockIdx.x;
-  int id = ids[t];
-  id = id < 0 ? 0 : (id >= V ? V - 1 : id);
-  const u32x4* src = reinterpret_cast<const u32x4*>(E + (int64_t)id * H);
+  const int id = ids[t];
+  const bool ok = id >= 0 && id < V;
   u32x4* dst = reinterpret_cast<u32x4*>(x + t * H);
+  if (!ok) {
+    if (status != nullptr && threadIdx.x == 0) *status = 1;
+    for (int i = threadIdx.x; i < H / 8; i += 256) dst[i] = u32x4{0, 0, 0, 0};
+    return;
+  }
+  const u32x4* src = reinterpret_cast<const u32x4*>(E + (int64_t)id * H);
   for (int i = threadIdx.x; i < H / 8; i += 256) dst[i] = src[i];
 }
 
@@ -260,11 +267,16 @@ __device__ __forceinline__ void grad_row(const float* __restrict__ z, int V, flo
 }
 
 // Next-token label of row t (the id one position on) and whether row t has
-// one: the last position of each sequence is unlabelled.
+// one: the last position of each sequence is unlabelled, and so is a row whose
+// label lies outside [0, V) (the embedding gather reports such ids).
 __device__ __forceinline__ int row_label(const int32_t* __restrict__ ids, int64_t t, int seq, int V, bool& valid) {
   valid = (t % seq) < seq - 1;
-  int label = valid ? ids[t + 1] : 0;
-  return label < 0 ? 0 : (label >= V ? V - 1 : label);
+  const int label = valid ? ids[t + 1] : 0;
+  if (label < 0 || label >= V) {
+    valid = false;
+    return 0;
+  }
+  return label;
 }
 
 // One workgroup per row of logits: the loss term and softmax minus one-hot, scaled.
@@ -352,6 +364,18 @@ __global__ void fill_kernel(float* p, int64_t n) {
     p[i] = 0.0f;
 }
 
+// 16-byte stores of one 32-bit pattern over n16 vectors.
+__global__ void fill_pattern_kernel(u32x4* p, int64_t n16, uint32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = u32x4{v, v, v, v};
+}
+
+// A fixed-length wait: `iters` sleeps of about 64 x 127 clocks each, whatever
+// else runs.  It reads and writes nothing.
+__global__ void delay_kernel(int iters) {
+  for (int i = 0; i < iters; ++i) __builtin_amdgcn_s_sleep(127);
+}
+
 }  // namespace
 
 hipError_t rmsnorm_fwd(const uint16_t* x, const uint16_t* w, int T, int H, float eps, uint16_t* y, float* rstd,
@@ -384,9 +408,10 @@ hipError_t rope_apply(uint16_t* qk, int64_t ld, int T, int seq, int n_heads_tota
   return hipGetLastError();
 }
 
-hipError_t embed_gather(const int32_t* ids, const uint16_t* E, int T, int H, int V, uint16_t* x, hipStream_t s) {
+hipError_t embed_gather(const int32_t* ids, const uint16_t* E, int T, int H, int V, uint16_t* x, int32_t* status,
+                        hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(embed_kernel, dim3(T), dim3(256), 0, s, ids, E, H, V, x);
+  hipLaunchKernelGGL(embed_kernel, dim3(T), dim3(256), 0, s, ids, E, H, V, x, status);
   return hipGetLastError();
 }
 
@@ -418,6 +443,21 @@ hipError_t dpo_head_grad(const float* logits, const int32_t* ids, const float* l
   if (dlogits != nullptr)
     hipLaunchKernelGGL(ce_grad_kernel, dim3(batch * seq), dim3(kCeThreads), 0, s, logits, ids, lse, coef, seq, V,
                        dlogits);
+  return hipGetLastError();
+}
+
+hipError_t fill_pattern(void* p, int64_t bytes, uint32_t v, hipStream_t s) {
+  if (bytes <= 0) return hipSuccess;
+  if (bytes % 16 != 0 || reinterpret_cast<uintptr_t>(p) % 16 != 0) return hipErrorInvalidValue;
+  const int64_t n16 = bytes / 16;
+  const int grid = (int)std::min<int64_t>((n16 + 255) / 256, 4096);
+  hipLaunchKernelGGL(fill_pattern_kernel, dim3(grid), dim3(256), 0, s, static_cast<u32x4*>(p), n16, v);
+  return hipGetLastError();
+}
+
+hipError_t delay(int iters, hipStream_t s) {
+  if (iters <= 0) return hipSuccess;
+  hipLaunchKernelGGL(delay_kernel, dim3(1), dim3(64), 0, s, iters);
   return hipGetLastError();
 }
 

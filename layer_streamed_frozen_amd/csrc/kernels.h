@@ -136,7 +136,10 @@ hipError_t rope_table(int seq, int d, float theta, float2* tab, hipStream_t s);
 // In-place rotation of the q and k heads of a [T, ld] buffer; inverse = backward.
 hipError_t rope_apply(uint16_t* qk, int64_t ld, int T, int seq, int n_heads_total, int d, const float2* tab,
                       bool inverse, hipStream_t s);
-hipError_t embed_gather(const int32_t* ids, const uint16_t* E, int T, int H, int V, uint16_t* x, hipStream_t s);
+// x[t] = E[ids[t]]; an id outside [0, V) gives a zero row and sets *status = 1
+// (status may be NULL).
+hipError_t embed_gather(const int32_t* ids, const uint16_t* E, int T, int H, int V, uint16_t* x, int32_t* status,
+                        hipStream_t s);
 // CE over next-token labels; writes per-row loss terms, dlogits (bf16) and the mean loss.
 hipError_t cross_entropy(const float* logits, const int32_t* ids, int batch, int seq, int V, float loss_scale,
                          uint16_t* dlogits, float* row_loss, float* loss, hipStream_t s);
@@ -186,5 +189,9 @@ hipError_t attention_bwd(const AttnArgs& a, hipStream_t s);
 inline int64_t attention_dsum_floats(int64_t batch, int64_t nq, int64_t seq) { return (batch * nq * seq + 63) / 64 * 64; }
 
 hipError_t zero_f32(float* p, int64_t n, hipStream_t s);
+// Fill bytes (a multiple of 16, 16-byte aligned) with the 32-bit pattern v.
+hipError_t fill_pattern(void* p, int64_t bytes, uint32_t v, hipStream_t s);
+// A kernel that only waits, for `iters` fixed-length sleeps.
+hipError_t delay(int iters, hipStream_t s);
 
 }  // namespace lsf

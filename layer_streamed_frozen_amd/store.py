@@ -286,6 +286,8 @@ class Stack:
         self.logits = torch.empty((T, vocab), dtype=torch.float32, device=device)
         self.loss = torch.zeros(1, dtype=torch.float32, device=device)
         self.seq_logp = torch.zeros((2, batch), dtype=torch.float32, device=device)  # DPO: policy, reference
+        # set to 1 by a step that meets a token id outside [0, vocab); zeroed only here and by clear_id_status
+        self.id_status = torch.zeros(1, dtype=torch.int32, device=device)
         # every layer's forward intermediates, when the backward skips the recompute
         self.act = None
         if keep_activations:
@@ -307,6 +309,7 @@ class Stack:
         io.ws_bytes = self.ws.numel()
         io.loss_scale = loss_scale
         io.mode = mode
+        io.id_status = self.id_status.data_ptr()
         if self.act is not None:
             io.mode |= B.MODE_KEEP_ACTIVATIONS
             io.act = self.act.data_ptr()
@@ -345,6 +348,14 @@ class Stack:
 
     def stats(self):
         return B.stack_stats(self.handle)
+
+    def ids_were_valid(self):
+        """False if a step since the last clear_id_status met a token id
+        outside [0, vocab) (synchronises with the device)."""
+        return int(self.id_status.item()) == 0
+
+    def clear_id_status(self):
+        self.id_status.zero_()
 
     def close(self):
         if self.handle is not None:

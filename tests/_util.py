@@ -6,6 +6,8 @@ from layer_streamed_frozen_amd import synth
 from oracle import nf4 as onf4
 
 TOL = 2e-2  # relative Frobenius error bound for bf16 results against the fp64 oracle
+ROW_TOL = 5e-2  # bound on every row's relative error (rows: the last axis of the result)
+ROW_FLOOR = 0.5  # a row's error is measured against at least this fraction of the RMS row norm
 
 
 def rel_fro(got, ref):
@@ -18,9 +20,34 @@ def max_abs(got, ref):
     return float(np.max(np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64))))
 
 
+def worst_row(got, ref):
+    """Largest per-row relative error (rows = last axis; a 1-D result is one
+    value per row).  Each row is measured against max(its own norm,
+    ROW_FLOOR x the RMS row norm), so rows that are legitimately tiny are not
+    judged by their own noise, while a handful of bad rows in a large result
+    cannot hide under the overall Frobenius figure."""
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    g = g.reshape(-1, g.shape[-1]) if g.ndim >= 2 else g.reshape(-1, 1)
+    r = r.reshape(g.shape)
+    rn = np.linalg.norm(r, axis=1)
+    floor = ROW_FLOOR * np.sqrt(np.mean(rn * rn))
+    den = np.maximum(rn, max(floor, 1e-300))
+    err = np.linalg.norm(g - r, axis=1) / den
+    i = int(np.argmax(err))
+    rms = np.sqrt(np.mean(rn * rn))
+    return float(err[i]), i, float(rn[i] / rms) if rms > 0 else 0.0
+
+
 def report(name, got, ref):
+    """Print the relative Frobenius error, the largest absolute error and the
+    worst row; assert the worst row is within ROW_TOL; return the Frobenius
+    error (callers compare it with TOL)."""
     e, m = rel_fro(got, ref), max_abs(got, ref)
-    print(f"  {name:>10s}: rel_fro={e:.3e} max_abs={m:.3e}", flush=True)
+    w, i, rel_norm = worst_row(got, ref)
+    print(f"  {name:>10s}: rel_fro={e:.3e} max_abs={m:.3e} worst_row={w:.3e} (row {i}, norm {rel_norm:.2f} x RMS)",
+          flush=True)
+    assert w < ROW_TOL, f"{name}: row {i} relative error {w:.3e} >= {ROW_TOL}"
     return e
 
 

@@ -163,3 +163,23 @@ def test_optimizer_arguments_are_rejected_before_any_launch(lib):
     st = L.adamw8_step(16, 16, 16, 16, 16, 16, 16, ctypes.byref(B.AdamwCfg(**good)), None, 16, 64, None)
     assert st == B.LSF_ERR_WORKSPACE
     assert B.adamw8_state_blocks(4097) == 3 and B.adamw8_workspace_bytes() > B.adamw_workspace_bytes()
+
+
+def test_linear_sizes_are_bounded(lib):
+    L = lib
+    big = 1 << 21
+    assert B.linear_workspace_bytes(big, 256, 256, 8) == 0
+    assert B.linear_workspace_bytes(64, big * 64, 256, 8) == 0
+    w = B.Weight(16, 16, None)
+    st = L.linear_fwd(ctypes.byref(w), B.FMT_NF4, 256, 256, None, None, 0, 1.0, 16, big, 16, 16, 1 << 40, None)
+    assert st == B.LSF_ERR_SHAPE and b"at most" in L.lsf_last_error()
+
+
+def test_stack_io_layout_matches_the_header(lib):
+    # the binding's StackIO must end with id_status, as lsf_stack_io does
+    names = [f[0] for f in B.StackIO._fields_]
+    assert names[-1] == "id_status"
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct {\n  const int32_t* ids;"):text.index("} lsf_stack_io;")]
+    fields = re.findall(r"^\s+[\w\s\*]+?[\s\*](\w+);", re.sub(r"/\*.*?\*/", "", body, flags=re.S), flags=re.M)
+    assert fields == names, (fields, names)

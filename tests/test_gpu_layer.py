@@ -126,6 +126,22 @@ def test_full_8b_layer_seq512():
     _assert_all(res)
 
 
+# A layer above the size at which the pages' README (preprint / v3 paragraph)
+# reports a silent gradient error while the forward stays exact: hidden 5120,
+# intermediate 27648, 40 query / 8 kv heads (a 14B-class shape), 274 MB of NF4
+# codes and absmax, against the 8B layer's 123 MB.
+LARGE = S.LayerShape(hidden=5120, intermediate=27648, n_heads=40, n_kv_heads=8, head_dim=128, rank=16, alpha=16.0,
+                     rope_theta=500000.0)
+
+
+def test_layer_above_165_mib_gradients_match_oracle():
+    lay = B.layer_blob_layout(LARGE.cfg(1, 512), B.FMT_NF4)
+    print(f"  NF4 blob of the layer: {lay.bytes / 2**20:.1f} MiB", flush=True)
+    assert lay.bytes > 165 * 2**20
+    res, _ = run_layer(LARGE, 1, 512, "l14b", norms_random=False)
+    _assert_all(res)
+
+
 def test_small_layer_double_quantised():
     res, _ = run_layer(SMALL, 2, 90, "sldq", fmt=B.FMT_NF4_DQ)
     _assert_all(res)

@@ -11,7 +11,7 @@ from layer_streamed_frozen_amd import synth
 from oracle import model as M
 from oracle import nf4 as onf4
 from tests._util import TOL, bf16_tensor_to_np, report
-from tests.test_gpu_layer import SMALL, bf16_weights, oracle_layer_weights, oracle_shape
+from tests.test_gpu_layer import LARGE, SMALL, bf16_weights, oracle_layer_weights, oracle_shape
 
 pytestmark = pytest.mark.gpu
 
@@ -292,6 +292,41 @@ def test_full_8b_shapes_two_layers_match_oracle():
         for n in S.PROJ:
             assert report(f"L{i}.dA_{n}", g[n][0], ref["grads"][i][n][0]) < TOL
             assert report(f"L{i}.dB_{n}", g[n][1], ref["grads"][i][n][1]) < TOL
+
+
+def test_layers_above_165_mib_stream_bit_equal():
+    # two 274 MB layers (hidden 5120, intermediate 27648): every copy moves more
+    # than 165 MiB, and the streamed step must give the resident step's bits,
+    # forward and backward
+    s = Setup(LARGE, 2, 1024, 1, 512, "s14b", resident=True, random_norms=False)
+    s.step(mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+    a = s.snapshot()
+    st = s.stack.stats()
+    assert st.copies == 2 and st.bytes == 2 * s.store.blob_bytes() and s.store.blob_bytes() > 165 * 2**20
+    s.step(mode=B.MODE_RESIDENT | B.MODE_ZERO_GRADS)
+    assert same(a, s.snapshot())
+    assert all(torch.isfinite(a[2][i][n][k]).all() for i in range(2) for n in S.PROJ for k in range(2))
+    s.stack.close()
+
+
+def test_out_of_range_ids_set_the_status_word():
+    s = Setup(SMALL, 2, 512, 2, 40, "badid")
+    s.step(mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+    assert s.stack.ids_were_valid()
+    good_logits = s.stack.logits.clone()
+    for bad in (512, -1, 1 << 30):
+        ids = s.ids.clone()
+        ids[1, 7] = bad
+        s.stack.clear_id_status()
+        s.step(mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS, ids=ids)
+        assert not s.stack.ids_were_valid(), bad
+        # the bad position embeds as zeros; the rows of the other sequence are untouched
+        assert torch.count_nonzero(s.stack.ckpt[0, 40 + 7]) == 0
+        assert torch.equal(s.stack.logits[:40], good_logits[:40])
+        assert torch.isfinite(s.stack.loss).all()
+    s.stack.clear_id_status()
+    s.step(mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+    assert s.stack.ids_were_valid() and torch.equal(s.stack.logits, good_logits)
 
 
 @pytest.mark.parametrize("fmt", [B.FMT_NF4_DQ, B.FMT_BF16])
