@@ -34,7 +34,9 @@
  *     until stack_destroy.  Device pointers must come from device memory
  *     (hipMalloc / torch); "host" pointers are host memory.
  *   - No call allocates device memory: scratch space is a caller-provided
- *     workspace whose size a *_workspace_bytes() query gives.
+ *     workspace whose size a *_workspace_bytes() query gives, except for
+ *     linear_fwd_noalloc, whose scratch is a fixed device array the library
+ *     holds from load to process end.
  *   - Work is enqueued on the given HIP stream (lsf_stream is a hipStream_t;
  *     NULL is the null stream) and the call returns without waiting; faults
  *     surface at the caller's next synchronisation.
@@ -197,6 +199,20 @@ LSF_API lsf_status linear_fwd(const lsf_weight* w, int32_t format, int32_t n_out
                       const float* A, const float* B, int32_t rank, float scale,
                       const uint16_t* x, int32_t tokens, uint16_t* y,
                       void* ws, size_t ws_bytes, lsf_stream stream);
+/* linear_fwd for callers that cannot allocate device memory or hand over a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same kernels, launch shapes and bits as linear_fwd,
+ * with the scratch in a library-owned device array of
+ * linear_noalloc_max_bytes() bytes (32 MiB) on each GPU, kept until the
+ * process ends.  Sizes whose linear_workspace_bytes() exceed that give
+ * LSF_ERR_WORKSPACE and enqueue nothing.  The call allocates nothing.  All
+ * calls on one GPU share its array: calls that overlap in time on one GPU
+ * (on different streams, or from different threads) race and must be ordered
+ * by the caller.  Other arguments and errors as linear_fwd. */
+LSF_API size_t linear_noalloc_max_bytes(void);
+LSF_API lsf_status linear_fwd_noalloc(const lsf_weight* w, int32_t format, int32_t n_out, int32_t n_in,
+                                      const float* A, const float* B, int32_t rank, float scale,
+                                      const uint16_t* x, int32_t tokens, uint16_t* y, lsf_stream stream);
 /* Backward of linear_fwd: dx = dy W + s (dy B) A (the input gradient through the
  * frozen weight, [TUTORIAL] item 3); dA += s (dy B)^T x; dB += s dy^T (x A^T).
  * dx: device bf16 [tokens, n_in]. dA/dB accumulate. */

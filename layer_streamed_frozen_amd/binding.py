@@ -117,6 +117,9 @@ _PROTOS = {
     "linear_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
     "linear_fwd": (c_int32, [ctypes.POINTER(Weight), c_int32, c_int32, c_int32, c_void_p, c_void_p, c_int32,
                              c_float, c_void_p, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "linear_noalloc_max_bytes": (c_size_t, []),
+    "linear_fwd_noalloc": (c_int32, [ctypes.POINTER(Weight), c_int32, c_int32, c_int32, c_void_p, c_void_p, c_int32,
+                                     c_float, c_void_p, c_int32, c_void_p, c_void_p]),
     "linear_bwd": (c_int32, [ctypes.POINTER(Weight), c_int32, c_int32, c_int32, c_void_p, c_void_p, c_int32,
                              c_float, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                              c_size_t, c_void_p]),
@@ -251,6 +254,16 @@ def linear_workspace_bytes(tokens, n_out, n_in, rank):
 def linear_fwd(w, fmt, n_out, n_in, A, B, rank, scale, x, y, ws, stream=None):
     check(lib().linear_fwd(ctypes.byref(w), fmt, n_out, n_in, ptr(A), ptr(B), rank, scale, ptr(x), x.shape[0],
                            ptr(y), ptr(ws), ws.numel() * ws.element_size(), stream_ptr(stream)))
+
+
+def linear_noalloc_max_bytes():
+    return int(lib().linear_noalloc_max_bytes())
+
+
+def linear_fwd_noalloc(w, fmt, n_out, n_in, A, B, rank, scale, x, y, stream=None):
+    """linear_fwd with the library's own device scratch (no workspace)."""
+    check(lib().linear_fwd_noalloc(ctypes.byref(w), fmt, n_out, n_in, ptr(A), ptr(B), rank, scale, ptr(x),
+                                   x.shape[0], ptr(y), stream_ptr(stream)))
 
 
 def linear_bwd(w, fmt, n_out, n_in, A, B, rank, scale, x, dy, dx, dA, dB, ws, stream=None):

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <algorithm>
@@ -155,6 +156,35 @@ void weights_from_blob(const lsf_layer_cfg& c, int fmt, const void* blob, lsf_la
   w->norm2 = reinterpret_cast<const uint16_t*>(base + b.off[9]);
 }
 
+// ---------------------------------------------- allocation-free scratch
+// The scratch of linear_fwd_noalloc: a device array the code object carries,
+// so the loader places one copy on every GPU the library runs on.  Its name is
+// a host-side stand-in in host code; the device address of each GPU's copy
+// comes from hipGetSymbolAddress with that GPU current, once, and is the only
+// form host code passes on.
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+lsf_status noalloc_scratch(void** out) {
+  int dev = -1;
+  HIPCK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(LSF_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(LSF_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LSF_OK;
+}
+
 }  // namespace
 
 // ================================================================ C ABI ==
@@ -234,7 +264,8 @@ size_t linear_workspace_bytes(int32_t tokens, int32_t n_out, int32_t n_in, int32
 }
 
 static lsf_status linear_common(const lsf_weight* w, int32_t format, int32_t n_out, int32_t n_in, const float* A,
-                                const float* B, int32_t rank, int32_t tokens, void* ws, size_t ws_bytes) {
+                                const float* B, int32_t rank, int32_t tokens, void* ws, size_t ws_bytes,
+                                bool check_ws = true) {
   if (w == nullptr) return fail(LSF_ERR_INVALID_ARG, "weight is NULL");
   if (format != LSF_FMT_NF4 && format != LSF_FMT_BF16 && format != LSF_FMT_NF4_DQ)
     return fail(LSF_ERR_INVALID_ARG, "unknown weight format %d", format);
@@ -248,7 +279,7 @@ static lsf_status linear_common(const lsf_weight* w, int32_t format, int32_t n_o
   if (A != nullptr && !aligned(A, 16)) return fail(LSF_ERR_ALIGN, "A not 16-byte aligned");
   lsf_status s = check_weight(*w, format, "w");
   if (s) return s;
-  if (ws == nullptr || ws_bytes < linear_workspace_bytes(tokens, n_out, n_in, rank))
+  if (check_ws && (ws == nullptr || ws_bytes < linear_workspace_bytes(tokens, n_out, n_in, rank)))
     return fail(LSF_ERR_WORKSPACE, "workspace too small (need %zu bytes)", linear_workspace_bytes(tokens, n_out, n_in, rank));
   return LSF_OK;
 }
@@ -296,6 +327,25 @@ lsf_status linear_fwd(const lsf_weight* w, int32_t format, int32_t n_out, int32_
   lsf_status s = linear_common(w, format, n_out, n_in, A, B, rank, tokens, ws, ws_bytes);
   if (s) return s;
   if ((s = check_dev(x, "x")) || (s = check_dev(y, "y"))) return s;
+  return linear_fwd_impl(w, format, n_out, n_in, A, B, rank, scale, x, tokens, y, ws, stream);
+}
+
+size_t linear_noalloc_max_bytes(void) { return kNoallocScratchBytes; }
+
+lsf_status linear_fwd_noalloc(const lsf_weight* w, int32_t format, int32_t n_out, int32_t n_in, const float* A,
+                              const float* B, int32_t rank, float scale, const uint16_t* x, int32_t tokens,
+                              uint16_t* y, lsf_stream stream) {
+  const size_t need = linear_workspace_bytes(tokens, n_out, n_in, rank);
+  if (need > kNoallocScratchBytes)
+    return fail(LSF_ERR_WORKSPACE,
+                "linear_fwd_noalloc: %d tokens x %d x %d needs %zu bytes of scratch, more than the %zu the library "
+                "holds; use linear_fwd with a workspace",
+                (int)tokens, (int)n_out, (int)n_in, need, kNoallocScratchBytes);
+  lsf_status s = linear_common(w, format, n_out, n_in, A, B, rank, tokens, nullptr, 0, /*check_ws=*/false);
+  if (s) return s;
+  if ((s = check_dev(x, "x")) || (s = check_dev(y, "y"))) return s;
+  void* ws = nullptr;
+  if ((s = noalloc_scratch(&ws))) return s;
   return linear_fwd_impl(w, format, n_out, n_in, A, B, rank, scale, x, tokens, y, ws, stream);
 }
 

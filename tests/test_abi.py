@@ -165,6 +165,20 @@ def test_optimizer_arguments_are_rejected_before_any_launch(lib):
     assert B.adamw8_state_blocks(4097) == 3 and B.adamw8_workspace_bytes() > B.adamw_workspace_bytes()
 
 
+def test_noalloc_linear_limits_without_a_device(lib):
+    L = lib
+    assert L.linear_noalloc_max_bytes() == 32 << 20
+    # more scratch than the library holds: refused before anything is enqueued
+    w = B.Weight(16, 16, None)
+    st = L.linear_fwd_noalloc(ctypes.byref(w), B.FMT_NF4, 4096, 4096, None, None, 0, 1.0, 16, 512, 16, None)
+    assert st == B.LSF_ERR_WORKSPACE and b"scratch" in L.lsf_last_error()
+    # ordinary argument errors as linear_fwd
+    st = L.linear_fwd_noalloc(ctypes.byref(w), B.FMT_NF4, 100, 256, None, None, 0, 1.0, 16, 8, 16, None)
+    assert st == B.LSF_ERR_SHAPE
+    st = L.linear_fwd_noalloc(None, B.FMT_NF4, 256, 256, None, None, 0, 1.0, 16, 8, 16, None)
+    assert st == B.LSF_ERR_INVALID_ARG
+
+
 def test_linear_sizes_are_bounded(lib):
     L = lib
     big = 1 << 21
