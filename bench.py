@@ -406,7 +406,7 @@ def main():
     log(f"{value:.1f} +- {value_sd:.1f} tok/s over {len(runs)} runs, {ms_step:.2f} ms/step, loss {loss:.4f}")
 
     bytes_step = st.bytes / n_timed
-    h2d = {"bytes_per_step": int(bytes_step), "copies_per_step": st.copies / args.steps,
+    h2d = {"bytes_per_step": int(bytes_step), "copies_per_step": st.copies / n_timed,
            "GBps_over_step": round(bytes_step / (ms_step * 1e-3) / 1e9, 2),
            "measured_link_peak_GBps": round(link_peak, 2), "pcie5_x16_theoretical_GBps": PCIE5_X16_GBPS}
     flops = gemm_flops(T, shape)
