@@ -80,6 +80,11 @@ def parse():
     p.add_argument("--workload", choices=["stack1", "stack4", "dpo", "dpo-unfused", "layer", "linear"],
                    default="stack1")
     p.add_argument("--layers", type=int, default=32)
+    p.add_argument("--tokens", type=int, default=512,
+                   help="layer workload: tokens per call (sequences of 512)")
+    p.add_argument("--wide-tile", type=int, choices=[0, 1, 256, 512], default=1,
+                   help="diagnostics: kernel of the wide forward GEMMs (1: by shape, 256/512: that tile's rows, "
+                        "0: the general kernel); every choice gives the same bits")
     p.add_argument("--format", choices=["nf4", "nf4dq", "bf16"], default="nf4",
                    help="frozen-base storage: NF4 with fp32 absmax, NF4 with 8-bit double-quantised absmax, "
                         "or unquantised bf16")
@@ -306,6 +311,8 @@ def main():
 
     B.lib()  # fail loudly if the HIP library is missing
     torch.cuda.set_device(0)
+    if args.wide_tile != 1:
+        B.gemm_set_wide(args.wide_tile if args.wide_tile else False)
     shape = S.LLAMA8B
     if args.workload in ("linear", "layer"):
         out = (run_linear if args.workload == "linear" else run_layer)(args, torch, B, S, synth)
@@ -574,10 +581,12 @@ def run_layer(args, torch, B, S, synth):
     """One 8B-shaped NF4 decoder layer (LoRA r16 on all seven projections) at
     512 tokens, resident: forward, then the recomputing backward."""
     shape = S.LLAMA8B
-    T, H = 512, shape.hidden
+    T, H = args.tokens, shape.hidden
+    if T % 512:
+        raise SystemExit("--tokens must be a multiple of 512")
     W = S.layer_weights_fp32("layer0", shape)
     blob = S.build_layer_blob(shape, W)
-    cfg = shape.cfg(1, T)
+    cfg = shape.cfg(T // 512, 512)
     lw = B.layer_weights_from_blob(cfg, B.FMT_NF4, blob.data_ptr())
     lora = S.LoraSet(shape, 1)
     bits = lambda name: torch.from_numpy(synth.bf16_exact(synth.normal(name, (T, H)))[1].view(np.int16)) \
@@ -606,13 +615,13 @@ def run_layer(args, torch, B, S, synth):
     # per-kernel classes: the same layer as a one-layer resident stack with every kernel timed
     store = S.Store(shape, 1, resident=True, pinned=True, weights_fn=lambda i: W)
     V = 1024
-    stack = S.Stack(shape, store, 1, T, V, flags=B.STACK_TIMING)
+    stack = S.Stack(shape, store, T // 512, 512, V, flags=B.STACK_TIMING)
     emb = torch.from_numpy(synth.bf16_exact(synth.normal("layer.embed", (V, H), 1.0))[1].view(np.int16)) \
         .view(torch.bfloat16).cuda()
     head = torch.from_numpy(synth.bf16_exact(synth.normal("layer.head", (V, H), 0.02))[1].view(np.int16)) \
         .view(torch.bfloat16).cuda()
     fnorm = torch.ones(H, dtype=torch.bfloat16, device="cuda")
-    ids = torch.from_numpy(synth.token_ids("layer.ids", (1, T), V)).cuda()
+    ids = torch.from_numpy(synth.token_ids("layer.ids", (T // 512, 512), V)).cuda()
     arr = lora.array()
     stack.step(ids, emb, fnorm, head, arr, mode=B.MODE_RESIDENT | B.MODE_ZERO_GRADS)
     torch.cuda.synchronize()
@@ -655,8 +664,8 @@ def run_layer(args, torch, B, S, synth):
             "ms_per_step": round(tf + tb, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "bf16", "data": "synthetic (seeded random weights and activations)",
             "config": {"workload": "one Llama-3.1-8B-shaped decoder layer, NF4 base (bs 64, fp32 absmax), LoRA r16 on "
-                                   "q,k,v,o,gate,up,down, batch 1 x seq 512, resident, forward + recomputing backward",
-                       "parallelism": "single GPU"},
+                                   f"q,k,v,o,gate,up,down, batch {T // 512} x seq 512, resident, forward + recomputing "
+                                   "backward", "parallelism": "single GPU"},
             "t_fwd_ms": round(tf, 4), "t_bwd_ms": round(tb, 4),
             "roofline": roof, "layer_gemms": layer_gemms, "kernels": kernels,
             "kernels_from": f"the same layer as a one-layer resident stack, {n_diag} steps with every kernel timed"}

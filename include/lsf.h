@@ -85,12 +85,12 @@ LSF_API const char* lsf_version(void);
  * whole 256-column tiles, K >= 2048, at least 256 tokens, no split-K, and
  * either N >= 16384 or at least 192 tiles of 256 x 256: the gate|up
  * projection of an 8B-shaped layer, and q|k|v from 2048 tokens on, with the
- * bf16 or SwiGLU epilogue).  enable = 1 (the default):
- * the 256 x 256 ping-pong kernel; 0: the general 128-column kernel.  Both
- * compute the same contraction in the same order and give bitwise-identical
- * results; the switch lets tests and profiles compare them.  Process-wide;
- * GEMMs already enqueued are not affected.  enable must be 0 or 1
- * (LSF_ERR_INVALID_ARG). */
+ * bf16 or SwiGLU epilogue).  enable = 1 (the default) or 512: the ping-pong
+ * kernel on 512 x 128 tiles; 256: the same kernel on 256 x 256 tiles; 0: the
+ * general 128-column kernel.  All compute the same contraction in the same
+ * order and give bitwise-identical results; the switch lets tests and
+ * profiles compare them.  Process-wide; GEMMs already enqueued are not
+ * affected.  Other values: LSF_ERR_INVALID_ARG. */
 LSF_API lsf_status gemm_set_wide(int32_t enable);
 /* Diagnostics: number of GEMMs launched on the wide kernel so far in this
  * process (lets a test confirm which kernel ran). */
@@ -329,7 +329,7 @@ typedef struct {
   float* logits;               /* device fp32 [batch*seq, vocab] */
   float* loss;                 /* device fp32 [1]: mean CE over batch*(seq-1) positions */
   void* ws;                    /* device workspace */
-  size_t ws_bytes;             /* >= stack_workspace_bytes(cfg, vocab) */
+  size_t ws_bytes;             /* >= stack_workspace_bytes(cfg, vocab, n_layers) */
   float loss_scale;            /* multiplies dL/dlogits (e.g. 1/accumulation) */
   uint32_t mode;               /* LSF_MODE_* */
   void* act;                   /* LSF_MODE_KEEP_ACTIVATIONS: device, 256-B aligned; else ignored */
@@ -344,7 +344,10 @@ typedef struct {
   int32_t* id_status;
 } lsf_stack_io;
 
-LSF_API size_t stack_workspace_bytes(const lsf_layer_cfg* cfg, int32_t vocab);
+/* Device workspace of one micro-batch's step over n_layers layers (it holds,
+ * besides the layer and head scratch, every layer's LoRA activations from the
+ * forward walk, which the backward walk's recompute reuses). */
+LSF_API size_t stack_workspace_bytes(const lsf_layer_cfg* cfg, int32_t vocab, int32_t n_layers);
 /* Device bytes LSF_MODE_KEEP_ACTIVATIONS needs for n_layers layers. */
 LSF_API size_t stack_activation_bytes(const lsf_layer_cfg* cfg, int32_t n_layers);
 /* One SFT micro-batch: embedding gather, streamed forward, final RMSNorm,
@@ -364,10 +367,11 @@ LSF_API lsf_status stream_stack_step(lsf_stack* st, const lsf_stack_io* io);
  * stream_stack_step calls on io[0], io[1], ... in turn with
  * LSF_MODE_ZERO_GRADS (if set) on the first only, bit for bit: each layer's
  * gradients receive the micro-batches' contributions in the same order.
- * ws: at least stack_accum_workspace_bytes(cfg, vocab, n_micro); act
+ * ws: at least stack_accum_workspace_bytes(cfg, vocab, n_layers, n_micro); act
  * (LSF_MODE_KEEP_ACTIVATIONS): n_micro * stack_activation_bytes(cfg, n_layers).
  * Errors: LSF_ERR_INVALID_ARG for n_micro < 1, plus those of stream_stack_step. */
-LSF_API size_t stack_accum_workspace_bytes(const lsf_layer_cfg* cfg, int32_t vocab, int32_t n_micro);
+LSF_API size_t stack_accum_workspace_bytes(const lsf_layer_cfg* cfg, int32_t vocab, int32_t n_layers,
+                                           int32_t n_micro);
 LSF_API lsf_status stream_stack_accum_step(lsf_stack* st, const lsf_stack_io* io, int32_t n_micro);
 
 /* One DPO micro-batch ([README] paragraph on preference losses with layer
@@ -387,7 +391,7 @@ LSF_API lsf_status stream_stack_accum_step(lsf_stack* st, const lsf_stack_io* io
  * NULL): device fp32 [2, batch], policy log-probabilities then reference.
  * Errors: LSF_ERR_SHAPE for an odd batch, LSF_ERR_INVALID_ARG for beta <= 0
  * or non-finite, plus every error of stream_stack_step.  Workspace: the same
- * stack_workspace_bytes. */
+ * stack_workspace_bytes(cfg, vocab, n_layers). */
 typedef struct {
   lsf_stack_io base;
   float beta;               /* DPO temperature, e.g. 0.1 */

@@ -133,9 +133,9 @@ _PROTOS = {
                                           ctypes.POINTER(LayerWeights)]),
     "stack_create": (c_int32, [ctypes.POINTER(LayerCfg), ctypes.POINTER(StackDesc), ctypes.POINTER(c_void_p)]),
     "stack_destroy": (c_int32, [c_void_p]),
-    "stack_workspace_bytes": (c_size_t, [ctypes.POINTER(LayerCfg), c_int32]),
+    "stack_workspace_bytes": (c_size_t, [ctypes.POINTER(LayerCfg), c_int32, c_int32]),
     "stream_stack_step": (c_int32, [c_void_p, ctypes.POINTER(StackIO)]),
-    "stack_accum_workspace_bytes": (c_size_t, [ctypes.POINTER(LayerCfg), c_int32, c_int32]),
+    "stack_accum_workspace_bytes": (c_size_t, [ctypes.POINTER(LayerCfg), c_int32, c_int32, c_int32]),
     "stream_stack_accum_step": (c_int32, [c_void_p, ctypes.POINTER(StackIO), c_int32]),
     "dpo_stack_step": (c_int32, [c_void_p, ctypes.POINTER(DpoIO)]),
     "stack_stats": (c_int32, [c_void_p, ctypes.POINTER(StackStats)]),
@@ -192,10 +192,12 @@ def layer_cfg(hidden, intermediate, n_heads, n_kv_heads, head_dim, rank, lora_sc
 # ----------------------------------------------------------------- calls
 
 def gemm_set_wide(enable):
-    """Select the kernel of the wide forward NF4 GEMMs (True: 256x256
-    ping-pong kernel, the default; False: the general kernel).  Results are
-    bitwise identical either way."""
-    check(lib().gemm_set_wide(1 if enable else 0))
+    """Select the kernel of the wide forward NF4 GEMMs (True or 512: the
+    ping-pong kernel on 512 x 128 tiles, the default; 256: on 256 x 256
+    tiles; False: the general kernel).  Results are bitwise identical
+    whichever runs."""
+    v = enable if enable in (256, 512) else (1 if enable else 0)
+    check(lib().gemm_set_wide(v))
 
 
 def gemm_wide_launch_count():
@@ -308,16 +310,16 @@ def stack_destroy(h):
     check(lib().stack_destroy(h))
 
 
-def stack_workspace_bytes(cfg, vocab):
-    return lib().stack_workspace_bytes(ctypes.byref(cfg), vocab)
+def stack_workspace_bytes(cfg, vocab, n_layers):
+    return lib().stack_workspace_bytes(ctypes.byref(cfg), vocab, n_layers)
 
 
 def stream_stack_step(h, io):
     check(lib().stream_stack_step(h, ctypes.byref(io)))
 
 
-def stack_accum_workspace_bytes(cfg, vocab, n_micro):
-    return lib().stack_accum_workspace_bytes(ctypes.byref(cfg), vocab, n_micro)
+def stack_accum_workspace_bytes(cfg, vocab, n_layers, n_micro):
+    return lib().stack_accum_workspace_bytes(ctypes.byref(cfg), vocab, n_layers, n_micro)
 
 
 def stream_stack_accum_step(h, ios):

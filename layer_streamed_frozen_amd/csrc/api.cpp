@@ -194,8 +194,10 @@ const char* lsf_last_error(void) { return g_err.c_str(); }
 const char* lsf_version(void) { return "lsf 0.1.0 (gfx950)"; }
 
 lsf_status gemm_set_wide(int32_t enable) {
-  if (enable != 0 && enable != 1) return fail(LSF_ERR_INVALID_ARG, "enable must be 0 or 1 (got %d)", (int)enable);
+  if (enable != 0 && enable != 1 && enable != 256 && enable != 512)
+    return fail(LSF_ERR_INVALID_ARG, "enable must be 0, 1, 256 or 512 (got %d)", (int)enable);
   set_gemm_wide(enable != 0);
+  set_gemm_wide_tile(enable > 1 ? enable : 0);
   return ok();
 }
 
@@ -260,7 +262,8 @@ size_t linear_workspace_bytes(int32_t tokens, int32_t n_out, int32_t n_in, int32
   if (tokens > kLinearMaxDim || n_out > kLinearMaxDim || n_in > kLinearMaxDim) return 0;
   const size_t T = tokens, r = rank > 0 ? rank : 1;
   const size_t N = n_out > n_in ? n_out : n_in;
-  return 3 * 256 + (T * r * 4 + 255) / 256 * 256 * 2 + (size_t)8 * T * N * 4;
+  return 4 * 256 + (T * r * 4 + 255) / 256 * 256 * 2 + (size_t)8 * T * N * 4 +
+         (lora_part_floats(tokens, 1, (int)r) * 4 + 255) / 256 * 256;
 }
 
 static lsf_status linear_common(const lsf_weight* w, int32_t format, int32_t n_out, int32_t n_in, const float* A,
@@ -285,8 +288,8 @@ static lsf_status linear_common(const lsf_weight* w, int32_t format, int32_t n_o
 }
 
 struct LinWs {
-  float *U, *dU, *part;
-  size_t part_floats;
+  float *U, *dU, *part, *lpart;
+  size_t part_floats, lpart_floats;
 };
 static LinWs lin_ws(void* ws, int32_t tokens, int32_t n_out, int32_t n_in, int32_t rank) {
   uintptr_t p = ((uintptr_t)ws + 255) / 256 * 256;
@@ -298,6 +301,9 @@ static LinWs lin_ws(void* ws, int32_t tokens, int32_t n_out, int32_t n_in, int32
   p += (T * r * 4 + 255) / 256 * 256;
   l.part = (float*)p;
   l.part_floats = (size_t)8 * T * (n_out > n_in ? n_out : n_in);
+  p += (l.part_floats * 4 + 255) / 256 * 256;
+  l.lpart = (float*)p;
+  l.lpart_floats = lora_part_floats(tokens, 1, (int)r);
   return l;
 }
 
@@ -311,7 +317,7 @@ static lsf_status linear_fwd_impl(const lsf_weight* w, int32_t format, int32_t n
   if (A != nullptr) {
     LoraDown d;
     d.M = tokens; d.K = n_in; d.X = x; d.ldx = n_in; d.nsec = 1; d.r = rank; d.mat[0] = A; d.scale = 1.0f;
-    d.U = l.U; d.ldu = rank; d.part = l.part; d.part_floats = l.part_floats;
+    d.U = l.U; d.ldu = rank; d.part = l.lpart; d.part_floats = l.lpart_floats;
     HIPCK(lora_down(d, S(stream)));
     g.ext.kx = rank; g.ext.u = l.U; g.ext.ldu = rank; g.ext.uscale = scale; g.ext.nsec = 1; g.ext.r = rank;
     g.ext.mat[0] = B; g.ext.row_off[1] = n_out;
@@ -361,11 +367,11 @@ lsf_status linear_bwd(const lsf_weight* w, int32_t format, int32_t n_out, int32_
   if (A != nullptr) {
     LoraDown d;
     d.M = tokens; d.K = n_in; d.X = x; d.ldx = n_in; d.nsec = 1; d.r = rank; d.mat[0] = A; d.scale = 1.0f;
-    d.U = l.U; d.ldu = rank; d.part = l.part; d.part_floats = l.part_floats;
+    d.U = l.U; d.ldu = rank; d.part = l.lpart; d.part_floats = l.lpart_floats;
     HIPCK(lora_down(d, S(stream)));
     LoraDown b;
     b.M = tokens; b.K = n_out; b.X = dy; b.ldx = n_out; b.nsec = 1; b.r = rank; b.mat[0] = B; b.bside = true;
-    b.ksec[0] = n_out; b.scale = scale; b.U = l.dU; b.ldu = rank; b.part = l.part; b.part_floats = l.part_floats;
+    b.ksec[0] = n_out; b.scale = scale; b.U = l.dU; b.ldu = rank; b.part = l.lpart; b.part_floats = l.lpart_floats;
     HIPCK(lora_down(b, S(stream)));
     g.ext.kx = rank; g.ext.u = l.dU; g.ext.ldu = rank; g.ext.nsec = 1; g.ext.r = rank; g.ext.mat[0] = A;
     g.ext.ldmat = n_in;
@@ -373,12 +379,18 @@ lsf_status linear_bwd(const lsf_weight* w, int32_t format, int32_t n_out, int32_
   EpiArgs e; e.kind = EPI_BF16; e.C = dx; e.ldc = n_in;
   HIPCK(run_gemm(true, g, e, l.part, l.part_floats, S(stream)));
   if (A != nullptr) {
-    LoraGradSec ga, gb;
-    ga.P = l.dU; ga.ldp = rank; ga.Q = x; ga.ldq = n_in; ga.nq = n_in; ga.out = dA; ga.scale = 1.0f;
-    gb.P = l.U; gb.ldp = rank; gb.Q = dy; gb.ldq = n_out; gb.nq = n_out; gb.out = dB; gb.transposed = true;
-    gb.scale = scale;
-    if (dA) HIPCK(lora_grad(&ga, 1, tokens, rank, l.part, l.part_floats, S(stream)));
-    if (dB) HIPCK(lora_grad(&gb, 1, tokens, rank, l.part, l.part_floats, S(stream)));
+    LoraGradSec gs[2];
+    int n = 0;
+    if (dA) {
+      LoraGradSec& ga = gs[n++];
+      ga.P = l.dU; ga.ldp = rank; ga.Q = x; ga.ldq = n_in; ga.nq = n_in; ga.out = dA; ga.scale = 1.0f;
+    }
+    if (dB) {
+      LoraGradSec& gb = gs[n++];
+      gb.P = l.U; gb.ldp = rank; gb.Q = dy; gb.ldq = n_out; gb.nq = n_out; gb.out = dB; gb.transposed = true;
+      gb.scale = scale;
+    }
+    HIPCK(lora_grad(gs, n, tokens, rank, l.part, l.part_floats, S(stream)));
   }
   return ok();
 }
@@ -599,6 +611,8 @@ struct StackWs {
   float *rstdN, *row_loss, *part, *lse, *lp, *coef;
   size_t part_floats;
   uint16_t* dx_more;  // micro-batches 1.. of an accumulated step: two [T, H] each
+  char* uarena;       // every layer's LoRA activations, per micro-batch (LayerWs::u_bytes each)
+  int n_layers;
 };
 
 size_t head_part_floats(const lsf_layer_cfg& c) { return (size_t)8 * c.batch * c.seq * c.hidden; }
@@ -615,13 +629,16 @@ size_t stack_ws_bytes(const lsf_layer_cfg& c, int V) {
 }
 
 // With n micro-batches per walk, each keeps its own pair of gradient buffers
-// between the head and the backward walk.
-size_t stack_accum_ws_bytes(const lsf_layer_cfg& c, int V, int n) {
+// between the head and the backward walk; and every layer keeps the LoRA
+// activations U its forward computed, per micro-batch, for the recompute in
+// the backward walk (which then reuses them instead of recomputing them).
+size_t stack_accum_ws_bytes(const lsf_layer_cfg& c, int V, int L, int n) {
   const size_t T = (size_t)c.batch * c.seq, H = c.hidden;
-  return n <= 1 ? stack_ws_bytes(c, V) : stack_ws_bytes(c, V) + 256 + (size_t)(n - 1) * 2 * al256(T * H * 2);
+  return stack_ws_bytes(c, V) + 256 + (size_t)(n - 1) * 2 * al256(T * H * 2) + 256 +
+         (size_t)L * n * LayerWs::u_bytes(c);
 }
 
-StackWs carve_stack(const lsf_layer_cfg& c, int V, void* base) {
+StackWs carve_stack(const lsf_layer_cfg& c, int V, int L, int n, void* base) {
   const size_t T = (size_t)c.batch * c.seq, H = c.hidden;
   StackWs w;
   w.layer = LayerWs::carve(c, base);
@@ -645,7 +662,10 @@ StackWs carve_stack(const lsf_layer_cfg& c, int V, void* base) {
   w.coef = (float*)take((size_t)c.batch * 4);
   w.part_floats = head_part_floats(c);
   w.part = (float*)take(w.part_floats * 4);
-  w.dx_more = (uint16_t*)((p + 255) / 256 * 256);  // used only with the accumulated workspace size
+  w.dx_more = (uint16_t*)((p + 255) / 256 * 256);
+  const uintptr_t ua = (uintptr_t)w.dx_more + (size_t)(n - 1) * 2 * al256(T * H * 2);
+  w.uarena = (char*)((ua + 255) / 256 * 256);
+  w.n_layers = L;
   return w;
 }
 
@@ -755,7 +775,7 @@ lsf_status run_step(lsf_stack* st, const lsf_stack_io* io_all, int n_micro, cons
   const bool resident = io->mode & LSF_MODE_RESIDENT;
   if (resident && st->d.resident_store == nullptr) return fail(LSF_ERR_INVALID_ARG, "RESIDENT mode needs a resident store");
   if (!resident && st->d.host_store == nullptr) return fail(LSF_ERR_INVALID_ARG, "STREAMED mode needs a host store");
-  const size_t ws_need = stack_accum_ws_bytes(c, V, n_micro);
+  const size_t ws_need = stack_accum_ws_bytes(c, V, L, n_micro);
   if (io->ws == nullptr || io->ws_bytes < ws_need) return fail(LSF_ERR_WORKSPACE, "workspace too small (need %zu bytes)", ws_need);
   const bool keep = io->mode & LSF_MODE_KEEP_ACTIVATIONS;
   const size_t saved = LayerWs::saved_bytes(c);
@@ -774,7 +794,7 @@ lsf_status run_step(lsf_stack* st, const lsf_stack_io* io_all, int n_micro, cons
   }
 
   hipStream_t cs = S(st->d.compute);
-  StackWs w = carve_stack(c, V, io->ws);
+  StackWs w = carve_stack(c, V, L, n_micro, io->ws);
   const uint32_t all_classes = (1u << LSF_K_COUNT) - 1u;
   const uint32_t class_mask = (st->d.flags & (LSF_STACK_TIMING | LSF_STACK_KERNEL_TIMING))
                                   ? all_classes
@@ -846,11 +866,15 @@ lsf_status run_step(lsf_stack* st, const lsf_stack_io* io_all, int n_micro, cons
   auto kept = [&](int m, int i) {
     return w.layer.with_saved(c, static_cast<char*>(io->act) + ((size_t)m * L + i) * saved);
   };
+  // Otherwise the workspace with layer i's LoRA activations for micro-batch m
+  // in their own slot, so that the backward walk's recompute finds them.
+  const size_t ub = LayerWs::u_bytes(c);
+  auto with_u = [&](int m, int i) { return w.layer.with_u(c, w.uarena + ((size_t)m * L + i) * ub); };
   // Policy forward of layer i for micro-batch m: ckpt[i] -> ckpt[i+1] (kept for the backward).
   auto policy_fwd = [&](int m, int i, const lsf_layer_weights& lw) {
     uint16_t* ck = io_all[m].ckpt;
     return layer_forward(c, lw, &io->lora[i], ck + (size_t)i * act, ck + (size_t)(i + 1) * act,
-                         keep ? kept(m, i) : w.layer, keep, true, cs);
+                         keep ? kept(m, i) : with_u(m, i), keep, true, cs);
   };
   auto all_fwd = [&](int i, const lsf_layer_weights& lw) {
     for (int m = 0; m < n_micro; ++m) {
@@ -914,7 +938,8 @@ lsf_status run_step(lsf_stack* st, const lsf_stack_io* io_all, int n_micro, cons
   // ---- backward: layers L-1 .. 0, each read again and recomputed
   auto all_bwd = [&](int j, const lsf_layer_weights& lw) {
     for (int m = 0; m < n_micro; ++m) {
-      LayerWs lws = keep ? kept(m, j) : w.layer;
+      LayerWs lws = keep ? kept(m, j) : with_u(m, j);
+      lws.u_ready = !keep;  // the recompute reuses the forward's LoRA activations
       lws.grads_overwrite = overwrite && m == 0;
       const hipError_t e = layer_backward(c, lw, &io->lora[j], io_all[m].ckpt + (size_t)j * act,
                                           dx_buf(w, c, m, (j + 1) & 1), dx_buf(w, c, m, j & 1), lws, true, cs, !keep);
@@ -1003,14 +1028,14 @@ size_t stack_activation_bytes(const lsf_layer_cfg* cfg, int32_t n_layers) {
   return LayerWs::saved_bytes(*cfg) * (size_t)n_layers;
 }
 
-size_t stack_workspace_bytes(const lsf_layer_cfg* cfg, int32_t vocab) {
-  if (check_cfg(cfg) != LSF_OK || vocab <= 0) return 0;
-  return stack_ws_bytes(*cfg, vocab);
+size_t stack_workspace_bytes(const lsf_layer_cfg* cfg, int32_t vocab, int32_t n_layers) {
+  if (check_cfg(cfg) != LSF_OK || vocab <= 0 || n_layers < 1) return 0;
+  return stack_accum_ws_bytes(*cfg, vocab, n_layers, 1);
 }
 
-size_t stack_accum_workspace_bytes(const lsf_layer_cfg* cfg, int32_t vocab, int32_t n_micro) {
-  if (check_cfg(cfg) != LSF_OK || vocab <= 0 || n_micro < 1) return 0;
-  return stack_accum_ws_bytes(*cfg, vocab, n_micro);
+size_t stack_accum_workspace_bytes(const lsf_layer_cfg* cfg, int32_t vocab, int32_t n_layers, int32_t n_micro) {
+  if (check_cfg(cfg) != LSF_OK || vocab <= 0 || n_layers < 1 || n_micro < 1) return 0;
+  return stack_accum_ws_bytes(*cfg, vocab, n_layers, n_micro);
 }
 
 lsf_status stream_stack_step(lsf_stack* st, const lsf_stack_io* io) {

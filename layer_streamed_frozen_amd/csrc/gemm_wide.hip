@@ -41,9 +41,20 @@
 namespace lsf {
 namespace {
 
-constexpr int WBM = 256, WBN = 256, WBK = 32, WNST = 4;
-constexpr int WTILE = WBM * WBK;  // bf16 elements of one A (or B) tile
-constexpr int WSTAGE = 2 * WTILE;  // A tile then B tile: 32 KB
+// C tile TM x TN with TM * TN = 65536 (8 waves of 128 x 64): 256 x 256, or
+// 512 x 128 when the rows fit one tile (every weight is then decoded once,
+// half the decode work per MFMA of the square tile; the A tile doubles).
+constexpr int WBK = 32, WNST = 4;
+template <int TM>
+struct WCfg {
+  static constexpr int TN = 65536 / TM;
+  static constexpr int ATILE = TM * WBK;        // bf16 elements of the A tile
+  static constexpr int BTILE = TN * WBK;        // and of the B tile
+  static constexpr int STAGE = ATILE + BTILE;   // 32 KB (256 x 256) or 40 KB (512 x 128)
+  static constexpr int NCW = TN / 64;           // waves across N in one group
+  static constexpr int DMA = TM / 128;          // LDS-DMA instructions of A per wave and phase
+  static constexpr int DEC = TN * WBK / 512;    // weights each thread decodes per tile: 16 or 8
+};
 
 // Tile rows of 32 bf16 (4 chunks of 16 B), chunk' = chunk ^ ((row >> 1) & 3):
 // the 8 lanes of a 16-byte read phase hit 8 distinct 16-byte bank groups.
@@ -71,70 +82,88 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* src, uint16_t* dst) {
                                    (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
 }
 
-// Weight row feeding tile column c (0..255) of column tile `ntile`; in pair
-// mode gate row j and up row pair_I + j sit 16 columns apart, so one lane
-// holds both in its accumulators.
+// Weight row feeding tile column c of column tile `ntile` (TN columns); in
+// pair mode gate row j and up row pair_I + j sit 16 columns apart, so one
+// lane holds both in its accumulators.
+template <int TN>
 __device__ __forceinline__ int64_t wide_wrow(const GemmArgs& g, int ntile, int c) {
   if (g.pair_I > 0) {
-    const int j = ntile * (WBN / 2) + (c >> 5) * 16 + (c & 15);
+    const int j = ntile * (TN / 2) + (c >> 5) * 16 + (c & 15);
     return ((c >> 4) & 1) ? (int64_t)g.pair_I + j : (int64_t)j;
   }
-  return (int64_t)ntile * WBN + c;
+  return (int64_t)ntile * TN + c;
 }
 
-// Vector-memory operations of one memory phase: two LDS-DMA of A, the codes,
+// Vector-memory operations of one memory phase: the LDS-DMA of A, the codes,
 // and the absmax (one load for fp32 absmax; code + group pair for NF4_DQ).
-template <int FMT>
-constexpr int phase_vm_ops() { return FMT == FMT_NF4_DQ ? 5 : 4; }
+template <int TM, int FMT>
+constexpr int phase_vm_ops() { return WCfg<TM>::DMA + (FMT == FMT_NF4_DQ ? 3 : 2); }
 
-template <int FMT>
+// One thread's packed codes of one tile (16 or 8 weights) and its block's absmax.
+template <int DEC>
 struct CodeSet {
   u32x2 c;
   float am;
 };
 
-template <int FMT>
-__device__ __forceinline__ CodeSet<FMT> load_codes(const WeightRef& w, const uint8_t* cp, int64_t e0, int t) {
-  CodeSet<FMT> s;
-  s.c = *reinterpret_cast<const u32x2*>(cp + t * 16);
-  s.am = block_absmax_t<FMT>(w, e0 + (int64_t)t * WBK);
+// Codes of tile t from this thread's code pointer cp, and the absmax of their
+// 64-block from its absmax pointer ap (tiles 2j and 2j + 1 share block j).
+// Both pointers are per-thread values computed before the k loop, so no kernel
+// argument is reloaded inside it (a scalar reload there costs a wait for every
+// LDS read in flight).
+template <int DEC>
+__device__ __forceinline__ CodeSet<DEC> load_codes(const uint8_t* cp, const float* ap, int t) {
+  CodeSet<DEC> s;
+  if constexpr (DEC == 16) {
+    s.c = *reinterpret_cast<const u32x2*>(cp + t * 16);
+  } else {
+    s.c.x = *reinterpret_cast<const uint32_t*>(cp + t * 16);
+    s.c.y = 0;
+  }
+  s.am = ap[t >> 1];
   return s;
 }
 
 __device__ __forceinline__ float wsilu(float x) { return x / (1.0f + __expf(-x)); }
 
-template <int FMT, int EPI>
+template <int TM, int FMT, int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g, EpiArgs e) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[WNST * WSTAGE];
+  using C = WCfg<TM>;
+  constexpr int TN = C::TN, DEC = C::DEC;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[WNST * C::STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wid >> 2, q = wid & 3, tg = tid & 255;
   const int lr = lane & 15, lg = lane >> 4;
-  const int mt = (g.M + WBM - 1) / WBM, nt = g.N / WBN, total = mt * nt;
+  // wave (grp, q): rows wr .. wr + 128, columns wc .. wc + 64 of the tile
+  const int wr = grp * (TM / 2) + (q / C::NCW) * 128, wc = (q % C::NCW) * 64;
+  const int mt = (g.M + TM - 1) / TM, nt = g.N / TN, total = mt * nt;
   int t0 = blockIdx.x;
   if ((total & 7) == 0) t0 = (t0 & 7) * (total >> 3) + (t0 >> 3);  // neighbouring tiles on one XCD
   const int mtile = t0 % mt, ntile = t0 / mt;
-  const int m0 = mtile * WBM;
+  const int m0 = mtile * TM;
   const int nk = g.K / WBK;
 
-  // LDS-DMA of A: wave (grp, q) moves rows grp*128 + q*32 + j*16 + lane/4,
+  // LDS-DMA of A: wave (grp, q) moves rows grp*TM/2 + q*TM/8 + j*16 + lane/4,
   // 16 bytes each, into consecutive 16-byte slots; the source chunk is the
   // one the swizzle puts in that slot.  Rows past M repeat row M-1 (their C
   // rows are never stored).
-  const uint16_t* asrc[2];
-  int adst[2];
+  const uint16_t* asrc[C::DMA];
+  int adst[C::DMA];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int rbase = grp * 128 + q * 32 + j * 16;
+  for (int j = 0; j < C::DMA; ++j) {
+    const int rbase = grp * (TM / 2) + q * (TM / 8) + j * 16;
     const int row = rbase + (lane >> 2);
     const int lch = (lane & 3) ^ ((row >> 1) & 3);
     asrc[j] = g.A + (int64_t)min(m0 + row, g.M - 1) * g.lda + lch * 8;
     adst[j] = rbase * 32;
   }
-  // Decode share: tile column dcol, k half dh (16 weights per tile).
-  const int dcol = grp * 128 + (tg >> 1), dh = tg & 1;
-  const int64_t e0 = wide_wrow(g, ntile, dcol) * g.W.ld + dh * 16;  // element index at tile 0
+  // Decode share: tile column dcol and DEC consecutive k of it per tile.
+  const int dcol = grp * (TN / 2) + tg / (WBK / DEC), dk = tg % (WBK / DEC);
+  const int64_t e0 = wide_wrow<TN>(g, ntile, dcol) * g.W.ld + dk * DEC;  // element index at tile 0
   const uint8_t* cp = g.W.packed + (e0 >> 1);
+  const float* ap = g.W.absmax + (e0 >> 6);  // rows are whole 64-blocks (K % 64 == 0)
+  static_assert(FMT == FMT_NF4, "the wide kernel reads fp32 absmax");
 
   f32x4 acc[8][4];
 #pragma unroll
@@ -143,30 +172,33 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g, EpiArgs e
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
 
   auto issue_a = [&](int tsrc, int tdst) {
-    uint16_t* st = lds + (tdst & 3) * WSTAGE;
+    uint16_t* st = lds + (tdst & 3) * C::STAGE;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) lds_dma16(asrc[j] + tsrc * WBK, st + adst[j]);
+    for (int j = 0; j < C::DMA; ++j) lds_dma16(asrc[j] + tsrc * WBK, st + adst[j]);
   };
   auto decode_b = [&](int t, const u32x2& c, const Nf4Table& tb) {
-    uint16_t* bs = lds + (t & 3) * WSTAGE + WTILE;
-    uint32_t o0[4], o1[4];
+    uint16_t* bs = lds + (t & 3) * C::STAGE + C::ATILE;
+    uint32_t o0[4];
     nf4_decode8(tb, c.x, o0);
-    nf4_decode8(tb, c.y, o1);
-    *reinterpret_cast<u32x4*>(bs + woff(dcol, 2 * dh)) = u32x4{o0[0], o0[1], o0[2], o0[3]};
-    *reinterpret_cast<u32x4*>(bs + woff(dcol, 2 * dh + 1)) = u32x4{o1[0], o1[1], o1[2], o1[3]};
+    *reinterpret_cast<u32x4*>(bs + woff(dcol, (DEC / 8) * dk)) = u32x4{o0[0], o0[1], o0[2], o0[3]};
+    if constexpr (DEC == 16) {
+      uint32_t o1[4];
+      nf4_decode8(tb, c.y, o1);
+      *reinterpret_cast<u32x4*>(bs + woff(dcol, 2 * dk + 1)) = u32x4{o1[0], o1[1], o1[2], o1[3]};
+    }
   };
 
   // Prologue: tiles 0..2 in LDS, the codes of tiles 3 and 4 in registers.
-  CodeSet<FMT> cs[3];
+  CodeSet<DEC> cs[3];
   {
-    CodeSet<FMT> pc[3];
+    CodeSet<DEC> pc[3];
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
       issue_a(t, t);
-      pc[t] = load_codes<FMT>(g.W, cp, e0, t);
+      pc[t] = load_codes<DEC>(cp, ap, t);
     }
-    cs[0] = load_codes<FMT>(g.W, cp, e0, 3);
-    cs[1] = load_codes<FMT>(g.W, cp, e0, 4);
+    cs[0] = load_codes<DEC>(cp, ap, 3);
+    cs[1] = load_codes<DEC>(cp, ap, 4);
     cs[2] = cs[1];
     wait_vm<0>();
 #pragma unroll
@@ -178,26 +210,26 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g, EpiArgs e
 
   // One k tile: the memory phase, the barrier, the compute phase, the barrier.
   // The codes of tile t+3 are in `cdec`; tile t+5 loads into `cld`.
-  auto step = [&](int t, CodeSet<FMT>& cdec, CodeSet<FMT>& cld) {
+  auto step = [&](int t, CodeSet<DEC>& cdec, CodeSet<DEC>& cld) {
     __builtin_amdgcn_sched_barrier(0);
     // Fragment reads first: tile t landed two phases ago, and their LDS
     // latency then overlaps the loads and the decode instead of ending the
     // phase (this order also keeps the kernel within 256 registers).
     u32x4 af[8], bf[4];
     {
-      const uint16_t* st = lds + (t & 3) * WSTAGE;
+      const uint16_t* st = lds + (t & 3) * C::STAGE;
 #pragma unroll
       for (int mf = 0; mf < 8; ++mf)
-        af[mf] = *reinterpret_cast<const u32x4*>(st + woff(grp * 128 + mf * 16 + lr, lg));
+        af[mf] = *reinterpret_cast<const u32x4*>(st + woff(wr + mf * 16 + lr, lg));
 #pragma unroll
       for (int nf = 0; nf < 4; ++nf)
-        bf[nf] = *reinterpret_cast<const u32x4*>(st + WTILE + woff(q * 64 + nf * 16 + lr, lg));
+        bf[nf] = *reinterpret_cast<const u32x4*>(st + C::ATILE + woff(wc + nf * 16 + lr, lg));
     }
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm<phase_vm_ops<FMT>()>();
+    wait_vm<phase_vm_ops<TM, FMT>()>();
     issue_a(min(t + 3, nk - 1), t + 3);
     __builtin_amdgcn_sched_barrier(0);  // the LDS-DMA goes out before the register loads
-    cld = load_codes<FMT>(g.W, cp, e0, min(t + 5, nk - 1));
+    cld = load_codes<DEC>(cp, ap, min(t + 5, nk - 1));
     __builtin_amdgcn_sched_barrier(0);
     if (((t + 3) & 1) == 0) tb = nf4_table(cdec.am);  // first half of a 64-block
     decode_b(t + 3, cdec.c, tb);
@@ -225,15 +257,17 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g, EpiArgs e
   wait_vm<0>();
   wbar();
 
-  // LoRA extension: 32-wide steps of [uscale * U | adapter B] in stage 0.
+  // LoRA extension: 32-wide steps of [uscale * U | adapter B] in stage 0;
+  // each unit is one row and 16 of the step's 32 columns.
   const LoraExt& x = g.ext;
   const int next = x.kx > 0 ? (x.kx + WBK - 1) / WBK : 0;
+  uint16_t* As = lds;
+  uint16_t* Bs = lds + C::ATILE;
   for (int xt = 0; xt < next; ++xt) {
-    const int row = tid >> 1, h = tid & 1;
-    const int jb = xt * WBK + h * 16;
-    uint16_t* As = lds;
-    uint16_t* Bs = lds + WTILE;
-    {
+#pragma unroll
+    for (int u0 = 0; u0 < 2 * TM; u0 += 512) {
+      const int row = (u0 + tid) >> 1, h = tid & 1;
+      const int jb = xt * WBK + h * 16;
       const int gm = m0 + row;
       uint32_t w[8];
 #pragma unroll
@@ -249,13 +283,15 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g, EpiArgs e
       *reinterpret_cast<u32x4*>(As + woff(row, 2 * h)) = u32x4{w[0], w[1], w[2], w[3]};
       *reinterpret_cast<u32x4*>(As + woff(row, 2 * h + 1)) = u32x4{w[4], w[5], w[6], w[7]};
     }
-    {
-      const int64_t wr = wide_wrow(g, ntile, row);
+    if (tid < 2 * TN) {
+      const int row = tid >> 1, h = tid & 1;
+      const int jb = xt * WBK + h * 16;
+      const int64_t wrow = wide_wrow<TN>(g, ntile, row);
       int sec = 0;
       for (int s = 1; s < x.nsec; ++s)
-        if (wr >= x.row_off[s]) sec = s;
+        if (wrow >= x.row_off[s]) sec = s;
       const float* bm = x.mat[sec];
-      const int64_t lrow = wr - x.row_off[sec];
+      const int64_t lrow = wrow - x.row_off[sec];
       uint32_t w[8];
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
@@ -274,9 +310,9 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g, EpiArgs e
     wbar();
     u32x4 af[8], bf[4];
 #pragma unroll
-    for (int mf = 0; mf < 8; ++mf) af[mf] = *reinterpret_cast<const u32x4*>(As + woff(grp * 128 + mf * 16 + lr, lg));
+    for (int mf = 0; mf < 8; ++mf) af[mf] = *reinterpret_cast<const u32x4*>(As + woff(wr + mf * 16 + lr, lg));
 #pragma unroll
-    for (int nf = 0; nf < 4; ++nf) bf[nf] = *reinterpret_cast<const u32x4*>(Bs + woff(q * 64 + nf * 16 + lr, lg));
+    for (int nf = 0; nf < 4; ++nf) bf[nf] = *reinterpret_cast<const u32x4*>(Bs + woff(wc + nf * 16 + lr, lg));
 #pragma unroll
     for (int mf = 0; mf < 8; ++mf)
 #pragma unroll
@@ -284,16 +320,16 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g, EpiArgs e
     wbar();
   }
 
-  // Epilogue.  Lane holds C[m0 + grp*128 + mf*16 + lg*4 + i][tile column q*64 + nf*16 + lr].
+  // Epilogue.  Lane holds C[m0 + wr + mf*16 + lg*4 + i][tile column wc + nf*16 + lr].
   if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
     for (int mf = 0; mf < 8; ++mf)
 #pragma unroll
       for (int np = 0; np < 2; ++np) {
-        const int j = ntile * (WBN / 2) + (q * 2 + np) * 16 + lr;
+        const int j = ntile * (TN / 2) + ((wc >> 6) * 2 + np) * 16 + lr;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int m = m0 + grp * 128 + mf * 16 + lg * 4 + i;
+          const int m = m0 + wr + mf * 16 + lg * 4 + i;
           if (m >= g.M) continue;
           const float gv = acc[mf][2 * np][i], uv = acc[mf][2 * np + 1][i];
           static_cast<uint16_t*>(e.C)[(int64_t)m * e.ldc + j] = f32_to_bf16(wsilu(gv) * uv);
@@ -308,10 +344,10 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g, EpiArgs e
     for (int mf = 0; mf < 8; ++mf)
 #pragma unroll
       for (int nf = 0; nf < 4; ++nf) {
-        const int n = ntile * WBN + q * 64 + nf * 16 + lr;
+        const int n = ntile * TN + wc + nf * 16 + lr;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int m = m0 + grp * 128 + mf * 16 + lg * 4 + i;
+          const int m = m0 + wr + mf * 16 + lg * 4 + i;
           if (m >= g.M) continue;
           const float v = acc[mf][nf][i];
           static_cast<uint16_t*>(e.C)[(int64_t)m * e.ldc + n] = f32_to_bf16(v);
@@ -320,49 +356,59 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g, EpiArgs e
   }
 }
 
-template <int FMT>
-hipError_t launch_wide_fmt(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
-  const dim3 grid(((g.M + WBM - 1) / WBM) * (g.N / WBN)), block(512);
+template <int TM>
+hipError_t launch_wide(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
+  constexpr int TN = WCfg<TM>::TN;
+  const dim3 grid(((g.M + TM - 1) / TM) * (g.N / TN)), block(512);
   switch (e.kind) {
-    case EPI_BF16: hipLaunchKernelGGL((gemm_wide_kernel<FMT, EPI_BF16>), grid, block, 0, s, g, e); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_wide_kernel<FMT, EPI_SWIGLU>), grid, block, 0, s, g, e); break;
+    case EPI_BF16: hipLaunchKernelGGL((gemm_wide_kernel<TM, FMT_NF4, EPI_BF16>), grid, block, 0, s, g, e); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_wide_kernel<TM, FMT_NF4, EPI_SWIGLU>), grid, block, 0, s, g, e); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+// Tile rows of the wide kernel: 512 (x 128 columns), which decodes each
+// weight half as often as 256 x 256 tiles and measured faster at 512 and 2048
+// tokens (gate|up 150 vs 156 us and 582 vs 594 us).
+int wide_tile_rows(const GemmArgs&) { return 512; }
+
 }  // namespace
 
-// The wide kernel needs whole 256-column tiles (and 128-row halves of them in
-// pair mode), 64-deep absmax blocks, 16-byte aligned A rows, 8-byte aligned
-// codes, and no split-K.  It is chosen for N >= 16384 (gate|up), or when
-// there are at least 192 of its 256 x 256 tiles, three quarters of the 256
-// compute units (q|k|v from 2048 tokens: 144 vs 174 us there, measured), and
-// K >= 2048: with short contractions its prologue dominates (measured 1.7x
-// slower than the general kernel at K = 512).
+// The wide kernel needs whole column tiles (and halves of them in pair mode),
+// 64-deep absmax blocks, 16-byte aligned A rows, 8-byte aligned codes, and no
+// split-K.  It is chosen for N >= 16384 (gate|up), or when there are at least
+// 192 of its 256 x 256 tiles, three quarters of the 256 compute units (q|k|v
+// from 2048 tokens: 144 vs 174 us there, measured), and K >= 2048: with short
+// contractions its prologue dominates (measured 1.7x slower than the general
+// kernel at K = 512).
 bool gemm_wide_applies(const GemmArgs& g, const EpiArgs& e) {
-  if (g.splits != 1 || g.M < 256 || g.N % WBN != 0) return false;
-  if (g.N < 16384 && (int64_t)((g.M + WBM - 1) / WBM) * (g.N / WBN) < 192) return false;
+  if (g.splits != 1 || g.M < 256 || g.N % 256 != 0) return false;
+  if (g.N < 16384 && (int64_t)((g.M + 255) / 256) * (g.N / 256) < 192) return false;
   // fp32 absmax only: with the double-quantised absmax (two more loads in
   // flight per code set) the kernel no longer fits its 256 registers.
   if (g.W.fmt != FMT_NF4) return false;
   if (g.K % 64 != 0 || g.K < 2048 || g.W.ld != g.K || g.lda % 8 != 0) return false;
   if (((uintptr_t)g.A & 15) != 0 || ((uintptr_t)g.W.packed & 7) != 0) return false;
-  if (g.pair_I > 0 && (g.pair_I * 2 != g.N || g.pair_I % (WBN / 2) != 0)) return false;
+  if (g.pair_I > 0 && (g.pair_I * 2 != g.N || g.pair_I % 128 != 0)) return false;
   if (e.kind == EPI_SWIGLU) return g.pair_I > 0;
   return e.kind == EPI_BF16 && g.pair_I == 0;
 }
 
 namespace {
 std::atomic<int64_t> g_wide_launches{0};
+std::atomic<int> g_wide_tile{0};  // 0: by shape; 256 or 512: forced (diagnostics)
 }  // namespace
 
 int64_t gemm_wide_launches() { return g_wide_launches.load(std::memory_order_relaxed); }
+void set_gemm_wide_tile(int rows) { g_wide_tile.store(rows, std::memory_order_relaxed); }
 
 hipError_t gemm_nt_wide(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
   if (!gemm_wide_applies(g, e)) return hipErrorInvalidValue;
   g_wide_launches.fetch_add(1, std::memory_order_relaxed);
-  return launch_wide_fmt<FMT_NF4>(g, e, s);
+  const int forced = g_wide_tile.load(std::memory_order_relaxed);
+  const int tm = forced != 0 ? forced : wide_tile_rows(g);
+  return tm == 512 ? launch_wide<512>(g, e, s) : launch_wide<256>(g, e, s);
 }
 
 }  // namespace lsf

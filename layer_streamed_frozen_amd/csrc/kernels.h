@@ -71,6 +71,7 @@ hipError_t gemm_nt(const GemmArgs& g, const EpiArgs& e, hipStream_t s);
 // uses it by itself where gemm_wide_applies.
 bool gemm_wide_applies(const GemmArgs& g, const EpiArgs& e);
 void set_gemm_wide(bool enable);  // process-wide; default on
+void set_gemm_wide_tile(int rows);  // 0: tile rows by shape; 256 or 512: forced (diagnostics)
 int64_t gemm_wide_launches();      // wide-kernel launches so far
 hipError_t gemm_nt_wide(const GemmArgs& g, const EpiArgs& e, hipStream_t s);
 // C = A W (+ LoRA), contraction over W rows.
@@ -90,6 +91,8 @@ hipError_t nf4dq_dequantize_launch(const uint8_t* packed, const uint8_t* absq, c
 // LoRA side paths.
 //  down_fwd: U[m, sec*r + j] = scale * sum_k X[m, k] * A_sec[j, k]  (all sections read X)
 //  down_bwd: U[m, sec*r + j] = scale * sum_{n in sec} X[m, xoff_sec + n] * B_sec[n, j]
+// The contraction is cut into at most 8 chunks per section; lora_down writes
+// one partial product per chunk into part and their ordered sum into U.
 struct LoraDown {
   int M = 0, K = 0;  // K: columns of X read per section
   const uint16_t* X = nullptr;
@@ -102,9 +105,11 @@ struct LoraDown {
   float* U = nullptr;
   int ldu = 0;
   bool bside = false;  // false: A-side [r, K]; true: B-side [K, r]
-  float* part = nullptr;  // scratch for the per-chunk partial products
+  float* part = nullptr;  // the per-chunk partial products (lora_part_floats of them)
   size_t part_floats = 0;
 };
+// Floats of partials lora_down writes for M rows, nsec sections of rank r.
+inline size_t lora_part_floats(int64_t M, int nsec, int r) { return (size_t)nsec * 8 * M * r; }
 hipError_t lora_down(const LoraDown& a, hipStream_t s);
 
 // out += scale * sum_t P[t, pcol0 + j] * Q[t, qoff + q] for j < r, q < nq.
@@ -121,8 +126,10 @@ struct LoraGradSec {
   float scale = 1.0f;
   bool overwrite = false;  // out = ... instead of out += ... (the first accumulation)
 };
-// part (part_floats floats of scratch, may be NULL) holds per-token-split
-// partials when the token range is split across workgroups.
+// Up to kLoraGradSecs sections in one launch.  part (part_floats floats of
+// scratch, may be NULL) holds per-token-split partials when there are too few
+// workgroups without splitting the tokens.
+constexpr int kLoraGradSecs = 6;
 hipError_t lora_grad(const LoraGradSec* secs, int nsec, int T, int r, float* part, size_t part_floats,
                      hipStream_t s);
 

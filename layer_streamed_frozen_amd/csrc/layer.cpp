@@ -45,6 +45,7 @@ size_t LayerWs::bytes(const lsf_layer_cfg& c) {
   b += up(z.seq * (c.head_dim / 2) * 8);      // rope table
   b += up((attention_dsum_floats(z.batch, z.nq, z.seq) + 2 * z.T * z.nq * 128) * 4);  // attention bwd scratch
   b += up((size_t)8 * z.T * z.maxN() * 4);    // split-K partials
+  b += up(lora_part_floats(z.T, 3, (int)z.r) * 4);  // LoRA down-projection partials
   return b + AL;
 }
 
@@ -84,6 +85,8 @@ LayerWs LayerWs::carve(const lsf_layer_cfg& c, void* base) {
   w.attn_scratch = (float*)take((attention_dsum_floats(z.batch, z.nq, z.seq) + 2 * z.T * z.nq * 128) * 4);
   w.part_floats = (size_t)8 * z.T * z.maxN();
   w.part = (float*)take(w.part_floats * 4);
+  w.lpart_floats = lora_part_floats(z.T, 3, (int)z.r);
+  w.lpart = (float*)take(w.lpart_floats * 4);
   return w;
 }
 
@@ -117,6 +120,27 @@ LayerWs LayerWs::with_saved(const lsf_layer_cfg& c, void* base) const {
   w.lse = (float*)take(z.batch * z.nq * z.seq * 4);
   w.rstd1 = (float*)take(z.T * 4);
   w.rstd2 = (float*)take(z.T * 4);
+  w.Uqkv = (float*)take(z.T * 3 * z.r * 4);
+  w.Uo = (float*)take(z.T * z.r * 4);
+  w.Ud = (float*)take(z.T * z.r * 4);
+  w.Ugu = (float*)take(z.T * 2 * z.r * 4);
+  return w;
+}
+
+size_t LayerWs::u_bytes(const lsf_layer_cfg& c) {
+  Sizes z(c);
+  return up(z.T * 3 * z.r * 4) + up(z.T * z.r * 4) * 2 + up(z.T * 2 * z.r * 4);
+}
+
+LayerWs LayerWs::with_u(const lsf_layer_cfg& c, void* base) const {
+  Sizes z(c);
+  uintptr_t p = (uintptr_t)base;
+  auto take = [&](size_t n) {
+    void* r = (void*)p;
+    p += up(n);
+    return r;
+  };
+  LayerWs w = *this;
   w.Uqkv = (float*)take(z.T * 3 * z.r * 4);
   w.Uo = (float*)take(z.T * z.r * 4);
   w.Ud = (float*)take(z.T * z.r * 4);
@@ -193,9 +217,9 @@ hipError_t layer_forward(const lsf_layer_cfg& c, const lsf_layer_weights& w, con
   {
     const lsf_lora_proj* pq[3] = {proj(lora, PQ), proj(lora, PK), proj(lora, PV)};
     const bool any = pq[0] || pq[1] || pq[2];
-    if (any) {
+    if (any && !ws.u_ready) {
       LoraDown d;
-      d.part = ws.part; d.part_floats = ws.part_floats;
+      d.part = ws.lpart; d.part_floats = ws.lpart_floats;
       d.M = T; d.K = H; d.X = ws.h1; d.ldx = H; d.nsec = 3; d.r = r;
       for (int i = 0; i < 3; ++i) d.mat[i] = pq[i] ? pq[i]->A : nullptr;
       d.scale = 1.0f; d.U = ws.Uqkv; d.ldu = 3 * r;
@@ -227,11 +251,13 @@ hipError_t layer_forward(const lsf_layer_cfg& c, const lsf_layer_weights& w, con
     const lsf_lora_proj* po = proj(lora, PO);
     g = GemmArgs(); g.M = T;
     if (po) {
-      LoraDown d;
-      d.part = ws.part; d.part_floats = ws.part_floats;
-      d.M = T; d.K = (int)z.Dq; d.X = ws.att; d.ldx = z.Dq; d.nsec = 1; d.r = r; d.mat[0] = po->A;
-      d.scale = 1.0f; d.U = ws.Uo; d.ldu = r;
-      CK(lora_down(d, s));
+      if (!ws.u_ready) {
+        LoraDown d;
+        d.part = ws.lpart; d.part_floats = ws.lpart_floats;
+        d.M = T; d.K = (int)z.Dq; d.X = ws.att; d.ldx = z.Dq; d.nsec = 1; d.r = r; d.mat[0] = po->A;
+        d.scale = 1.0f; d.U = ws.Uo; d.ldu = r;
+        CK(lora_down(d, s));
+      }
       g.ext.kx = r; g.ext.u = ws.Uo; g.ext.ldu = r; g.ext.uscale = sc; g.ext.nsec = 1; g.ext.r = r;
       g.ext.mat[0] = po->B; g.ext.row_off[1] = H;
     }
@@ -246,12 +272,14 @@ hipError_t layer_forward(const lsf_layer_cfg& c, const lsf_layer_weights& w, con
     const bool any = pg[0] || pg[1];
     g = GemmArgs(); g.M = T;
     if (any) {
-      LoraDown d;
-      d.part = ws.part; d.part_floats = ws.part_floats;
-      d.M = T; d.K = H; d.X = ws.h2; d.ldx = H; d.nsec = 2; d.r = r;
-      for (int i = 0; i < 2; ++i) d.mat[i] = pg[i] ? pg[i]->A : nullptr;
-      d.scale = 1.0f; d.U = ws.Ugu; d.ldu = 2 * r;
-      CK(lora_down(d, s));
+      if (!ws.u_ready) {
+        LoraDown d;
+        d.part = ws.lpart; d.part_floats = ws.lpart_floats;
+        d.M = T; d.K = H; d.X = ws.h2; d.ldx = H; d.nsec = 2; d.r = r;
+        for (int i = 0; i < 2; ++i) d.mat[i] = pg[i] ? pg[i]->A : nullptr;
+        d.scale = 1.0f; d.U = ws.Ugu; d.ldu = 2 * r;
+        CK(lora_down(d, s));
+      }
       g.ext.kx = 2 * r; g.ext.u = ws.Ugu; g.ext.ldu = 2 * r; g.ext.uscale = sc; g.ext.nsec = 2; g.ext.r = r;
       for (int i = 0; i < 2; ++i) g.ext.mat[i] = pg[i] ? pg[i]->B : nullptr;
       g.ext.row_off[1] = I; g.ext.row_off[2] = 2 * I;
@@ -263,9 +291,9 @@ hipError_t layer_forward(const lsf_layer_cfg& c, const lsf_layer_weights& w, con
   }
   {
     const lsf_lora_proj* pd = proj(lora, PD);
-    if (pd) {
+    if (pd && !ws.u_ready) {
       LoraDown d;
-      d.part = ws.part; d.part_floats = ws.part_floats;
+      d.part = ws.lpart; d.part_floats = ws.lpart_floats;
       d.M = T; d.K = I; d.X = ws.a; d.ldx = I; d.nsec = 1; d.r = r; d.mat[0] = pd->A;
       d.scale = 1.0f; d.U = ws.Ud; d.ldu = r;
       CK(lora_down(d, s));
@@ -290,8 +318,8 @@ namespace {
 hipError_t lora_dU(const uint16_t* dY, int64_t ld, int T, int r, float sc, int nsec, const lsf_lora_proj* const* p,
                    const int* xoff, const int* ksec, float* dU, const LayerWs& ws, hipStream_t s) {
   LoraDown d;
-  d.part = ws.part;
-  d.part_floats = ws.part_floats;
+  d.part = ws.lpart;
+  d.part_floats = ws.lpart_floats;
   d.M = T; d.X = dY; d.ldx = ld; d.nsec = nsec; d.r = r; d.bside = true; d.scale = sc; d.U = dU;
   d.ldu = nsec * r;
   d.K = ksec[0];
@@ -303,27 +331,27 @@ hipError_t lora_dU(const uint16_t* dY, int64_t ld, int T, int r, float sc, int n
   return lora_down(d, s);
 }
 
-// dA_sec += dU_sec^T X  and  dB_sec += s dY_sec^T U_sec.
+// dA_sec += dU_sec^T X  and  dB_sec += s dY_sec^T U_sec, every section of the
+// group in one launch.
 hipError_t lora_grads(int T, int r, float sc, int nsec, const lsf_lora_proj* const* p, const float* dU,
                       const uint16_t* X, int64_t ldx, int nx, const float* U, const uint16_t* dY, int64_t ldy,
                       const int* yoff, const int* ny, const LayerWs& ws, hipStream_t s) {
-  LoraGradSec ga[3], gb[3];
-  int na = 0, nb = 0;
+  LoraGradSec gs[2 * 3];
+  int n = 0;
   for (int i = 0; i < nsec; ++i) {
     if (!p[i]) continue;
     if (p[i]->dA) {
-      LoraGradSec& q = ga[na++];
+      LoraGradSec& q = gs[n++];
       q.P = dU; q.ldp = nsec * r; q.pcol0 = i * r; q.Q = X; q.ldq = ldx; q.qoff = 0; q.nq = nx;
       q.out = p[i]->dA; q.transposed = false; q.scale = 1.0f; q.overwrite = ws.grads_overwrite;
     }
     if (p[i]->dB) {
-      LoraGradSec& q = gb[nb++];
+      LoraGradSec& q = gs[n++];
       q.P = U; q.ldp = nsec * r; q.pcol0 = i * r; q.Q = dY; q.ldq = ldy; q.qoff = yoff[i]; q.nq = ny[i];
       q.out = p[i]->dB; q.transposed = true; q.scale = sc; q.overwrite = ws.grads_overwrite;
     }
   }
-  CK(lora_grad(ga, na, T, r, ws.part, ws.part_floats, s));
-  return lora_grad(gb, nb, T, r, ws.part, ws.part_floats, s);
+  return lora_grad(gs, n, T, r, ws.part, ws.part_floats, s);
 }
 
 }  // namespace

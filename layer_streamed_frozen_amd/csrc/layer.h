@@ -22,8 +22,13 @@ struct LayerWs {
   uint16_t *dgu, *dh, *dx2, *dob, *dqkv;
   float *dU, *attn_scratch, *part;
   size_t part_floats;
+  float* lpart;  // LoRA down-projection partials (never the split-K partials' memory)
+  size_t lpart_floats;
   Probe* probe = nullptr;
   bool grads_overwrite = false;  // the backward stores dA, dB instead of adding to them
+  // The LoRA activations (Uqkv, Uo, Ugu, Ud) already hold this layer's values
+  // for this input (kept from its forward): the forward does not recompute them.
+  bool u_ready = false;
   static size_t bytes(const lsf_layer_cfg& c);
   static LayerWs carve(const lsf_layer_cfg& c, void* base);
   // The tensors a forward with save = true leaves for the backward (h1, qkv,
@@ -31,6 +36,9 @@ struct LayerWs {
   // out from `base`: this workspace with those pointers moved there.
   static size_t saved_bytes(const lsf_layer_cfg& c);
   LayerWs with_saved(const lsf_layer_cfg& c, void* base) const;
+  // Only the LoRA activations (Uqkv, Uo, Ud, Ugu), laid out from `base`.
+  static size_t u_bytes(const lsf_layer_cfg& c);
+  LayerWs with_u(const lsf_layer_cfg& c, void* base) const;
 };
 
 WeightRef weight_ref(const lsf_weight& w, int fmt, int64_t ld);

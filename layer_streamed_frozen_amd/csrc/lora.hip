@@ -2,28 +2,32 @@
 //
 // lora_down: the rank-r projections U = X A^T (forward) and dU = s dY B
 // (backward): [M, K] x [K, r] with r <= 64 and K up to 28672.  The
-// contraction is cut into 256-wide chunks; a workgroup owns 64 rows and one
-// chunk of one section, stages that chunk of the adapter matrix in LDS as
-// bf16 [r][256] and runs v_mfma_f32_16x16x32_bf16 over it.  The per-chunk
-// partial products are then summed in a fixed order by a second kernel.
+// contraction is cut into at most 8 chunks (multiples of 256); a workgroup
+// owns 64 rows and one chunk of one section, stages the chunk's adapter
+// matrix 256 columns at a time in LDS as bf16 [r][256] and runs
+// v_mfma_f32_16x16x32_bf16 over it, loading the next 256 columns while it
+// multiplies these.  The per-chunk partial products are then summed in a fixed
+// order by a second kernel.
 //
 // lora_grad: the adapter gradients dA = dU^T X and dB = s dY^T U, reductions
 // over the tokens: Out[j, k] += scale * sum_t P[t, j] Q[t, k] (or = when the
-// section asks to overwrite: the first accumulation of a step).  A workgroup
+// section asks to overwrite: the first accumulation of a step).  The dA and dB
+// sections of a projection group share one launch.  A workgroup
 // owns 64 columns k, all r rows j and one share of the tokens; each wave takes
 // a quarter of that share in 32-row chunks, staged in its own LDS region so the
 // MFMA operands can run along the token axis (P transposed, Q read down its
 // rows with transposing loads), loading chunk i+1 while it multiplies chunk i.  The four wave tiles are summed in a fixed order; the
 // token shares, when there are several, are summed in order by a second
-// kernel, and the result is added (+=) into the fp32 gradient.  No atomics:
-// the same inputs give the same bits on every run.
+// kernel (the tokens are split only when the launch would otherwise have fewer
+// than 256 busy workgroups), and the result is added (+=) into the fp32
+// gradient.  No atomics: the same inputs give the same bits on every run.
 #include "common.h"
 #include "kernels.h"
 
 namespace lsf {
 namespace {
 
-constexpr int KC = 256;       // contraction chunk of lora_down
+constexpr int KC = 256;       // contraction columns lora_down stages per step
 constexpr int MS_LD = KC + 8; // LDS row stride (bf16) of the staged adapter chunk
 
 __device__ __forceinline__ int off_r8(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
@@ -32,76 +36,94 @@ __host__ __device__ __forceinline__ int sec_k(const LoraDown& a, int sec) {
   return a.ksec[sec] > 0 ? a.ksec[sec] : a.K;
 }
 
+// Workgroup (row block, section * nch_max + chunk): rows blockIdx.x * 64 ..
+// + 64, contraction columns [c * kc, (c + 1) * kc) of the section, 256 at a
+// time.
 template <int R, bool BSIDE>
-__global__ __launch_bounds__(256) void lora_down_part_kernel(LoraDown a, int nch_max) {
+__global__ __launch_bounds__(256) void lora_down_part_kernel(LoraDown a, int nch_max, int kc) {
   __shared__ __attribute__((aligned(16))) uint16_t Ms[64 * MS_LD];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, lr = lane & 15, lg = lane >> 4;
   const int sec = blockIdx.y / nch_max, c = blockIdx.y % nch_max;
   const int Ks = sec_k(a, sec);
-  const int k0 = c * KC;
+  const int kbeg = c * kc;
   const float* mat = a.mat[sec];
-  if (k0 >= Ks || mat == nullptr) return;  // uniform over the workgroup
-  const int kn = min(KC, Ks - k0);           // a multiple of 32
-  // Load order: the adapter chunk (16-byte vectors), then this lane's X
-  // fragments, then the chunk is converted and stored, so the stores wait only
-  // for the adapter loads while the X loads are still in flight.  Addresses
-  // are clamped into range and unused values zeroed afterwards: loads under a
-  // branch would each be waited for on the spot.
+  if (kbeg >= Ks || mat == nullptr) return;  // uniform over the workgroup
+  const int kend = min(Ks, kbeg + kc);
+  const int nsub = (kend - kbeg + KC - 1) / KC;
+  // Load order: the adapter sub-chunk (16-byte vectors), then this lane's X
+  // fragments; they are converted and stored only after the previous
+  // sub-chunk's MFMAs, so the loads overlap them.  Addresses are clamped into
+  // range and unused values zeroed afterwards: loads under a branch would each
+  // be waited for on the spot.
   constexpr int SMAX = (R * KC / 4 + 255) / 256;  // float4 per thread
-  const int n4 = R * kn / 4;
-  float4 sv[SMAX];
-#pragma unroll
-  for (int u = 0; u < SMAX; ++u) {
-    const int idx = min(tid + 256 * u, n4 - 1);
-    if constexpr (!BSIDE) {
-      const int q4 = kn / 4, j = idx / q4, k = (idx - j * q4) * 4;
-      sv[u] = *reinterpret_cast<const float4*>(mat + (int64_t)j * Ks + k0 + k);
-    } else {
-      sv[u] = reinterpret_cast<const float4*>(mat + (int64_t)k0 * R)[idx];
-    }
-  }
   const int m = blockIdx.x * 64 + wid * 16 + lr;
-  const uint16_t* xrow = a.X + (int64_t)min(m, a.M - 1) * a.ldx + a.xoff[sec] + k0 + lg * 8;
+  const uint16_t* xrow = a.X + (int64_t)min(m, a.M - 1) * a.ldx + a.xoff[sec] + lg * 8;
+  float4 sv[SMAX];
   u32x4 xa[KC / 32];
+  auto load = [&](int k0, int kn) {
+    const int n4 = R * kn / 4;
 #pragma unroll
-  for (int st = 0; st < KC / 32; ++st) xa[st] = *reinterpret_cast<const u32x4*>(xrow + (st * 32 < kn ? st * 32 : 0));
-  // the chunk as bf16 [j][k] (B-side: element f of the chunk is B[k0 + f / R][f % R])
-#pragma unroll
-  for (int u = 0; u < SMAX; ++u) {
-    const int idx = tid + 256 * u;
-    if (idx < n4) {
+    for (int u = 0; u < SMAX; ++u) {
+      const int idx = min(tid + 256 * u, n4 - 1);
       if constexpr (!BSIDE) {
         const int q4 = kn / 4, j = idx / q4, k = (idx - j * q4) * 4;
-        *reinterpret_cast<uint2*>(Ms + j * MS_LD + k) =
-            make_uint2(pack_bf16x2(sv[u].x, sv[u].y), pack_bf16x2(sv[u].z, sv[u].w));
+        sv[u] = *reinterpret_cast<const float4*>(mat + (int64_t)j * Ks + k0 + k);
       } else {
-        const int k = (4 * idx) / R, j = 4 * idx - k * R;  // R is a multiple of 4: one row k
-        Ms[j * MS_LD + k] = f32_to_bf16(sv[u].x);
-        Ms[(j + 1) * MS_LD + k] = f32_to_bf16(sv[u].y);
-        Ms[(j + 2) * MS_LD + k] = f32_to_bf16(sv[u].z);
-        Ms[(j + 3) * MS_LD + k] = f32_to_bf16(sv[u].w);
+        sv[u] = reinterpret_cast<const float4*>(mat + (int64_t)k0 * R)[idx];
       }
     }
-  }
-  __syncthreads();
-  // No branches around the MFMAs: steps past the chunk, rows past M and
-  // adapter rows past R multiply zeros.
+#pragma unroll
+    for (int st = 0; st < KC / 32; ++st)
+      xa[st] = *reinterpret_cast<const u32x4*>(xrow + k0 + (st * 32 < kn ? st * 32 : 0));
+  };
   constexpr int jt_n = (R + 15) / 16;
   f32x4 acc[jt_n];
 #pragma unroll
   for (int jt = 0; jt < jt_n; ++jt) acc[jt] = f32x4{0, 0, 0, 0};
+  load(kbeg, min(KC, kend - kbeg));
+  for (int sc = 0; sc < nsub; ++sc) {
+    const int k0 = kbeg + sc * KC;
+    const int kn = min(KC, kend - k0);  // a multiple of 32
+    if (sc > 0) __syncthreads();         // the previous sub-chunk's reads of Ms are done
+    // the sub-chunk as bf16 [j][k] (B-side: element f of it is B[k0 + f / R][f % R])
+    const int n4 = R * kn / 4;
 #pragma unroll
-  for (int st = 0; st < KC / 32; ++st) {
-    const uint32_t xkeep = (st * 32 < kn && m < a.M) ? 0xffffffffu : 0u;
-    const u32x4 x = {xa[st].x & xkeep, xa[st].y & xkeep, xa[st].z & xkeep, xa[st].w & xkeep};
-    const int k = (st * 32 < kn ? st * 32 : 0) + lg * 8;
+    for (int u = 0; u < SMAX; ++u) {
+      const int idx = tid + 256 * u;
+      if (idx < n4) {
+        if constexpr (!BSIDE) {
+          const int q4 = kn / 4, j = idx / q4, k = (idx - j * q4) * 4;
+          *reinterpret_cast<uint2*>(Ms + j * MS_LD + k) =
+              make_uint2(pack_bf16x2(sv[u].x, sv[u].y), pack_bf16x2(sv[u].z, sv[u].w));
+        } else {
+          const int k = (4 * idx) / R, j = 4 * idx - k * R;  // R is a multiple of 4: one row k
+          Ms[j * MS_LD + k] = f32_to_bf16(sv[u].x);
+          Ms[(j + 1) * MS_LD + k] = f32_to_bf16(sv[u].y);
+          Ms[(j + 2) * MS_LD + k] = f32_to_bf16(sv[u].z);
+          Ms[(j + 3) * MS_LD + k] = f32_to_bf16(sv[u].w);
+        }
+      }
+    }
+    u32x4 xc[KC / 32];
 #pragma unroll
-    for (int jt = 0; jt < jt_n; ++jt) {
-      const int j = jt * 16 + lr;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(Ms + min(j, R - 1) * MS_LD + k);
-      const uint32_t keep = (j < R) ? 0xffffffffu : 0u;
-      const u32x4 bb = {v.x & keep, v.y & keep, v.z & keep, v.w & keep};
-      acc[jt] = mfma16x16x32(x, bb, acc[jt]);
+    for (int st = 0; st < KC / 32; ++st) xc[st] = xa[st];
+    __syncthreads();
+    if (sc + 1 < nsub) load(k0 + KC, min(KC, kend - k0 - KC));
+    // No branches around the MFMAs: steps past the sub-chunk, rows past M and
+    // adapter rows past R multiply zeros.
+#pragma unroll
+    for (int st = 0; st < KC / 32; ++st) {
+      const uint32_t xkeep = (st * 32 < kn && m < a.M) ? 0xffffffffu : 0u;
+      const u32x4 x = {xc[st].x & xkeep, xc[st].y & xkeep, xc[st].z & xkeep, xc[st].w & xkeep};
+      const int k = (st * 32 < kn ? st * 32 : 0) + lg * 8;
+#pragma unroll
+      for (int jt = 0; jt < jt_n; ++jt) {
+        const int j = jt * 16 + lr;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(Ms + min(j, R - 1) * MS_LD + k);
+        const uint32_t keep = (j < R) ? 0xffffffffu : 0u;
+        const u32x4 bb = {v.x & keep, v.y & keep, v.z & keep, v.w & keep};
+        acc[jt] = mfma16x16x32(x, bb, acc[jt]);
+      }
     }
   }
   float* out = a.part + (size_t)(sec * nch_max + c) * a.M * R;
@@ -116,7 +138,7 @@ __global__ __launch_bounds__(256) void lora_down_part_kernel(LoraDown a, int nch
   }
 }
 
-__global__ __launch_bounds__(256) void lora_down_reduce_kernel(LoraDown a, int nch_max) {
+__global__ __launch_bounds__(256) void lora_down_reduce_kernel(LoraDown a, int nch_max, int kc) {
   const int64_t total = (int64_t)a.M * a.nsec * a.r;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
     const int j = (int)(i % a.r);
@@ -125,7 +147,7 @@ __global__ __launch_bounds__(256) void lora_down_reduce_kernel(LoraDown a, int n
     const int64_t t = rest / a.nsec;
     float v = 0.0f;
     if (a.mat[sec] != nullptr) {
-      const int nch = (sec_k(a, sec) + KC - 1) / KC;
+      const int nch = (sec_k(a, sec) + kc - 1) / kc;
       const size_t stride = (size_t)a.M * a.r;
       const float* p = a.part + (size_t)sec * nch_max * stride + (size_t)t * a.r + j;
       // eight loads in flight, then the adds in chunk order
@@ -143,7 +165,7 @@ __global__ __launch_bounds__(256) void lora_down_reduce_kernel(LoraDown a, int n
 }
 
 struct GradBatch {
-  LoraGradSec s[3];
+  LoraGradSec s[kLoraGradSecs];
 };
 
 constexpr int PS_LD = 40;  // LDS row stride (bf16) of the transposed P chunk
@@ -283,31 +305,43 @@ __global__ __launch_bounds__(256) void lora_grad_reduce_kernel(GradBatch gb, int
 }
 
 template <int R>
-void launch_down(const LoraDown& a, dim3 grid, int nch_max, hipStream_t s) {
-  if (a.bside) hipLaunchKernelGGL((lora_down_part_kernel<R, true>), grid, dim3(256), 0, s, a, nch_max);
-  else hipLaunchKernelGGL((lora_down_part_kernel<R, false>), grid, dim3(256), 0, s, a, nch_max);
+void launch_down(const LoraDown& a, dim3 grid, int nch_max, int kc, hipStream_t s) {
+  if (a.bside) hipLaunchKernelGGL((lora_down_part_kernel<R, true>), grid, dim3(256), 0, s, a, nch_max, kc);
+  else hipLaunchKernelGGL((lora_down_part_kernel<R, false>), grid, dim3(256), 0, s, a, nch_max, kc);
+}
+
+// Chunk length (a multiple of 256) that cuts the longest section into at
+// most 8 chunks, and the chunk count of that section.
+int down_chunk(const LoraDown& a, int* nch_max) {
+  int kmax = 0;
+  for (int i = 0; i < a.nsec; ++i) kmax = std::max(kmax, sec_k(a, i));
+  const int kc = KC * std::max(1, (kmax + 8 * KC - 1) / (8 * KC));
+  *nch_max = std::max(1, (kmax + kc - 1) / kc);
+  return kc;
 }
 
 }  // namespace
 
 hipError_t lora_down(const LoraDown& a, hipStream_t s) {
   if (a.M <= 0 || a.nsec <= 0) return hipSuccess;
-  if (a.r < 4 || a.r > 64 || (a.r & (a.r - 1)) != 0 || a.part == nullptr) return hipErrorInvalidValue;
+  if (a.r < 4 || a.r > 64 || (a.r & (a.r - 1)) != 0 || a.part == nullptr || a.U == nullptr)
+    return hipErrorInvalidValue;
   int nch_max = 0;
-  for (int i = 0; i < a.nsec; ++i) nch_max = std::max(nch_max, (sec_k(a, i) + KC - 1) / KC);
+  const int kc = down_chunk(a, &nch_max);
   if ((size_t)a.nsec * nch_max * a.M * a.r > a.part_floats) return hipErrorInvalidValue;
   dim3 grid((a.M + 63) / 64, a.nsec * nch_max);
   switch (a.r) {
-    case 4: launch_down<4>(a, grid, nch_max, s); break;
-    case 8: launch_down<8>(a, grid, nch_max, s); break;
-    case 16: launch_down<16>(a, grid, nch_max, s); break;
-    case 32: launch_down<32>(a, grid, nch_max, s); break;
-    case 64: launch_down<64>(a, grid, nch_max, s); break;
+    case 4: launch_down<4>(a, grid, nch_max, kc, s); break;
+    case 8: launch_down<8>(a, grid, nch_max, kc, s); break;
+    case 16: launch_down<16>(a, grid, nch_max, kc, s); break;
+    case 32: launch_down<32>(a, grid, nch_max, kc, s); break;
+    case 64: launch_down<64>(a, grid, nch_max, kc, s); break;
     default: return hipErrorInvalidValue;
   }
+  if (a.U == nullptr) return hipErrorInvalidValue;
   const int64_t total = (int64_t)a.M * a.nsec * a.r;
   const int blocks = (int)std::min<int64_t>((total + 255) / 256, 2048);
-  hipLaunchKernelGGL(lora_down_reduce_kernel, dim3(blocks), dim3(256), 0, s, a, nch_max);
+  hipLaunchKernelGGL(lora_down_reduce_kernel, dim3(blocks), dim3(256), 0, s, a, nch_max, kc);
   return hipGetLastError();
 }
 
@@ -316,9 +350,12 @@ hipError_t launch_grad(const GradBatch& gb, int nsec, int T, int maxq, float* pa
                        hipStream_t s) {
   const int tiles = (maxq + 63) / 64;
   const int chunks = (T + 31) / 32;
-  // token splits: enough workgroups to fill the chip, at least two 32-token
-  // chunks per wave, and partials that fit the scratch
-  int nz = std::max(1, std::min(std::min(8, (512 + tiles * nsec - 1) / (tiles * nsec)), chunks / 8));
+  int busy = 0;  // workgroups with columns to work on (sections narrower than maxq leave some idle)
+  for (int i = 0; i < nsec; ++i) busy += (gb.s[i].nq + 63) / 64;
+  // token splits: only as many as it takes to give at least 256 busy
+  // workgroups, at least two 32-token chunks per wave, and partials that fit
+  // the scratch
+  int nz = std::max(1, std::min(std::min(8, (256 + busy - 1) / std::max(busy, 1)), chunks / 8));
   while (nz > 1 && (part == nullptr || (size_t)nz * nsec * R * maxq > part_floats)) --nz;
   const int cpw = (chunks + 4 * nz - 1) / (4 * nz);
   nz = (chunks + 4 * cpw - 1) / (4 * cpw);
@@ -335,6 +372,7 @@ hipError_t launch_grad(const GradBatch& gb, int nsec, int T, int maxq, float* pa
 hipError_t lora_grad(const LoraGradSec* secs, int nsec, int T, int r, float* part, size_t part_floats,
                      hipStream_t s) {
   if (nsec <= 0 || T <= 0) return hipSuccess;
+  if (nsec > kLoraGradSecs) return hipErrorInvalidValue;
   GradBatch gb{};
   int maxq = 0;
   for (int i = 0; i < nsec; ++i) {

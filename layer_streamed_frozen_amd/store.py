@@ -278,7 +278,7 @@ class Stack:
         H = shape.hidden
         # n_micro > 1: accum_step keeps that many micro-batches' checkpoints
         self.n_micro = n_micro
-        self.ws = torch.empty(B.stack_accum_workspace_bytes(self.cfg, vocab, n_micro), dtype=torch.uint8,
+        self.ws = torch.empty(B.stack_accum_workspace_bytes(self.cfg, vocab, store.n_layers, n_micro), dtype=torch.uint8,
                               device=device)
         self.ckpts = [torch.empty((store.n_layers + 1, T, H), dtype=torch.bfloat16, device=device)
                       for _ in range(n_micro)]

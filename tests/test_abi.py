@@ -63,7 +63,9 @@ def test_workspace_sizes(lib):
     w1 = B.layer_workspace_bytes(LLAMA8B.cfg(1, 512))
     w4 = B.layer_workspace_bytes(LLAMA8B.cfg(4, 512))
     assert 0 < w1 < w4 < 8 * w1
-    assert B.stack_workspace_bytes(LLAMA8B.cfg(1, 512), 128256) > w1
+    assert B.stack_workspace_bytes(LLAMA8B.cfg(1, 512), 128256, 32) > B.stack_workspace_bytes(LLAMA8B.cfg(1, 512),
+                                                                                              128256, 1) > w1
+    assert B.stack_workspace_bytes(LLAMA8B.cfg(1, 512), 128256, 0) == 0
     assert B.linear_workspace_bytes(64, 256, 256, 8) > 0
     assert B.linear_workspace_bytes(0, 256, 256, 8) == 0
     # at most 2^20 tokens per call: one more and the size query reports 0
@@ -136,8 +138,12 @@ def test_binding_raises_with_message(lib):
 def test_gemm_schedule_switch_validates(lib):
     B.gemm_set_wide(False)
     B.gemm_set_wide(True)
+    assert lib.gemm_set_wide(128) == B.LSF_ERR_INVALID_ARG
     assert lib.gemm_set_wide(2) == B.LSF_ERR_INVALID_ARG
     assert "enable" in lib.lsf_last_error().decode()
+    B.gemm_set_wide(512)
+    B.gemm_set_wide(256)
+    B.gemm_set_wide(True)
     assert B.gemm_wide_launch_count() >= 0
 
 

@@ -172,3 +172,71 @@ def test_dpo_with_kept_activations_gives_the_same_bits(pair):
                 for i in range(pair.L)], kept.seq_logp.clone())
         assert same(a, got)
     kept.close()
+
+
+def _oracle_grads_at(s, dlp):
+    """The oracle's policy forward and backward with the per-sequence factors
+    dloss/dl(s) = dlp (the DPO gradient is linear in them)."""
+    from oracle import model as M
+    layers = [oracle_layer_weights(s.wfn(i), s.fmt) for i in range(s.L)]
+    loras = [s.lora.numpy(i) for i in range(s.L)]
+    oc = oracle_shape(s.shape)
+    fn, hd = s.fnorm_np.astype(np.float64), s.head_np.astype(np.float64)
+    logits, state = M.stack_forward(s.ids_np, s.emb_np, layers, loras, fn, hd, oc)
+    Bsz, T = s.ids_np.shape
+    labels, valid = M.shifted_labels(s.ids_np)
+    e = np.exp(logits - logits.max(axis=1, keepdims=True))
+    p = e / e.sum(axis=1, keepdims=True)
+    p[np.arange(p.shape[0]), labels] -= 1.0                  # softmax - onehot
+    dlogits = -np.repeat(np.asarray(dlp, np.float64), T)[:, None] * p
+    dlogits[~valid] = 0.0
+    grads, _ = M.stack_backward(dlogits, layers, loras, fn, hd, oc, state)
+    return grads
+
+
+def test_dpo_at_8b_shapes_full_vocabulary_matches_oracle():
+    # Two Llama-3.1-8B-shaped layers, the 128256-entry vocabulary, 2 pairs of
+    # 512 tokens sharing a 256-token prompt (the preference workload):
+    # sequence log-probabilities, loss and logits against the oracle's DPO step,
+    # so the multi-pass per-sequence sums (511 labelled rows) and the
+    # full-vocabulary head are covered.  Adapters at their initial scale: the
+    # preference margins h are then of the order of the bf16 noise of 511-term
+    # sums (about 0.5 here), and each pair's gradient factor beta sigma(-beta h)
+    # / P moves with that noise (a few percent), so the adapter gradients are
+    # compared with the oracle's backward at the factors the GPU derived from
+    # its own log-probabilities; the loss, which is that same function of the
+    # log-probabilities, is compared relatively.
+    s = DpoSetup(S.LLAMA8B, 2, 128256, 2, 512, "dpo8b", random_norms=False)
+    s.dpo()
+    a = s.snapshot()
+    s.dpo(mode=B.MODE_RESIDENT | B.MODE_ZERO_GRADS)
+    assert same(a, s.snapshot())
+    print("  oracle ...", flush=True)
+    ref = s.dpo_oracle()
+    lp = s.stack.seq_logp.double().cpu().numpy()
+    loss = float(s.stack.loss.item())
+    h_gpu = (lp[0, :2] - lp[1, :2]) - (lp[0, 2:] - lp[1, 2:])
+    h_ref = (ref["lp_pi"][:2] - ref["lp_ref"][:2]) - (ref["lp_pi"][2:] - ref["lp_ref"][2:])
+    print(f"  lp_pi  gpu={lp[0]} oracle={ref['lp_pi']}", flush=True)
+    print(f"  lp_ref gpu={lp[1]} oracle={ref['lp_ref']}", flush=True)
+    print(f"  h gpu={h_gpu} oracle={h_ref}; loss gpu={loss:.7f} oracle={ref['loss']:.7f}", flush=True)
+    assert abs(loss - float(np.mean(np.logaddexp(0.0, -BETA * h_gpu)))) < 1e-5
+    assert report("lp_pi", lp[0], ref["lp_pi"]) < TOL
+    assert report("lp_ref", lp[1], ref["lp_ref"]) < TOL
+    assert abs(loss - ref["loss"]) / abs(ref["loss"]) < TOL
+    assert report("logits", s.stack.logits.double().cpu().numpy(), ref["logits"]) < TOL
+    _, dlp_gpu = D.dpo_loss(lp[0], lp[1], BETA)
+    _, dlp_ref = D.dpo_loss(ref["lp_pi"], ref["lp_ref"], BETA)
+    print(f"  per-sequence factors gpu={dlp_gpu} oracle={dlp_ref}", flush=True)
+    grads = _oracle_grads_at(s, dlp_gpu)
+    for i in range(s.L):
+        g = s.lora.grads_numpy(i)
+        for n in S.PROJ:
+            assert report(f"L{i}.dA_{n}", g[n][0], grads[i][n][0]) < TOL
+            assert report(f"L{i}.dB_{n}", g[n][1], grads[i][n][1]) < TOL
+    # for the record: the same gradients against the oracle's own factors
+    for n in ("q", "down"):
+        print(f"  (at the oracle's factors) L1.dA_{n} rel_fro="
+              f"{np.linalg.norm(s.lora.grads_numpy(1)[n][0] - ref['grads'][1][n][0]) / np.linalg.norm(ref['grads'][1][n][0]):.3e}",
+              flush=True)
+    s.stack.close()

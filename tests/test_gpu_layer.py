@@ -185,23 +185,66 @@ def test_small_layer_other_ranks(rank):
 @pytest.mark.parametrize("rank", [16, 64])
 def test_wide_gate_up_kernel_matches_oracle_and_general_kernel(rank):
     # hidden 2048, intermediate 8192: the gate|up GEMM (N = 16384, K = 2048)
-    # runs on the 256x256 ping-pong kernel; 300 tokens leave the second
-    # 256-row tile ragged, and rank 64 gives four 32-wide LoRA steps.  The
-    # general kernel must give the same bits.
+    # runs on the ping-pong kernel, by default on one ragged 512-row tile
+    # (300 tokens), forced on two 256 x 256 row tiles (the second ragged);
+    # rank 64 gives four 32-wide LoRA steps.  Both tile shapes and the general
+    # kernel must give the same bits.
     shape = _shape(hidden=2048, n_heads=16, n_kv_heads=4, intermediate=8192, rank=rank, alpha=2.0 * rank)
     n0 = B.gemm_wide_launch_count()
     res, (y, dx, lora) = run_layer(shape, 1, 300, f"slwide{rank}")
     assert B.gemm_wide_launch_count() == n0 + 2  # forward and the recompute
     _assert_all(res)
-    B.gemm_set_wide(False)
-    try:
-        _, (y2, dx2, lora2) = run_layer(shape, 1, 300, f"slwide{rank}")
-    finally:
-        B.gemm_set_wide(True)
-    assert B.gemm_wide_launch_count() == n0 + 2
-    assert torch.equal(y, y2) and torch.equal(dx, dx2)
-    for n in S.PROJ:
-        assert torch.equal(lora.dA[0][n], lora2.dA[0][n]) and torch.equal(lora.dB[0][n], lora2.dB[0][n])
+    outs = []
+    for mode in (256, False):
+        B.gemm_set_wide(mode)
+        try:
+            outs.append(run_layer(shape, 1, 300, f"slwide{rank}")[1])
+        finally:
+            B.gemm_set_wide(True)
+    assert B.gemm_wide_launch_count() == n0 + 4
+    for y2, dx2, lora2 in outs:
+        assert torch.equal(y, y2) and torch.equal(dx, dx2)
+        for n in S.PROJ:
+            assert torch.equal(lora.dA[0][n], lora2.dA[0][n]) and torch.equal(lora.dB[0][n], lora2.dB[0][n])
+
+
+@pytest.mark.parametrize("tokens", [512, 2048])
+def test_wide_tile_shapes_give_identical_bits_at_8b_shapes(tokens):
+    # The 8B gate|up projection (512 x 28672 x 4096 and 2048 x 28672 x 4096) on
+    # 512 x 128 tiles, on 256 x 256 tiles and on the general kernel: one layer
+    # forward + backward each, every output and gradient bit for bit.
+    shape = S.LLAMA8B
+    print(f"[layer] wide tile shapes at {tokens} tokens", flush=True)
+    W = S.layer_weights_fp32("wts", shape)
+    blob = S.build_layer_blob(shape, W, B.FMT_NF4)
+    cfg = shape.cfg(tokens // 512, 512)
+    lw = B.layer_weights_from_blob(cfg, B.FMT_NF4, blob.data_ptr())
+    H = shape.hidden
+    _, xg = bf16_input("wts.x", (tokens, H))
+    _, dyg = bf16_input("wts.dy", (tokens, H))
+    ws = torch.empty(B.layer_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+    outs = []
+    for mode in (512, 256, False):
+        lora = S.LoraSet(shape, 1, prefix="wts.lora")
+        y = torch.empty((tokens, H), dtype=torch.bfloat16, device="cuda")
+        dx = torch.empty_like(y)
+        B.gemm_set_wide(mode)
+        try:
+            n0 = B.gemm_wide_launch_count()
+            B.layer_fwd(cfg, lw, lora.struct(0), xg, y, ws)
+            B.layer_bwd(cfg, lw, lora.struct(0), xg, dyg, dx, ws)
+            torch.cuda.synchronize()
+            launched = B.gemm_wide_launch_count() - n0
+        finally:
+            B.gemm_set_wide(True)
+        assert launched >= (2 if mode else 0)
+        outs.append((y, dx, lora))
+    y0, dx0, l0 = outs[0]
+    assert torch.isfinite(y0.float()).all() and torch.isfinite(dx0.float()).all()
+    for y, dx, lora in outs[1:]:
+        assert torch.equal(y0, y) and torch.equal(dx0, dx)
+        for n in S.PROJ:
+            assert torch.equal(l0.dA[0][n], lora.dA[0][n]) and torch.equal(l0.dB[0][n], lora.dB[0][n])
 
 
 def test_8b_layer_16x512_rows_and_gradient_sums():

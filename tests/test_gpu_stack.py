@@ -230,9 +230,9 @@ def test_accumulated_walk_argument_errors():
     with pytest.raises(B.LsfError) as e:
         B.stream_stack_accum_step(s.stack.handle, [io, io])
     assert e.value.status == B.LSF_ERR_WORKSPACE
-    assert B.stack_accum_workspace_bytes(s.stack.cfg, 256, 2) > B.stack_workspace_bytes(s.stack.cfg, 256)
-    assert B.stack_accum_workspace_bytes(s.stack.cfg, 256, 1) == B.stack_workspace_bytes(s.stack.cfg, 256)
-    assert B.stack_accum_workspace_bytes(s.stack.cfg, 256, 0) == 0
+    assert B.stack_accum_workspace_bytes(s.stack.cfg, 256, 2, 2) > B.stack_workspace_bytes(s.stack.cfg, 256, 2)
+    assert B.stack_accum_workspace_bytes(s.stack.cfg, 256, 2, 1) == B.stack_workspace_bytes(s.stack.cfg, 256, 2)
+    assert B.stack_accum_workspace_bytes(s.stack.cfg, 256, 2, 0) == 0
 
 
 def test_adapters_disabled_changes_only_through_lora():
@@ -292,6 +292,26 @@ def test_full_8b_shapes_two_layers_match_oracle():
         for n in S.PROJ:
             assert report(f"L{i}.dA_{n}", g[n][0], ref["grads"][i][n][0]) < TOL
             assert report(f"L{i}.dB_{n}", g[n][1], ref["grads"][i][n][1]) < TOL
+
+
+def test_full_8b_shapes_batch4_two_layers_match_oracle():
+    # The batch-4 micro-batch of the accumulation workload (4 x 512 tokens) on
+    # two 8B-shaped layers with the full vocabulary: the head at 2048 x 128256,
+    # the loss, logits and every adapter gradient against the oracle.
+    s = Setup(S.LLAMA8B, 2, 128256, 4, 512, "s8b4", random_norms=False)
+    s.step(mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS, loss_scale=0.25)
+    print("  oracle ...", flush=True)
+    ref = s.oracle(loss_scale=0.25)
+    loss = float(s.stack.loss.item())
+    print(f"  loss gpu={loss:.6f} oracle={ref['loss']:.6f}", flush=True)
+    assert abs(loss - ref["loss"]) / abs(ref["loss"]) < TOL
+    assert report("logits", s.stack.logits.double().cpu().numpy(), ref["logits"]) < TOL
+    for i in range(s.L):
+        g = s.lora.grads_numpy(i)
+        for n in S.PROJ:
+            assert report(f"L{i}.dA_{n}", g[n][0], ref["grads"][i][n][0]) < TOL
+            assert report(f"L{i}.dB_{n}", g[n][1], ref["grads"][i][n][1]) < TOL
+    s.stack.close()
 
 
 def test_layers_above_165_mib_stream_bit_equal():
