@@ -33,7 +33,17 @@ namespace {
 constexpr int HD = 128, BLK = 64, NTHR = 256;
 constexpr float LOG2E = 1.4426950408889634f;
 
-__device__ __forceinline__ int swz16(int row) { return (row & 15) ^ (((row >> 4) & 1) << 2); }
+// Tile rows of 128 bf16 (16 chunks of 16 B), chunk' = chunk ^ swz16(row).
+// The tiles are read two ways: 16-byte fragments (one chunk from each of 16
+// rows) and transposing 8-byte reads (chunks 2j, 2j+1 from each of 8 rows), and
+// written as whole rows.  swz16 = 13 r0 ^ 8 r1 ^ 2 r2 (XOR of the row bits'
+// multiples) was chosen by timing these three patterns on gfx950 for a set of
+// XOR-linear swizzles: it is the fastest for all three at once (transposing
+// reads 2 cycles per instruction instead of 4 with r & 15, fragment reads
+// and row stores unchanged).
+__device__ __forceinline__ int swz16(int row) {
+  return ((row & 1) ? 13 : 0) ^ (((row >> 1) & 1) << 3) ^ (((row >> 2) & 1) << 1);
+}
 __device__ __forceinline__ int off_r16(int row, int chunk) { return row * 128 + ((chunk ^ swz16(row)) << 3); }
 
 // A 64 x 128 bf16 tile (rows r0 .. r0 + 63 of a [rows, ld] matrix; zeros at or

@@ -42,8 +42,18 @@ struct Cfg {
 
 // LDS layouts (in bf16 elements).  R8: 64 bf16 per row (8 chunks of 16 B),
 // chunk' = chunk ^ (row & 7).  R16: 128 bf16 per row (16 chunks), chunk' =
-// chunk ^ swz16(row).
-__device__ __forceinline__ int swz16(int row) { return (row & 15) ^ (((row >> 4) & 1) << 2); }
+// chunk ^ swz16(row), for the weight tile of the input-gradient GEMM.  gfx950's
+// LDS has 64 banks (256 bytes per cycle) and serves each 32-lane half of a
+// wave separately; 8-byte reads, the transposing ones included, are free of
+// bank conflicts when no 8-byte slot (mod 256 B) repeats within a half.  The
+// transposing reads here take chunks 2j, 2j+1 of rows {0-3, 8-11} (or {4-7,
+// 12-15}) of a 16-row group, so swz16 gives those 8 rows 8 distinct values of
+// its upper three bits (r3, r0, r1); its low bit (r0) keeps the decode stores
+// at the fastest rate measured for them.  Measured with LDS pattern probes:
+// transposing reads 2 cycles per instruction (4 with the earlier r & 15).
+__device__ __forceinline__ int swz16(int row) {
+  return (((row >> 3) & 1) << 3) | ((row & 1) << 2) | (((row >> 1) & 1) << 1) | (row & 1);
+}
 __device__ __forceinline__ int off_r8(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
 __device__ __forceinline__ int off_r16(int row, int chunk) { return row * 128 + ((chunk ^ swz16(row)) << 3); }
 

@@ -1,6 +1,7 @@
 // Wide forward NF4 GEMM for gfx950, used when the output has many 256 x 256
-// tiles (the gate|up projection; q|k|v from 2048 tokens):
-// C[M, N] = A[M, K] . deq(W)[N, K]^T  (+ LoRA, + epilogue).
+// tiles (the gate|up projection; q|k|v from 2048 tokens), and as split-K with
+// fp32 partial sums for the narrower forward projections of a few hundred
+// tokens: C[M, N] = A[M, K] . deq(W)[N, K]^T  (+ LoRA, + epilogue).
 //
 // Same arithmetic as the general kernel in gemm.hip (every weight decoded to
 // bf16_rne(level * absmax), bf16 MFMA with fp32 accumulation, the k order of
@@ -36,6 +37,7 @@
 #include "kernels.h"
 #include "weight_decode.h"
 
+#include <algorithm>
 #include <atomic>
 
 namespace lsf {
@@ -55,6 +57,12 @@ struct WCfg {
   static constexpr int DMA = TM / 128;          // LDS-DMA instructions of A per wave and phase
   static constexpr int DEC = TN * WBK / 512;    // weights each thread decodes per tile: 16 or 8
 };
+
+// k tiles (32 deep) of each split but the last: whole 64-blocks, the same k
+// ranges as the general kernel's split-K, so both sum the same partials.
+__host__ __device__ __forceinline__ int wide_split_tiles(int K, int splits) {
+  return 2 * ((K / 64 + splits - 1) / splits);
+}
 
 // Tile rows of 32 bf16 (4 chunks of 16 B), chunk' = chunk ^ ((row >> 1) & 3):
 // the 8 lanes of a 16-byte read phase hit 8 distinct 16-byte bank groups.
@@ -137,12 +145,22 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g, EpiArgs e
   const int lr = lane & 15, lg = lane >> 4;
   // wave (grp, q): rows wr .. wr + 128, columns wc .. wc + 64 of the tile
   const int wr = grp * (TM / 2) + (q / C::NCW) * 128, wc = (q % C::NCW) * 64;
-  const int mt = (g.M + TM - 1) / TM, nt = g.N / TN, total = mt * nt;
+  // Split-K only for fp32 partial sums (the split index z and the k range
+  // stay compile-time zero and whole otherwise).
+  constexpr bool SPLIT = EPI == EPI_F32;
+  const int splits = SPLIT ? g.splits : 1;
+  const int mt = (g.M + TM - 1) / TM, nt = g.N / TN, tiles = mt * nt, total = tiles * splits;
   int t0 = blockIdx.x;
-  if ((total & 7) == 0) t0 = (t0 & 7) * (total >> 3) + (t0 >> 3);  // neighbouring tiles on one XCD
-  const int mtile = t0 % mt, ntile = t0 / mt;
+  // Neighbouring work items on one XCD; split z is the slow index, so an XCD
+  // mostly works on one k range of A.
+  if ((total & 7) == 0) t0 = (t0 & 7) * (total >> 3) + (t0 >> 3);
+  const int z = SPLIT ? t0 / tiles : 0, tile = t0 - z * tiles;
+  const int mtile = tile % mt, ntile = tile / mt;
   const int m0 = mtile * TM;
-  const int nk = g.K / WBK;
+  // This split's k tiles: whole 64-blocks, the same ranges as the general kernel.
+  const int per = SPLIT ? wide_split_tiles(g.K, splits) : g.K / WBK;
+  const int kt0 = z * per;
+  const int nk = min(g.K / WBK - kt0, per);
 
   // LDS-DMA of A: wave (grp, q) moves rows grp*TM/2 + q*TM/8 + j*16 + lane/4,
   // 16 bytes each, into consecutive 16-byte slots; the source chunk is the
@@ -155,12 +173,12 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g, EpiArgs e
     const int rbase = grp * (TM / 2) + q * (TM / 8) + j * 16;
     const int row = rbase + (lane >> 2);
     const int lch = (lane & 3) ^ ((row >> 1) & 3);
-    asrc[j] = g.A + (int64_t)min(m0 + row, g.M - 1) * g.lda + lch * 8;
+    asrc[j] = g.A + (int64_t)min(m0 + row, g.M - 1) * g.lda + (int64_t)kt0 * WBK + lch * 8;
     adst[j] = rbase * 32;
   }
   // Decode share: tile column dcol and DEC consecutive k of it per tile.
   const int dcol = grp * (TN / 2) + tg / (WBK / DEC), dk = tg % (WBK / DEC);
-  const int64_t e0 = wide_wrow<TN>(g, ntile, dcol) * g.W.ld + dk * DEC;  // element index at tile 0
+  const int64_t e0 = wide_wrow<TN>(g, ntile, dcol) * g.W.ld + (int64_t)kt0 * WBK + dk * DEC;  // at tile 0
   const uint8_t* cp = g.W.packed + (e0 >> 1);
   const float* ap = g.W.absmax + (e0 >> 6);  // rows are whole 64-blocks (K % 64 == 0)
   static_assert(FMT == FMT_NF4, "the wide kernel reads fp32 absmax");
@@ -260,7 +278,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g, EpiArgs e
   // LoRA extension: 32-wide steps of [uscale * U | adapter B] in stage 0;
   // each unit is one row and 16 of the step's 32 columns.
   const LoraExt& x = g.ext;
-  const int next = x.kx > 0 ? (x.kx + WBK - 1) / WBK : 0;
+  const int next = (x.kx > 0 && z == splits - 1) ? (x.kx + WBK - 1) / WBK : 0;  // last split only
   uint16_t* As = lds;
   uint16_t* Bs = lds + C::ATILE;
   for (int xt = 0; xt < next; ++xt) {
@@ -339,7 +357,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g, EpiArgs e
           }
         }
       }
-  } else {  // EPI_BF16
+  } else {  // EPI_BF16, EPI_RESID_BF16, EPI_F32 (split z's partial sums)
 #pragma unroll
     for (int mf = 0; mf < 8; ++mf)
 #pragma unroll
@@ -350,7 +368,14 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g, EpiArgs e
           const int m = m0 + wr + mf * 16 + lg * 4 + i;
           if (m >= g.M) continue;
           const float v = acc[mf][nf][i];
-          static_cast<uint16_t*>(e.C)[(int64_t)m * e.ldc + n] = f32_to_bf16(v);
+          if constexpr (EPI == EPI_F32) {
+            static_cast<float*>(e.C)[(int64_t)z * g.M * g.N + (int64_t)m * e.ldc + n] = v;
+          } else if constexpr (EPI == EPI_RESID_BF16) {
+            static_cast<uint16_t*>(e.C)[(int64_t)m * e.ldc + n] =
+                f32_to_bf16(bf16_to_f32(e.R[(int64_t)m * e.ldr + n]) + v);
+          } else {
+            static_cast<uint16_t*>(e.C)[(int64_t)m * e.ldc + n] = f32_to_bf16(v);
+          }
         }
       }
   }
@@ -359,9 +384,13 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g, EpiArgs e
 template <int TM>
 hipError_t launch_wide(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
   constexpr int TN = WCfg<TM>::TN;
-  const dim3 grid(((g.M + TM - 1) / TM) * (g.N / TN)), block(512);
+  const dim3 grid(((g.M + TM - 1) / TM) * (g.N / TN) * g.splits), block(512);
   switch (e.kind) {
     case EPI_BF16: hipLaunchKernelGGL((gemm_wide_kernel<TM, FMT_NF4, EPI_BF16>), grid, block, 0, s, g, e); break;
+    case EPI_RESID_BF16:
+      hipLaunchKernelGGL((gemm_wide_kernel<TM, FMT_NF4, EPI_RESID_BF16>), grid, block, 0, s, g, e);
+      break;
+    case EPI_F32: hipLaunchKernelGGL((gemm_wide_kernel<TM, FMT_NF4, EPI_F32>), grid, block, 0, s, g, e); break;
     case EPI_SWIGLU: hipLaunchKernelGGL((gemm_wide_kernel<TM, FMT_NF4, EPI_SWIGLU>), grid, block, 0, s, g, e); break;
     default: return hipErrorInvalidValue;
   }
@@ -375,24 +404,63 @@ int wide_tile_rows(const GemmArgs&) { return 512; }
 
 }  // namespace
 
-// The wide kernel needs whole column tiles (and halves of them in pair mode),
-// 64-deep absmax blocks, 16-byte aligned A rows, 8-byte aligned codes, and no
-// split-K.  It is chosen for N >= 16384 (gate|up), or when there are at least
-// 192 of its 256 x 256 tiles, three quarters of the 256 compute units (q|k|v
-// from 2048 tokens: 144 vs 174 us there, measured), and K >= 2048: with short
-// contractions its prologue dominates (measured 1.7x slower than the general
-// kernel at K = 512).
-bool gemm_wide_applies(const GemmArgs& g, const EpiArgs& e) {
-  if (g.splits != 1 || g.M < 256 || g.N % 256 != 0) return false;
-  if (g.N < 16384 && (int64_t)((g.M + 255) / 256) * (g.N / 256) < 192) return false;
+namespace {
+
+// What the wide kernel can run: whole column tiles (and halves of them in
+// pair mode), 64-deep absmax blocks, 16-byte aligned A rows, 8-byte aligned
+// codes; with split-K (fp32 partial sums, ldc = N) at least 8 of its 32-deep
+// k tiles in every split.
+bool wide_capable(const GemmArgs& g, const EpiArgs& e) {
+  if (g.splits < 1 || g.M < 256 || g.N % 256 != 0) return false;
   // fp32 absmax only: with the double-quantised absmax (two more loads in
   // flight per code set) the kernel no longer fits its 256 registers.
   if (g.W.fmt != FMT_NF4) return false;
-  if (g.K % 64 != 0 || g.K < 2048 || g.W.ld != g.K || g.lda % 8 != 0) return false;
+  if (g.K % 64 != 0 || g.W.ld != g.K || g.lda % 8 != 0) return false;
   if (((uintptr_t)g.A & 15) != 0 || ((uintptr_t)g.W.packed & 7) != 0) return false;
   if (g.pair_I > 0 && (g.pair_I * 2 != g.N || g.pair_I % 128 != 0)) return false;
+  if (g.splits > 1) {
+    if (e.kind != EPI_F32 || g.pair_I > 0 || e.ldc != g.N) return false;
+    const int per = wide_split_tiles(g.K, g.splits);
+    return per >= 8 && g.K / WBK - (g.splits - 1) * per >= 8;
+  }
   if (e.kind == EPI_SWIGLU) return g.pair_I > 0;
-  return e.kind == EPI_BF16 && g.pair_I == 0;
+  return (e.kind == EPI_BF16 || e.kind == EPI_RESID_BF16) && g.pair_I == 0;
+}
+
+}  // namespace
+
+// Forward GEMMs with long contractions (K >= 8192: down) and fewer than 192
+// tiles of 512 x 128 run split-K on the wide kernel: as many splits (up to 8)
+// as keep the tiles times splits within the 256 compute units.  Measured on
+// MI355X: down 95.5 vs 103 us at 512 tokens (8 splits), 276 vs 332 us at 2048
+// (2 splits); q|k|v and o (K = 4096) stay faster on the general kernel (at
+// 512 tokens q|k|v 71.7 us there against 73 - 108 us with 2 - 6 wide splits,
+// o 46.6 against 49.5 - 78.6 us with 2 - 8).
+int wide_splits(const GemmArgs& g) {
+  if (g.M < 256 || g.K < 8192 || g.N >= 16384 || g.N % 256 != 0 || g.pair_I > 0) return 0;
+  const int tiles = ((g.M + 511) / 512) * (g.N / 128);
+  if (tiles >= 192) return 0;
+  EpiArgs pe;
+  pe.kind = EPI_F32;
+  pe.ldc = g.N;
+  GemmArgs t = g;
+  for (int s = std::min(8, 256 / tiles); s > 1; --s) {
+    t.splits = s;
+    if (wide_capable(t, pe)) return s;
+  }
+  return 0;
+}
+
+// Without split-K the wide kernel is chosen for N >= 16384 (gate|up), or when
+// there are at least 192 of its tiles, three quarters of the 256 compute units
+// (q|k|v from 2048 tokens: 144 vs 174 us there, measured), and K >= 2048: with
+// short contractions its prologue dominates (measured 1.7x slower than the
+// general kernel at K = 512).  With split-K, where wide_splits chose it.
+bool gemm_wide_applies(const GemmArgs& g, const EpiArgs& e) {
+  if (!wide_capable(g, e)) return false;
+  if (g.splits > 1) return wide_splits(g) == g.splits;
+  if (g.K < 2048) return false;
+  return g.N >= 16384 || (int64_t)((g.M + 255) / 256) * (g.N / 256) >= 192;
 }
 
 namespace {

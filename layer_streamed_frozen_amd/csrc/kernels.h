@@ -67,9 +67,14 @@ struct EpiArgs {
 int gemm_tile_rows(int M, int N, bool nn);
 // C = A W^T (+ LoRA), W rows map to C columns.
 hipError_t gemm_nt(const GemmArgs& g, const EpiArgs& e, hipStream_t s);
-// The 256 x 256 ping-pong kernel for wide forward GEMMs (gate|up); gemm_nt
-// uses it by itself where gemm_wide_applies.
+// The ping-pong kernel for forward NF4 GEMMs (gate|up; with split-K also
+// q|k|v, o and down at a few hundred tokens); gemm_nt uses it by itself where
+// gemm_wide_applies.
 bool gemm_wide_applies(const GemmArgs& g, const EpiArgs& e);
+// Split count (2..8) with which the wide kernel serves a forward GEMM of few
+// tiles as split-K, or 0.  Depends on the shape only, so the general kernel
+// given the same count sums the same partials in the same order.
+int wide_splits(const GemmArgs& g);
 void set_gemm_wide(bool enable);  // process-wide; default on
 void set_gemm_wide_tile(int rows);  // 0: tile rows by shape; 256 or 512: forced (diagnostics)
 int64_t gemm_wide_launches();      // wide-kernel launches so far

@@ -174,8 +174,12 @@ int choose_splits(int tiles, int K) {
 hipError_t run_gemm(bool nn, GemmArgs g, const EpiArgs& e, float* part, size_t part_floats, hipStream_t s) {
   const int bm = gemm_tile_rows(g.M, g.N, nn);
   const int tiles = ((g.M + bm - 1) / bm) * (g.N / 128);
-  int splits = (e.kind == EPI_SWIGLU || part == nullptr) ? 1 : choose_splits(tiles, g.K);
-  while (splits > 1 && (size_t)splits * g.M * g.N > part_floats) splits /= 2;
+  int splits = 1;
+  if (e.kind != EPI_SWIGLU && part != nullptr) {
+    const int ws = nn ? 0 : wide_splits(g);
+    splits = ws > 0 ? ws : choose_splits(tiles, g.K);
+  }
+  while (splits > 1 && (size_t)splits * g.M * g.N > part_floats) --splits;
   g.splits = splits;
   if (splits == 1) return nn ? gemm_nn(g, e, s) : gemm_nt(g, e, s);
   EpiArgs pe;

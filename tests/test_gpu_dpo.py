@@ -204,8 +204,13 @@ def test_dpo_at_8b_shapes_full_vocabulary_matches_oracle():
     # sums (about 0.5 here), and each pair's gradient factor beta sigma(-beta h)
     # / P moves with that noise (a few percent), so the adapter gradients are
     # compared with the oracle's backward at the factors the GPU derived from
-    # its own log-probabilities; the loss, which is that same function of the
-    # log-probabilities, is compared relatively.
+    # its own log-probabilities.  The loss is the same function of the
+    # log-probabilities: a difference of four sums near -6400 feeds it, so
+    # its relative error is about 400 times theirs and is not held to the
+    # 2e-2 bound.  Instead each sequence log-probability (a sum of 511
+    # same-sign terms) must be within one bf16 unit roundoff (2^-9) of the
+    # oracle's relatively, and the loss within what that allows: it is
+    # beta-Lipschitz in every margin h, so |dloss| <= beta * mean |dh|.
     s = DpoSetup(S.LLAMA8B, 2, 128256, 2, 512, "dpo8b", random_norms=False)
     s.dpo()
     a = s.snapshot()
@@ -223,7 +228,9 @@ def test_dpo_at_8b_shapes_full_vocabulary_matches_oracle():
     assert abs(loss - float(np.mean(np.logaddexp(0.0, -BETA * h_gpu)))) < 1e-5
     assert report("lp_pi", lp[0], ref["lp_pi"]) < TOL
     assert report("lp_ref", lp[1], ref["lp_ref"]) < TOL
-    assert abs(loss - ref["loss"]) / abs(ref["loss"]) < TOL
+    for got, want in ((lp[0], ref["lp_pi"]), (lp[1], ref["lp_ref"])):
+        assert np.max(np.abs(got - want) / np.abs(want)) < 2.0 ** -9
+    assert abs(loss - ref["loss"]) <= BETA * float(np.mean(np.abs(h_gpu - h_ref))) + 1e-5
     assert report("logits", s.stack.logits.double().cpu().numpy(), ref["logits"]) < TOL
     _, dlp_gpu = D.dpo_loss(lp[0], lp[1], BETA)
     _, dlp_ref = D.dpo_loss(ref["lp_pi"], ref["lp_ref"], BETA)

@@ -87,6 +87,29 @@ def test_wide_forward_kernel_matches_oracle_and_general_kernel():
         assert np.array_equal(res[k][0], res2[k][0]), k
 
 
+@pytest.mark.parametrize("n_out,n_in,T", [(4096, 14336, 512), (6144, 8192, 300), (2048, 8192, 257)])
+def test_wide_split_k_matches_oracle_and_general_kernel(n_out, n_in, T):
+    # Long contractions over few 512 x 128 tiles (32, 48, 16): the forward
+    # GEMM runs split-K on the ping-pong kernel (8, 5, 8 splits), fp32 partial
+    # sums then the ordered reduction.  The second case has a shorter last
+    # split (48 of 52 k tiles), the others a ragged row tile; the LoRA steps
+    # ride on the last split.  The general kernel with the same splits gives
+    # the same bits.
+    n0 = B.gemm_wide_launch_count()
+    res = _run(f"linsk{n_out}", n_out, n_in, T, 16, 16.0)
+    assert B.gemm_wide_launch_count() == n0 + 1
+    for k, (g, r) in res.items():
+        assert report(k, g, r) < TOL, k
+    B.gemm_set_wide(False)
+    try:
+        res2 = _run(f"linsk{n_out}", n_out, n_in, T, 16, 16.0)
+    finally:
+        B.gemm_set_wide(True)
+    assert B.gemm_wide_launch_count() == n0 + 1
+    for k in res:
+        assert np.array_equal(res[k][0], res2[k][0]), k
+
+
 def test_wide_kernel_chosen_by_tile_count():
     # 6144 outputs (the q|k|v width) over 2048 tokens: 8 x 24 = 192 tiles of
     # 256 x 256, enough for the wide kernel; it matches the oracle and gives the
@@ -103,7 +126,8 @@ def test_wide_kernel_chosen_by_tile_count():
         B.gemm_set_wide(True)
     for k in res:
         assert np.array_equal(res[k][0], res2[k][0]), k
-    # 512 tokens of the same width: 48 tiles, the general kernel
+    # 512 tokens of the same width: 48 tiles, and a contraction too short for
+    # split-K on the wide kernel: the general kernel
     n1 = B.gemm_wide_launch_count()
     _run("linwq5", 6144, 2048, 512, 16, 16.0)
     assert B.gemm_wide_launch_count() == n1
