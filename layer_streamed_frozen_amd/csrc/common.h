@@ -114,6 +114,16 @@ __device__ __forceinline__ void nf4_decode8(const Nf4Table& t, uint32_t w, uint3
   out[3] = __builtin_amdgcn_perm(o23, e23, 0x07060302u);  // e6 | e7
 }
 
+// dg and du of one element from the input gradient v of a = silu(g) u, with
+// no contraction into fused multiply-adds, so every kernel that applies it
+// gets the same bits.
+__device__ __forceinline__ void swiglu_grad(float v, float gv, float uv, float& dg, float& du) {
+#pragma clang fp contract(off)
+  const float sg = 1.0f / (1.0f + __expf(-gv));
+  dg = v * uv * sg * (1.0f + gv * (1.0f - sg));
+  du = v * gv * sg;
+}
+
 __device__ __forceinline__ float warp_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

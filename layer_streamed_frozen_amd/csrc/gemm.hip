@@ -282,13 +282,6 @@ __device__ __forceinline__ void compute_and_stage(const uint16_t* As, const uint
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 
-// dg and du of one element from the input gradient v of a = silu(g) u.
-__device__ __forceinline__ void swiglu_grad(float v, float gv, float uv, float& dg, float& du) {
-  const float sg = 1.0f / (1.0f + __expf(-gv));
-  dg = v * uv * sg * (1.0f + gv * (1.0f - sg));
-  du = v * gv * sg;
-}
-
 // This wave's LDS accesses so far are complete, and neither the compiler nor
 // the hardware moves later ones ahead of them.
 __device__ __forceinline__ void wave_lds_fence() {
@@ -549,12 +542,11 @@ __global__ void splitk_reduce_kernel(const float* part, int splits, int M, int N
         static_cast<uint16_t*>(e.C)[m * e.ldc + n] = f32_to_bf16(bf16_to_f32(e.R[m * e.ldr + n]) + v);
         break;
       case EPI_SWIGLU_BWD: {
-        const float gv = bf16_to_f32(e.g[m * e.ldgu + n]);
-        const float uv = bf16_to_f32(e.u[m * e.ldgu + n]);
-        const float sg = 1.0f / (1.0f + __expf(-gv));
+        float dg, du;
+        swiglu_grad(v, bf16_to_f32(e.g[m * e.ldgu + n]), bf16_to_f32(e.u[m * e.ldgu + n]), dg, du);
         uint16_t* C = static_cast<uint16_t*>(e.C);
-        C[m * e.ldc + n] = f32_to_bf16(v * uv * sg * (1.0f + gv * (1.0f - sg)));
-        C[m * e.ldc + N + n] = f32_to_bf16(v * gv * sg);
+        C[m * e.ldc + n] = f32_to_bf16(dg);
+        C[m * e.ldc + N + n] = f32_to_bf16(du);
         break;
       }
       default: break;
@@ -586,7 +578,10 @@ hipError_t gemm_nt(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
   if (g_wide_enabled.load(std::memory_order_relaxed) && gemm_wide_applies(g, e)) return gemm_nt_wide(g, e, s);
   return launch<false>(g, e, s);
 }
-hipError_t gemm_nn(const GemmArgs& g, const EpiArgs& e, hipStream_t s) { return launch<true>(g, e, s); }
+hipError_t gemm_nn(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
+  if (g_wide_enabled.load(std::memory_order_relaxed) && gemm_wide_nn_applies(g, e)) return gemm_nn_wide(g, e, s);
+  return launch<true>(g, e, s);
+}
 
 hipError_t splitk_reduce(const float* part, int splits, int M, int N, const EpiArgs& e, hipStream_t s) {
   if (splits < 1 || splits > 8) return hipErrorInvalidValue;

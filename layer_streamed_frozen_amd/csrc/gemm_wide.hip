@@ -75,6 +75,15 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x3f70 | N);
 }
 
+// This wave's LDS accesses so far are complete, and neither the compiler nor
+// the hardware moves later ones ahead of them (no workgroup barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Workgroup barrier: this wave's LDS reads and writes complete (lgkmcnt 0),
 // then s_barrier.  The empty asm statements keep the compiler from moving
 // memory accesses across it.
@@ -381,6 +390,315 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g, EpiArgs e
   }
 }
 
+// ---------------------------------------------------------------------------
+// Input-gradient variant: C[M, N] = A[M, K] . deq(W)[K, N], W stored [K][N]
+// (the frozen weight's own layout: the contraction runs down its rows).  The
+// schedule is the forward kernel's (two groups half a tile apart, A by
+// LDS-DMA three tiles ahead, codes five ahead, four LDS stages); the weight
+// tile is 32 k rows x TN columns, decoded along its rows (each k row has its
+// own absmax blocks, so every decode builds its table) into a row-major LDS
+// tile, and each wave reads its B operand from it with transposing loads
+// (ds_read_b64_tr_b16), 4 k rows per load.  Same k order and MFMA as the
+// general kernel's input-gradient GEMM, so both give the same bits.
+
+// B tile rows of TN bf16 (TN / 8 chunks of 16 B), chunk' = chunk ^ nn_swz(row):
+// the transposing reads take chunks 2j, 2j+1 of rows {0-3, 8-11} (or {4-7,
+// 12-15}) of a 16-row group, and nn_swz gives those 8 rows 8 distinct values
+// of its upper three bits, so no 8-byte slot repeats within a 32-lane half
+// (gfx950 serves each half at 256 bytes per cycle).
+__device__ __forceinline__ int nn_swz(int row) {
+  return (((row >> 3) & 1) << 3) | ((row & 1) << 2) | (((row >> 1) & 1) << 1) | (row & 1);
+}
+template <int TN>
+__device__ __forceinline__ int nboff(int row, int chunk) { return row * TN + ((chunk ^ nn_swz(row)) << 3); }
+
+template <int TM, int EPI>
+__global__ __launch_bounds__(512, 1) void gemm_wide_nn_kernel(GemmArgs g, EpiArgs e) {
+  using C = WCfg<TM>;
+  constexpr int TN = C::TN;
+  constexpr int CPR = TN / 8;              // 16-byte chunks per B row
+  constexpr int NDEC = TN * WBK / 512;     // weights each thread decodes per tile: 8 or 16
+  constexpr int NC = NDEC / 8;             // its chunks
+  __shared__ __attribute__((aligned(16))) uint16_t lds[WNST * C::STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wid >> 2, q = wid & 3, tg = tid & 255;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int wr = grp * (TM / 2) + (q / C::NCW) * 128, wc = (q % C::NCW) * 64;
+  constexpr bool SPLIT = EPI == EPI_F32;
+  const int splits = SPLIT ? g.splits : 1;
+  const int mt = (g.M + TM - 1) / TM, nt = g.N / TN, tiles = mt * nt, total = tiles * splits;
+  int t0 = blockIdx.x;
+  if ((total & 7) == 0) t0 = (t0 & 7) * (total >> 3) + (t0 >> 3);
+  const int z = SPLIT ? t0 / tiles : 0, tile = t0 - z * tiles;
+  const int mtile = tile % mt, ntile = tile / mt;
+  const int m0 = mtile * TM;
+  const int per = SPLIT ? wide_split_tiles(g.K, splits) : g.K / WBK;
+  const int kt0 = z * per;
+  const int nk = min(g.K / WBK - kt0, per);
+
+  const uint16_t* asrc[C::DMA];
+  int adst[C::DMA];
+#pragma unroll
+  for (int j = 0; j < C::DMA; ++j) {
+    const int rbase = grp * (TM / 2) + q * (TM / 8) + j * 16;
+    const int row = rbase + (lane >> 2);
+    const int lch = (lane & 3) ^ ((row >> 1) & 3);
+    asrc[j] = g.A + (int64_t)min(m0 + row, g.M - 1) * g.lda + (int64_t)kt0 * WBK + lch * 8;
+    adst[j] = rbase * 32;
+  }
+  // Decode share: group grp decodes k rows 16 grp .. + 16 of every B tile;
+  // thread tg takes row drow, chunks dch .. dch + NC (NDEC columns, inside
+  // one 64-column absmax block).
+  const int drow = 16 * grp + tg / (CPR / NC), dch = (tg % (CPR / NC)) * NC;
+  const int64_t e0 = ((int64_t)kt0 * WBK + drow) * g.W.ld + (int64_t)ntile * TN + dch * 8;
+  const uint8_t* cp = g.W.packed + (e0 >> 1);
+  const float* ap = g.W.absmax + (e0 >> 6);
+  const int64_t cstride = (int64_t)WBK * g.W.ld / 2, astride = (int64_t)WBK * g.W.ld / 64;  // per k tile
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+
+  auto issue_a = [&](int tsrc, int tdst) {
+    uint16_t* st = lds + (tdst & 3) * C::STAGE;
+#pragma unroll
+    for (int j = 0; j < C::DMA; ++j) lds_dma16(asrc[j] + tsrc * WBK, st + adst[j]);
+  };
+  auto ld_codes = [&](int t) {
+    CodeSet<NDEC> cs;
+    const uint8_t* p = cp + t * cstride;
+    if constexpr (NDEC == 16) {
+      cs.c = *reinterpret_cast<const u32x2*>(p);
+    } else {
+      cs.c.x = *reinterpret_cast<const uint32_t*>(p);
+      cs.c.y = 0;
+    }
+    cs.am = ap[t * astride];
+    return cs;
+  };
+  auto decode_b = [&](int t, const CodeSet<NDEC>& cs) {
+    uint16_t* bs = lds + (t & 3) * C::STAGE + C::ATILE;
+    const Nf4Table tb = nf4_table(cs.am);
+    uint32_t o[4];
+    nf4_decode8(tb, cs.c.x, o);
+    *reinterpret_cast<u32x4*>(bs + nboff<TN>(drow, dch)) = u32x4{o[0], o[1], o[2], o[3]};
+    if constexpr (NDEC == 16) {
+      nf4_decode8(tb, cs.c.y, o);
+      *reinterpret_cast<u32x4*>(bs + nboff<TN>(drow, dch + 1)) = u32x4{o[0], o[1], o[2], o[3]};
+    }
+  };
+  // This wave's B operand of tile stage `bs`: column wc + nf*16 + lr, k rows
+  // lg*8 .. + 8, from two transposing loads.
+  auto read_b = [&](const uint16_t* bs, u32x4 (&bf)[4]) {
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf) {
+      const int col = wc + nf * 16 + 4 * (lr & 3);
+      const int row = lg * 8 + (lr >> 2);
+      const u32x2 lo = lds_read_tr4(bs, nboff<TN>(row, col >> 3) + (col & 7));
+      const u32x2 hi = lds_read_tr4(bs, nboff<TN>(row + 4, col >> 3) + (col & 7));
+      bf[nf] = u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
+  };
+
+  CodeSet<NDEC> cs[3];
+  {
+    CodeSet<NDEC> pc[3];
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      issue_a(t, t);
+      pc[t] = ld_codes(t);
+    }
+    cs[0] = ld_codes(3);
+    cs[1] = ld_codes(4);
+    cs[2] = cs[1];
+    wait_vm<0>();
+#pragma unroll
+    for (int t = 0; t < 3; ++t) decode_b(t, pc[t]);
+  }
+  wbar();
+  if (grp == 1) wbar();
+
+  auto step = [&](int t, CodeSet<NDEC>& cdec, CodeSet<NDEC>& cld) {
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 af[8], bf[4];
+    {
+      const uint16_t* st = lds + (t & 3) * C::STAGE;
+#pragma unroll
+      for (int mf = 0; mf < 8; ++mf)
+        af[mf] = *reinterpret_cast<const u32x4*>(st + woff(wr + mf * 16 + lr, lg));
+      read_b(st + C::ATILE, bf);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<phase_vm_ops<TM, FMT_NF4>()>();
+    issue_a(min(t + 3, nk - 1), t + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    cld = ld_codes(min(t + 5, nk - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    decode_b(t + 3, cdec);
+    __builtin_amdgcn_sched_barrier(0);
+    wbar();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mf = 0; mf < 8; ++mf)
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mfma16x16x32(af[mf], bf[nf], acc[mf][nf]);
+    __builtin_amdgcn_sched_barrier(0);
+    wbar();
+  };
+  int t = 0;
+  for (; t + 3 <= nk; t += 3) {
+    step(t, cs[0], cs[2]);
+    step(t + 1, cs[1], cs[0]);
+    step(t + 2, cs[2], cs[1]);
+  }
+  if (t < nk) step(t, cs[0], cs[2]);
+  if (t + 1 < nk) step(t + 1, cs[1], cs[0]);
+  if (grp == 0) wbar();
+  wait_vm<0>();
+  wbar();
+
+  // LoRA extension (last split only): 32-wide steps of [U | adapter A rows].
+  const LoraExt& x = g.ext;
+  const int next = (x.kx > 0 && z == splits - 1) ? (x.kx + WBK - 1) / WBK : 0;
+  uint16_t* As = lds;
+  uint16_t* Bs = lds + C::ATILE;
+  for (int xt = 0; xt < next; ++xt) {
+#pragma unroll
+    for (int u0 = 0; u0 < 2 * TM; u0 += 512) {
+      const int row = (u0 + tid) >> 1, h = tid & 1;
+      const int jb = xt * WBK + h * 16;
+      const int gm = m0 + row;
+      uint32_t w[8];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        float v[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int j = jb + 2 * p + k;
+          v[k] = (gm < g.M && j < x.kx) ? x.uscale * x.u[(int64_t)gm * x.ldu + j] : 0.0f;
+        }
+        w[p] = pack_bf16x2(v[0], v[1]);
+      }
+      *reinterpret_cast<u32x4*>(As + woff(row, 2 * h)) = u32x4{w[0], w[1], w[2], w[3]};
+      *reinterpret_cast<u32x4*>(As + woff(row, 2 * h + 1)) = u32x4{w[4], w[5], w[6], w[7]};
+    }
+#pragma unroll
+    for (int u0 = 0; u0 < WBK * CPR; u0 += 512) {
+      const int idx = u0 + tid, row = idx / CPR, ch = idx % CPR;
+      const int j = xt * WBK + row;
+      const int sec = x.r > 0 ? j / x.r : 0;
+      const float* am = (j < x.kx && sec < x.nsec) ? x.mat[sec] : nullptr;
+      const int64_t n0 = (int64_t)ntile * TN + ch * 8;
+      uint32_t w[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        float v0 = 0.0f, v1 = 0.0f;
+        if (am != nullptr) {
+          const float* src = am + (int64_t)(j - sec * x.r) * x.ldmat + n0 + 2 * p;
+          v0 = src[0];
+          v1 = src[1];
+        }
+        w[p] = pack_bf16x2(v0, v1);
+      }
+      *reinterpret_cast<u32x4*>(Bs + nboff<TN>(row, ch)) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+    wbar();
+    u32x4 af[8], bf[4];
+#pragma unroll
+    for (int mf = 0; mf < 8; ++mf) af[mf] = *reinterpret_cast<const u32x4*>(As + woff(wr + mf * 16 + lr, lg));
+    read_b(Bs, bf);
+#pragma unroll
+    for (int mf = 0; mf < 8; ++mf)
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mfma16x16x32(af[mf], bf[nf], acc[mf][nf]);
+    wbar();
+  }
+
+  // Epilogue.  Lane holds C[m0 + wr + mf*16 + lg*4 + i][ntile*TN + wc + nf*16 + lr].
+  if constexpr (EPI == EPI_SWIGLU_BWD) {
+    // Through LDS (free once the k loop is over): each wave stages 32 rows
+    // of its 128 x 64 tile at a time in its own 32 x 68 fp32 block (8.5 KB),
+    // then every lane takes 8 consecutive columns of one row, so the gate/up
+    // reads and the dg/du writes are 16-byte accesses, 128 contiguous bytes
+    // per 8 lanes.  Rows past M read a clamped row and store nothing.
+    constexpr int SLD = 68;
+    static_assert(8 * 32 * SLD * 4 <= WNST * C::STAGE * 2, "staging fits the LDS ring");
+    float* my = reinterpret_cast<float*>(lds) + wid * (32 * SLD);
+    const int cq = (lane & 7) * 8;
+    const int n = ntile * TN + wc + cq;
+    uint16_t* Cp = static_cast<uint16_t*>(e.C);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+#pragma unroll
+      for (int mf = 0; mf < 2; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) my[(mf * 16 + lg * 4 + i) * SLD + nf * 16 + lr] = acc[2 * h + mf][nf][i];
+      wave_lds_sync();
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int r = p * 8 + (lane >> 3);
+        const int m = m0 + wr + h * 32 + r;
+        const int64_t mc = min(m, g.M - 1);
+        const u32x4 gq = *reinterpret_cast<const u32x4*>(e.g + mc * e.ldgu + n);
+        const u32x4 uq = *reinterpret_cast<const u32x4*>(e.u + mc * e.ldgu + n);
+        const float4 v0 = *reinterpret_cast<const float4*>(my + r * SLD + cq);
+        const float4 v1 = *reinterpret_cast<const float4*>(my + r * SLD + cq + 4);
+        const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        u32x4 dgo, duo;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          float dg0, du0, dg1, du1;
+          swiglu_grad(v[2 * k], bf16lo(gq[k]), bf16lo(uq[k]), dg0, du0);
+          swiglu_grad(v[2 * k + 1], bf16hi(gq[k]), bf16hi(uq[k]), dg1, du1);
+          dgo[k] = pack_bf16x2(dg0, dg1);
+          duo[k] = pack_bf16x2(du0, du1);
+        }
+        if (m < g.M) {
+          *reinterpret_cast<u32x4*>(Cp + (int64_t)m * e.ldc + n) = dgo;
+          *reinterpret_cast<u32x4*>(Cp + (int64_t)m * e.ldc + g.N + n) = duo;
+        }
+      }
+      wave_lds_sync();
+    }
+    return;
+  }
+#pragma unroll
+  for (int mf = 0; mf < 8; ++mf)
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf) {
+      const int n = ntile * TN + wc + nf * 16 + lr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wr + mf * 16 + lg * 4 + i;
+        if (m >= g.M) continue;
+        const float v = acc[mf][nf][i];
+        if constexpr (EPI == EPI_F32) {
+          static_cast<float*>(e.C)[(int64_t)z * g.M * g.N + (int64_t)m * e.ldc + n] = v;
+        } else {
+          static_cast<uint16_t*>(e.C)[(int64_t)m * e.ldc + n] = f32_to_bf16(v);
+        }
+      }
+    }
+}
+
+template <int TM>
+hipError_t launch_wide_nn(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
+  constexpr int TN = WCfg<TM>::TN;
+  const dim3 grid(((g.M + TM - 1) / TM) * (g.N / TN) * g.splits), block(512);
+  switch (e.kind) {
+    case EPI_BF16: hipLaunchKernelGGL((gemm_wide_nn_kernel<TM, EPI_BF16>), grid, block, 0, s, g, e); break;
+    case EPI_F32: hipLaunchKernelGGL((gemm_wide_nn_kernel<TM, EPI_F32>), grid, block, 0, s, g, e); break;
+    case EPI_SWIGLU_BWD: hipLaunchKernelGGL((gemm_wide_nn_kernel<TM, EPI_SWIGLU_BWD>), grid, block, 0, s, g, e); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int TM>
 hipError_t launch_wide(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
   constexpr int TN = WCfg<TM>::TN;
@@ -464,12 +782,67 @@ bool gemm_wide_applies(const GemmArgs& g, const EpiArgs& e) {
 }
 
 namespace {
+
+// What the wide input-gradient kernel can run: W stored [K][N] with whole
+// column tiles (N a multiple of 256 covers both tile shapes and the 64-column
+// absmax blocks), 64-deep k steps, 16-byte aligned A rows, 8-byte aligned
+// codes; fp32 partial sums (ldc = N, every split at least 8 k tiles) with
+// split-K, else a bf16 or SwiGLU-backward epilogue.
+bool wide_nn_capable(const GemmArgs& g, const EpiArgs& e) {
+  if (g.splits < 1 || g.M < 256 || g.N % 256 != 0 || g.pair_I != 0) return false;
+  if (g.W.fmt != FMT_NF4 || g.W.ld != g.N || g.K % 64 != 0 || g.K < 256 || g.lda % 8 != 0) return false;
+  if (((uintptr_t)g.A & 15) != 0 || ((uintptr_t)g.W.packed & 7) != 0) return false;
+  if (g.splits > 1) {
+    if (e.kind != EPI_F32 || e.ldc != g.N) return false;
+    const int per = wide_split_tiles(g.K, g.splits);
+    return per >= 8 && g.K / WBK - (g.splits - 1) * per >= 8;
+  }
+  if (e.kind == EPI_SWIGLU_BWD)  // 16-byte accesses to g, u and both halves of C
+    return e.g != nullptr && e.u != nullptr && ((uintptr_t)e.C | (uintptr_t)e.g | (uintptr_t)e.u) % 16 == 0 &&
+           e.ldc % 8 == 0 && e.ldgu % 8 == 0;
+  return e.kind == EPI_BF16;
+}
+
+}  // namespace
+
+// Input-gradient GEMMs with a long contraction or a wide output (K or N at
+// least 8192: gate|up, down) run on the wide kernel: without split-K from 192
+// of its 512 x 128 tiles on, else with as many splits (up to 8) as keep tiles
+// times splits within the 256 compute units.
+int wide_nn_splits(const GemmArgs& g) {
+  if (g.M < 256 || (g.K < 8192 && g.N < 8192) || g.N % 256 != 0) return 0;
+  const int tiles = ((g.M + 511) / 512) * (g.N / 128);
+  if (tiles >= 192) return 1;
+  EpiArgs pe;
+  pe.kind = EPI_F32;
+  pe.ldc = g.N;
+  GemmArgs t = g;
+  for (int s = std::min(8, 256 / tiles); s > 1; --s) {
+    t.splits = s;
+    if (wide_nn_capable(t, pe)) return s;
+  }
+  return 0;
+}
+
+bool gemm_wide_nn_applies(const GemmArgs& g, const EpiArgs& e) {
+  return wide_nn_capable(g, e) && wide_nn_splits(g) == g.splits;
+}
+
+namespace {
 std::atomic<int64_t> g_wide_launches{0};
 std::atomic<int> g_wide_tile{0};  // 0: by shape; 256 or 512: forced (diagnostics)
 }  // namespace
 
 int64_t gemm_wide_launches() { return g_wide_launches.load(std::memory_order_relaxed); }
 void set_gemm_wide_tile(int rows) { g_wide_tile.store(rows, std::memory_order_relaxed); }
+
+hipError_t gemm_nn_wide(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
+  if (!gemm_wide_nn_applies(g, e)) return hipErrorInvalidValue;
+  g_wide_launches.fetch_add(1, std::memory_order_relaxed);
+  const int forced = g_wide_tile.load(std::memory_order_relaxed);
+  const int tm = forced != 0 ? forced : wide_tile_rows(g);
+  return tm == 512 ? launch_wide_nn<512>(g, e, s) : launch_wide_nn<256>(g, e, s);
+}
 
 hipError_t gemm_nt_wide(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
   if (!gemm_wide_applies(g, e)) return hipErrorInvalidValue;

@@ -79,6 +79,13 @@ void set_gemm_wide(bool enable);  // process-wide; default on
 void set_gemm_wide_tile(int rows);  // 0: tile rows by shape; 256 or 512: forced (diagnostics)
 int64_t gemm_wide_launches();      // wide-kernel launches so far
 hipError_t gemm_nt_wide(const GemmArgs& g, const EpiArgs& e, hipStream_t s);
+// The same schedule for input-gradient GEMMs (gate|up and down backward);
+// gemm_nn uses it by itself where gemm_wide_nn_applies.  wide_nn_splits: the
+// split count (1 = none) it serves a shape with, or 0; like wide_splits it
+// depends on the shape only.
+bool gemm_wide_nn_applies(const GemmArgs& g, const EpiArgs& e);
+int wide_nn_splits(const GemmArgs& g);
+hipError_t gemm_nn_wide(const GemmArgs& g, const EpiArgs& e, hipStream_t s);
 // C = A W (+ LoRA), contraction over W rows.
 hipError_t gemm_nn(const GemmArgs& g, const EpiArgs& e, hipStream_t s);
 // Sum `splits` (1..8) fp32 partials [splits, M, N] in fixed order and apply e.

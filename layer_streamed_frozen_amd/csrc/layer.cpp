@@ -176,7 +176,7 @@ hipError_t run_gemm(bool nn, GemmArgs g, const EpiArgs& e, float* part, size_t p
   const int tiles = ((g.M + bm - 1) / bm) * (g.N / 128);
   int splits = 1;
   if (e.kind != EPI_SWIGLU && part != nullptr) {
-    const int ws = nn ? 0 : wide_splits(g);
+    const int ws = nn ? wide_nn_splits(g) : wide_splits(g);
     splits = ws > 0 ? ws : choose_splits(tiles, g.K);
   }
   while (splits > 1 && (size_t)splits * g.M * g.N > part_floats) --splits;

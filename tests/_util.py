@@ -51,6 +51,31 @@ def report(name, got, ref):
     return e
 
 
+def report_sum(name, got, ref, part):
+    """Like report, for a result that is the sum of two parts computed with
+    bf16 rounding, ref = part + (ref - part), which may cancel (the DPO
+    adapter gradients: chosen minus rejected sequences).  Each part held to
+    TOL bounds the error of the sum by TOL (|part| + |ref - part|) (triangle
+    inequality), so that is the scale, overall and per row (with the row floor
+    of worst_row).  Returns the error over that scale."""
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    a = np.asarray(part, dtype=np.float64)
+    b = r - a
+    scale = np.linalg.norm(a) + np.linalg.norm(b)
+    e = float(np.linalg.norm(g - r) / max(scale, 1e-300))
+    g2, r2 = g.reshape(-1, g.shape[-1]), r.reshape(-1, r.shape[-1])
+    a2, b2 = a.reshape(g2.shape), b.reshape(g2.shape)
+    rs = np.linalg.norm(a2, axis=1) + np.linalg.norm(b2, axis=1)
+    rms = np.sqrt(np.mean(rs * rs))
+    err = np.linalg.norm(g2 - r2, axis=1) / np.maximum(rs, max(ROW_FLOOR * rms, 1e-300))
+    i = int(np.argmax(err))
+    print(f"  {name:>10s}: err/(|part|+|rest|)={e:.3e} rel_fro={rel_fro(g, r):.3e} "
+          f"cancellation={scale / max(np.linalg.norm(r), 1e-300):.2f} worst_row={err[i]:.3e} (row {i})", flush=True)
+    assert err[i] < ROW_TOL, f"{name}: row {i} error {err[i]:.3e} >= {ROW_TOL} of |part| + |rest|"
+    return e
+
+
 def bf16_tensor_to_np(t):
     """bf16 torch tensor -> fp64 numpy values."""
     return t.float().cpu().numpy().astype(np.float64)

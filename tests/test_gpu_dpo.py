@@ -10,7 +10,7 @@ from layer_streamed_frozen_amd import binding as B
 from layer_streamed_frozen_amd import store as S
 from layer_streamed_frozen_amd import synth
 from oracle import dpo as D
-from tests._util import TOL, report
+from tests._util import TOL, report, report_sum
 from tests.test_gpu_layer import SMALL, oracle_layer_weights, oracle_shape
 from tests.test_gpu_stack import Setup
 
@@ -174,9 +174,10 @@ def test_dpo_with_kept_activations_gives_the_same_bits(pair):
     kept.close()
 
 
-def _oracle_grads_at(s, dlp):
-    """The oracle's policy forward and backward with the per-sequence factors
-    dloss/dl(s) = dlp (the DPO gradient is linear in them)."""
+def _oracle_grads_at(s, *dlps):
+    """The oracle's policy forward, then one backward per vector of
+    per-sequence factors dloss/dl(s) = dlp (the DPO gradient is linear in
+    them)."""
     from oracle import model as M
     layers = [oracle_layer_weights(s.wfn(i), s.fmt) for i in range(s.L)]
     loras = [s.lora.numpy(i) for i in range(s.L)]
@@ -188,10 +189,15 @@ def _oracle_grads_at(s, dlp):
     e = np.exp(logits - logits.max(axis=1, keepdims=True))
     p = e / e.sum(axis=1, keepdims=True)
     p[np.arange(p.shape[0]), labels] -= 1.0                  # softmax - onehot
-    dlogits = -np.repeat(np.asarray(dlp, np.float64), T)[:, None] * p
-    dlogits[~valid] = 0.0
-    grads, _ = M.stack_backward(dlogits, layers, loras, fn, hd, oc, state)
-    return grads
+    del e, logits
+    out = []
+    for dlp in dlps:
+        dlogits = -np.repeat(np.asarray(dlp, np.float64), T)[:, None] * p
+        dlogits[~valid] = 0.0
+        grads, _ = M.stack_backward(dlogits, layers, loras, fn, hd, oc, state)
+        out.append(grads)
+        del dlogits
+    return out[0] if len(out) == 1 else out
 
 
 def test_dpo_at_8b_shapes_full_vocabulary_matches_oracle():
@@ -235,12 +241,16 @@ def test_dpo_at_8b_shapes_full_vocabulary_matches_oracle():
     _, dlp_gpu = D.dpo_loss(lp[0], lp[1], BETA)
     _, dlp_ref = D.dpo_loss(ref["lp_pi"], ref["lp_ref"], BETA)
     print(f"  per-sequence factors gpu={dlp_gpu} oracle={dlp_ref}", flush=True)
-    grads = _oracle_grads_at(s, dlp_gpu)
+    # The gradient is the chosen sequences' part plus the rejected ones', of
+    # opposite sign over a shared prompt; the oracle also gives the chosen
+    # part alone, and each part held to TOL bounds the error of the sum.
+    chosen = np.array([1.0, 1.0, 0.0, 0.0]) * dlp_gpu
+    grads, grads_c = _oracle_grads_at(s, dlp_gpu, chosen)
     for i in range(s.L):
         g = s.lora.grads_numpy(i)
         for n in S.PROJ:
-            assert report(f"L{i}.dA_{n}", g[n][0], grads[i][n][0]) < TOL
-            assert report(f"L{i}.dB_{n}", g[n][1], grads[i][n][1]) < TOL
+            for k, nm in ((0, "dA"), (1, "dB")):
+                assert report_sum(f"L{i}.{nm}_{n}", g[n][k], grads[i][n][k], grads_c[i][n][k]) < TOL
     # for the record: the same gradients against the oracle's own factors
     for n in ("q", "down"):
         print(f"  (at the oracle's factors) L1.dA_{n} rel_fro="

@@ -190,12 +190,13 @@ def test_wide_gate_up_kernel_matches_oracle_and_general_kernel(rank):
     # rank 64 gives four 32-wide LoRA steps.  Both tile shapes and the general
     # kernel must give the same bits.
     # The down projection (16 tiles of 512 x 128, K = 8192) runs split-K on
-    # the same kernel.
+    # the same kernel, and the input gradients of gate|up (contraction 16384)
+    # and down (8192 outputs) on its input-gradient variant.
     shape = _shape(hidden=2048, n_heads=16, n_kv_heads=4, intermediate=8192, rank=rank, alpha=2.0 * rank)
     n0 = B.gemm_wide_launch_count()
     res, (y, dx, lora) = run_layer(shape, 1, 300, f"slwide{rank}")
     per_run = B.gemm_wide_launch_count() - n0
-    assert per_run == 3  # gate|up and down; the recompute without down
+    assert per_run == 5  # forward gate|up and down, recompute gate|up, backward gate|up and down
     _assert_all(res)
     outs = []
     for mode in (256, False):
