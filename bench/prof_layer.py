@@ -2,10 +2,10 @@
 
 Runs a plain fp32 scale kernel over a buffer of known size (the calibration
 for the byte counters), then one Llama-3.1-8B-shaped layer (NF4 base, LoRA
-rank 16 on all seven projections, 512 tokens): forward, and the backward that
-recomputes it, ``--reps`` times.
+rank 16 on all seven projections, ``--tokens`` tokens as sequences of
+``--seq``): forward, and the backward that recomputes it, ``--reps`` times.
 
-    python3 bench/prof_layer.py [--reps 2] [--tokens 512]
+    python3 bench/prof_layer.py [--reps 2] [--tokens 512] [--seq 512]
 """
 import argparse
 import os
@@ -24,7 +24,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--reps", type=int, default=2)
     ap.add_argument("--tokens", type=int, default=512)
+    ap.add_argument("--seq", type=int, default=512)
     args = ap.parse_args()
+    if args.tokens % args.seq:
+        raise SystemExit("--tokens must be a multiple of --seq")
     B.lib()
     torch.cuda.set_device(0)
     # calibration: reads 256 MiB and writes 256 MiB in one elementwise kernel
@@ -37,7 +40,7 @@ def main():
     shape = S.LLAMA8B
     W = S.layer_weights_fp32("prof.layer", shape)
     blob = S.build_layer_blob(shape, W)
-    cfg = shape.cfg(1, args.tokens)
+    cfg = shape.cfg(args.tokens // args.seq, args.seq)
     lw = B.layer_weights_from_blob(cfg, B.FMT_NF4, blob.data_ptr())
     lora = S.LoraSet(shape, 1, prefix="prof.lora")
     H = shape.hidden

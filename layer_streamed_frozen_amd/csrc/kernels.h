@@ -103,8 +103,10 @@ hipError_t nf4dq_dequantize_launch(const uint8_t* packed, const uint8_t* absq, c
 // LoRA side paths.
 //  down_fwd: U[m, sec*r + j] = scale * sum_k X[m, k] * A_sec[j, k]  (all sections read X)
 //  down_bwd: U[m, sec*r + j] = scale * sum_{n in sec} X[m, xoff_sec + n] * B_sec[n, j]
-// The contraction is cut into at most 8 chunks per section; lora_down writes
-// one partial product per chunk into part and their ordered sum into U.
+// The contraction is cut into at most kLoraDownChunks chunks per section;
+// lora_down writes one partial product per chunk into part and their ordered
+// sum into U.
+constexpr int kLoraDownChunks = 16;
 struct LoraDown {
   int M = 0, K = 0;  // K: columns of X read per section
   const uint16_t* X = nullptr;
@@ -121,7 +123,7 @@ struct LoraDown {
   size_t part_floats = 0;
 };
 // Floats of partials lora_down writes for M rows, nsec sections of rank r.
-inline size_t lora_part_floats(int64_t M, int nsec, int r) { return (size_t)nsec * 8 * M * r; }
+inline size_t lora_part_floats(int64_t M, int nsec, int r) { return (size_t)nsec * kLoraDownChunks * M * r; }
 hipError_t lora_down(const LoraDown& a, hipStream_t s);
 
 // out += scale * sum_t P[t, pcol0 + j] * Q[t, qoff + q] for j < r, q < nq.

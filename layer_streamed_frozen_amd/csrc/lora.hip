@@ -2,7 +2,9 @@
 //
 // lora_down: the rank-r projections U = X A^T (forward) and dU = s dY B
 // (backward): [M, K] x [K, r] with r <= 64 and K up to 28672.  The
-// contraction is cut into at most 8 chunks (multiples of 256); a workgroup
+// contraction is cut into at most 16 chunks (multiples of 256, one 256-column
+// step each up to K = 4096, so most workgroups wait for one round of loads
+// only); a workgroup
 // owns 64 rows and one chunk of one section, stages the chunk's adapter
 // matrix 256 columns at a time in LDS as bf16 [r][256] and runs
 // v_mfma_f32_16x16x32_bf16 over it, loading the next 256 columns while it
@@ -311,11 +313,11 @@ void launch_down(const LoraDown& a, dim3 grid, int nch_max, int kc, hipStream_t 
 }
 
 // Chunk length (a multiple of 256) that cuts the longest section into at
-// most 8 chunks, and the chunk count of that section.
+// most kLoraDownChunks chunks, and the chunk count of that section.
 int down_chunk(const LoraDown& a, int* nch_max) {
   int kmax = 0;
   for (int i = 0; i < a.nsec; ++i) kmax = std::max(kmax, sec_k(a, i));
-  const int kc = KC * std::max(1, (kmax + 8 * KC - 1) / (8 * KC));
+  const int kc = KC * std::max(1, (kmax + kLoraDownChunks * KC - 1) / (kLoraDownChunks * KC));
   *nch_max = std::max(1, (kmax + kc - 1) / kc);
   return kc;
 }
