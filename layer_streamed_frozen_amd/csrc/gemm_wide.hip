@@ -94,6 +94,21 @@ __device__ __forceinline__ void wbar() {
   asm volatile("" ::: "memory");
 }
 
+// Workgroup barrier that lets this wave's last NW LDS stores stay in flight:
+// LDS operations of one wave complete in issue order, so lgkmcnt(NW) after
+// NW trailing stores means every earlier LDS read has returned.  The stores
+// finish before the next wbar() (lgkmcnt 0), and their stage is read only
+// after that.  NW must not exceed the number of LDS stores issued after the
+// last LDS read.
+template <int NW>
+__device__ __forceinline__ void wbar_stores() {
+  static_assert(NW >= 0 && NW < 16, "lgkmcnt immediate");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f & ~0x0f00 | (NW << 8));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ void lds_dma16(const uint16_t* src, uint16_t* dst) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                    (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
@@ -261,7 +276,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g, EpiArgs e
     if (((t + 3) & 1) == 0) tb = nf4_table(cdec.am);  // first half of a 64-block
     decode_b(t + 3, cdec.c, tb);
     __builtin_amdgcn_sched_barrier(0);
-    wbar();
+    wbar_stores<DEC / 8>();  // the decoded stores land during the compute phase
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mf = 0; mf < 8; ++mf)
@@ -539,7 +554,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_nn_kernel(GemmArgs g, EpiArg
     __builtin_amdgcn_sched_barrier(0);
     decode_b(t + 3, cdec);
     __builtin_amdgcn_sched_barrier(0);
-    wbar();
+    wbar_stores<NDEC / 8>();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mf = 0; mf < 8; ++mf)
