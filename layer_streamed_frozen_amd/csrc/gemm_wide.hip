@@ -254,9 +254,16 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g, EpiArgs e
   // The codes of tile t+3 are in `cdec`; tile t+5 loads into `cld`.
   auto step = [&](int t, CodeSet<DEC>& cdec, CodeSet<DEC>& cld) {
     __builtin_amdgcn_sched_barrier(0);
-    // Fragment reads first: tile t landed two phases ago, and their LDS
-    // latency then overlaps the loads and the decode instead of ending the
-    // phase (this order also keeps the kernel within 256 registers).
+    // The LDS-DMA of tile t+3 and the codes of tile t+5 go out first (their
+    // stage was last read in the previous phase, before the barrier), then
+    // the fragment reads of tile t, which landed two phases ago: their LDS
+    // latency overlaps the decode instead of ending the phase.  Waiting for
+    // the loads of two phases ago only after issuing this phase's keeps the
+    // loads from queueing behind that wait (2-4% faster than waiting first).
+    issue_a(min(t + 3, nk - 1), t + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    cld = load_codes<DEC>(cp, ap, min(t + 5, nk - 1));
+    __builtin_amdgcn_sched_barrier(0);
     u32x4 af[8], bf[4];
     {
       const uint16_t* st = lds + (t & 3) * C::STAGE;
@@ -268,10 +275,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmArgs g, EpiArgs e
         bf[nf] = *reinterpret_cast<const u32x4*>(st + C::ATILE + woff(wc + nf * 16 + lr, lg));
     }
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm<phase_vm_ops<TM, FMT>()>();
-    issue_a(min(t + 3, nk - 1), t + 3);
-    __builtin_amdgcn_sched_barrier(0);  // the LDS-DMA goes out before the register loads
-    cld = load_codes<DEC>(cp, ap, min(t + 5, nk - 1));
+    wait_vm<2 * phase_vm_ops<TM, FMT>()>();  // tile t+3's codes (loaded two phases ago)
     __builtin_amdgcn_sched_barrier(0);
     if (((t + 3) & 1) == 0) tb = nf4_table(cdec.am);  // first half of a 64-block
     decode_b(t + 3, cdec.c, tb);
@@ -538,6 +542,9 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_nn_kernel(GemmArgs g, EpiArg
 
   auto step = [&](int t, CodeSet<NDEC>& cdec, CodeSet<NDEC>& cld) {
     __builtin_amdgcn_sched_barrier(0);
+    // Unlike the forward kernel, the fragment reads go out before this
+    // phase's LDS-DMA: the compiler waits for every LDS-DMA in flight before
+    // a transposing LDS read that follows one, which serialises the phase.
     u32x4 af[8], bf[4];
     {
       const uint16_t* st = lds + (t & 3) * C::STAGE;
