@@ -554,6 +554,57 @@ __global__ void splitk_reduce_kernel(const float* part, int splits, int M, int N
   }
 }
 
+// The same reduction four elements of one row at a time: 16-byte loads of
+// every partial and 8-byte bf16 stores (the scalar form moves 4 bytes per lane
+// and load).  The same fp32 adds in the same order per element, so the same
+// bits.  Needs N % 4 == 0 and the aligned pointers and strides the host checks.
+__device__ __forceinline__ void add4(float4& v, const float4& q) {
+  v.x += q.x;
+  v.y += q.y;
+  v.z += q.z;
+  v.w += q.w;
+}
+__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
+  return uint2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+}
+
+template <int EPI>
+__global__ void splitk_reduce4_kernel(const float* part, int splits, int M, int N, EpiArgs e) {
+  const int64_t MN = (int64_t)M * N, n4 = MN / 4;
+  for (int64_t i4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i4 < n4; i4 += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = i4 * 4;
+    float4 q[8];
+#pragma unroll
+    for (int zz = 0; zz < 8; ++zz)  // splits <= 8
+      q[zz] = (zz < splits) ? *reinterpret_cast<const float4*>(part + zz * MN + i) : float4{0, 0, 0, 0};
+    float4 v = q[0];
+#pragma unroll
+    for (int zz = 1; zz < 8; ++zz)
+      if (zz < splits) add4(v, q[zz]);
+    const int64_t m = i / N, n = i - m * N;
+    if constexpr (EPI == EPI_F32) {
+      *reinterpret_cast<float4*>(static_cast<float*>(e.C) + m * e.ldc + n) = v;
+    } else if constexpr (EPI == EPI_BF16) {
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(e.C) + m * e.ldc + n) = pack4_bf16(v.x, v.y, v.z, v.w);
+    } else if constexpr (EPI == EPI_RESID_BF16) {
+      const uint2 r = *reinterpret_cast<const uint2*>(e.R + m * e.ldr + n);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(e.C) + m * e.ldc + n) =
+          pack4_bf16(bf16lo(r.x) + v.x, bf16hi(r.x) + v.y, bf16lo(r.y) + v.z, bf16hi(r.y) + v.w);
+    } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+      const uint2 gq = *reinterpret_cast<const uint2*>(e.g + m * e.ldgu + n);
+      const uint2 uq = *reinterpret_cast<const uint2*>(e.u + m * e.ldgu + n);
+      float dg[4], du[4];
+      swiglu_grad(v.x, bf16lo(gq.x), bf16lo(uq.x), dg[0], du[0]);
+      swiglu_grad(v.y, bf16hi(gq.x), bf16hi(uq.x), dg[1], du[1]);
+      swiglu_grad(v.z, bf16lo(gq.y), bf16lo(uq.y), dg[2], du[2]);
+      swiglu_grad(v.w, bf16hi(gq.y), bf16hi(uq.y), dg[3], du[3]);
+      uint16_t* C = static_cast<uint16_t*>(e.C);
+      *reinterpret_cast<uint2*>(C + m * e.ldc + n) = pack4_bf16(dg[0], dg[1], dg[2], dg[3]);
+      *reinterpret_cast<uint2*>(C + m * e.ldc + N + n) = pack4_bf16(du[0], du[1], du[2], du[3]);
+    }
+  }
+}
+
 }  // namespace
 
 // Measured on MI355X at 512 and 2048 tokens: 256-row tiles are faster for the
@@ -586,6 +637,32 @@ hipError_t gemm_nn(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
 hipError_t splitk_reduce(const float* part, int splits, int M, int N, const EpiArgs& e, hipStream_t s) {
   if (splits < 1 || splits > 8) return hipErrorInvalidValue;
   const int64_t MN = (int64_t)M * N;
+  // Four elements per thread where every access of the epilogue is aligned.
+  auto al = [](const void* p, int64_t ld, int bytes) {
+    return p == nullptr || ((uintptr_t)p % bytes == 0 && ld % 4 == 0);
+  };
+  bool vec = N % 4 == 0 && (uintptr_t)part % 16 == 0;
+  switch (e.kind) {
+    case EPI_F32: vec = vec && al(e.C, e.ldc, 16); break;
+    case EPI_BF16: vec = vec && al(e.C, e.ldc, 8); break;
+    case EPI_RESID_BF16: vec = vec && al(e.C, e.ldc, 8) && al(e.R, e.ldr, 8); break;
+    case EPI_SWIGLU_BWD: vec = vec && al(e.C, e.ldc, 8) && al(e.g, e.ldgu, 8) && al(e.u, e.ldgu, 8); break;
+    default: vec = false; break;
+  }
+  if (vec) {
+    const int blocks = (int)std::min<int64_t>((MN / 4 + 255) / 256, 4096);
+    switch (e.kind) {
+      case EPI_F32: hipLaunchKernelGGL(splitk_reduce4_kernel<EPI_F32>, dim3(blocks), dim3(256), 0, s, part, splits, M, N, e); break;
+      case EPI_BF16: hipLaunchKernelGGL(splitk_reduce4_kernel<EPI_BF16>, dim3(blocks), dim3(256), 0, s, part, splits, M, N, e); break;
+      case EPI_RESID_BF16:
+        hipLaunchKernelGGL(splitk_reduce4_kernel<EPI_RESID_BF16>, dim3(blocks), dim3(256), 0, s, part, splits, M, N, e);
+        break;
+      default:
+        hipLaunchKernelGGL(splitk_reduce4_kernel<EPI_SWIGLU_BWD>, dim3(blocks), dim3(256), 0, s, part, splits, M, N, e);
+        break;
+    }
+    return hipGetLastError();
+  }
   const int blocks = (int)std::min<int64_t>((MN + 255) / 256, 4096);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, part, splits, M, N, e);
   return hipGetLastError();
