@@ -3,9 +3,13 @@ copied on its own: from a pinned store of --layers such blobs into one of two
 device buffers, one hipMemcpyAsync per copy, with and without a bf16 GEMM load
 on another stream, and the same copy cut in two on two streams.
 
-    python3 bench/prof_h2d.py [--layers 32] [--reps 64]
+    python3 bench/prof_h2d.py [--layers 32] [--reps 64] [--sustain SECONDS [--idle]]
 
 Prints, per variant, the median, minimum and maximum copy time (event-timed).
+With --sustain, instead copies back to back for about that long while bf16
+GEMMs keep another stream busy, without synchronising in between (as in the
+streamed step), and prints the median copy time of each tenth of the run;
+--idle leaves the GPU without other work.
 """
 import argparse
 import statistics
@@ -19,6 +23,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--reps", type=int, default=64)
+    ap.add_argument("--sustain", type=float, default=0.0)
+    ap.add_argument("--idle", action="store_true")
     args = ap.parse_args()
     nl = args.layers
     src = torch.empty(nl * BLOB, dtype=torch.uint8, pin_memory=True)
@@ -63,6 +69,33 @@ def main():
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1) * 1e3)
         return ts
+
+    if args.sustain > 0:
+        n = max(20, int(args.sustain * 1e6 / 2200))
+        evs = []
+        for r in range(n):
+            j = r % nl
+            if not args.idle:
+                load(4)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s1)
+            with torch.cuda.stream(s1):
+                dst[r % 2].copy_(src[j * BLOB:(j + 1) * BLOB], non_blocking=True)
+            e1.record(s1)
+            evs.append((e0, e1))
+            if r % 64 == 63:  # keep the host at most a few hundred copies ahead
+                evs[r - 32][1].synchronize()
+        torch.cuda.synchronize()
+        ts = [a.elapsed_time(b) * 1e3 for a, b in evs]
+        k = max(1, n // 10)
+        for i in range(0, n - k + 1, k):
+            blk = ts[i:i + k]
+            slow = sum(1 for t in blk if t > 2300)
+            print(f"[prof_h2d] sustained copies{' (idle GPU)' if args.idle else ''} {i}..{i + k - 1}: "
+                  f"median {statistics.median(blk):.0f} us, mean {statistics.mean(blk):.0f}, max {max(blk):.0f}, "
+                  f"over 2.3 ms {slow}/{len(blk)}", flush=True)
+        return
 
     for busy in (False, True):
         for pieces in (1, 2):
