@@ -1,7 +1,8 @@
-// Wide forward NF4 GEMM for gfx950, used when the output has many 256 x 256
-// tiles (the gate|up projection; q|k|v from 2048 tokens), and as split-K with
-// fp32 partial sums for the narrower forward projections of a few hundred
-// tokens: C[M, N] = A[M, K] . deq(W)[N, K]^T  (+ LoRA, + epilogue).
+// Wide NF4 GEMMs for gfx950 ("ping-pong" kernels).  Forward, used when the
+// output has many tiles (the gate|up projection; q|k|v from 2048 tokens), and
+// as split-K with fp32 partial sums for long contractions over few tiles (the
+// down projection): C[M, N] = A[M, K] . deq(W)[N, K]^T  (+ LoRA, + epilogue);
+// and the input gradient of gate|up and down: C = A . deq(W)[K, N].
 //
 // Same arithmetic as the general kernel in gemm.hip (every weight decoded to
 // bf16_rne(level * absmax), bf16 MFMA with fp32 accumulation, the k order of
@@ -9,30 +10,37 @@
 // ones), so both kernels give bitwise-identical results; only the schedule
 // differs:
 //
-// * 256 x 256 C tile, 512 threads = two groups of four waves.  The hardware
-//   places wave w and wave w+4 of a workgroup on the same SIMD, so every SIMD
-//   holds one wave of each group.  Wave (g, q) owns rows g*128..+128 and
-//   columns q*64..+64 (8 x 4 fragments of v_mfma_f32_16x16x32_bf16).
-// * 32-deep k tiles in a ring of four LDS stages (32 KB each).  The groups run
-//   half a tile apart (ping-pong): while one group issues its 32 MFMAs, the
-//   other runs its memory phase: read its own fragments of the current tile,
-//   wait for the LDS-DMA issued two phases ago, issue the LDS-DMA of A three
-//   tiles ahead (global_load_lds_dwordx4, no register round trip), load the
-//   packed codes of the tile five ahead into registers, and decode its half
-//   of the weight tile three ahead into LDS; the fragment reads complete
-//   meanwhile instead of ending the phase.  A workgroup barrier between the
-//   phases swaps the roles.
-// * Every memory phase issues the same vector-memory operations, the two
-//   LDS-DMA first (past the last tile they repeat it into a stage nobody reads
-//   again), then the code and absmax loads.  Loads complete in issue order, so
-//   `s_waitcnt vmcnt(4)` before this phase's own loads means "the LDS-DMA of
-//   two phases ago has landed"; it stays safe if the compiler emits more loads
-//   per phase (it then waits longer) or merges the two register loads into
-//   one (the last operation of the older phase is still a register load).
-//   The fragment reads of tile t may precede that wait: the DMA of tile t was
-//   waited for one phase earlier and two barriers have passed since.
+// * TM x TN C tile (512 x 128 by default, 256 x 256 selectable), 512 threads
+//   = two groups of four waves.  The hardware places wave w and wave w+4 of a
+//   workgroup on the same SIMD, so every SIMD holds one wave of each group.
+//   Each wave owns 128 rows x 64 columns (8 x 4 fragments of
+//   v_mfma_f32_16x16x32_bf16); group g owns rows g*TM/2 .. + TM/2.
+// * 32-deep k tiles in a ring of four LDS stages (40 or 32 KB each).  The
+//   groups run half a tile apart (ping-pong): while one group issues its 32
+//   MFMAs, the other runs its memory phase: issue the LDS-DMA of its half of
+//   A three tiles ahead (global_load_lds_dwordx4, no register round trip) and
+//   load the packed codes and absmax of the tile five ahead into registers,
+//   read its own fragments of the current tile, wait for the loads of two
+//   phases ago, and decode its half of the weight tile three ahead into LDS.
+//   A workgroup barrier between the phases swaps the roles; the one ending a
+//   memory phase waits only for the fragment reads (LDS operations of a wave
+//   complete in issue order), so the decoded tile's stores land during the
+//   compute phase, and the barrier ending the compute phase waits for them.
+// * Every memory phase issues the same vector-memory operations: the LDS-DMA
+//   of A (past the last tile it repeats the last tile into a stage nobody
+//   reads again), then the code and absmax loads.  Loads complete in issue
+//   order, so after this phase's own loads `s_waitcnt vmcnt(2n)`, n the
+//   operations of one phase, means "everything issued two phases ago has
+//   landed": the codes decoded now and the A tile read in the next phase.
+//   Every LDS-DMA is an explicit instruction and the two register loads read
+//   different arrays, so no phase issues fewer than n; more would only make
+//   the wait stricter.  Reusing a stage is safe: the stage written in phase t
+//   (tile t+3) held tile t-1, whose fragment reads both groups finished
+//   before the barriers that ended their phases t-1.
 //   Barriers carry no memory-model fence: a release fence would wait for
 //   every LDS-DMA in flight.
+// * The input-gradient kernel below keeps its fragment reads ahead of its
+//   loads (see its comment).
 #include "common.h"
 #include "kernels.h"
 #include "weight_decode.h"
