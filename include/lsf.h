@@ -367,6 +367,11 @@ LSF_API lsf_status stream_stack_step(lsf_stack* st, const lsf_stack_io* io);
  * stream_stack_step calls on io[0], io[1], ... in turn with
  * LSF_MODE_ZERO_GRADS (if set) on the first only, bit for bit: each layer's
  * gradients receive the micro-batches' contributions in the same order.
+ * With n_micro > 1 (recomputing backward, no per-kernel timing flag) the odd micro-batches run
+ * on a second stream the stack owns, overlapping with the even ones within
+ * each layer visit; every visit starts after the work already on the compute
+ * stream and ends with the compute stream waiting for it, so to the caller the
+ * step is ordered on the compute stream as before, with the same bits.
  * ws: at least stack_accum_workspace_bytes(cfg, vocab, n_layers, n_micro); act
  * (LSF_MODE_KEEP_ACTIVATIONS): n_micro * stack_activation_bytes(cfg, n_layers).
  * Errors: LSF_ERR_INVALID_ARG for n_micro < 1, plus those of stream_stack_step. */

@@ -531,6 +531,13 @@ struct lsf_stack {
   hipEvent_t ready[2], freed[2];
   bool used[2];
   int slot_layer[2];
+  // A second compute stream for accumulated steps: micro-batches alternate
+  // between the caller's compute stream and this one within each layer visit
+  // (fork and join events around the visit; gorder[m & 1][k] orders the k-th
+  // gradient accumulation of micro-batch m before that of m + 1).
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t gorder[2][4] = {};
   // timing (LSF_STACK_TIMING), accumulated until stack_reset_stats
   EventPool events;
   KernelProbe probe;
@@ -607,6 +614,7 @@ lsf_status wait_ready(lsf_stack* st, int b) {
 
 struct StackWs {
   LayerWs layer;
+  LayerWs layer2;  // the second stream's layer workspace (accumulated steps)
   uint16_t *hN, *dhN, *dlog, *dx[2], *rx[2];
   float *rstdN, *row_loss, *part, *lse, *lp, *coef;
   size_t part_floats;
@@ -635,7 +643,7 @@ size_t stack_ws_bytes(const lsf_layer_cfg& c, int V) {
 size_t stack_accum_ws_bytes(const lsf_layer_cfg& c, int V, int L, int n) {
   const size_t T = (size_t)c.batch * c.seq, H = c.hidden;
   return stack_ws_bytes(c, V) + 256 + (size_t)(n - 1) * 2 * al256(T * H * 2) + 256 +
-         (size_t)L * n * LayerWs::u_bytes(c);
+         (size_t)L * n * LayerWs::u_bytes(c) + (n > 1 ? 256 + al256(LayerWs::bytes(c)) : 0);
 }
 
 StackWs carve_stack(const lsf_layer_cfg& c, int V, int L, int n, void* base) {
@@ -666,6 +674,12 @@ StackWs carve_stack(const lsf_layer_cfg& c, int V, int L, int n, void* base) {
   const uintptr_t ua = (uintptr_t)w.dx_more + (size_t)(n - 1) * 2 * al256(T * H * 2);
   w.uarena = (char*)((ua + 255) / 256 * 256);
   w.n_layers = L;
+  w.layer2 = w.layer;
+  if (n > 1) {
+    const uintptr_t l2 = (uintptr_t)w.uarena + (size_t)L * n * LayerWs::u_bytes(c);
+    w.layer2 = LayerWs::carve(c, (void*)((l2 + 255) / 256 * 256));
+    w.layer2.rope = w.layer.rope;  // one RoPE table, built once per step, read by both
+  }
   return w;
 }
 
@@ -862,26 +876,53 @@ lsf_status run_step(lsf_stack* st, const lsf_stack_io* io_all, int n_micro, cons
   for (int m = 0; m < n_micro; ++m)
     HIPCK(embed_gather(io_all[m].ids, io->embed, T, H, V, io_all[m].ckpt, io_all[m].id_status, cs));
 
+  // With several micro-batches, recomputing backward and no per-kernel timing
+  // (whose events time each launch alone), the odd ones run on the second
+  // stream with their own layer workspace, so that two micro-batches' kernels
+  // overlap (measured at 4 x 2048 tokens: 4.6% more tokens/s; with kept
+  // activations 0.9% fewer, so that mode keeps one stream): within each
+  // layer visit the second stream waits for everything before the visit on
+  // the compute stream (fork), and the compute stream waits for the second
+  // stream's work before the visit ends (join), so the buffer-free event and
+  // the head see both.  Gradient accumulations keep the order 0, 1, ..., n-1
+  // through the gorder events, so the bits are those of one stream.
+  const bool two = n_micro > 1 && !keep && !(st->d.flags & (LSF_STACK_TIMING | LSF_STACK_KERNEL_TIMING));
+  w.layer2.probe = w.layer.probe;
+  auto stream_of = [&](int m) { return (two && (m & 1)) ? st->side : cs; };
+  const LayerWs& lbase0 = w.layer;
+  auto lbase = [&](int m) -> const LayerWs& { return (two && (m & 1)) ? w.layer2 : lbase0; };
+  auto fork_side = [&]() -> hipError_t {
+    hipError_t e;
+    if (!two) return hipSuccess;
+    if ((e = hipEventRecord(st->fork, cs)) != hipSuccess) return e;
+    return hipStreamWaitEvent(st->side, st->fork, 0);
+  };
+  auto join_side = [&]() -> hipError_t {
+    hipError_t e;
+    if (!two) return hipSuccess;
+    if ((e = hipEventRecord(st->join, st->side)) != hipSuccess) return e;
+    return hipStreamWaitEvent(cs, st->join, 0);
+  };
   // Layer i's saved intermediates for micro-batch m (LSF_MODE_KEEP_ACTIVATIONS).
   auto kept = [&](int m, int i) {
-    return w.layer.with_saved(c, static_cast<char*>(io->act) + ((size_t)m * L + i) * saved);
+    return lbase(m).with_saved(c, static_cast<char*>(io->act) + ((size_t)m * L + i) * saved);
   };
   // Otherwise the workspace with layer i's LoRA activations for micro-batch m
   // in their own slot, so that the backward walk's recompute finds them.
   const size_t ub = LayerWs::u_bytes(c);
-  auto with_u = [&](int m, int i) { return w.layer.with_u(c, w.uarena + ((size_t)m * L + i) * ub); };
+  auto with_u = [&](int m, int i) { return lbase(m).with_u(c, w.uarena + ((size_t)m * L + i) * ub); };
   // Policy forward of layer i for micro-batch m: ckpt[i] -> ckpt[i+1] (kept for the backward).
   auto policy_fwd = [&](int m, int i, const lsf_layer_weights& lw) {
     uint16_t* ck = io_all[m].ckpt;
     return layer_forward(c, lw, &io->lora[i], ck + (size_t)i * act, ck + (size_t)(i + 1) * act,
-                         keep ? kept(m, i) : with_u(m, i), keep, true, cs);
+                         keep ? kept(m, i) : with_u(m, i), keep, true, stream_of(m));
   };
   auto all_fwd = [&](int i, const lsf_layer_weights& lw) {
-    for (int m = 0; m < n_micro; ++m) {
-      const hipError_t e = policy_fwd(m, i, lw);
-      if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    hipError_t e;
+    if ((e = fork_side()) != hipSuccess) return e;
+    for (int m = 0; m < n_micro; ++m)
+      if ((e = policy_fwd(m, i, lw)) != hipSuccess) return e;
+    return join_side();
   };
   // Reference (adapters off) forward of layer i, through the rx ping-pong:
   // input rx[i % 2] (the embeddings for layer 0), output rx[(i + 1) % 2].
@@ -937,15 +978,22 @@ lsf_status run_step(lsf_stack* st, const lsf_stack_io* io_all, int n_micro, cons
 
   // ---- backward: layers L-1 .. 0, each read again and recomputed
   auto all_bwd = [&](int j, const lsf_layer_weights& lw) {
+    hipError_t e;
+    if ((e = fork_side()) != hipSuccess) return e;
     for (int m = 0; m < n_micro; ++m) {
       LayerWs lws = keep ? kept(m, j) : with_u(m, j);
       lws.u_ready = !keep;  // the recompute reuses the forward's LoRA activations
       lws.grads_overwrite = overwrite && m == 0;
-      const hipError_t e = layer_backward(c, lw, &io->lora[j], io_all[m].ckpt + (size_t)j * act,
-                                          dx_buf(w, c, m, (j + 1) & 1), dx_buf(w, c, m, j & 1), lws, true, cs, !keep);
+      if (two)
+        for (int k = 0; k < 4; ++k) {
+          lws.grad_after[k] = m > 0 ? st->gorder[(m - 1) & 1][k] : nullptr;
+          lws.grad_done[k] = m + 1 < n_micro ? st->gorder[m & 1][k] : nullptr;
+        }
+      e = layer_backward(c, lw, &io->lora[j], io_all[m].ckpt + (size_t)j * act, dx_buf(w, c, m, (j + 1) & 1),
+                         dx_buf(w, c, m, j & 1), lws, true, stream_of(m), !keep);
       if (e != hipSuccess) return e;
     }
-    return hipSuccess;
+    return join_side();
   };
   if ((s = walk_layers(st, resident, false, reuse, all_bwd))) return s;
   return ok();
@@ -1007,6 +1055,16 @@ lsf_status stack_create(const lsf_layer_cfg* cfg, const lsf_stack_desc* desc, ls
     }
   }
   std::memset(&st->stats, 0, sizeof(st->stats));
+  bool evs_ok = hipStreamCreateWithFlags(&st->side, hipStreamNonBlocking) == hipSuccess &&
+                hipEventCreateWithFlags(&st->fork, hipEventDisableTiming) == hipSuccess &&
+                hipEventCreateWithFlags(&st->join, hipEventDisableTiming) == hipSuccess;
+  for (int i = 0; i < 2 && evs_ok; ++i)
+    for (int k = 0; k < 4 && evs_ok; ++k)
+      evs_ok = hipEventCreateWithFlags(&st->gorder[i][k], hipEventDisableTiming) == hipSuccess;
+  if (!evs_ok) {
+    (void)stack_destroy(st);
+    return fail(LSF_ERR_HIP, "creating the second compute stream or its events failed");
+  }
   *out = st;
   return ok();
 }
@@ -1019,6 +1077,13 @@ lsf_status stack_destroy(lsf_stack* st) {
   }
   (void)harvest_all(st, true);  // no event may be destroyed while still pending
   for (hipEvent_t e : st->events.all) (void)hipEventDestroy(e);
+  if (st->side) (void)hipStreamSynchronize(st->side);
+  if (st->fork) (void)hipEventDestroy(st->fork);
+  if (st->join) (void)hipEventDestroy(st->join);
+  for (int i = 0; i < 2; ++i)
+    for (int k = 0; k < 4; ++k)
+      if (st->gorder[i][k]) (void)hipEventDestroy(st->gorder[i][k]);
+  if (st->side) (void)hipStreamDestroy(st->side);
   delete st;
   return ok();
 }

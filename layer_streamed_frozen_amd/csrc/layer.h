@@ -29,6 +29,12 @@ struct LayerWs {
   // The LoRA activations (Uqkv, Uo, Ugu, Ud) already hold this layer's values
   // for this input (kept from its forward): the forward does not recompute them.
   bool u_ready = false;
+  // Order of the adapter-gradient accumulations when several workspaces run
+  // on different streams: before its k-th gradient launch (k = 0..3: down,
+  // gate|up, o, q|k|v) the backward makes its stream wait for grad_after[k],
+  // and afterwards records grad_done[k] (each only when set).
+  hipEvent_t grad_after[4] = {nullptr, nullptr, nullptr, nullptr};
+  hipEvent_t grad_done[4] = {nullptr, nullptr, nullptr, nullptr};
   static size_t bytes(const lsf_layer_cfg& c);
   static LayerWs carve(const lsf_layer_cfg& c, void* base);
   // The tensors a forward with save = true leaves for the backward (h1, qkv,
