@@ -3,7 +3,7 @@
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--repeat 3]
                     [--workload stack1|stack4|dpo|dpo-unfused|layer|linear]
                     [--format nf4|nf4dq|bf16] [--optimizer adamw|adamw8] [--lora-targets all|qv]
-                    [--accum-order layer|micro] [--keep-activations] [--no-cpu-baseline]
+                    [--accum-order layer|micro] [--keep-activations] [--no-cpu-baseline] [--no-extra]
 
 Workload (default "stack1"): 32 Llama-3.1-8B-shaped decoder layers (hidden
 4096, intermediate 14336, 32 query / 8 kv heads of 128, RoPE theta 500000),
@@ -35,7 +35,9 @@ every kernel class and every copy (``kernels``, ``layer_gemms`` and the
 copy-engine figures in ``h2d``), since events on every kernel and copy slow
 the step by a few percent.  The timed region runs ``--repeat`` times (each
 ``--steps`` steps); ``value`` is the mean, and ``repeat`` lists every run with
-the standard deviation.
+the standard deviation.  With every option at its default, the same run then
+times a few steps of "stack4" and "dpo" on the same store (``other_workloads``;
+``--no-extra`` skips them).
 """
 import argparse
 import json
@@ -103,6 +105,9 @@ def parse():
     p.add_argument("--accum-order", choices=["layer", "micro"], default="layer",
                    help="gradient accumulation: every layer serves all micro-batches in one walk (layer) or "
                         "the stack is walked once per micro-batch (micro)")
+    p.add_argument("--no-extra", action="store_true",
+                   help="stack1 with the defaults also times the stack4 and fused-DPO steps on the same store "
+                        "(a few steps each, in the same run); this skips them")
     p.add_argument("--diag-steps", type=int, default=5,
                    help="steps of the diagnostic pass that times every kernel class and copy (0: none)")
     return p.parse_args()
@@ -529,10 +534,71 @@ def main():
         "peak_device_GB": round(peak_gb, 3),
         "loss": loss,
     }
+    default_cfg = (args.workload == "stack1" and args.format == "nf4" and args.lora_targets == "all"
+                   and args.optimizer == "adamw" and not args.keep_activations and L == 32)
+    if default_cfg and not args.no_extra:
+        out["other_workloads"] = other_workloads(torch, B, S, synth, shape, store, lora, arr, opt, emb, fnorm,
+                                                 head, V, seq)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(shape, args.workload)
     print(json.dumps(out), flush=True)
+
+
+def other_workloads(torch, B, S, synth, shape, store, lora, arr, opt, emb, fnorm, head, V, seq, warmup=1, steps=3,
+                    repeat=2):
+    """The compute-bound steps on the store the headline was measured on, a
+    few steps each (the same step code as --workload stack4 and --workload
+    dpo, without per-kernel events): 4 micro-batches of 4 x 512 tokens served
+    by one walk over the stack per direction, and DPO over 2 chosen/rejected
+    pairs x 512 with the reference pass fused into the policy's layer visit.
+    Each step ends with one AdamW update."""
+    res = {}
+    for kind in ("stack4", "dpo"):
+        batch, accum = (4, 4) if kind == "stack4" else (4, 1)
+        if kind == "dpo":
+            ids = [torch.from_numpy(synth.preference_pairs("pairs", batch // 2, seq, V, seq // 2)).cuda()]
+        else:
+            ids = [torch.from_numpy(synth.token_ids(f"ids{m}", (batch, seq), V)).cuda() for m in range(accum)]
+        stk = S.Stack(shape, store, batch, seq, V, flags=0, n_micro=accum if kind == "stack4" else 1)
+
+        def one():
+            if kind == "dpo":
+                stk.dpo_step(ids[0], emb, fnorm, head, arr, beta=0.1, fused=True,
+                             mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+            else:
+                stk.accum_step(ids, emb, fnorm, head, arr, mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+            opt.step()
+
+        log(f"other workload {kind}: {warmup} warm-up + {repeat} x {steps} steps")
+        for _ in range(warmup):
+            one()
+        torch.cuda.synchronize()
+        B.stack_reset_stats(stk.handle)
+        runs = []
+        for _ in range(repeat):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                one()
+            torch.cuda.synchronize()
+            runs.append(time.perf_counter() - t0)
+        st = stk.stats()
+        stk.close()
+        tokens = steps * accum * batch * seq
+        rates = [tokens / e for e in runs]
+        v, sd = mean_sd(rates)
+        n = steps * len(runs)
+        res[kind] = {"tokens_per_s": round(v, 2), "sd": round(sd, 2), "runs": len(runs), "steps": steps,
+                     "warmup": warmup, "ms_per_step": round(sum(runs) / n * 1e3, 3),
+                     "copies_per_step": st.copies / n,
+                     "GBps_over_step": round(st.bytes / n / (sum(runs) / n) / 1e9, 2),
+                     "workload": ("batch 4 x seq 512, accumulation 4, one walk over the stack per direction "
+                                  "for all micro-batches" if kind == "stack4" else
+                                  "DPO beta 0.1, 2 chosen/rejected pairs x seq 512, reference = adapters off, "
+                                  "fused into the policy's layer visit")}
+        log(f"other workload {kind}: {v:.1f} +- {sd:.1f} tok/s")
+    return res
 
 
 def _events(torch, fn, n):
