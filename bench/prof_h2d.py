@@ -3,13 +3,19 @@ copied on its own: from a pinned store of --layers such blobs into one of two
 device buffers, one hipMemcpyAsync per copy, with and without a bf16 GEMM load
 on another stream, and the same copy cut in two on two streams.
 
-    python3 bench/prof_h2d.py [--layers 32] [--reps 64] [--sustain SECONDS [--idle]]
+    python3 bench/prof_h2d.py [--layers 32] [--reps 64] [--sustain SECONDS [--idle]] [--probe-gaps]
 
 Prints, per variant, the median, minimum and maximum copy time (event-timed).
 With --sustain, instead copies back to back for about that long while bf16
 GEMMs keep another stream busy, without synchronising in between (as in the
 streamed step), and prints the median copy time of each tenth of the run;
---idle leaves the GPU without other work.
+--idle leaves the GPU without other work.  With --probe-gaps, instead times
+runs of 24 back-to-back copies on one stream (the average per copy, so any idle
+time between copies counts): plain; each followed by an event record; each
+preceded by a wait on an event of another stream that completed long before;
+each preceded by a wait on an event recorded on another stream just before;
+then 64 copies cycling over 8 and over all --layers blobs of the store, in
+order and in a stride-7 order.
 """
 import argparse
 import statistics
@@ -25,6 +31,7 @@ def main():
     ap.add_argument("--reps", type=int, default=64)
     ap.add_argument("--sustain", type=float, default=0.0)
     ap.add_argument("--idle", action="store_true")
+    ap.add_argument("--probe-gaps", action="store_true")
     args = ap.parse_args()
     nl = args.layers
     src = torch.empty(nl * BLOB, dtype=torch.uint8, pin_memory=True)
@@ -70,6 +77,10 @@ def main():
             ts.append(e0.elapsed_time(e1) * 1e3)
         return ts
 
+    if args.probe_gaps:
+        probe_gaps(torch, src, dst, s1, s2, nl)
+        return
+
     if args.sustain > 0:
         n = max(20, int(args.sustain * 1e6 / 2200))
         evs = []
@@ -104,6 +115,56 @@ def main():
             med = statistics.median(ts)
             print(f"[prof_h2d] GEMM load on another stream: {busy}, streams: {pieces}: median {med:.0f} us "
                   f"({BLOB / med / 1e3:.2f} GB/s), min {min(ts):.0f}, max {max(ts):.0f}", flush=True)
+
+
+def probe_gaps(torch, src, dst, s1, s2, nl):
+    def timed(n, body):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s1)
+        for r in range(n):
+            body(r)
+        e1.record(s1)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    def copy(r, j):
+        with torch.cuda.stream(s1):
+            dst[r % 2].copy_(src[j * BLOB:(j + 1) * BLOB], non_blocking=True)
+
+    done = torch.cuda.Event()
+    done.record(s2)
+    torch.cuda.synchronize()
+
+    def plain(r):
+        copy(r, r % 8)
+
+    def record(r):
+        copy(r, r % 8)
+        torch.cuda.Event().record(s1)
+
+    def wait_done(r):
+        s1.wait_event(done)
+        copy(r, r % 8)
+        torch.cuda.Event().record(s1)
+
+    def wait_fresh(r):
+        ev = torch.cuda.Event()
+        ev.record(s2)
+        s1.wait_event(ev)
+        copy(r, r % 8)
+        torch.cuda.Event().record(s1)
+
+    for rep in range(2):
+        for name, body in (("plain", plain), ("event record after", record),
+                           ("wait on a completed event", wait_done), ("wait on a fresh event", wait_fresh)):
+            print(f"[prof_h2d] gaps, pass {rep}: 24 copies, {name}: {timed(24, body):.1f} us per copy", flush=True)
+    for n_blobs in sorted({8, nl}):
+        for order in ("in order", "stride 7"):
+            step = 1 if order == "in order" else 7
+            us = timed(64, lambda r: copy(r, (r * step) % n_blobs))
+            print(f"[prof_h2d] working set {n_blobs} blobs ({n_blobs * BLOB / 1e9:.2f} GB), 64 copies {order}: "
+                  f"{us:.1f} us per copy", flush=True)
 
 
 if __name__ == "__main__":
