@@ -1,7 +1,7 @@
 """Throughput of the streamed NF4 + LoRA training step on one MI355X.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--repeat 3]
-                    [--workload stack1|stack4|dpo|dpo-unfused|layer|linear]
+                    [--workload stack1|stack4|stack16|dpo|dpo-unfused|layer|linear]
                     [--format nf4|nf4dq|bf16] [--optimizer adamw|adamw8] [--lora-targets all|qv]
                     [--accum-order layer|micro] [--keep-activations] [--no-cpu-baseline] [--no-extra]
 
@@ -15,7 +15,8 @@ cross-entropy loss; forward, head, recomputing backward (all LoRA gradients)
 and one AdamW update of every adapter per step.  "stack4" is 4 sequences of 512 per micro-batch and 4 micro-batches
 (gradient accumulation) per step, by default in one walk over the stack per direction
 (each layer copied once for all four micro-batches; ``--accum-order micro`` streams
-the stack once per micro-batch instead; both give the same bits).  "dpo" is the preference-loss step: 2
+the stack once per micro-batch instead; both give the same bits).  "stack16" is the
+same 16 sequences of 512 as one batch of 8192 tokens (no accumulation).  "dpo" is the preference-loss step: 2
 chosen/rejected pairs of 512 tokens (4 sequences, pair p sharing a 256-token
 prompt), DPO with beta 0.1, the reference log-probabilities from the same
 streamed base with the adapters off, computed in the policy's layer visit
@@ -79,7 +80,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--repeat", type=int, default=3, help="timed runs of --steps steps each (mean and sd)")
-    p.add_argument("--workload", choices=["stack1", "stack4", "dpo", "dpo-unfused", "layer", "linear"],
+    p.add_argument("--workload", choices=["stack1", "stack4", "stack16", "dpo", "dpo-unfused", "layer", "linear"],
                    default="stack1")
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--tokens", type=int, default=512,
@@ -328,7 +329,8 @@ def main():
         print(json.dumps(out), flush=True)
         return
     L, V, seq = args.layers, 128256, 512
-    batch, accum = {"stack1": (1, 1), "stack4": (4, 4), "dpo": (4, 1), "dpo-unfused": (4, 1)}[args.workload]
+    batch, accum = {"stack1": (1, 1), "stack4": (4, 4), "stack16": (16, 1), "dpo": (4, 1),
+                    "dpo-unfused": (4, 1)}[args.workload]
     dpo = args.workload.startswith("dpo")
     T = batch * seq
 
