@@ -58,7 +58,7 @@ PCIE5_X16_GBPS = 63.0            # theoretical per direction after 128b/130b enc
 # (the calibration kernel's ratio) + WRITE_SIZE 28737.24 KiB scaled by 1.0.  Valid only
 # for the sources of that kernel they were taken on (hash below); otherwise null.
 GATE_UP_TRAFFIC_BYTES = (50043.05 * 1.99975 + 28737.24 * 1.0) * 1024
-GATE_UP_TRAFFIC_SRC = "c899027d5702b579"
+GATE_UP_TRAFFIC_SRC = "895059a4b4dea2d0"
 # Algorithmic bytes of one such launch: NF4 codes 58.72 MB + absmax 7.34 MB + x 4.19 MB +
 # LoRA (U, B) 1.9 MB read; a 14.7 MB (forward) or a, g, u 44.0 MB (recompute) written.
 GATE_UP_ALGO_BYTES = (58.72 + 7.34 + 4.19 + 1.9 + (14.68 + 44.04) / 2) * 1e6

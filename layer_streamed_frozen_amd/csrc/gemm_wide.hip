@@ -112,7 +112,7 @@ template <int NW>
 __device__ __forceinline__ void wbar_stores() {
   static_assert(NW >= 0 && NW < 16, "lgkmcnt immediate");
   asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xc07f & ~0x0f00 | (NW << 8));
+  __builtin_amdgcn_s_waitcnt((0xc07f & ~0x0f00) | (NW << 8));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
