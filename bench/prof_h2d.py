@@ -4,6 +4,7 @@ device buffers, one hipMemcpyAsync per copy, with and without a bf16 GEMM load
 on another stream, and the same copy cut in two on two streams.
 
     python3 bench/prof_h2d.py [--layers 32] [--reps 64] [--sustain SECONDS [--idle]] [--probe-gaps]
+                              [--step-pattern]
 
 Prints, per variant, the median, minimum and maximum copy time (event-timed).
 With --sustain, instead copies back to back for about that long while bf16
@@ -15,7 +16,14 @@ time between copies counts): plain; each followed by an event record; each
 preceded by a wait on an event of another stream that completed long before;
 each preceded by a wait on an event recorded on another stream just before;
 then 64 copies cycling over 8 and over all --layers blobs of the store, in
-order and in a stride-7 order.
+order and in a stride-7 order.  With --step-pattern, replays the streamed
+512-token step's schedule outside the library's stack: a forward walk over the
+32 layers (this library's layer_fwd of one 8B-shaped NF4 layer), the two
+lm_head GEMMs of the head, a backward walk (layer_bwd, recomputing), and an
+optimizer-sized HBM pass, the layer copies on their own stream ordered by
+events exactly as the streamer does (two device buffers, the last two layers
+of a walk reused by the next), and prints every copy's duration for three
+steps and the per-step time over ten.
 """
 import argparse
 import statistics
@@ -32,8 +40,12 @@ def main():
     ap.add_argument("--sustain", type=float, default=0.0)
     ap.add_argument("--idle", action="store_true")
     ap.add_argument("--probe-gaps", action="store_true")
+    ap.add_argument("--step-pattern", action="store_true")
     args = ap.parse_args()
     nl = args.layers
+    if args.step_pattern:
+        step_pattern(torch, nl)
+        return
     src = torch.empty(nl * BLOB, dtype=torch.uint8, pin_memory=True)
     src.fill_(1)
     dst = [torch.empty(BLOB, dtype=torch.uint8, device="cuda") for _ in range(2)]
@@ -115,6 +127,103 @@ def main():
             med = statistics.median(ts)
             print(f"[prof_h2d] GEMM load on another stream: {busy}, streams: {pieces}: median {med:.0f} us "
                   f"({BLOB / med / 1e3:.2f} GB/s), min {min(ts):.0f}, max {max(ts):.0f}", flush=True)
+
+
+def step_pattern(torch, L):
+    import os
+    import sys
+    import numpy as np
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    from layer_streamed_frozen_amd import binding as B
+    from layer_streamed_frozen_amd import store as S
+    from layer_streamed_frozen_amd import synth
+    B.lib()
+    shape = S.LLAMA8B
+    W = S.layer_weights_fp32("h2d.layer", shape)
+    blob = S.build_layer_blob(shape, W)
+    cfg = shape.cfg(1, 512)
+    H, V = shape.hidden, 128256
+    lora = S.LoraSet(shape, 1, prefix="h2d.lora")
+
+    def bf16_in(name):
+        return torch.from_numpy(synth.bf16_exact(synth.normal(name, (512, H)))[1].view(np.int16)) \
+            .view(torch.bfloat16).cuda()
+
+    x, dy = bf16_in("h2d.x"), bf16_in("h2d.dy")
+    ws = torch.empty(B.layer_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    ls = lora.struct(0)
+    src = torch.empty(L * BLOB, dtype=torch.uint8, pin_memory=True)
+    hb = blob.cpu()
+    for j in range(L):  # every layer the same bytes: only the copies' timing matters here
+        src[j * BLOB:(j + 1) * BLOB].copy_(hb[:BLOB])
+    dst = [torch.empty(BLOB, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    lws = [B.layer_weights_from_blob(cfg, B.FMT_NF4, d.data_ptr()) for d in dst]
+    head = torch.randn(V, H, device="cuda", dtype=torch.bfloat16) * 0.02
+    opt_buf = torch.empty(1170 * 1000 * 1000 // 4, dtype=torch.float32, device="cuda")
+    cs, cp = torch.cuda.current_stream(), torch.cuda.Stream()
+    slot, ready, freed, cev = [None, None], [None, None], [None, None], []
+
+    def acquire(j, b):
+        if slot[b] == j:
+            return
+        if freed[b] is not None:
+            cp.wait_event(freed[b])
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(cp)
+        with torch.cuda.stream(cp):
+            dst[b].copy_(src[j * BLOB:(j + 1) * BLOB], non_blocking=True)
+        e1.record(cp)
+        cev.append((e0, e1))
+        ready[b] = torch.cuda.Event()
+        ready[b].record(cp)
+        slot[b] = j
+
+    def walk(forward):
+        order = list(range(L)) if forward else list(range(L - 1, -1, -1))
+        acquire(order[0], order[0] & 1)
+        acquire(order[1], order[1] & 1)
+        for n, j in enumerate(order):
+            b = j & 1
+            cs.wait_event(ready[b])
+            if forward:
+                B.layer_fwd(cfg, lws[b], ls, x, y, ws, stream=cs)
+            else:
+                B.layer_bwd(cfg, lws[b], ls, x, dy, dx, ws, stream=cs)
+            freed[b] = torch.cuda.Event()
+            freed[b].record(cs)
+            if n + 2 < L:
+                acquire(order[n + 2], b)
+
+    def step():
+        walk(True)
+        logits = x @ head.t()
+        _ = logits @ head
+        walk(False)
+        opt_buf.mul_(0.999)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    cev.clear()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    n_steps = 10
+    t0.record(cs)
+    for _ in range(n_steps):
+        step()
+    t1.record(cs)
+    torch.cuda.synchronize()
+    d = [a.elapsed_time(b) * 1e3 for a, b in cev]
+    per = len(d) // n_steps
+    for k in range(3):
+        print(f"[prof_h2d] step pattern, copy durations of step {k} (ms): "
+              + " ".join(f"{v / 1000:.2f}" for v in d[k * per:(k + 1) * per]), flush=True)
+    total = t0.elapsed_time(t1)
+    print(f"[prof_h2d] step pattern: {total / n_steps:.2f} ms per step, {per} copies per step, copy median "
+          f"{statistics.median(d):.0f} us, mean {statistics.mean(d):.0f} us, copy engine busy "
+          f"{sum(d) / 1e3 / total:.3f} of the time", flush=True)
 
 
 def probe_gaps(torch, src, dst, s1, s2, nl):
