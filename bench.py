@@ -4,6 +4,7 @@
                     [--workload stack1|stack4|stack16|dpo|dpo-unfused|layer|linear]
                     [--format nf4|nf4dq|bf16] [--optimizer adamw|adamw8] [--lora-targets all|qv]
                     [--accum-order layer|micro] [--keep-activations] [--no-cpu-baseline] [--no-extra]
+                    [--one-copy-stream]
 
 Workload (default "stack1"): 32 Llama-3.1-8B-shaped decoder layers (hidden
 4096, intermediate 14336, 32 query / 8 kv heads of 128, RoPE theta 500000),
@@ -106,6 +107,8 @@ def parse():
     p.add_argument("--accum-order", choices=["layer", "micro"], default="layer",
                    help="gradient accumulation: every layer serves all micro-batches in one walk (layer) or "
                         "the stack is walked once per micro-batch (micro)")
+    p.add_argument("--one-copy-stream", action="store_true",
+                   help="copy each layer as one transfer on one copy stream (default: two halves on two)")
     p.add_argument("--no-extra", action="store_true",
                    help="stack1 with the defaults also times the stack4 and fused-DPO steps on the same store "
                         "(a few steps each, in the same run); this skips them")
@@ -372,6 +375,8 @@ def main():
         flags = B.STACK_TIMING
     else:
         flags = B.STACK_TIME_KERNEL(dom_k)
+    copy_flags = B.STACK_ONE_COPY_STREAM if args.one_copy_stream else 0
+    flags |= copy_flags
     layer_major = accum > 1 and args.accum_order == "layer"
     stack = S.Stack(shape, store, batch, seq, V, flags=flags, keep_activations=args.keep_activations,
                     n_micro=accum if layer_major else 1)
@@ -420,7 +425,8 @@ def main():
     log(f"{value:.1f} +- {value_sd:.1f} tok/s over {len(runs)} runs, {ms_step:.2f} ms/step, loss {loss:.4f}")
 
     bytes_step = st.bytes / n_timed
-    h2d = {"bytes_per_step": int(bytes_step), "copies_per_step": st.copies / n_timed,
+    h2d = {"copy_streams": 1 if args.one_copy_stream else 2,
+           "bytes_per_step": int(bytes_step), "copies_per_step": st.copies / n_timed,
            "GBps_over_step": round(bytes_step / (ms_step * 1e-3) / 1e9, 2),
            "measured_link_peak_GBps": round(link_peak, 2), "pcie5_x16_theoretical_GBps": PCIE5_X16_GBPS}
     flops = gemm_flops(T, shape)
@@ -450,7 +456,8 @@ def main():
         stack.close()
         del stack
         log(f"diagnostic pass: {diag_steps} steps with every kernel and copy timed")
-        diag = S.Stack(shape, store, batch, seq, V, flags=B.STACK_TIMING, keep_activations=args.keep_activations,
+        diag = S.Stack(shape, store, batch, seq, V, flags=B.STACK_TIMING | copy_flags,
+                       keep_activations=args.keep_activations,
                        n_micro=accum if layer_major else 1)
         step(diag)
         torch.cuda.synchronize()
@@ -537,7 +544,8 @@ def main():
         "loss": loss,
     }
     default_cfg = (args.workload == "stack1" and args.format == "nf4" and args.lora_targets == "all"
-                   and args.optimizer == "adamw" and not args.keep_activations and L == 32)
+                   and args.optimizer == "adamw" and not args.keep_activations and L == 32
+                   and not args.one_copy_stream)
     if default_cfg and not args.no_extra:
         out["other_workloads"] = other_workloads(torch, B, S, synth, shape, store, lora, arr, opt, emb, fnorm,
                                                  head, V, seq)

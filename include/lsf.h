@@ -259,7 +259,8 @@ LSF_API lsf_status layer_weights_from_blob(const lsf_layer_cfg* cfg, int32_t for
 /* --------------------------------------------------- the streamed stack --
  * [REVIEW], [BLOG], [TUTORIAL] item 2: two fixed device buffers; while layer i
  * computes from one, a dedicated copy stream loads layer i+1 into the other
- * from page-locked host memory with an asynchronous host-to-device copy.
+ * from page-locked host memory with asynchronous host-to-device copies (two
+ * halves on two copy streams, see LSF_STACK_ONE_COPY_STREAM).
  * Order of one micro-batch: forward layers 0..L-1, head and loss, backward
  * layers L-1..0 (each re-read and recomputed; [TUTORIAL] item 3).  The two
  * layers still resident at the turn are reused, and so are layers 0 and 1,
@@ -289,6 +290,12 @@ typedef struct lsf_stack lsf_stack;
  *   that did not wait for the copy would read the previous contents. */
 #define LSF_STACK_DEBUG_POISON 0x20u
 #define LSF_STACK_DEBUG_COPY_DELAY 0x40u
+/* Copy each layer from a page-locked store as one transfer on the copy stream.
+ * By default it goes out as two halves, the second on a copy stream the stack
+ * owns (forked after the buffer's release, joined before the layer is marked
+ * ready), so that two copy engines share it; the bytes are the same either
+ * way. */
+#define LSF_STACK_ONE_COPY_STREAM 0x80u
 /* Record only kernel class k (an LSF_K_* value; several may be or-ed), for a
  * measurement that must disturb the step as little as possible. */
 #define LSF_STACK_TIME_KERNEL(k) (0x100u << (k))

@@ -25,7 +25,7 @@ STATUS_NAMES = ["LSF_OK", "LSF_ERR_INVALID_ARG", "LSF_ERR_SHAPE", "LSF_ERR_ALIGN
 FMT_NF4, FMT_BF16, FMT_NF4_DQ = 0, 1, 2
 
 STACK_ALLOW_PAGEABLE, STACK_NO_TURN_REUSE, STACK_TIMING, STACK_KERNEL_TIMING, STACK_SOURCE_DISK = 0x1, 0x2, 0x4, 0x8, 0x10
-STACK_DEBUG_POISON, STACK_DEBUG_COPY_DELAY = 0x20, 0x40
+STACK_DEBUG_POISON, STACK_DEBUG_COPY_DELAY, STACK_ONE_COPY_STREAM = 0x20, 0x40, 0x80
 
 
 def STACK_TIME_KERNEL(k):

@@ -537,6 +537,12 @@ struct lsf_stack {
   // gradient accumulation of micro-batch m before that of m + 1).
   hipStream_t side = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
+  // A second copy stream: each layer copy from a page-locked store goes out as
+  // two halves, the second on this stream, forked from and joined back to the
+  // caller's copy stream by events (unless LSF_STACK_ONE_COPY_STREAM).
+  hipStream_t copy2 = nullptr;
+  hipEvent_t cfork = nullptr, cjoin = nullptr;
+  bool split_copies = false;
   hipEvent_t gorder[2][4] = {};
   // timing (LSF_STACK_TIMING), accumulated until stack_reset_stats
   EventPool events;
@@ -581,7 +587,26 @@ lsf_status acquire(lsf_stack* st, int j, int b, bool allow_reuse) {
     HIPCK(hipEventRecord(e0, cs));
   }
   const char* src = static_cast<const char*>(st->d.host_store) + (uint64_t)j * st->d.blob_stride;
-  HIPCK(hipMemcpyAsync(st->d.dev_buf[b], src, st->blob.bytes, hipMemcpyHostToDevice, cs));
+  if (st->split_copies) {
+    // Two halves on two copy streams, so two copy engines share the layer:
+    // measured on MI355X, a single engine's layer copies settle for runs of
+    // dozens of copies at one of a few slower rates (2.42, 3.06, 3.38 ms
+    // instead of 2.17 per 8B-shaped layer) that two engines do not show
+    // (streamed 512-token step 148.6 -> 138.1 ms, replayed outside the stack).
+    // The second stream starts after everything before it on this one (the
+    // buffer's release, the stress modes), and this one waits for it before
+    // the buffer is marked ready.
+    const uint64_t half = st->blob.bytes / 2 / 4096 * 4096;
+    char* dst = static_cast<char*>(st->d.dev_buf[b]);
+    HIPCK(hipEventRecord(st->cfork, cs));
+    HIPCK(hipStreamWaitEvent(st->copy2, st->cfork, 0));
+    HIPCK(hipMemcpyAsync(dst, src, half, hipMemcpyHostToDevice, cs));
+    HIPCK(hipMemcpyAsync(dst + half, src + half, st->blob.bytes - half, hipMemcpyHostToDevice, st->copy2));
+    HIPCK(hipEventRecord(st->cjoin, st->copy2));
+    HIPCK(hipStreamWaitEvent(cs, st->cjoin, 0));
+  } else {
+    HIPCK(hipMemcpyAsync(st->d.dev_buf[b], src, st->blob.bytes, hipMemcpyHostToDevice, cs));
+  }
   if (timing) {
     HIPCK(hipEventRecord(e1, cs));
     st->copy_ev.emplace_back(e0, e1);
@@ -1012,7 +1037,7 @@ lsf_status stack_create(const lsf_layer_cfg* cfg, const lsf_stack_desc* desc, ls
   {
     const uint32_t known = LSF_STACK_ALLOW_PAGEABLE | LSF_STACK_NO_TURN_REUSE | LSF_STACK_TIMING |
                            LSF_STACK_KERNEL_TIMING | LSF_STACK_SOURCE_DISK | LSF_STACK_DEBUG_POISON |
-                           LSF_STACK_DEBUG_COPY_DELAY |
+                           LSF_STACK_DEBUG_COPY_DELAY | LSF_STACK_ONE_COPY_STREAM |
                            LSF_STACK_TIME_KERNEL(0) * ((1u << LSF_K_COUNT) - 1u);
     if (desc->flags & ~known) return fail(LSF_ERR_INVALID_ARG, "unknown stack flags 0x%x", desc->flags & ~known);
     if (desc->flags & LSF_STACK_SOURCE_DISK)
@@ -1030,12 +1055,13 @@ lsf_status stack_create(const lsf_layer_cfg* cfg, const lsf_stack_desc* desc, ls
     return fail(LSF_ERR_ALIGN, "device buffers must be 256-byte aligned");
   if (desc->resident_store != nullptr && !aligned(desc->resident_store, 256))
     return fail(LSF_ERR_ALIGN, "resident store must be 256-byte aligned");
+  bool pinned = false;
   if (desc->host_store == nullptr) {
     if (desc->resident_store == nullptr) return fail(LSF_ERR_INVALID_ARG, "no host store and no resident store");
   } else {
     hipPointerAttribute_t attr;
     const hipError_t e = hipPointerGetAttributes(&attr, desc->host_store);
-    bool pinned = (e == hipSuccess) && (attr.type == hipMemoryTypeHost);
+    pinned = (e == hipSuccess) && (attr.type == hipMemoryTypeHost);
     if (e != hipSuccess) (void)hipGetLastError();  // clear the sticky error of a pageable query
     if (!pinned && !(desc->flags & LSF_STACK_ALLOW_PAGEABLE))
       return fail(LSF_ERR_NOT_PINNED, "host store is not page-locked (pass LSF_STACK_ALLOW_PAGEABLE to accept it)");
@@ -1058,12 +1084,17 @@ lsf_status stack_create(const lsf_layer_cfg* cfg, const lsf_stack_desc* desc, ls
   bool evs_ok = hipStreamCreateWithFlags(&st->side, hipStreamNonBlocking) == hipSuccess &&
                 hipEventCreateWithFlags(&st->fork, hipEventDisableTiming) == hipSuccess &&
                 hipEventCreateWithFlags(&st->join, hipEventDisableTiming) == hipSuccess;
+  st->split_copies = pinned && !(desc->flags & LSF_STACK_ONE_COPY_STREAM);
+  if (evs_ok && st->split_copies)
+    evs_ok = hipStreamCreateWithFlags(&st->copy2, hipStreamNonBlocking) == hipSuccess &&
+             hipEventCreateWithFlags(&st->cfork, hipEventDisableTiming) == hipSuccess &&
+             hipEventCreateWithFlags(&st->cjoin, hipEventDisableTiming) == hipSuccess;
   for (int i = 0; i < 2 && evs_ok; ++i)
     for (int k = 0; k < 4 && evs_ok; ++k)
       evs_ok = hipEventCreateWithFlags(&st->gorder[i][k], hipEventDisableTiming) == hipSuccess;
   if (!evs_ok) {
     (void)stack_destroy(st);
-    return fail(LSF_ERR_HIP, "creating the second compute stream or its events failed");
+    return fail(LSF_ERR_HIP, "creating the second compute or copy stream or their events failed");
   }
   *out = st;
   return ok();
@@ -1078,12 +1109,16 @@ lsf_status stack_destroy(lsf_stack* st) {
   (void)harvest_all(st, true);  // no event may be destroyed while still pending
   for (hipEvent_t e : st->events.all) (void)hipEventDestroy(e);
   if (st->side) (void)hipStreamSynchronize(st->side);
+  if (st->copy2) (void)hipStreamSynchronize(st->copy2);
   if (st->fork) (void)hipEventDestroy(st->fork);
   if (st->join) (void)hipEventDestroy(st->join);
+  if (st->cfork) (void)hipEventDestroy(st->cfork);
+  if (st->cjoin) (void)hipEventDestroy(st->cjoin);
   for (int i = 0; i < 2; ++i)
     for (int k = 0; k < 4; ++k)
       if (st->gorder[i][k]) (void)hipEventDestroy(st->gorder[i][k]);
   if (st->side) (void)hipStreamDestroy(st->side);
+  if (st->copy2) (void)hipStreamDestroy(st->copy2);
   delete st;
   return ok();
 }

@@ -168,6 +168,25 @@ def test_no_turn_reuse_and_timing_give_same_bits():
     assert same(a, s.snapshot())
 
 
+@pytest.mark.parametrize("flags", [0, B.STACK_ONE_COPY_STREAM, B.STACK_TIMING, B.STACK_ONE_COPY_STREAM | B.STACK_TIMING])
+def test_one_and_two_copy_streams_give_same_bits(flags):
+    # Each layer copy as two halves on two copy streams (the default) or as one
+    # transfer: the same bytes in the buffers, so the streamed step equals the
+    # resident one bit for bit either way, over two steps (turn and step
+    # boundary reuse included); with timing, every copy is counted once.
+    s = Setup(SMALL, 3, 1024, 1, 64, "cs", flags=flags)
+    B.stack_reset_stats(s.stack.handle)
+    s.step(mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+    s.step(mode=B.MODE_STREAMED | B.MODE_ZERO_GRADS)
+    st = s.stack.stats()
+    assert st.copies == (2 * s.L - 2) + (2 * s.L - 4)
+    if flags & B.STACK_TIMING:
+        assert st.copy_ms > 0.0
+    a = s.snapshot()
+    s.step(mode=B.MODE_RESIDENT | B.MODE_ZERO_GRADS)
+    assert same(a, s.snapshot())
+
+
 def test_gradient_accumulation_matches_oracle():
     s = Setup(SMALL, 2, 512, 1, 80, "acc", random_norms=False)
     ids2 = synth.token_ids("acc.ids2", (1, 80), 512)
