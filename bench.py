@@ -129,10 +129,12 @@ def gemm_flops(T, shape):
 
 
 def measure_link_peak(torch, nbytes=1 << 30, reps=5):
-    """Best pinned host -> device copy rate (GB/s) of one large hipMemcpyAsync."""
+    """Best pinned host -> device copy rate (GB/s) of one large hipMemcpyAsync,
+    on the copy stream the stacks use (no extra stream for HIP to place)."""
+    from layer_streamed_frozen_amd.store import copy_stream
     src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
     dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    s = torch.cuda.Stream()
+    s = copy_stream()
     best = 0.0
     with torch.cuda.stream(s):
         for _ in range(reps):

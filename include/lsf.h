@@ -311,6 +311,16 @@ typedef struct {
   lsf_stream copy;          /* dedicated stream for host-to-device layer copies */
   uint32_t flags;           /* LSF_STACK_* */
 } lsf_stack_desc;
+/* HIP runs a process's streams on a few hardware queues (GPU_MAX_HW_QUEUES,
+ * four by default) and lets later streams share them.  Work queued on a
+ * hardware queue runs in order, so a copy stream (the caller's, or the
+ * stack's second one) that shares the compute stream's queue makes the layer
+ * kernels wait for the copies: the step then takes the copies' time plus the
+ * compute's instead of the larger of the two.  A stack uses the compute and
+ * copy streams given here plus up to two of its own (the second copy stream,
+ * and a second compute stream for several micro-batches); keep the process's
+ * streams in use within the queue count, e.g. by giving every stack the same
+ * copy stream. */
 
 LSF_API lsf_status stack_create(const lsf_layer_cfg* cfg, const lsf_stack_desc* desc, lsf_stack** out);
 LSF_API lsf_status stack_destroy(lsf_stack* st);

@@ -252,6 +252,25 @@ class AdamW8:
                       self.cfg, self.grad_norm, self.ws, stream=stream)
 
 
+_COPY_STREAMS = {}
+
+
+def copy_stream(torch_device=None):
+    """One host-to-device copy stream per device for the whole process.
+
+    HIP runs a process's streams on a few hardware queues (four unless
+    GPU_MAX_HW_QUEUES says otherwise) and makes later streams share them.  A
+    copy stream that lands on the compute stream's queue makes every kernel
+    queued behind a copy wait for that copy, and torch never releases a
+    stream it hands out, so a new stream per stack would, after a few stacks,
+    put one there.  Every stack therefore reuses this one."""
+    dev = torch.device("cuda") if torch_device is None else torch.device(torch_device)
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    if idx not in _COPY_STREAMS:
+        _COPY_STREAMS[idx] = torch.cuda.Stream(device=idx)
+    return _COPY_STREAMS[idx]
+
+
 class Stack:
     """A streamed stack: store + two device buffers + streams + handle."""
 
@@ -261,7 +280,7 @@ class Stack:
         nbytes = store.layout.bytes
         self.bufs = [torch.empty(nbytes, dtype=torch.uint8, device=device) for _ in range(2)]
         self.compute = torch.cuda.current_stream()
-        self.copy = torch.cuda.Stream()
+        self.copy = copy_stream(device)
         d = B.StackDesc()
         d.n_layers = store.n_layers
         d.format = store.fmt
