@@ -4,7 +4,7 @@ device buffers, one hipMemcpyAsync per copy, with and without a bf16 GEMM load
 on another stream, and the same copy cut in two on two streams.
 
     python3 bench/prof_h2d.py [--layers 32] [--reps 64] [--sustain SECONDS [--idle]] [--probe-gaps]
-                              [--step-pattern]
+                              [--step-pattern [--pieces N]]
 
 Prints, per variant, the median, minimum and maximum copy time (event-timed).
 With --sustain, instead copies back to back for about that long while bf16
@@ -23,7 +23,9 @@ lm_head GEMMs of the head, a backward walk (layer_bwd, recomputing), and an
 optimizer-sized HBM pass, the layer copies on their own stream ordered by
 events exactly as the streamer does (two device buffers, the last two layers
 of a walk reused by the next), and prints every copy's duration for three
-steps and the per-step time over ten.
+steps and the per-step time over ten; --pieces N sends each layer as N equal
+pieces (4 KiB multiples) on N copy streams that fork from and join back into
+the first, as the library's stack does with two.
 """
 import argparse
 import statistics
@@ -41,10 +43,11 @@ def main():
     ap.add_argument("--idle", action="store_true")
     ap.add_argument("--probe-gaps", action="store_true")
     ap.add_argument("--step-pattern", action="store_true")
+    ap.add_argument("--pieces", type=int, default=1)
     args = ap.parse_args()
     nl = args.layers
     if args.step_pattern:
-        step_pattern(torch, nl)
+        step_pattern(torch, nl, args.pieces)
         return
     src = torch.empty(nl * BLOB, dtype=torch.uint8, pin_memory=True)
     src.fill_(1)
@@ -129,7 +132,7 @@ def main():
                   f"({BLOB / med / 1e3:.2f} GB/s), min {min(ts):.0f}, max {max(ts):.0f}", flush=True)
 
 
-def step_pattern(torch, L):
+def step_pattern(torch, L, pieces=1):
     import os
     import sys
     import numpy as np
@@ -162,6 +165,8 @@ def step_pattern(torch, L):
     head = torch.randn(V, H, device="cuda", dtype=torch.bfloat16) * 0.02
     opt_buf = torch.empty(1170 * 1000 * 1000 // 4, dtype=torch.float32, device="cuda")
     cs, cp = torch.cuda.current_stream(), torch.cuda.Stream()
+    extra = [torch.cuda.Stream() for _ in range(pieces - 1)]
+    cut = [0] + [BLOB // pieces // 4096 * 4096 * k for k in range(1, pieces)] + [BLOB]
     slot, ready, freed, cev = [None, None], [None, None], [None, None], []
 
     def acquire(j, b):
@@ -172,8 +177,15 @@ def step_pattern(torch, L):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(cp)
-        with torch.cuda.stream(cp):
-            dst[b].copy_(src[j * BLOB:(j + 1) * BLOB], non_blocking=True)
+        for s in extra:
+            s.wait_event(e0)
+        for k, s in enumerate([cp] + extra):
+            with torch.cuda.stream(s):
+                dst[b][cut[k]:cut[k + 1]].copy_(src[j * BLOB + cut[k]:j * BLOB + cut[k + 1]], non_blocking=True)
+        for s in extra:
+            done = torch.cuda.Event()
+            done.record(s)
+            cp.wait_event(done)
         e1.record(cp)
         cev.append((e0, e1))
         ready[b] = torch.cuda.Event()
@@ -221,7 +233,8 @@ def step_pattern(torch, L):
         print(f"[prof_h2d] step pattern, copy durations of step {k} (ms): "
               + " ".join(f"{v / 1000:.2f}" for v in d[k * per:(k + 1) * per]), flush=True)
     total = t0.elapsed_time(t1)
-    print(f"[prof_h2d] step pattern: {total / n_steps:.2f} ms per step, {per} copies per step, copy median "
+    print(f"[prof_h2d] step pattern, {pieces} piece(s) per copy: {total / n_steps:.2f} ms per step, {per} copies "
+          f"per step, copy median "
           f"{statistics.median(d):.0f} us, mean {statistics.mean(d):.0f} us, copy engine busy "
           f"{sum(d) / 1e3 / total:.3f} of the time", flush=True)
 
