@@ -292,9 +292,12 @@ typedef struct lsf_stack lsf_stack;
 #define LSF_STACK_DEBUG_COPY_DELAY 0x40u
 /* Copy each layer from a page-locked store as one transfer on the copy stream.
  * By default it goes out as two halves, the second on a copy stream the stack
- * owns (forked after the buffer's release, joined before the layer is marked
- * ready), so that two copy engines share it; the bytes are the same either
- * way. */
+ * owns, so that two copy engines share it; the bytes are the same either way.
+ * Each copy stream waits for the buffer's release and the compute stream for
+ * both halves; with LSF_STACK_TIMING or a stress mode the second stream is
+ * instead forked from the first after the release (and the stress work) and
+ * joined back before the layer is marked ready, so that one pair of events
+ * times the whole layer copy. */
 #define LSF_STACK_ONE_COPY_STREAM 0x80u
 /* Record only kernel class k (an LSF_K_* value; several may be or-ed), for a
  * measurement that must disturb the step as little as possible. */

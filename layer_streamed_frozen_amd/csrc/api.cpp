@@ -543,6 +543,12 @@ struct lsf_stack {
   hipStream_t copy2 = nullptr;
   hipEvent_t cfork = nullptr, cjoin = nullptr;
   bool split_copies = false;
+  // Without per-copy timing or a stress mode the two copy streams are not
+  // linked: each waits for the buffer's release itself, and the second half's
+  // arrival in buffer b is ready2[b], which the compute stream waits for too
+  // (two_ready[b]: the last copy into buffer b went out that way).
+  hipEvent_t ready2[2] = {};
+  bool two_ready[2] = {};
   hipEvent_t gorder[2][4] = {};
   // timing (LSF_STACK_TIMING), accumulated until stack_reset_stats
   EventPool events;
@@ -593,17 +599,31 @@ lsf_status acquire(lsf_stack* st, int j, int b, bool allow_reuse) {
     // dozens of copies at one of a few slower rates (2.42, 3.06, 3.38 ms
     // instead of 2.17 per 8B-shaped layer) that two engines do not show
     // (streamed 512-token step 148.6 -> 138.1 ms, replayed outside the stack).
-    // The second stream starts after everything before it on this one (the
-    // buffer's release, the stress modes), and this one waits for it before
-    // the buffer is marked ready.
+    // With per-copy timing or a stress mode the second stream starts after
+    // everything before it on this one (the buffer's release, the stress
+    // modes) and this one waits for it before the buffer is marked ready, so
+    // one pair of timing events brackets the whole layer; otherwise both
+    // streams wait for the release and the compute stream for both halves.
     const uint64_t half = st->blob.bytes / 2 / 4096 * 4096;
     char* dst = static_cast<char*>(st->d.dev_buf[b]);
-    HIPCK(hipEventRecord(st->cfork, cs));
-    HIPCK(hipStreamWaitEvent(st->copy2, st->cfork, 0));
+    const bool linked = timing || (st->d.flags & (LSF_STACK_DEBUG_POISON | LSF_STACK_DEBUG_COPY_DELAY));
+    if (linked) {
+      HIPCK(hipEventRecord(st->cfork, cs));
+      HIPCK(hipStreamWaitEvent(st->copy2, st->cfork, 0));
+    } else if (st->used[b]) {
+      // Each stream waits for the release on its own, so the wait that
+      // separates one stream's copies overlaps the other stream's copy.
+      HIPCK(hipStreamWaitEvent(st->copy2, st->freed[b], 0));
+    }
     HIPCK(hipMemcpyAsync(dst, src, half, hipMemcpyHostToDevice, cs));
     HIPCK(hipMemcpyAsync(dst + half, src + half, st->blob.bytes - half, hipMemcpyHostToDevice, st->copy2));
-    HIPCK(hipEventRecord(st->cjoin, st->copy2));
-    HIPCK(hipStreamWaitEvent(cs, st->cjoin, 0));
+    if (linked) {
+      HIPCK(hipEventRecord(st->cjoin, st->copy2));
+      HIPCK(hipStreamWaitEvent(cs, st->cjoin, 0));
+    } else {
+      HIPCK(hipEventRecord(st->ready2[b], st->copy2));
+    }
+    st->two_ready[b] = !linked;
   } else {
     HIPCK(hipMemcpyAsync(st->d.dev_buf[b], src, st->blob.bytes, hipMemcpyHostToDevice, cs));
   }
@@ -630,6 +650,7 @@ lsf_status wait_ready(lsf_stack* st, int b) {
     HIPCK(hipEventRecord(e0, cs));
   }
   HIPCK(hipStreamWaitEvent(cs, st->ready[b], 0));
+  if (st->two_ready[b]) HIPCK(hipStreamWaitEvent(cs, st->ready2[b], 0));
   if (timing) {
     HIPCK(hipEventRecord(e1, cs));
     st->wait_ev.emplace_back(e0, e1);
@@ -1088,7 +1109,9 @@ lsf_status stack_create(const lsf_layer_cfg* cfg, const lsf_stack_desc* desc, ls
   if (evs_ok && st->split_copies)
     evs_ok = hipStreamCreateWithFlags(&st->copy2, hipStreamNonBlocking) == hipSuccess &&
              hipEventCreateWithFlags(&st->cfork, hipEventDisableTiming) == hipSuccess &&
-             hipEventCreateWithFlags(&st->cjoin, hipEventDisableTiming) == hipSuccess;
+             hipEventCreateWithFlags(&st->cjoin, hipEventDisableTiming) == hipSuccess &&
+             hipEventCreateWithFlags(&st->ready2[0], hipEventDisableTiming) == hipSuccess &&
+             hipEventCreateWithFlags(&st->ready2[1], hipEventDisableTiming) == hipSuccess;
   for (int i = 0; i < 2 && evs_ok; ++i)
     for (int k = 0; k < 4 && evs_ok; ++k)
       evs_ok = hipEventCreateWithFlags(&st->gorder[i][k], hipEventDisableTiming) == hipSuccess;
@@ -1114,6 +1137,8 @@ lsf_status stack_destroy(lsf_stack* st) {
   if (st->join) (void)hipEventDestroy(st->join);
   if (st->cfork) (void)hipEventDestroy(st->cfork);
   if (st->cjoin) (void)hipEventDestroy(st->cjoin);
+  for (int i = 0; i < 2; ++i)
+    if (st->ready2[i]) (void)hipEventDestroy(st->ready2[i]);
   for (int i = 0; i < 2; ++i)
     for (int k = 0; k < 4; ++k)
       if (st->gorder[i][k]) (void)hipEventDestroy(st->gorder[i][k]);
