@@ -481,7 +481,10 @@ def main():
                     "copy_busy_frac_of_step": round(dst.copy_ms / (delapsed * 1e3), 4),
                     "compute_wait_ms_per_step": round(dst.wait_ms / diag_steps, 3),
                     "busy_figures_from": f"diagnostic pass of {diag_steps} steps, "
-                                         f"{diag_steps * accum * T / delapsed:.1f} tokens/s with all events on"})
+                                         f"{diag_steps * accum * T / delapsed:.1f} tokens/s with all events on"
+                                         + ("" if args.one_copy_stream else
+                                            "; per-copy timing forks and joins the two copy streams per layer "
+                                            "(one event pair per layer copy), the timed steps do not")})
     kernels = {}
     for k, name in enumerate(B.KERNELS):
         n = dst.kernel_launches[k]
